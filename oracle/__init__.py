@@ -1,0 +1,12 @@
+"""CPU float64 oracle (test infrastructure only; never imported by the GPU library).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg use it.
+Parity of every function here is pinned by tests/test_oracle_pins.py.
+"""
+from .attention import (INCLUDE_SELF, SlotRing, as_f64, bruteforce_joint, default_scale,
+                        joint, masked_attention, mfalcon_mask, pool_write, prefill,
+                        prefill_rows, rank_decode, rank_decode_rows)
+
+__all__ = ["INCLUDE_SELF", "SlotRing", "as_f64", "bruteforce_joint", "default_scale", "joint",
+           "masked_attention", "mfalcon_mask", "pool_write", "prefill", "prefill_rows",
+           "rank_decode", "rank_decode_rows"]
