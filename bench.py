@@ -1,0 +1,223 @@
+"""Throughput of the M-FALCON attention hot path on one MI355X.
+
+One step = one batch of 64 requests through the 12-layer serving shape
+(L=12 layers, S=64 pool slots, H=8 heads, history n=512, D=64, k=1000 candidates per
+request, bf16): acquire a slot per request (round-robin), 12 causal prefills that
+write each layer's history K/V into the slots, then 12 ranking decodes in which every
+candidate attends to its request's cached history plus itself.  Inputs are seeded
+synthetic draws resident in HBM before timing starts.
+
+Prints one JSON line.  `value` = ranked candidates per second through the whole step
+(64 x 1000 candidates per step).  The roofline object describes the dominant kernel
+(the ranking decode), its algorithmic bytes per launch over its average launch time
+(HIP events on the launch stream).  The CPU baseline is the float64 oracle timed on a
+bounded sample of the same work on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ranked candidates/sec + TFLOP/s (frac of MFMA/HBM roofline), 1 MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published (no sparsity)
+KERNEL_SRC = os.path.join(ROOT, "falcon_attention_kv_amd", "csrc", "attn_bf16.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "rank_decode_serving_shape_pmc.txt")
+
+
+def parse_args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="approximate CPU time budget of the oracle baseline sample")
+    return p.parse_args()
+
+
+def algorithmic(w, lens):
+    """Algorithmic FLOPs and bytes of one prefill and one decode launch (one layer).
+
+    Prefill: per (user, head) with N history rows, N(N+1)/2 allowed pairs, 4D FLOPs per
+    pair (QK and PV); bytes read q, k, v and write o and the two pool rows: 6 N D e.
+    Decode: k(N+1) allowed pairs per (user, head), 4D FLOPs each; bytes read the slot's
+    K and V once (2 N D e) and the candidates' q, k, v and write o (4 k D e).
+    """
+    e = 2
+    pf = sum(4 * w.D * N * (N + 1) // 2 for N in lens) * w.H
+    pb = sum(6 * N * w.D * e for N in lens) * w.H
+    df = sum(4 * w.D * w.k * (N + 1) for N in lens) * w.H
+    db = sum((2 * N + 4 * w.k) * w.D * e for N in lens) * w.H
+    return pf, pb, df, db
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, or None
+    when it is missing or was taken on a different kernel source."""
+    try:
+        fields = {}
+        with open(PMC_SUMMARY) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, layers_cpu, lens, budget_s):
+    """The oracle, as it stands, on (layer, user, head) units of the step until the budget
+    is spent; scaled to candidates/s of a whole step."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    rng = np.random.default_rng(0)
+    units, t_total = 0, 0.0
+    while t_total < budget_s and units < w.L * w.B * w.H:
+        l, b, h = int(rng.integers(w.L)), int(rng.integers(w.B)), int(rng.integers(w.H))
+        x = layers_cpu[l]
+        N = lens[b]
+        t0 = time.perf_counter()
+        oracle.prefill(x["q"][b:b + 1, h:h + 1], x["k"][b:b + 1, h:h + 1], x["v"][b:b + 1, h:h + 1], [N])
+        pk = oracle.as_f64(x["k"][b:b + 1, h:h + 1, :N]).reshape(1, 1, 1, N, w.D)
+        pv = oracle.as_f64(x["v"][b:b + 1, h:h + 1, :N]).reshape(1, 1, 1, N, w.D)
+        oracle.rank_decode(x["qc"][b:b + 1, h:h + 1], x["kc"][b:b + 1, h:h + 1],
+                           x["vc"][b:b + 1, h:h + 1], pk, pv, [0], [N], 0)
+        t_total += time.perf_counter() - t0
+        units += 1
+    per_unit = t_total / units
+    step_s = per_unit * w.L * w.B * w.H
+    return {"value": w.B * w.k / step_s, "unit": "candidates/s", "cores": threads, "kind": "oracle",
+            "sample": f"{units} (layer, user, head) units of prefill + rank decode "
+                      f"(float64 numpy, {t_total:.1f} s), scaled x{w.L * w.B * w.H} to one step"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import falcon_attention_kv_amd as fa
+    import workloads as W
+
+    w = W.WORKLOADS[3]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lens = W.history_lengths(w).tolist()
+    lens_d = torch.as_tensor(lens, dtype=torch.int32, device=dev)
+    layers = [W.layer_inputs(w, l, dev) for l in range(w.L)]
+    outs = [torch.empty_like(x["q"]) for x in layers]
+    outc = [torch.empty_like(x["qc"]) for x in layers]
+    pool = fa.Pool.allocate(w.L, w.S, w.H, w.n, w.D, w.dtype, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        slots = torch.tensor(pool.acquire_many(w.B), dtype=torch.int32).pin_memory()
+        slots_d = slots.to(dev, non_blocking=True)
+        for l, x in enumerate(layers):
+            if events is not None:
+                events["pf"][l][0].record(stream)
+            fa.prefill(x["q"], x["k"], x["v"], lens_d, pool, slots_d, l, o=outs[l])
+            if events is not None:
+                events["pf"][l][1].record(stream)
+        for l, x in enumerate(layers):
+            if events is not None:
+                events["dc"][l][0].record(stream)
+            fa.rank_decode(x["qc"], x["kc"], x["vc"], pool, slots_d, lens_d, l, oc=outc[l])
+            if events is not None:
+                events["dc"][l][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    mk = lambda: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(w.L)]
+    all_events = [{"pf": mk(), "dc": mk()} for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(all_events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if fa.device_status(dev) != 0:
+        raise RuntimeError("a kernel flagged an invalid slot or length")
+
+    pf_ms = [s.elapsed_time(e) for ev in all_events for (s, e) in ev["pf"]]
+    dc_ms = [s.elapsed_time(e) for ev in all_events for (s, e) in ev["dc"]]
+    pf_avg = sum(pf_ms) / len(pf_ms)
+    dc_avg = sum(dc_ms) / len(dc_ms)
+
+    pflop, pbytes, dflop, dbytes = algorithmic(w, lens)
+    ms_per_step = wall * 1e3 / args.steps
+    cand_per_step = w.B * w.k
+    value = cand_per_step / (ms_per_step / 1e3)
+    step_tflops = w.L * (pflop + dflop) / (ms_per_step / 1e3) / 1e12
+
+    dc_gbs = dbytes / (dc_avg / 1e3) / 1e9
+    traffic = measured_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "candidates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "12-layer serving shape: L=12 S=64 H=8 n=512 D=64, "
+                               "64 requests x k=1000 candidates, bf16",
+                   "L": w.L, "S": w.S, "B": w.B, "H": w.H, "n": w.n, "D": w.D, "k": w.k},
+        "tflops": round(step_tflops, 2),
+        "roofline": {"bound": "hbm", "achieved": round(dc_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dc_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "rank_decode (one layer, 64 users x 8 heads)",
+                     "algorithmic_bytes_per_launch": dbytes,
+                     "avg_launch_ms": round(dc_avg, 5)},
+        "kernels": {
+            "prefill": {"avg_ms": round(pf_avg, 5), "tflops": round(pflop / (pf_avg / 1e3) / 1e12, 2),
+                        "gbs": round(pbytes / (pf_avg / 1e3) / 1e9, 1),
+                        "hbm_frac": round(pbytes / (pf_avg / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "mfma_frac": round(pflop / (pf_avg / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+            "rank_decode": {"avg_ms": round(dc_avg, 5), "tflops": round(dflop / (dc_avg / 1e3) / 1e12, 2),
+                            "gbs": round(dc_gbs, 1), "hbm_frac": round(dc_gbs / HBM_PEAK_GBS, 4),
+                            "mfma_frac": round(dflop / (dc_avg / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                            "decode_candidates_per_s": round(cand_per_step / (w.L * dc_avg / 1e3), 1)},
+        },
+    }
+    if not args.no_cpu_baseline:
+        layers_cpu = [{k: v.cpu() for k, v in x.items()} for x in layers]
+        out["cpu_baseline"] = cpu_baseline(w, layers_cpu, lens, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,221 @@
+"""Python binding of libunipin.so: M-FALCON masked attention over a slotted KV pool.
+
+Argument marshalling only.  Every step of the computation runs in the library's HIP
+kernels; PyTorch provides device memory and the current stream.  There is no CPU
+fallback: if the library cannot be loaded, importing this package raises.
+
+    pool = Pool.allocate(L, S, H, n_max, D, torch.bfloat16, device="cuda")
+    slots = pool.acquire_many(B)                     # round-robin slot ids
+    o = prefill(q, k, v, lens, pool, slots, layer)   # writes the slot's K/V rows
+    oc = rank_decode(qc, kc, vc, pool, slots, lens, layer)
+
+Functions mirror the C entry points of include/unipin.h (unipin_prefill,
+unipin_rank_decode, unipin_pool_*), with the same argument meaning.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libunipin.so")
+
+FP32, BF16 = 0, 1
+OK, EINVAL, ERANGE, EDTYPE, EALIGN, EDEVICE, EHIP, ENOMEM = 0, -1, -2, -3, -4, -5, -6, -7
+FLAG_BAD_SLOT, FLAG_BAD_LEN = 1, 2
+
+# Every symbol include/unipin.h declares.
+EXPORTS = ("unipin_pool_create", "unipin_pool_destroy", "unipin_pool_acquire",
+           "unipin_pool_generation", "unipin_pool_dims", "unipin_prefill",
+           "unipin_rank_decode", "unipin_device_status", "unipin_strerror", "unipin_version")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m falcon_attention_kv_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64p, u64p = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_uint64)
+    ip = ctypes.POINTER(ctypes.c_int)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.unipin_pool_create.argtypes = [ctypes.POINTER(vp), vp, vp, i32, i32, i32, i32, i32, i32]
+    lib.unipin_pool_destroy.argtypes = [vp]
+    lib.unipin_pool_acquire.argtypes = [vp, i32p, u64p]
+    lib.unipin_pool_generation.argtypes = [vp, ctypes.c_int32, u64p]
+    lib.unipin_pool_dims.argtypes = [vp, ip, ip, ip, ip, ip, ip]
+    lib.unipin_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp]
+    lib.unipin_rank_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp]
+    lib.unipin_device_status.argtypes = [vp, ip]
+    lib.unipin_strerror.argtypes = [i32]
+    lib.unipin_strerror.restype = ctypes.c_char_p
+    lib.unipin_version.argtypes = []
+    for name in EXPORTS:
+        if name not in ("unipin_strerror",):
+            getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+class UnipinError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = lib.unipin_strerror(status).decode()
+        super().__init__(f"{what}: {msg} (status {status})" if what else f"{msg} (status {status})")
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        raise UnipinError(status, what)
+
+
+def _dtype_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return BF16
+    if dtype == torch.float32:
+        return FP32
+    raise UnipinError(EDTYPE, f"unsupported dtype {dtype}")
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class Pool:
+    """KV pool: K and V device tensors [L, S, H, n_max, D] plus the library descriptor."""
+
+    def __init__(self, k_pool: torch.Tensor, v_pool: torch.Tensor):
+        if k_pool.shape != v_pool.shape or k_pool.dim() != 5:
+            raise UnipinError(EINVAL, "k_pool and v_pool must both be [L, S, H, n_max, D]")
+        if k_pool.dtype != v_pool.dtype or not k_pool.is_contiguous() or not v_pool.is_contiguous():
+            raise UnipinError(EINVAL, "pool tensors must be contiguous and of one dtype")
+        self.k, self.v = k_pool, v_pool
+        self.L, self.S, self.H, self.n_max, self.D = k_pool.shape
+        self.dtype = k_pool.dtype
+        h = ctypes.c_void_p()
+        _check(lib.unipin_pool_create(ctypes.byref(h), k_pool.data_ptr(), v_pool.data_ptr(),
+                                      self.L, self.S, self.H, self.n_max, self.D,
+                                      _dtype_code(k_pool.dtype)), "unipin_pool_create")
+        self._h = h
+
+    @classmethod
+    def allocate(cls, L, S, H, n_max, D, dtype=torch.bfloat16, device="cuda") -> "Pool":
+        shape = (L, S, H, n_max, D)
+        return cls(torch.empty(shape, dtype=dtype, device=device),
+                   torch.empty(shape, dtype=dtype, device=device))
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._h is None:
+            raise UnipinError(EINVAL, "pool already closed")
+        return self._h
+
+    def acquire(self):
+        """Next slot, round-robin; returns (slot, generation)."""
+        s, g = ctypes.c_int32(), ctypes.c_uint64()
+        _check(lib.unipin_pool_acquire(self.handle, ctypes.byref(s), ctypes.byref(g)), "unipin_pool_acquire")
+        return s.value, g.value
+
+    def acquire_many(self, count: int) -> List[int]:
+        return [self.acquire()[0] for _ in range(count)]
+
+    def generation(self, slot: int) -> int:
+        g = ctypes.c_uint64()
+        _check(lib.unipin_pool_generation(self.handle, slot, ctypes.byref(g)), "unipin_pool_generation")
+        return g.value
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            lib.unipin_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _i32_on(x, device) -> torch.Tensor:
+    t = torch.as_tensor(x, dtype=torch.int32)
+    if t.device != device:
+        t = t.to(device, non_blocking=True)
+    return t.contiguous()
+
+
+def _check_tensor(t: torch.Tensor, name: str, shape, dtype, device) -> None:
+    if t.dtype != dtype:
+        raise UnipinError(EDTYPE, f"{name} has dtype {t.dtype}, pool holds {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise UnipinError(EINVAL, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise UnipinError(EINVAL, f"{name} must be contiguous")
+    if t.device != device:
+        raise UnipinError(EINVAL, f"{name} is on {t.device}, pool is on {device}")
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lens, pool: Pool, slot,
+            layer: int, o: Optional[torch.Tensor] = None, scale: Optional[float] = None) -> torch.Tensor:
+    """unipin_prefill: causal attention over each history, K/V written to pool slots.
+
+    q, k, v [B, H, n, D]; lens, slot: B ints (device tensor or anything torch.as_tensor takes).
+    Returns o [B, H, n, D] (rows >= lens[b] are left as they were).
+    """
+    dev = pool.k.device
+    B, H, n, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(t, name, (B, pool.H, n, pool.D), pool.dtype, dev)
+    if o is None:
+        o = torch.empty_like(q)
+    _check_tensor(o, "o", q.shape, pool.dtype, dev)
+    lens_t, slot_t = _i32_on(lens, dev), _i32_on(slot, dev)
+    if lens_t.numel() != B or slot_t.numel() != B:
+        raise UnipinError(EINVAL, "lens and slot need one entry per user")
+    _check(lib.unipin_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), lens_t.data_ptr(),
+                              pool.handle, slot_t.data_ptr(), layer, B, n,
+                              0.0 if scale is None else float(scale), o.data_ptr(),
+                              _stream_handle(dev)), "unipin_prefill")
+    return o
+
+
+def rank_decode(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, pool: Pool, slot, lens,
+                layer: int, oc: Optional[torch.Tensor] = None, scale: Optional[float] = None) -> torch.Tensor:
+    """unipin_rank_decode: candidates attend to their slot's cached history plus themselves.
+
+    qc, kc, vc [B, H, k, D]; slot, lens: B ints.  Returns oc [B, H, k, D].
+    """
+    dev = pool.k.device
+    B, H, kk, D = qc.shape
+    for name, t in (("qc", qc), ("kc", kc), ("vc", vc)):
+        _check_tensor(t, name, (B, pool.H, kk, pool.D), pool.dtype, dev)
+    if oc is None:
+        oc = torch.empty_like(qc)
+    _check_tensor(oc, "oc", qc.shape, pool.dtype, dev)
+    lens_t, slot_t = _i32_on(lens, dev), _i32_on(slot, dev)
+    if lens_t.numel() != B or slot_t.numel() != B:
+        raise UnipinError(EINVAL, "lens and slot need one entry per user")
+    _check(lib.unipin_rank_decode(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), pool.handle,
+                                  slot_t.data_ptr(), lens_t.data_ptr(), layer, B, kk,
+                                  0.0 if scale is None else float(scale), oc.data_ptr(),
+                                  _stream_handle(dev)), "unipin_rank_decode")
+    return oc
+
+
+def device_status(device=None) -> int:
+    """Sticky device flags (FLAG_BAD_SLOT | FLAG_BAD_LEN) raised since the last call; clears them.
+
+    Synchronises the current stream.
+    """
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    flags = ctypes.c_int()
+    st = lib.unipin_device_status(_stream_handle(dev), ctypes.byref(flags))
+    if st not in (OK, EDEVICE):
+        raise UnipinError(st, "unipin_device_status")
+    return flags.value
+
+
+def version() -> int:
+    return lib.unipin_version()

@@ -1,0 +1,45 @@
+// Internal interface between the C ABI (unipin.cpp) and the HIP kernels.
+// Not installed; the public interface is include/unipin.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace unipin {
+
+// Arguments of one attention launch.  Both kernels of the library take this struct by
+// value.  "rows" are the query rows of the call: the history rows for the prefill, the
+// candidate rows for the ranking decode.
+struct AttnArgs {
+    const void *q, *k, *v;        // prefill: q, k, v [B,H,n,D]; decode: qc, kc, vc [B,H,k,D]
+    void *o;                      // [B,H,rows,D]
+    const int32_t *lens;          // [B] device
+    const int32_t *slot;          // [B] device
+    void *pool_k, *pool_v;        // K/V pool arrays, already offset to `layer`: [S,H,n_max,D]
+    int B, H, rows;               // rows = n (prefill) or k (decode)
+    int n_max, S;
+    int len_limit;                // largest valid lens[b]: n (prefill) or n_max (decode)
+    int tiles;                    // query tiles per (user, head)
+    int xcd_remap;                // 1: map blocks so all tiles of a (user, head) share an XCD
+    float c;                      // scale * log2(e)
+    unsigned int *status;         // sticky per-device flags
+};
+
+// Flags raised on the device (mirrors UNIPIN_FLAG_* of the public header).
+constexpr unsigned int kFlagBadSlot = 1u;
+constexpr unsigned int kFlagBadLen = 2u;
+
+// Number of query rows one workgroup covers, per element type.
+constexpr int kBf16RowsPerBlock = 256;
+constexpr int kFp32RowsPerBlock = 64;
+
+hipError_t launch_prefill_bf16(const AttnArgs &a, int D, hipStream_t stream);
+hipError_t launch_decode_bf16(const AttnArgs &a, int D, hipStream_t stream);
+hipError_t launch_prefill_fp32(const AttnArgs &a, int D, hipStream_t stream);
+hipError_t launch_decode_fp32(const AttnArgs &a, int D, hipStream_t stream);
+
+// Device address of the sticky status word of the current device (looked up once
+// per device with hipGetSymbolAddress).
+hipError_t device_status_word(unsigned int **out);
+
+}  // namespace unipin

@@ -1,0 +1,193 @@
+"""Host-side tests of the C ABI (no GPU needed: no call here reaches a kernel).
+
+Every argument check of include/unipin.h runs before any HIP call, so these tests use
+fake (aligned, never dereferenced) device addresses.
+"""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import falcon_attention_kv_amd as fa
+import oracle
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "unipin.h"
+lib = fa.lib
+vp = ctypes.c_void_p
+
+FAKE = 0x10000          # aligned fake device address
+FAKE_ODD = 0x10002      # misaligned
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w[\w\s\*]*?\b(unipin_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == len(fa.EXPORTS)
+    assert set(names) == set(fa.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strerror():
+    assert lib.unipin_version() == 10000
+    for code in (fa.OK, fa.EINVAL, fa.ERANGE, fa.EDTYPE, fa.EALIGN, fa.EDEVICE, fa.EHIP, fa.ENOMEM):
+        text = lib.unipin_strerror(code).decode()
+        assert text and text != "unknown status"
+    assert lib.unipin_strerror(-99).decode() == "unknown status"
+
+
+def make_pool(L=2, S=3, H=2, n_max=16, D=64, dtype=fa.BF16):
+    h = vp()
+    rc = lib.unipin_pool_create(ctypes.byref(h), FAKE, FAKE * 2, L, S, H, n_max, D, dtype)
+    assert rc == fa.OK
+    return h
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, FAKE, 1, 1, 1, 8, 64, fa.BF16), fa.EINVAL),        # null k pool
+    ((FAKE, 0, 1, 1, 1, 8, 64, fa.BF16), fa.EINVAL),        # null v pool
+    ((FAKE, FAKE, 0, 1, 1, 8, 64, fa.BF16), fa.EINVAL),     # L = 0
+    ((FAKE, FAKE, 1, 0, 1, 8, 64, fa.BF16), fa.EINVAL),     # S = 0
+    ((FAKE, FAKE, 1, 1, 0, 8, 64, fa.BF16), fa.EINVAL),     # H = 0
+    ((FAKE, FAKE, 1, 1, 1, 0, 64, fa.BF16), fa.EINVAL),     # n_max = 0
+    ((FAKE, FAKE, 1, 1, 1, 8, 48, fa.BF16), fa.EINVAL),     # unsupported D
+    ((FAKE, FAKE, 1, 1, 1, 8, 64, 7), fa.EDTYPE),
+    ((FAKE_ODD, FAKE, 1, 1, 1, 8, 64, fa.BF16), fa.EALIGN),
+])
+def test_pool_create_rejects(args, code):
+    h = vp(123)
+    assert lib.unipin_pool_create(ctypes.byref(h), *args) == code
+    assert h.value is None
+
+
+def test_pool_create_null_out():
+    assert lib.unipin_pool_create(None, FAKE, FAKE, 1, 1, 1, 8, 64, fa.BF16) == fa.EINVAL
+
+
+def test_pool_dims():
+    h = make_pool(L=3, S=5, H=4, n_max=32, D=128, dtype=fa.FP32)
+    out = [ctypes.c_int() for _ in range(6)]
+    assert lib.unipin_pool_dims(h, *[ctypes.byref(x) for x in out]) == fa.OK
+    assert [x.value for x in out] == [3, 5, 4, 32, 128, fa.FP32]
+    assert lib.unipin_pool_dims(None, None, None, None, None, None, None) == fa.EINVAL
+    lib.unipin_pool_destroy(h)
+
+
+def test_acquire_matches_round_robin_oracle():
+    S = 5
+    h = make_pool(S=S)
+    ring = oracle.SlotRing(S)
+    for _ in range(3 * S + 2):
+        s, g = ctypes.c_int32(), ctypes.c_uint64()
+        assert lib.unipin_pool_acquire(h, ctypes.byref(s), ctypes.byref(g)) == fa.OK
+        assert (s.value, g.value) == ring.acquire()
+    for slot in range(S):
+        g = ctypes.c_uint64()
+        assert lib.unipin_pool_generation(h, slot, ctypes.byref(g)) == fa.OK
+        assert g.value == ring.gen[slot]
+    g = ctypes.c_uint64()
+    assert lib.unipin_pool_generation(h, S, ctypes.byref(g)) == fa.ERANGE
+    assert lib.unipin_pool_generation(h, -1, ctypes.byref(g)) == fa.ERANGE
+    s = ctypes.c_int32()
+    assert lib.unipin_pool_acquire(h, ctypes.byref(s), None) == fa.OK   # generation optional
+    assert lib.unipin_pool_acquire(None, ctypes.byref(s), None) == fa.EINVAL
+    assert lib.unipin_pool_acquire(h, None, None) == fa.EINVAL
+    lib.unipin_pool_destroy(h)
+
+
+def test_acquire_is_thread_safe():
+    import threading
+    S, per, threads = 7, 500, 8
+    h = make_pool(S=S)
+    seen = []
+    lock = threading.Lock()
+
+    def work():
+        mine = []
+        for _ in range(per):
+            s = ctypes.c_int32()
+            assert lib.unipin_pool_acquire(h, ctypes.byref(s), None) == fa.OK
+            mine.append(s.value)
+        with lock:
+            seen.extend(mine)
+
+    ts = [threading.Thread(target=work) for _ in range(threads)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    total = per * threads
+    counts = [seen.count(s) for s in range(S)]
+    # round-robin over `total` hand-outs: every slot gets floor or ceil of total / S
+    assert sorted(counts) == sorted([total // S + (1 if i < total % S else 0) for i in range(S)])
+    for s in range(S):
+        g = ctypes.c_uint64()
+        lib.unipin_pool_generation(h, s, ctypes.byref(g))
+        assert g.value == counts[s]
+    lib.unipin_pool_destroy(h)
+
+
+def test_destroy_null_is_ok():
+    assert lib.unipin_pool_destroy(None) == fa.OK
+
+
+def _prefill(h, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, slot=FAKE, layer=0, B=1, n=8, scale=0.0, o=FAKE):
+    return lib.unipin_prefill(q, k, v, lens, h, slot, layer, B, n, scale, o, None)
+
+
+def _decode(h, qc=FAKE, kc=FAKE, vc=FAKE, slot=FAKE, lens=FAKE, layer=0, B=1, k=8, scale=0.0, oc=FAKE):
+    return lib.unipin_rank_decode(qc, kc, vc, h, slot, lens, layer, B, k, scale, oc, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), fa.EINVAL), (dict(k=0), fa.EINVAL), (dict(v=0), fa.EINVAL),
+    (dict(lens=0), fa.EINVAL), (dict(slot=0), fa.EINVAL), (dict(o=0), fa.EINVAL),
+    (dict(B=0), fa.EINVAL), (dict(n=0), fa.EINVAL), (dict(n=17), fa.EINVAL),
+    (dict(layer=-1), fa.ERANGE), (dict(layer=2), fa.ERANGE),
+    (dict(q=FAKE_ODD), fa.EALIGN), (dict(o=FAKE_ODD), fa.EALIGN), (dict(lens=FAKE + 2), fa.EALIGN),
+    (dict(scale=float("inf")), fa.EINVAL),
+])
+def test_prefill_host_checks(kw, code):
+    h = make_pool(L=2, n_max=16)
+    assert _prefill(h, **kw) == code
+    lib.unipin_pool_destroy(h)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qc=0), fa.EINVAL), (dict(kc=0), fa.EINVAL), (dict(vc=0), fa.EINVAL),
+    (dict(lens=0), fa.EINVAL), (dict(slot=0), fa.EINVAL), (dict(oc=0), fa.EINVAL),
+    (dict(B=0), fa.EINVAL), (dict(k=0), fa.EINVAL),
+    (dict(layer=-1), fa.ERANGE), (dict(layer=2), fa.ERANGE),
+    (dict(kc=FAKE_ODD), fa.EALIGN), (dict(slot=FAKE + 1), fa.EALIGN),
+    (dict(scale=float("-inf")), fa.EINVAL),
+])
+def test_decode_host_checks(kw, code):
+    h = make_pool(L=2, n_max=16)
+    assert _decode(h, **kw) == code
+    lib.unipin_pool_destroy(h)
+
+
+def test_null_pool_rejected():
+    assert _prefill(None) == fa.EINVAL
+    assert _decode(None) == fa.EINVAL
+
+
+def test_binding_rejects_mismatched_tensors():
+    import torch
+    # host-side checks in the binding run before the library is called
+    k = torch.empty((1, 1, 2, 8, 64), dtype=torch.bfloat16)
+    pool = fa.Pool(k, torch.empty_like(k))
+    q = torch.empty((1, 2, 8, 64), dtype=torch.float32)
+    with pytest.raises(fa.UnipinError):
+        fa.prefill(q, q, q, [8], pool, [0], 0)
+    q = torch.empty((1, 3, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(fa.UnipinError):
+        fa.prefill(q, q, q, [8], pool, [0], 0)
+    with pytest.raises(fa.UnipinError):
+        fa.Pool(k, torch.empty((1, 1, 2, 8, 32), dtype=torch.bfloat16))
+    pool.close()

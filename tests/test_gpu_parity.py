@@ -1,0 +1,326 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances (applied to history rows t < lens[b] and to every candidate row):
+  * fp32: normwise max|gpu - oracle| / max|oracle| <= 1e-5 per output tensor;
+  * bf16 inputs with fp32 accumulation: max|gpu - oracle| <= 2e-2 and
+    mean|gpu - oracle| <= 2e-3.
+The oracle runs on the exact bits the GPU received (upcast to float64).  Integer and
+byte results (pool contents, rows that must stay untouched, permutation and
+composition invariance of a candidate's output) are compared bit for bit.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import falcon_attention_kv_amd as fa
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def announce(msg: str) -> None:
+    sys.__stderr__.write(f"[gpu case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def check_close(got: torch.Tensor, ref: np.ndarray, dtype: torch.dtype, what: str):
+    g = got.detach().to("cpu").to(torch.float64).numpy()
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    diff = np.abs(g - r)
+    if dtype == torch.float32:
+        rel = diff.max() / max(np.abs(r).max(), 1e-30)
+        assert rel <= 1e-5, f"{what}: normwise relative error {rel:.3e} > 1e-5"
+        return rel
+    mx, mean = diff.max(), diff.mean()
+    assert mx <= 2e-2, f"{what}: max abs error {mx:.3e} > 2e-2"
+    assert mean <= 2e-3, f"{what}: mean abs error {mean:.3e} > 2e-3"
+    return mx
+
+
+def hist_rows(x: torch.Tensor, lens) -> list:
+    return [x[b, :, : int(n)] for b, n in enumerate(lens)]
+
+
+def run_layer(pool, inp, lens, slots, layer, scale=None):
+    lens_d = torch.as_tensor(lens, dtype=torch.int32).to(DEV)
+    slots_d = torch.as_tensor(slots, dtype=torch.int32).to(DEV)
+    o = fa.prefill(inp["q"], inp["k"], inp["v"], lens_d, pool, slots_d, layer, scale=scale)
+    oc = fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, slots_d, lens_d, layer, scale=scale)
+    torch.cuda.synchronize()
+    return o, oc
+
+
+def full_check(inp, lens, o, oc, pool, slots, layer, dtype, users=None, scale=None, tag=""):
+    """Oracle on selected users (all heads, all rows); pool rows compared bit for bit."""
+    users = range(len(lens)) if users is None else users
+    for b in users:
+        N = int(lens[b])
+        sub = {k: v[b : b + 1].cpu() for k, v in inp.items() if k in ("q", "k", "v", "qc", "kc", "vc")}
+        ref_o = oracle.prefill(sub["q"], sub["k"], sub["v"], [N], scale)
+        if N:
+            check_close(o[b : b + 1, :, :N], ref_o[:, :, :N], dtype, f"{tag} prefill user {b} N={N}")
+        s = int(slots[b])
+        pk = pool.k[layer, s, :, :N].cpu()
+        pv = pool.v[layer, s, :, :N].cpu()
+        assert torch.equal(pk, inp["k"][b, :, :N].cpu()), f"{tag} pool K user {b}"
+        assert torch.equal(pv, inp["v"][b, :, :N].cpu()), f"{tag} pool V user {b}"
+        # decode against the oracle reading the (bitwise-checked) pool rows
+        ref_c = oracle.rank_decode(sub["qc"], sub["kc"], sub["vc"],
+                                   oracle.as_f64(pk).reshape(1, 1, *pk.shape),
+                                   oracle.as_f64(pv).reshape(1, 1, *pv.shape), [0], [N], 0, scale)
+        check_close(oc[b : b + 1], ref_c, dtype, f"{tag} decode user {b} N={N}")
+
+
+# ------------------------------------------------------------------ workload configs
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_workload_full(idx):
+    w = W.WORKLOADS[idx]
+    announce(f"workload {idx} full: {w.name}")
+    lens = W.history_lengths(w).tolist()
+    pool = fa.Pool.allocate(w.L, w.S, w.H, w.n, w.D, w.dtype, DEV)
+    slots = pool.acquire_many(w.B)
+    inp = W.layer_inputs(w, 0, DEV)
+    o, oc = run_layer(pool, inp, lens, slots, 0)
+    full_check(inp, lens, o, oc, pool, slots, 0, w.dtype, tag=f"w{idx}")
+    assert fa.device_status() == 0
+
+
+def test_workload_ragged_sampled_users():
+    w = W.WORKLOADS[2]
+    announce(f"workload 2 sampled users: {w.name}")
+    lens = W.history_lengths(w).tolist()
+    pool = fa.Pool.allocate(w.L, w.S, w.H, w.n, w.D, w.dtype, DEV)
+    slots = pool.acquire_many(w.B)
+    inp = W.layer_inputs(w, 0, DEV)
+    o, oc = run_layer(pool, inp, lens, slots, 0)
+    order = np.argsort(lens)
+    users = sorted(set([int(order[0]), int(order[-1]), 0, 17, 31, 63]))
+    full_check(inp, lens, o, oc, pool, slots, 0, w.dtype, users=users, tag="w2")
+    assert fa.device_status() == 0
+
+
+def test_serving_shape_twelve_layers_sampled():
+    """The 12-layer serving shape: 12 prefills into rotating slots, then 12 decodes; two
+    request batches so the 64 slots are handed out twice."""
+    w = W.WORKLOADS[3]
+    announce(f"workload 3 (12 layers), sampled heads: {w.name}")
+    lens = W.history_lengths(w).tolist()
+    pool = fa.Pool.allocate(w.L, w.S, w.H, w.n, w.D, w.dtype, DEV)
+    rng = np.random.default_rng(3)
+    for batch in range(2):
+        slots = pool.acquire_many(w.B)
+        assert slots == list(range(64))
+        assert pool.generation(0) == batch + 1
+        lens_d = torch.as_tensor(lens, dtype=torch.int32, device=DEV)
+        slots_d = torch.as_tensor(slots, dtype=torch.int32, device=DEV)
+        layers = [W.layer_inputs(w, l + 100 * batch, DEV) for l in range(w.L)]
+        outs = [fa.prefill(x["q"], x["k"], x["v"], lens_d, pool, slots_d, l) for l, x in enumerate(layers)]
+        outc = [fa.rank_decode(x["qc"], x["kc"], x["vc"], pool, slots_d, lens_d, l) for l, x in enumerate(layers)]
+        torch.cuda.synchronize()
+        for l in (0, 6, 11):
+            x = layers[l]
+            assert torch.equal(pool.k[l].cpu(), x["k"].cpu()), f"pool K layer {l}"
+            assert torch.equal(pool.v[l].cpu(), x["v"].cpu()), f"pool V layer {l}"
+            for _ in range(3):
+                b, h = int(rng.integers(64)), int(rng.integers(8))
+                ref_o = oracle.prefill(x["q"][b:b+1, h:h+1].cpu(), x["k"][b:b+1, h:h+1].cpu(),
+                                       x["v"][b:b+1, h:h+1].cpu(), [512])
+                check_close(outs[l][b:b+1, h:h+1], ref_o, w.dtype, f"prefill layer {l} b{b} h{h}")
+                ref_c = oracle.rank_decode_rows(x["qc"][b, h].cpu(), x["kc"][b, h].cpu(), x["vc"][b, h].cpu(),
+                                                pool.k[l, slots[b], h].cpu(), pool.v[l, slots[b], h].cpu(),
+                                                range(1000))
+                check_close(outc[l][b, h], ref_c, w.dtype, f"decode layer {l} b{b} h{h}")
+    assert fa.device_status() == 0
+
+
+def test_long_history_sampled():
+    w = W.WORKLOADS[4]
+    announce(f"workload 4 sampled rows: {w.name}")
+    lens = W.history_lengths(w).tolist()
+    pool = fa.Pool.allocate(w.L, w.S, w.H, w.n, w.D, w.dtype, DEV)
+    slots = pool.acquire_many(w.B)
+    inp = W.layer_inputs(w, 0, DEV)
+    o, oc = run_layer(pool, inp, lens, slots, 0)
+    rng = np.random.default_rng(4)
+    order = np.argsort(lens)
+    for b in (int(order[0]), int(order[-1]), 5):
+        h = int(rng.integers(w.H))
+        N = lens[b]
+        assert torch.equal(pool.k[0, slots[b], :, :N].cpu(), inp["k"][b, :, :N].cpu())
+        assert torch.equal(pool.v[0, slots[b], :, :N].cpu(), inp["v"][b, :, :N].cpu())
+        rows = sorted(set([0, 1, 63, 64, 255, 256, N - 1] + rng.integers(0, N, 40).tolist()))
+        ref = oracle.prefill_rows(inp["q"][b, h].cpu(), inp["k"][b, h].cpu(), inp["v"][b, h].cpu(), N, rows)
+        check_close(o[b, h, rows], ref, w.dtype, f"prefill b{b} h{h} N={N}")
+        crow = sorted(set([0, 255, 256, 2047] + rng.integers(0, w.k, 60).tolist()))
+        ref = oracle.rank_decode_rows(inp["qc"][b, h].cpu(), inp["kc"][b, h].cpu(), inp["vc"][b, h].cpu(),
+                                      inp["k"][b, h, :N].cpu(), inp["v"][b, h, :N].cpu(), crow)
+        check_close(oc[b, h, crow], ref, w.dtype, f"decode b{b} h{h} N={N}")
+    assert fa.device_status() == 0
+
+
+# ------------------------------------------------------------------ edge cases
+
+EDGE = [
+    # (dtype, B, H, D, n, k, lens)
+    (torch.bfloat16, 3, 2, 64, 300, 70, [0, 1, 300]),       # empty and one-token history, ragged tails
+    (torch.bfloat16, 4, 2, 64, 130, 1, [63, 64, 65, 129]),    # k = 1, lengths around a tile edge
+    (torch.bfloat16, 2, 4, 32, 257, 257, [257, 100]),          # D = 32, no XCD remap (B*H = 8 -> remap)
+    (torch.bfloat16, 1, 3, 128, 520, 300, [511]),              # D = 128, B*H not a multiple of 8
+    (torch.bfloat16, 8, 1, 64, 512, 256, [512, 256, 255, 257, 1, 2, 500, 384]),
+    (torch.float32, 2, 2, 64, 100, 33, [100, 37]),
+    (torch.float32, 1, 2, 128, 70, 5, [0]),
+    (torch.float32, 3, 1, 32, 65, 64, [65, 64, 1]),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: f"{str(c[0])[6:]}-B{c[1]}H{c[2]}D{c[3]}n{c[4]}k{c[5]}")
+def test_edge_shapes(case):
+    dtype, B, H, D, n, k, lens = case
+    announce(f"edge {case}")
+    inp = W.small_case(B, H, D, n, k, lens, dtype=dtype, seed=1000 + n + k, device=DEV)
+    pool = fa.Pool.allocate(2, B + 1, H, n, D, dtype, DEV)
+    pool.k.fill_(float("nan"))
+    pool.v.fill_(float("nan"))
+    slots = list(range(B, 0, -1))  # not the identity, to catch slot mix-ups
+    o, oc = run_layer(pool, inp, lens, slots, 1)
+    full_check(inp, lens, o, oc, pool, slots, 1, dtype, tag="edge")
+    # rows past each history, other slots and the other layer are untouched (NaN sentinel)
+    for b, N in enumerate(lens):
+        assert torch.isnan(pool.k[1, slots[b], :, N:]).all() and torch.isnan(pool.v[1, slots[b], :, N:]).all()
+    assert torch.isnan(pool.k[0]).all() and torch.isnan(pool.k[1, 0]).all()
+    if 0 in lens:
+        b = lens.index(0)
+        assert torch.equal(oc[b], inp["vc"][b]), "empty history must return vc exactly"
+    assert fa.device_status() == 0
+
+
+def test_nan_poison_rows_past_history_are_never_read():
+    """Inputs and pool rows at or past lens[b] are NaN; outputs must equal the clean run bit for bit."""
+    B, H, D, n, k = 4, 2, 64, 333, 90
+    lens = [333, 200, 64, 7]
+    announce("nan poison")
+    clean = W.small_case(B, H, D, n, k, lens, seed=77, device=DEV)
+    pois = dict(clean)
+    lens_t = torch.as_tensor(lens)
+    for name in ("q", "k", "v"):
+        pois[name] = W.poison_tail(clean[name], lens_t)
+    outs = []
+    for inp in (clean, pois):
+        pool = fa.Pool.allocate(1, B, H, n, D, torch.bfloat16, DEV)
+        pool.k.fill_(float("nan"))
+        pool.v.fill_(float("nan"))
+        o, oc = run_layer(pool, inp, lens, list(range(B)), 0)
+        outs.append((o, oc))
+    for b, N in enumerate(lens):
+        assert torch.equal(outs[0][0][b, :, :N], outs[1][0][b, :, :N])
+    assert torch.equal(outs[0][1], outs[1][1])
+    assert torch.isfinite(outs[1][1]).all()
+
+
+# ------------------------------------------------------------------ invariants
+
+def test_joint_invariant():
+    """prefill + rank_decode on the GPU == one pass over [history || candidates] (oracle)."""
+    B, H, D, n, k = 3, 2, 64, 200, 50
+    lens = [200, 77, 0]
+    announce("joint invariant")
+    inp = W.small_case(B, H, D, n, k, lens, seed=5, device=DEV)
+    pool = fa.Pool.allocate(3, 4, H, n, D, torch.bfloat16, DEV)
+    o, oc = run_layer(pool, inp, lens, [3, 1, 0], 2)
+    cpu = {key: v.cpu() for key, v in inp.items()}
+    jo, jc = oracle.joint(cpu["q"], cpu["k"], cpu["v"], cpu["qc"], cpu["kc"], cpu["vc"], lens)
+    for b, N in enumerate(lens):
+        if N:
+            check_close(o[b, :, :N], jo[b, :, :N], torch.bfloat16, f"joint hist {b}")
+    check_close(oc, jc, torch.bfloat16, "joint candidates")
+
+
+def test_candidate_independence_bitwise():
+    """A candidate's output does not depend on the other candidates of the call."""
+    B, H, D, n, k = 2, 4, 64, 300, 400
+    lens = [300, 123]
+    announce("candidate independence")
+    inp = W.small_case(B, H, D, n, k, lens, seed=9, device=DEV)
+    pool = fa.Pool.allocate(1, 2, H, n, D, torch.bfloat16, DEV)
+    lens_d = torch.as_tensor(lens, dtype=torch.int32, device=DEV)
+    slots_d = torch.tensor([0, 1], dtype=torch.int32, device=DEV)
+    fa.prefill(inp["q"], inp["k"], inp["v"], lens_d, pool, slots_d, 0)
+    dec = lambda qc, kc, vc: fa.rank_decode(qc.contiguous(), kc.contiguous(), vc.contiguous(),
+                                            pool, slots_d, lens_d, 0)
+    base = dec(inp["qc"], inp["kc"], inp["vc"])
+    perm = torch.randperm(k, generator=torch.Generator().manual_seed(1)).to(DEV)
+    out = dec(inp["qc"][:, :, perm], inp["kc"][:, :, perm], inp["vc"][:, :, perm])
+    assert torch.equal(out, base[:, :, perm])
+    keep = torch.arange(0, k, 7, device=DEV)
+    out = dec(inp["qc"][:, :, keep], inp["kc"][:, :, keep], inp["vc"][:, :, keep])
+    assert torch.equal(out, base[:, :, keep])
+    extra = W.small_case(B, H, D, n, 300, lens, seed=10, device=DEV)
+    cat = lambda a, e: torch.cat([a, e], dim=2)
+    out = dec(cat(inp["qc"], extra["qc"]), cat(inp["kc"], extra["kc"]), cat(inp["vc"], extra["vc"]))
+    assert torch.equal(out[:, :, :k], base)
+
+
+def test_same_data_other_slot_or_layer_is_bitwise_identical():
+    B, H, D, n, k = 2, 2, 64, 256, 128
+    lens = [256, 190]
+    announce("slot/layer placement")
+    inp = W.small_case(B, H, D, n, k, lens, seed=11, device=DEV)
+    pool = fa.Pool.allocate(3, 5, H, n, D, torch.bfloat16, DEV)
+    a = run_layer(pool, inp, lens, [0, 1], 0)
+    b = run_layer(pool, inp, lens, [4, 2], 2)
+    assert torch.equal(a[1], b[1])
+    for i, N in enumerate(lens):
+        assert torch.equal(a[0][i, :, :N], b[0][i, :, :N])
+
+
+@pytest.mark.parametrize("kind", ["peaky", "dominant_key", "scale_arg"])
+def test_adversarial_numerics(kind):
+    B, H, D, n, k = 2, 2, 64, 384, 128
+    lens = [384, 250]
+    announce(f"adversarial {kind}")
+    inp = W.small_case(B, H, D, n, k, lens, seed=12, device=DEV)
+    scale = None
+    if kind == "peaky":
+        for name in ("q", "qc"):
+            inp[name] = (inp[name].float() * 8).to(torch.bfloat16)
+    elif kind == "dominant_key":
+        # one late history key aligned with every query: the running max jumps late
+        kk = inp["k"].clone()
+        kk[:, :, 200] = (inp["qc"][:, :, 0].float() * 4).to(torch.bfloat16)
+        inp["k"] = kk
+        inp["q"] = inp["q"].clone()
+        inp["q"][:, :, :] = inp["qc"][:, :, :1]
+        inp["qc"] = inp["qc"][:, :, :1].expand(-1, -1, k, -1).contiguous()
+    else:
+        scale = 0.37
+    pool = fa.Pool.allocate(1, 2, H, n, D, torch.bfloat16, DEV)
+    o, oc = run_layer(pool, inp, lens, [1, 0], 0, scale=scale)
+    full_check(inp, lens, o, oc, pool, [1, 0], 0, torch.bfloat16, scale=scale, tag=kind)
+
+
+def test_device_side_invalid_user_is_skipped_and_flagged():
+    B, H, D, n, k = 3, 2, 64, 128, 64
+    announce("device status flags")
+    inp = W.small_case(B, H, D, n, k, [128, 64, 10], seed=13, device=DEV)
+    pool = fa.Pool.allocate(1, 2, H, n, D, torch.bfloat16, DEV)
+    assert fa.device_status() == 0
+    o = torch.full_like(inp["q"], 7.0)
+    fa.prefill(inp["q"], inp["k"], inp["v"], [128, 64, 10], pool, [0, 5, 1], 0, o=o)  # slot 5 >= S
+    assert fa.device_status() == fa.FLAG_BAD_SLOT
+    assert (o[1] == 7.0).all(), "a skipped user's output must stay untouched"
+    fa.prefill(inp["q"], inp["k"], inp["v"], [128, 129, 10], pool, [0, 1, 1], 0, o=o)  # len > n
+    assert fa.device_status() == fa.FLAG_BAD_LEN
+    oc = torch.full_like(inp["qc"], 7.0)
+    fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, [0, -1, 1], [128, 64, 10], 0, oc=oc)
+    assert fa.device_status() == fa.FLAG_BAD_SLOT
+    assert (oc[1] == 7.0).all()
+    assert torch.isfinite(oc[0]).all() and torch.isfinite(oc[2]).all()
+    assert fa.device_status() == 0
