@@ -42,6 +42,9 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline sample")
+    p.add_argument("--copy-calib-mib", type=int, default=0,
+                   help="after timing, run 3 plain device copies of this many MiB (a known-size "
+                        "reference for the HBM byte counters of a profiler run)")
     return p.parse_args()
 
 
@@ -213,6 +216,14 @@ def main():
                             "decode_candidates_per_s": round(cand_per_step / (w.L * dc_avg / 1e3), 1)},
         },
     }
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n * 4
     if not args.no_cpu_baseline:
         layers_cpu = [{k: v.cpu() for k, v in x.items()} for x in layers]
         out["cpu_baseline"] = cpu_baseline(w, layers_cpu, lens, args.cpu_seconds)

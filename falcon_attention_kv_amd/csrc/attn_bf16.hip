@@ -8,24 +8,32 @@
 // Work decomposition (both kernels):
 //   * one workgroup = 4 waves of 64 lanes; each wave owns 64 query rows, held in
 //     registers for the whole kernel as the B operand of v_mfma_f32_32x32x16_bf16;
-//   * the workgroup streams 64-key tiles of K and V through LDS (double buffered,
-//     16-byte coalesced global loads issued one tile ahead);
+//   * 64-key tiles of K and V are copied HBM -> LDS by the buffer-to-LDS DMA path
+//     (buffer_load_dwordx4 ... lds), three tiles in flight: no staging registers, no
+//     VALU work, and every row past the history reads as zero (the buffer's record
+//     count is the history length), so ragged histories need no branches;
 //   * scores are computed transposed, S^T = K Q^T, so that in the MFMA result each lane
-//     holds one query and 16 keys: the softmax row statistics are lane-local plus one
+//     holds one query and 16 keys: softmax row statistics are lane-local plus one
 //     exchange with the lane 32 away;
 //   * the PV product is computed as O^T = V^T P^T: P^T, rounded to bf16, is used in the
-//     very registers the score MFMA left it in, and O^T again keeps one query per lane,
-//     so rescaling by the running max is lane-local;
+//     very registers the score MFMA left it in; V stays in its natural [key][d] layout
+//     in LDS and ds_read_b64_tr_b16 delivers it transposed;
 //   * fp32 online softmax in the log2 domain (scale*log2(e) folded into one FMA), with a
 //     lazy rescale: the running max only moves when a tile's max exceeds it by more
 //     than 2^8, which bounds P by 256 and skips almost every rescale;
 //   * the row sum is accumulated from the bf16-rounded P (v_dot2 with ones), so the
-//     normaliser matches the weights the PV product used.
+//     normaliser matches the weights the PV product used;
+//   * masking code runs only on tiles that cross the history end or the causal diagonal.
 //
-// Layout facts of v_mfma_f32_32x32x16_bf16 this relies on: result element i of lane l
-// is row 8*(i/4) + 4*(l/32) + (i%4), column l%32; the A and B operands distribute the
-// contraction index over (lane/32, element) in the same way, so any consistent
-// assignment of keys to (lane/32, element) is a valid contraction order.
+// Hardware facts relied on (checked on gfx950 with small in-bounds probes):
+//   * v_mfma_f32_32x32x16_bf16 result element i of lane l is row 8*(i/4) + 4*(l/32)
+//     + (i%4), column l%32; A and B spread the contraction index over (lane/32,
+//     element) in the same way, so any consistent assignment of keys to (lane/32,
+//     element) is a valid contraction order;
+//   * ds_read_b64_tr_b16: in each group of 16 lanes, lane c receives element c%4 of the
+//     8-byte rows addressed by lanes 4e + c/4 (e = 0..3): a 4 x 16 -> 16 x 4 transpose;
+//   * buffer loads to LDS write 16 bytes per lane at consecutive LDS addresses (M0 base
+//     + 16 * lane) and write zeros for offsets past the record count.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,10 +42,13 @@
 namespace unipin {
 namespace {
 
+#define LDS_AS __attribute__((address_space(3)))
+
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -47,132 +58,80 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kQW = 64;                   // query rows per wave
 constexpr int kQT = kWaves * kQW;         // query rows per workgroup
 constexpr int kTK = 64;                   // keys per LDS tile
+constexpr int kBufs = 3;                  // LDS tiles in flight
 static_assert(kQT == kBf16RowsPerBlock, "rows per block must match the host's grid math");
 static_assert(kQT % kTK == 0, "a query tile must cover whole key tiles");
+
+constexpr uint32_t kBufferWord3 = 0x00020000u;   // gfx9 buffer descriptor, raw 32-bit access
 
 // Lazy-rescale threshold in log2 units: P stays below 2^8.
 constexpr float kRescaleThreshold = 8.0f;
 
 template <int D>
 struct Tile {
-    static constexpr int KC = D / 16;           // 16-deep contraction chunks over the head dim
-    static constexpr int DB = D / 32;           // 32-row blocks of the head dim in O^T
-    static constexpr int KSTR = D + 8;          // K tile row stride in elements (16 B pad)
-    static constexpr int K_ELEMS = kTK * KSTR;  // K tile, [key][d], padded rows
-    static constexpr int V_ELEMS = D * kTK;     // V^T tile, [d][key position], XOR-swizzled
-    static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-    static constexpr int C8 = D / 8;            // 16-byte chunks per row
-    static constexpr int K_CHUNKS = kTK * C8 / kThreads;          // K chunks per thread
-    static constexpr int V_UNITS = (kTK / 2) * C8;                // key pairs x chunks
-    static constexpr int V_PER_THREAD = (V_UNITS + kThreads - 1) / kThreads;
-    static_assert(kTK * C8 % kThreads == 0, "K tile must split evenly over the threads");
+    static constexpr int KC = D / 16;                 // 16-deep contraction chunks of the head dim
+    static constexpr int DB = D / 32;                 // 32-row blocks of the head dim in O^T
+    static constexpr int R = D / 8;                   // 16-byte blocks per key row
+    static constexpr int ROW_BYTES = D * 2;
+    static constexpr int MAT_BYTES = kTK * ROW_BYTES;  // one K or V tile
+    static constexpr int BUF_BYTES = 2 * MAT_BYTES;    // K tile then V tile
+    static constexpr int DMA_PER_MAT = MAT_BYTES / 1024;              // 1 KB per wave-wide DMA
+    static constexpr int DMA_PER_WAVE = 2 * DMA_PER_MAT / kWaves;     // per wave per tile
+    static_assert(2 * DMA_PER_MAT % kWaves == 0, "tile DMA must split evenly over the waves");
 };
 
-// Position of key offset r (0..63) inside a V^T row: the two middle 4-key groups of
-// every 16-key chunk are swapped, so that the 8 keys one lane needs for one PV MFMA
-// (keys 16c + 8(e/4) + 4(l/32) + e%4 for e = 0..7, dictated by the score layout) sit at
-// 8 consecutive positions.  The map is its own inverse.
-__device__ __forceinline__ int vt_pos(int r) {
-    return (r & ~12) | ((r >> 1) & 4) | ((r << 1) & 8);
-}
-
-// Element index of (d, position p) in the V^T tile.  16-byte blocks of a row are
-// XOR-swizzled with a function of d so that both the transposing writes (8 lanes, same
-// key pair, 8 different d-groups) and the operand reads (8 lanes, 8 consecutive d, same
-// block) spread over all LDS banks.
-__device__ __forceinline__ int vt_index(int d, int p) {
-    const int sw = (d ^ (d >> 3)) & 7;
-    return d * kTK + ((((p >> 3) ^ sw)) << 3) + (p & 7);
-}
-
-__device__ __forceinline__ u32x4 load16(const bf16 *p) {
-    return *reinterpret_cast<const u32x4 *>(p);
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) {
-    return __builtin_bit_cast(bf16x8, x);
-}
-
-// Staged copy of one K/V tile held in registers between its global load and its LDS
-// store (and, for the prefill's own rows, its pool store).
+// 16-byte block swizzles inside a key row (XOR keeps the block inside the row).  K is
+// read 8 lanes at a time, one row each, same logical block; V is read with transpose
+// loads, 16 lanes covering 4 consecutive rows x 32 bytes.  Both patterns then touch
+// every LDS bank exactly once.
 template <int D>
-struct Stage {
-    u32x4 k[Tile<D>::K_CHUNKS];
-    u32x4 v0[Tile<D>::V_PER_THREAD];
-    u32x4 v1[Tile<D>::V_PER_THREAD];
-};
-
+__device__ __forceinline__ int k_swz(int key) {
+    return Tile<D>::R >= 8 ? (key & 7) : ((key >> 1) & 3);
+}
 template <int D>
-__device__ __forceinline__ void stage_load(Stage<D> &st, const bf16 *ksrc, const bf16 *vsrc,
-                                           int kbase, int N, int tid) {
+__device__ __forceinline__ int v_swz(int key) {
+    return Tile<D>::R >= 8 ? ((key & 3) << 1) : (((key >> 1) & 1) << 1);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, (int)kBufferWord3);
+}
+
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+// DMA of one K/V tile (keys kbase .. kbase+63) into LDS buffer `buf`.  Wave w moves
+// its share of the 1 KB pieces; lane l of piece j fills LDS block 64*j + l, i.e. key row
+// (64*j + l) / R, swizzled block (64*j + l) % R, taken from the matching unswizzled block.
+template <int D>
+__device__ __forceinline__ void dma_tile(LDS_AS char *buf, __amdgpu_buffer_rsrc_t rk,
+                                         __amdgpu_buffer_rsrc_t rv, int kbase, int wave, int lane) {
     using T = Tile<D>;
 #pragma unroll
-    for (int i = 0; i < T::K_CHUNKS; ++i) {
-        const int c = tid + i * kThreads;
-        const int r = c / T::C8, c8 = c % T::C8;
-        const int key = kbase + r;
-        st.k[i] = key < N ? load16(ksrc + (long)key * D + c8 * 8) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < T::V_PER_THREAD; ++i) {
-        const int u = tid + i * kThreads;
-        const int rp = u / T::C8, c8 = u % T::C8;
-        const int key = kbase + 2 * rp;
-        const bool in = u < T::V_UNITS;
-        st.v0[i] = (in && key < N) ? load16(vsrc + (long)key * D + c8 * 8) : u32x4{0, 0, 0, 0};
-        st.v1[i] = (in && key + 1 < N) ? load16(vsrc + (long)(key + 1) * D + c8 * 8)
-                                       : u32x4{0, 0, 0, 0};
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void stage_store_lds(const Stage<D> &st, bf16 *buf, int tid) {
-    using T = Tile<D>;
-    bf16 *ks = buf;
-    bf16 *vt = buf + T::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < T::K_CHUNKS; ++i) {
-        const int c = tid + i * kThreads;
-        const int r = c / T::C8, c8 = c % T::C8;
-        *reinterpret_cast<u32x4 *>(ks + r * T::KSTR + c8 * 8) = st.k[i];
-    }
-#pragma unroll
-    for (int i = 0; i < T::V_PER_THREAD; ++i) {
-        const int u = tid + i * kThreads;
-        if (u >= T::V_UNITS) break;
-        const int rp = u / T::C8, c8 = u % T::C8;
-        const int p = vt_pos(2 * rp);  // even; the pair's second key sits at p + 1
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t a = st.v0[i][j], b = st.v1[i][j];
-            const uint32_t lo = (a & 0xffffu) | (b << 16);          // d = c8*8 + 2j
-            const uint32_t hi = (a >> 16) | (b & 0xffff0000u);      // d = c8*8 + 2j + 1
-            const int d = c8 * 8 + 2 * j;
-            *reinterpret_cast<uint32_t *>(vt + vt_index(d, p)) = lo;
-            *reinterpret_cast<uint32_t *>(vt + vt_index(d + 1, p)) = hi;
-        }
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void stage_store_pool(const Stage<D> &st, bf16 *pk, bf16 *pv,
-                                                 int kbase, int N, int tid) {
-    using T = Tile<D>;
-#pragma unroll
-    for (int i = 0; i < T::K_CHUNKS; ++i) {
-        const int c = tid + i * kThreads;
-        const int r = c / T::C8, c8 = c % T::C8;
-        const int key = kbase + r;
-        if (key < N) *reinterpret_cast<u32x4 *>(pk + (long)key * D + c8 * 8) = st.k[i];
-    }
-#pragma unroll
-    for (int i = 0; i < T::V_PER_THREAD; ++i) {
-        const int u = tid + i * kThreads;
-        if (u >= T::V_UNITS) break;
-        const int rp = u / T::C8, c8 = u % T::C8;
-        const int key = kbase + 2 * rp;
-        if (key < N) *reinterpret_cast<u32x4 *>(pv + (long)key * D + c8 * 8) = st.v0[i];
-        if (key + 1 < N) *reinterpret_cast<u32x4 *>(pv + (long)(key + 1) * D + c8 * 8) = st.v1[i];
+    for (int j = 0; j < T::DMA_PER_WAVE; ++j) {
+        const int piece = wave * T::DMA_PER_WAVE + j;          // wave-uniform
+        const bool is_v = piece >= T::DMA_PER_MAT;
+        const int pj = is_v ? piece - T::DMA_PER_MAT : piece;
+        const int p = pj * 64 + lane;
+        const int key = p / T::R, blks = p % T::R;
+        const int blk = blks ^ (is_v ? v_swz<D>(key) : k_swz<D>(key));
+        const uint32_t goff = (uint32_t)((kbase + key) * T::ROW_BYTES + blk * 16);
+        LDS_AS char *dst = buf + (is_v ? T::MAT_BYTES : 0) + pj * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_v ? rv : rk, (LDS_AS void *)dst, 16, (int)goff, 0, 0, 0);
     }
 }
 
@@ -192,10 +151,135 @@ __device__ __forceinline__ void block_coords(const AttnArgs &a, int &group, int 
     }
 }
 
-template <int D, bool PREFILL>
-__global__ void __launch_bounds__(kThreads, D <= 64 ? 2 : 1) attn_bf16_kernel(AttnArgs a) {
+// Per-wave attention state and the per-tile step.
+template <int D>
+struct WaveState {
+    bf16x8 qreg[2][Tile<D>::KC];   // B operand: query rows wq0 + qb*32 + col, dims c*16 + g*8 ..
+    f32x16 acc[Tile<D>::DB][2];    // O^T accumulators: lane = query, 16 head dims per block
+    float m[2];                    // running max (log2 domain), shared by both lane halves
+    float l[2];                    // this lane half's share of the row sum
+};
+
+template <int D, bool PREFILL, bool MASK>
+__device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *kt, const LDS_AS char *vt,
+                                          int kbase, int kend, int wq0, int col, int g,
+                                          int k_off0, const int *k_xor, int v_off, const int *v_blk, float c) {
     using T = Tile<D>;
-    __shared__ __attribute__((aligned(16))) bf16 smem[2 * T::BUF_ELEMS];
+    // ---- S^T = K Q^T: 2 key blocks x 2 query blocks of 32x32.
+    f32x16 sc[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) sc[kb][qb] = f32x16{};
+#pragma unroll
+    for (int cc = 0; cc < T::KC; ++cc) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 ka = *reinterpret_cast<const LDS_AS bf16x8 *>(kt + k_off0 + kb * 32 * T::ROW_BYTES + k_xor[cc]);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+                sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, ws.qreg[qb][cc], sc[kb][qb], 0, 0, 0);
+        }
+    }
+
+    // ---- mask: keys past the history, and (prefill) keys after the query.  Element i
+    // of block (kb, qb) is key kbase + kb*32 + 4g + off(i), off(i) = 8*(i/4) + i%4, so
+    // one per-lane bound per block decides all 16: the key is visible iff off(i) <= lim.
+    if constexpr (MASK) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int base = kbase + kb * 32 + 4 * g;
+                int lim = kend - 1 - base;
+                if (PREFILL) lim = min(lim, wq0 + qb * 32 + col - base);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int off = 8 * (i >> 2) + (i & 3);
+                    sc[kb][qb][i] = off > lim ? -INFINITY : sc[kb][qb][i];
+                }
+            }
+    }
+
+    // ---- running max (log2 domain) with lazy rescale.  The rescale branch is wave-wide
+    // and rare (first visible tile, or a late jump of the max by more than 2^8).
+    float mt[2];
+    bool grow[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        float mx = sc[0][qb][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[0][qb][i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[1][qb][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mt[qb] = mx * c;
+        grow[qb] = mt[qb] > ws.m[qb] + kRescaleThreshold;
+    }
+    if (__any(grow[0] || grow[1])) {
+        // keeps the compiler from flattening this rare path into the hot block
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const float mn = grow[qb] ? fmaxf(ws.m[qb], mt[qb]) : ws.m[qb];
+            const float alpha = grow[qb] ? __builtin_amdgcn_exp2f(ws.m[qb] - mn) : 1.f;
+            ws.l[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db) ws.acc[db][qb] *= alpha;
+            ws.m[qb] = mn;
+        }
+    }
+
+    // ---- per 32-key block: P = exp2(s*c - m), rounded to bf16 in the B-operand layout
+    // of the PV MFMA (the row sum takes the rounded values), then O^T += V^T P^T.
+    // Lane (d, g) needs, for chunk (kb, c2), V at keys kb*32 + 16*c2 + {4g..4g+3}
+    // (elements 0..3) and kb*32 + 16*c2 + 8 + {4g..4g+3} (elements 4..7): two transpose
+    // loads of 4 keys x 16 dims each.
+    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 pb[2][2];  // [chunk of 16 keys][qb]
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const float nm = -ws.m[qb];
+            float lsum = 0.f;
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                bf16x8 p;
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][c2 * 8 + e], c, nm));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][c2 * 8 + e + 1], c, nm));
+                    const bf16x2 pp = {(bf16)p0, (bf16)p1};
+                    p[e] = pp[0];
+                    p[e + 1] = pp[1];
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+                }
+                pb[c2][qb] = p;
+            }
+            ws.l[qb] += lsum;
+        }
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const LDS_AS char *src = vt + v_off + v_blk[db] + (kb * 32 + 16 * c2) * T::ROW_BYTES;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)src);
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(src + 8 * T::ROW_BYTES));
+                const i16x4 lh[2] = {lo, hi};
+                const bf16x8 va = __builtin_bit_cast(bf16x8, lh);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+                    ws.acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c2][qb], ws.acc[db][qb], 0, 0, 0);
+            }
+    }
+}
+
+template <int D, bool PREFILL>
+__device__ __forceinline__ void attn_body(const AttnArgs &a) {
+    using T = Tile<D>;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[kBufs * T::BUF_BYTES];
+    LDS_AS char *smem = (LDS_AS char *)smem_raw;
 
     int group, tile;
     block_coords(a, group, tile);
@@ -228,214 +312,122 @@ __global__ void __launch_bounds__(kThreads, D <= 64 ? 2 : 1) attn_bf16_kernel(At
     const bf16 *vsrc = PREFILL ? static_cast<const bf16 *>(a.v) + bh * a.rows * D : pv;
     const int kend = PREFILL ? min(q0 + kQT, N) : N;
     const int ntiles = (kend + kTK - 1) / kTK;
+    // Rows at or past kend read as zeros.
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(ksrc, (uint32_t)kend * T::ROW_BYTES);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vsrc, (uint32_t)kend * T::ROW_BYTES);
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 31, g = lane >> 5;
     const int wq0 = q0 + wave * kQW;
 
-    // Query rows of this lane: wq0 + qb*32 + col, qb in {0,1}.  Operand layout: chunk c
-    // holds head dims c*16 + g*8 .. +7.
-    bf16x8 qreg[2][T::KC];
+    // Start the first two tiles' DMA before anything else.
+    if (ntiles > 0) dma_tile<D>(smem, rk, rv, 0, wave, lane);
+    if (ntiles > 1) dma_tile<D>(smem + T::BUF_BYTES, rk, rv, kTK, wave, lane);
+
+    WaveState<D> ws;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qsrc, (uint32_t)qlimit * T::ROW_BYTES);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        const int row = wq0 + qb * 32 + col;
+        const uint32_t row = (uint32_t)(wq0 + qb * 32 + col);
 #pragma unroll
-        for (int c = 0; c < T::KC; ++c)
-            qreg[qb][c] = as_bf16x8(row < qlimit ? load16(qsrc + (long)row * D + c * 16 + g * 8)
-                                                 : u32x4{0, 0, 0, 0});
+        for (int cc = 0; cc < T::KC; ++cc)
+            ws.qreg[qb][cc] = as_bf16x8(bload16(rq, row * T::ROW_BYTES + cc * 32 + g * 16));
     }
 
-    // Online-softmax state per query block: running max m (log2 domain), this half's
-    // share of the row sum l, and O^T accumulators (lane = query, 16 head dims per block).
-    float m[2], l[2];
-    f32x16 acc[T::DB][2];
     if constexpr (PREFILL) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            m[qb] = -INFINITY;
-            l[qb] = 0.f;
+            ws.m[qb] = -INFINITY;
+            ws.l[qb] = 0.f;
 #pragma unroll
-            for (int db = 0; db < T::DB; ++db) acc[db][qb] = f32x16{};
+            for (int db = 0; db < T::DB; ++db) ws.acc[db][qb] = f32x16{};
         }
     } else {
         // The candidate's own key enters first: it sets the running max, contributes
         // weight exp2(0) = 1 to the row sum (counted once, by the lower half) and its
         // value vc_j to the accumulator.  An empty history therefore yields vc_j exactly.
-        const bf16 *kcs = static_cast<const bf16 *>(a.k) + bh * a.rows * D;
-        const bf16 *vcs = static_cast<const bf16 *>(a.v) + bh * a.rows * D;
+        const __amdgpu_buffer_rsrc_t rkc =
+            make_rsrc(static_cast<const bf16 *>(a.k) + bh * a.rows * D, (uint32_t)qlimit * T::ROW_BYTES);
+        const __amdgpu_buffer_rsrc_t rvc =
+            make_rsrc(static_cast<const bf16 *>(a.v) + bh * a.rows * D, (uint32_t)qlimit * T::ROW_BYTES);
+        const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+        (void)ones;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            const int row = wq0 + qb * 32 + col;
-            const bool ok = row < qlimit;
+            const uint32_t row = (uint32_t)(wq0 + qb * 32 + col);
             float part = 0.f;
 #pragma unroll
-            for (int c = 0; c < T::KC; ++c) {
-                const bf16x8 kk =
-                    as_bf16x8(ok ? load16(kcs + (long)row * D + c * 16 + g * 8) : u32x4{0, 0, 0, 0});
+            for (int cc = 0; cc < T::KC; ++cc) {
+                const bf16x8 kk = as_bf16x8(bload16(rkc, row * T::ROW_BYTES + cc * 32 + g * 16));
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                    const bf16x2 qa = {qreg[qb][c][e], qreg[qb][c][e + 1]};
+                    const bf16x2 qa = {ws.qreg[qb][cc][e], ws.qreg[qb][cc][e + 1]};
                     const bf16x2 ka = {kk[e], kk[e + 1]};
                     part = __builtin_amdgcn_fdot2_f32_bf16(qa, ka, part, false);
                 }
             }
             const float self = part + __shfl_xor(part, 32);
-            m[qb] = self * a.c;
-            l[qb] = g == 0 ? 1.f : 0.f;
+            ws.m[qb] = self * a.c;
+            ws.l[qb] = g == 0 ? 1.f : 0.f;
 #pragma unroll
             for (int db = 0; db < T::DB; ++db) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int d0 = db * 32 + 8 * j + 4 * g;
-                    u32x2 raw = ok ? *reinterpret_cast<const u32x2 *>(vcs + (long)row * D + d0)
-                                   : u32x2{0, 0};
-                    const bf16x4 vv = __builtin_bit_cast(bf16x4, raw);
+                    const bf16x4 vv = __builtin_bit_cast(bf16x4, bload8(rvc, row * T::ROW_BYTES + d0 * 2));
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[db][qb][4 * j + e] = (float)vv[e];
+                    for (int e = 0; e < 4; ++e) ws.acc[db][qb][4 * j + e] = (float)vv[e];
                 }
             }
         }
     }
 
-    Stage<D> st;
-    if (ntiles > 0) {
-        stage_load<D>(st, ksrc, vsrc, 0, kend, tid);
-        if (PREFILL && q0 == 0) stage_store_pool<D>(st, pk, pv, 0, kend, tid);
-        stage_store_lds<D>(st, smem, tid);
-    }
-    __syncthreads();
+    // Per-lane LDS offsets.  K operand: row kb*32 + col, logical block 2*cc + g.
+    const int k_off0 = col * T::ROW_BYTES;
+    int k_xor[T::KC];
+#pragma unroll
+    for (int cc = 0; cc < T::KC; ++cc) k_xor[cc] = ((2 * cc + g) ^ k_swz<D>(col)) * 16;
+    // V transpose loads: in 16-lane group (g, sub), lane i addresses key 4g + i/4 (plus the
+    // chunk's key base) and head dims db*32 + 16*sub + 4*(i%4) .. +3.
+    const int ti = lane & 15, sub = (lane >> 4) & 1;
+    const int vkey = 4 * g + (ti >> 2);
+    const int v_off = vkey * T::ROW_BYTES + (ti & 1) * 8;
+    int v_blk[T::DB];
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+        v_blk[db] = ((db * 4 + 2 * sub + ((ti & 3) >> 1)) ^ v_swz<D>(vkey)) * 16;
 
-    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int kbase = t * kTK;
-        const bool has_next = t + 1 < ntiles;
-        if (has_next) stage_load<D>(st, ksrc, vsrc, kbase + kTK, kend, tid);
-
-        const bf16 *buf = smem + (t & 1) * T::BUF_ELEMS;
-        const bf16 *ks = buf;
-        const bf16 *vt = buf + T::K_ELEMS;
-
-        // A wave skips tiles it cannot see (causal) and waves with no valid row.
-        const bool active = wq0 < qlimit && (!PREFILL || kbase <= wq0 + kQW - 1);
-        if (active) {
-            // ---- S^T = K Q^T: 2 key blocks x 2 query blocks of 32x32.
-            f32x16 sc[2][2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) sc[kb][qb] = f32x16{};
-#pragma unroll
-            for (int c = 0; c < T::KC; ++c) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 ka = as_bf16x8(
-                        *reinterpret_cast<const u32x4 *>(ks + (kb * 32 + col) * T::KSTR + c * 16 + g * 8));
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb)
-                        sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][c], sc[kb][qb], 0, 0, 0);
-                }
-            }
-
-            // ---- mask: keys past the history, and (prefill) keys after the query.
-            const bool need_mask = (kbase + kTK > kend) || (PREFILL && kbase + kTK - 1 > wq0);
-            if (need_mask) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) {
-                        const int query = wq0 + qb * 32 + col;
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int key = kbase + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                            const bool off = key >= kend || (PREFILL && key > query);
-                            sc[kb][qb][i] = off ? -INFINITY : sc[kb][qb][i];
-                        }
-                    }
-            }
-
-            // ---- running max (log2 domain) with lazy rescale.
-            float mt[2];
-            bool grow = false;
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                float mx = sc[0][qb][0];
-#pragma unroll
-                for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[0][qb][i]);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[1][qb][i]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                mt[qb] = mx * a.c;
-                grow |= mt[qb] > m[qb] + kRescaleThreshold;
-            }
-            if (__any(grow)) {
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    const float mn = fmaxf(m[qb], mt[qb]);
-                    if (mt[qb] > m[qb] + kRescaleThreshold) {
-                        const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
-                        l[qb] *= alpha;
-#pragma unroll
-                        for (int db = 0; db < T::DB; ++db) acc[db][qb] *= alpha;
-                        m[qb] = mn;
-                    }
-                }
-            }
-
-            // ---- P = exp2(s*c - m), rounded to bf16 in the B-operand layout of the PV
-            // MFMA; the row sum takes the rounded values.
-            bf16x8 pb[2][2][2];  // [kb][chunk of 16 keys][qb]
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const float nm = -m[qb];
-                float lsum = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int c2 = 0; c2 < 2; ++c2) {
-                        bf16x8 p;
-#pragma unroll
-                        for (int e = 0; e < 8; e += 2) {
-                            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][c2 * 8 + e], a.c, nm));
-                            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][c2 * 8 + e + 1], a.c, nm));
-                            const bf16x2 pp = {(bf16)p0, (bf16)p1};
-                            p[e] = pp[0];
-                            p[e + 1] = pp[1];
-                            lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
-                        }
-                        pb[kb][c2][qb] = p;
-                    }
-                l[qb] += lsum;
-            }
-
-            // ---- O^T += V^T P^T.
-#pragma unroll
-            for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int c2 = 0; c2 < 2; ++c2) {
-                        const int d = db * 32 + col;
-                        const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-                            vt + vt_index(d, kb * 32 + c2 * 16 + g * 8)));
-#pragma unroll
-                        for (int qb = 0; qb < 2; ++qb)
-                            acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][c2][qb], acc[db][qb], 0, 0, 0);
-                    }
-        }
-
-        if (has_next) {
-            if (PREFILL && kbase + kTK >= q0) stage_store_pool<D>(st, pk, pv, kbase + kTK, kend, tid);
-            stage_store_lds<D>(st, smem + ((t + 1) & 1) * T::BUF_ELEMS, tid);
-        }
+    // Tiles [0, t_plain) need no mask for any wave of the block: they end before the
+    // history end and (prefill) at or before the block's first query.  The remaining
+    // tiles run the masked step; a wave skips tiles that lie wholly after its queries.
+    const int t_plain = PREFILL ? min(kend / kTK, q0 / kTK) : kend / kTK;
+    const bool wave_rows_valid = wq0 < qlimit;
+    auto pipeline = [&](int t) {
+        if (t + 1 < ntiles) wait_vmcnt<T::DMA_PER_WAVE>(); else wait_vmcnt<0>();
         __syncthreads();
+        if (t + 2 < ntiles) dma_tile<D>(smem + ((t + 2) % kBufs) * T::BUF_BYTES, rk, rv, (t + 2) * kTK, wave, lane);
+    };
+    for (int t = 0; t < t_plain; ++t) {
+        pipeline(t);
+        const LDS_AS char *kt = smem + (t % kBufs) * T::BUF_BYTES;
+        if (wave_rows_valid)
+            tile_step<D, PREFILL, false>(ws, kt, kt + T::MAT_BYTES, t * kTK, kend, wq0, col, g,
+                                         k_off0, k_xor, v_off, v_blk, a.c);
+    }
+    for (int t = t_plain; t < ntiles; ++t) {
+        pipeline(t);
+        const int kbase = t * kTK;
+        const LDS_AS char *kt = smem + (t % kBufs) * T::BUF_BYTES;
+        if (wave_rows_valid && (!PREFILL || kbase <= wq0 + kQW - 1))
+            tile_step<D, PREFILL, true>(ws, kt, kt + T::MAT_BYTES, kbase, kend, wq0, col, g,
+                                        k_off0, k_xor, v_off, v_blk, a.c);
     }
 
     // ---- epilogue: combine the two halves' row sums, normalise, store bf16 rows.
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        const float lt = l[qb] + __shfl_xor(l[qb], 32);
+        const float lt = ws.l[qb] + __shfl_xor(ws.l[qb], 32);
         const float inv = 1.f / lt;
         const int row = wq0 + qb * 32 + col;
         if (row < qlimit) {
@@ -446,11 +438,32 @@ __global__ void __launch_bounds__(kThreads, D <= 64 ? 2 : 1) attn_bf16_kernel(At
                     const int d0 = db * 32 + 8 * j + 4 * g;
                     bf16x4 ov;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) ov[e] = (bf16)(acc[db][qb][4 * j + e] * inv);
+                    for (int e = 0; e < 4; ++e) ov[e] = (bf16)(ws.acc[db][qb][4 * j + e] * inv);
                     *reinterpret_cast<u32x2 *>(odst + (long)row * D + d0) = __builtin_bit_cast(u32x2, ov);
                 }
         }
     }
+
+    // ---- prefill: fused pool write of this block's own history rows, bit for bit.
+    if constexpr (PREFILL) {
+        const int r1 = min(q0 + kQT, N);
+        const int chunks = (r1 - q0) * T::R;
+        for (int i = tid; i < chunks; i += kThreads) {
+            const long off = (long)q0 * D + (long)i * 8;
+            *reinterpret_cast<u32x4 *>(pk + off) = *reinterpret_cast<const u32x4 *>(ksrc + off);
+            *reinterpret_cast<u32x4 *>(pv + off) = *reinterpret_cast<const u32x4 *>(vsrc + off);
+        }
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, D <= 64 ? 2 : 1) prefill_bf16_kernel(AttnArgs a) {
+    attn_body<D, true>(a);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, D <= 64 ? 2 : 1) rank_decode_bf16_kernel(AttnArgs a) {
+    attn_body<D, false>(a);
 }
 
 template <bool PREFILL>
@@ -459,12 +472,16 @@ hipError_t launch_bf16(const AttnArgs &a, int D, hipStream_t stream) {
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks), block(kThreads);
+#define UNIPIN_LAUNCH(DD)                                                                      \
+    if (PREFILL) hipLaunchKernelGGL(prefill_bf16_kernel<DD>, grid, block, 0, stream, a);       \
+    else hipLaunchKernelGGL(rank_decode_bf16_kernel<DD>, grid, block, 0, stream, a);
     switch (D) {
-        case 32: hipLaunchKernelGGL((attn_bf16_kernel<32, PREFILL>), grid, block, 0, stream, a); break;
-        case 64: hipLaunchKernelGGL((attn_bf16_kernel<64, PREFILL>), grid, block, 0, stream, a); break;
-        case 128: hipLaunchKernelGGL((attn_bf16_kernel<128, PREFILL>), grid, block, 0, stream, a); break;
+        case 32: UNIPIN_LAUNCH(32) break;
+        case 64: UNIPIN_LAUNCH(64) break;
+        case 128: UNIPIN_LAUNCH(128) break;
         default: return hipErrorInvalidValue;
     }
+#undef UNIPIN_LAUNCH
     return hipGetLastError();
 }
 
