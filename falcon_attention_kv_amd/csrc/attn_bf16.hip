@@ -5,16 +5,17 @@
 // sections 3 and 6): history tokens attend causally; each candidate attends to every
 // cached history key of its user plus its own key, never to another candidate.
 //
-// Work decomposition (both kernels):
-//   * one workgroup = 4 waves of 64 lanes; each wave owns 64 query rows, held in
-//     registers for the whole kernel as the B operand of v_mfma_f32_32x32x16_bf16;
+// Work decomposition:
+//   * a workgroup = 4 waves of 64 lanes; each wave owns 64 query rows, held in
+//     registers as the B operand of v_mfma_f32_32x32x16_bf16;
 //   * 64-key tiles of K and V are copied HBM -> LDS by the buffer-to-LDS DMA path
-//     (buffer_load_dwordx4 ... lds), three tiles in flight: no staging registers, no
-//     VALU work, and every row past the history reads as zero (the buffer's record
-//     count is the history length), so ragged histories need no branches;
+//     (buffer_load_dwordx4 ... lds) into a ring of LDS buffers, up to three tiles ahead
+//     of use: no staging registers, no VALU work, and every row past the history reads
+//     as zero (the buffer's record count is the history length), so ragged histories
+//     need no branches;
 //   * scores are computed transposed, S^T = K Q^T, so that in the MFMA result each lane
 //     holds one query and 16 keys: softmax row statistics are lane-local plus one
-//     exchange with the lane 32 away;
+//     v_permlane32_swap with the lane 32 away;
 //   * the PV product is computed as O^T = V^T P^T: P^T, rounded to bf16, is used in the
 //     very registers the score MFMA left it in; V stays in its natural [key][d] layout
 //     in LDS and ds_read_b64_tr_b16 delivers it transposed;
@@ -23,7 +24,13 @@
 //     than 2^8, which bounds P by 256 and skips almost every rescale;
 //   * the row sum is accumulated from the bf16-rounded P (v_dot2 with ones), so the
 //     normaliser matches the weights the PV product used;
-//   * masking code runs only on tiles that cross the history end or the causal diagonal.
+//   * masking runs only on tiles that cross the history end or the causal diagonal.
+//
+// The prefill launches one workgroup per (user, head, 256-row query tile).  The ranking
+// decode's workgroups each walk a sequence of (user, head, 256-candidate tile) items
+// with a K/V DMA ring that runs on across item boundaries; the default launch gives
+// every item its own workgroup, and a persistent grid (a few workgroups per CU) is a
+// build-time option.
 //
 // Hardware facts relied on (checked on gfx950 with small in-bounds probes):
 //   * v_mfma_f32_32x32x16_bf16 result element i of lane l is row 8*(i/4) + 4*(l/32)
@@ -33,7 +40,9 @@
 //   * ds_read_b64_tr_b16: in each group of 16 lanes, lane c receives element c%4 of the
 //     8-byte rows addressed by lanes 4e + c/4 (e = 0..3): a 4 x 16 -> 16 x 4 transpose;
 //   * buffer loads to LDS write 16 bytes per lane at consecutive LDS addresses (M0 base
-//     + 16 * lane) and write zeros for offsets past the record count.
+//     + 16 * lane) and write zeros for offsets past the record count;
+//   * a wave's vector-memory loads complete in issue order, so waiting until at most X
+//     loads are outstanding guarantees every load older than the X most recent.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -53,14 +62,30 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;                 // waves per workgroup
-constexpr int kThreads = kWaves * 64;
 constexpr int kQW = 64;                   // query rows per wave
-constexpr int kQT = kWaves * kQW;         // query rows per workgroup
 constexpr int kTK = 64;                   // keys per LDS tile
-constexpr int kBufs = 3;                  // LDS tiles in flight
-static_assert(kQT == kBf16RowsPerBlock, "rows per block must match the host's grid math");
-static_assert(kQT % kTK == 0, "a query tile must cover whole key tiles");
+constexpr int kBufs = 4;                  // LDS tile buffers
+// Tiles whose DMA is in flight beyond the one in use.  A tile is finished before the
+// barrier that makes the next one current, so the DMA issued at that barrier may reuse
+// the finished tile's buffer: with 4 buffers, 3 tiles ahead.
+constexpr int kAhead = 3;
+
+// Waves per workgroup: 4 (a 256-row query tile) for both kernels.  At D <= 64 two
+// workgroups share a CU (2 waves per SIMD, 256 registers per lane each); at D = 128 a
+// wave needs the whole register file.  Build-time knobs for tuning: the decode's waves
+// per workgroup, and its grid (workgroups resident per CU for a persistent grid, or 0
+// for one workgroup per work item, which measured fastest).
+#ifndef UNIPIN_DECODE_WAVES
+#define UNIPIN_DECODE_WAVES 4
+#endif
+#ifndef UNIPIN_DECODE_GRID_PER_CU
+#define UNIPIN_DECODE_GRID_PER_CU 0
+#endif
+template <int D> constexpr int prefill_waves() { return 4; }
+template <int D> constexpr int decode_waves() { return D <= 64 ? UNIPIN_DECODE_WAVES : 4; }
+// Minimum resident workgroups per CU the decode is compiled for: 2 waves per SIMD at
+// D <= 64, 1 at D = 128.
+template <int D> constexpr int decode_min_blocks() { return D <= 64 ? 8 / decode_waves<D>() : 1; }
 
 constexpr uint32_t kBufferWord3 = 0x00020000u;   // gfx9 buffer descriptor, raw 32-bit access
 
@@ -76,25 +101,51 @@ struct Tile {
     static constexpr int MAT_BYTES = kTK * ROW_BYTES;  // one K or V tile
     static constexpr int BUF_BYTES = 2 * MAT_BYTES;    // K tile then V tile
     static constexpr int DMA_PER_MAT = MAT_BYTES / 1024;              // 1 KB per wave-wide DMA
-    static constexpr int DMA_PER_WAVE = 2 * DMA_PER_MAT / kWaves;     // per wave per tile
-    static_assert(2 * DMA_PER_MAT % kWaves == 0, "tile DMA must split evenly over the waves");
 };
 
-// 16-byte block swizzles inside a key row (XOR keeps the block inside the row).  K is
-// read 8 lanes at a time, one row each, same logical block; V is read with transpose
-// loads, 16 lanes covering 4 consecutive rows x 32 bytes.  Both patterns then touch
-// every LDS bank exactly once.
+// DMA work split of one K/V tile over W waves: the first W/2 waves move K, the others V.
+template <int D, int W>
+struct KvDma {
+    static constexpr int PER_WAVE = 2 * Tile<D>::DMA_PER_MAT / W;
+    static_assert(PER_WAVE >= 1 && 2 * Tile<D>::DMA_PER_MAT == PER_WAVE * W, "tile DMA must split evenly");
+};
+
+// 16-byte block swizzles inside a key row (XOR keeps the block inside the row).  The
+// gfx950 LDS has 64 four-byte banks: a 16-byte-per-lane read is served 16 lanes at a
+// time, an 8-byte transpose read 32 lanes at a time.  K is read 16 rows at a time, same
+// logical block; V with transpose loads, 4 consecutive rows x 64 bytes per 32 lanes.
+// These swizzles put each such group on 64 distinct banks.
 template <int D>
 __device__ __forceinline__ int k_swz(int key) {
-    return Tile<D>::R >= 8 ? (key & 7) : ((key >> 1) & 3);
+    constexpr int R = Tile<D>::R;
+    return R >= 16 ? (key & 15) : R == 8 ? ((key >> 1) & 7) : ((key >> 2) & 3);
 }
 template <int D>
 __device__ __forceinline__ int v_swz(int key) {
-    return Tile<D>::R >= 8 ? ((key & 3) << 1) : (((key >> 1) & 1) << 1);
+    constexpr int R = Tile<D>::R;
+    return R >= 16 ? ((key & 3) << 2) : R == 8 ? (((key >> 1) & 1) << 2) : 0;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, (int)kBufferWord3);
+}
+
+// Buffer descriptor as four scalar words, for the DMA issued from inline assembly.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
+    const uint64_t addr = reinterpret_cast<uint64_t>(base);
+    return i32x4{(int)(uint32_t)addr, (int)((uint32_t)(addr >> 32) & 0xffffu), (int)bytes, (int)kBufferWord3};
+}
+
+// One 16-byte-per-lane buffer-to-LDS DMA: lane l writes LDS bytes [lds + 16 l, +16) from
+// buffer offset voff + soff (zeros past the record count).  It is issued from inline
+// assembly so that the compiler does not treat it as a pending write to every LDS
+// address (which makes it wait for all outstanding DMA before each LDS read and defeats
+// the prefetch); the kernels wait for it explicitly (vmcnt, then a workgroup barrier).
+// The instruction has no register results and reads its operands at issue.
+__device__ __forceinline__ void dma16(uint32_t lds, i32x4 rsrc, int voff, int soff) {
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
+                 : "memory");
 }
 
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -114,58 +165,108 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
-// DMA of one K/V tile (keys kbase .. kbase+63) into LDS buffer `buf`.  Wave w moves
-// its share of the 1 KB pieces; lane l of piece j fills LDS block 64*j + l, i.e. key row
-// (64*j + l) / R, swizzled block (64*j + l) % R, taken from the matching unswizzled block.
-template <int D>
-__device__ __forceinline__ void dma_tile(LDS_AS char *buf, __amdgpu_buffer_rsrc_t rk,
-                                         __amdgpu_buffer_rsrc_t rv, int kbase, int wave, int lane) {
+// Waits until the tile in use has landed, allowing the `tiles_after` tiles issued after
+// it (at most kAhead - 1) to stay in flight.  Other loads issued after it only make the
+// wait longer, never shorter, since loads complete in issue order.
+template <int DPW>
+__device__ __forceinline__ void wait_tiles_after(int tiles_after) {
+    static_assert(kAhead == 3, "the cases below cover up to two tiles after the one in use");
+    if (tiles_after >= 2) wait_vmcnt<2 * DPW>();
+    else if (tiles_after == 1) wait_vmcnt<DPW>();
+    else wait_vmcnt<0>();
+}
+
+// Value exchange with the lane 32 away (v_permlane32_swap: no LDS round trip).  r[0]
+// holds the lower half's value in both halves, r[1] the upper half's.
+__device__ __forceinline__ float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Per-lane source offsets of this wave's DMA pieces within a tile.  Piece j of wave w
+// moves 1 KB: lane l fills LDS block 64*pj + l of its matrix (pj = the piece's index
+// within that matrix), i.e. key row (64*pj + l) / R at swizzled block (64*pj + l) % R,
+// taken from the matching unswizzled 16-byte block of that row.
+template <int D, int W>
+__device__ __forceinline__ void dma_offsets(int (&voff)[(KvDma<D, W>::PER_WAVE)], int wave, int lane) {
     using T = Tile<D>;
 #pragma unroll
-    for (int j = 0; j < T::DMA_PER_WAVE; ++j) {
-        const int piece = wave * T::DMA_PER_WAVE + j;          // wave-uniform
+    for (int j = 0; j < KvDma<D, W>::PER_WAVE; ++j) {
+        const int piece = wave * KvDma<D, W>::PER_WAVE + j;
         const bool is_v = piece >= T::DMA_PER_MAT;
         const int pj = is_v ? piece - T::DMA_PER_MAT : piece;
         const int p = pj * 64 + lane;
         const int key = p / T::R, blks = p % T::R;
         const int blk = blks ^ (is_v ? v_swz<D>(key) : k_swz<D>(key));
-        const uint32_t goff = (uint32_t)((kbase + key) * T::ROW_BYTES + blk * 16);
-        LDS_AS char *dst = buf + (is_v ? T::MAT_BYTES : 0) + pj * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_v ? rv : rk, (LDS_AS void *)dst, 16, (int)goff, 0, 0, 0);
+        voff[j] = key * T::ROW_BYTES + blk * 16;
     }
 }
 
-// Maps the linear block id to (user*H + head, query tile).  With xcd_remap, blocks are
-// dispatched round-robin over the 8 XCDs; the map makes the `tiles` consecutive blocks
-// an XCD receives belong to one (user, head), so that its K/V is fetched from HBM once
-// into that XCD's L2 and re-read from there by the other tiles.
-__device__ __forceinline__ void block_coords(const AttnArgs &a, int &group, int &tile) {
-    const int bid = blockIdx.x;
-    if (a.xcd_remap) {
-        const int xcd = bid & 7, local = bid >> 3;
-        group = (local / a.tiles) * 8 + xcd;
-        tile = local % a.tiles;
-    } else {
-        group = bid / a.tiles;
-        tile = bid % a.tiles;
-    }
+// DMA of this wave's share of one K/V tile (keys kbase .. kbase+63) into LDS buffer
+// `buf`; `rsrc` is the K or V buffer of the wave's half.
+template <int D, int W>
+__device__ __forceinline__ void dma_tile(LDS_AS char *buf, i32x4 rsrc, int kbase,
+                                         const int (&voff)[(KvDma<D, W>::PER_WAVE)], int wave) {
+    using T = Tile<D>;
+    const bool is_v = wave >= W / 2;
+    const int first = wave * KvDma<D, W>::PER_WAVE - (is_v ? T::DMA_PER_MAT : 0);
+    const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(buf) + (is_v ? T::MAT_BYTES : 0) + first * 1024;
+    const int soff = kbase * T::ROW_BYTES;
+#pragma unroll
+    for (int j = 0; j < KvDma<D, W>::PER_WAVE; ++j) dma16(dst + j * 1024, rsrc, voff[j], soff);
 }
 
-// Per-wave attention state and the per-tile step.
+// Per-wave attention state.
 template <int D>
 struct WaveState {
-    bf16x8 qreg[2][Tile<D>::KC];   // B operand: query rows wq0 + qb*32 + col, dims c*16 + g*8 ..
+    bf16x8 qreg[2][Tile<D>::KC];   // B operand: query rows wq0 + qb*32 + col, dims cc*16 + g*8 ..
     f32x16 acc[Tile<D>::DB][2];    // O^T accumulators: lane = query, 16 head dims per block
     float m[2];                    // running max (log2 domain), shared by both lane halves
     float l[2];                    // this lane half's share of the row sum
 };
 
-template <int D, bool PREFILL, bool MASK>
-__device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *kt, const LDS_AS char *vt,
-                                          int kbase, int kend, int wq0, int col, int g,
-                                          int k_off0, const int *k_xor, int v_off, const int *v_blk, float c) {
+// Per-lane LDS addressing of the operand reads, fixed for the whole kernel.
+template <int D>
+struct LaneAddr {
+    int k_off0;                 // K operand: row col of the block
+    int k_xor[Tile<D>::KC];     // swizzled 16-byte block 2*cc + g of that row
+    int v_off;                  // V transpose loads: key 4g + i/4, byte (i%2)*8 of the block
+    int v_blk[Tile<D>::DB];     // swizzled block of head dims db*32 + 16*sub + 4*(i%4)
+};
+
+template <int D>
+__device__ __forceinline__ LaneAddr<D> lane_addr(int lane) {
     using T = Tile<D>;
-    // ---- S^T = K Q^T: 2 key blocks x 2 query blocks of 32x32.
+    const int col = lane & 31, g = lane >> 5;
+    LaneAddr<D> la;
+    la.k_off0 = col * T::ROW_BYTES;
+#pragma unroll
+    for (int cc = 0; cc < T::KC; ++cc) la.k_xor[cc] = ((2 * cc + g) ^ k_swz<D>(col)) * 16;
+    // V transpose loads: in 16-lane group (g, sub), lane i addresses key 4g + i/4 (plus the
+    // chunk's key base) and head dims db*32 + 16*sub + 4*(i%4) .. +3.
+    const int ti = lane & 15, sub = (lane >> 4) & 1;
+    const int vkey = 4 * g + (ti >> 2);
+    la.v_off = vkey * T::ROW_BYTES + (ti & 1) * 8;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+        la.v_blk[db] = ((db * 4 + 2 * sub + ((ti & 3) >> 1)) ^ v_swz<D>(vkey)) * 16;
+    return la;
+}
+
+// One 64-key tile: S^T = K Q^T (2 key blocks x 2 query blocks), optional mask, running
+// max with lazy rescale, P in bf16, row sums, O^T += V^T P^T.
+// Masking: element i of block (kb, qb) is key kbase + kb*32 + 4g + off(i),
+// off(i) = 8*(i/4) + i%4; it is visible iff off(i) <= lim, with lim from the history end
+// and, for the prefill, the query's own position.
+template <int D, bool PREFILL>
+__device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *kt, const LDS_AS char *vt,
+                                          int kbase, int kend, int wq0, bool masked,
+                                          const LaneAddr<D> &la, int col, int g, float c) {
+    using T = Tile<D>;
     f32x16 sc[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -175,17 +276,14 @@ __device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *k
     for (int cc = 0; cc < T::KC; ++cc) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 ka = *reinterpret_cast<const LDS_AS bf16x8 *>(kt + k_off0 + kb * 32 * T::ROW_BYTES + k_xor[cc]);
+            const bf16x8 ka = *reinterpret_cast<const LDS_AS bf16x8 *>(kt + la.k_off0 + kb * 32 * T::ROW_BYTES + la.k_xor[cc]);
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
                 sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, ws.qreg[qb][cc], sc[kb][qb], 0, 0, 0);
         }
     }
 
-    // ---- mask: keys past the history, and (prefill) keys after the query.  Element i
-    // of block (kb, qb) is key kbase + kb*32 + 4g + off(i), off(i) = 8*(i/4) + i%4, so
-    // one per-lane bound per block decides all 16: the key is visible iff off(i) <= lim.
-    if constexpr (MASK) {
+    if (masked) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -201,8 +299,8 @@ __device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *k
             }
     }
 
-    // ---- running max (log2 domain) with lazy rescale.  The rescale branch is wave-wide
-    // and rare (first visible tile, or a late jump of the max by more than 2^8).
+    // running max (log2 domain) with lazy rescale: the branch is wave-wide and rare
+    // (first visible tile, or a late jump of the max by more than 2^8).
     float mt[2];
     bool grow[2];
 #pragma unroll
@@ -212,8 +310,7 @@ __device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *k
         for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[0][qb][i]);
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[1][qb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        mt[qb] = mx * c;
+        mt[qb] = half_max(mx) * c;
         grow[qb] = mt[qb] > ws.m[qb] + kRescaleThreshold;
     }
     if (__any(grow[0] || grow[1])) {
@@ -230,11 +327,11 @@ __device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *k
         }
     }
 
-    // ---- per 32-key block: P = exp2(s*c - m), rounded to bf16 in the B-operand layout
-    // of the PV MFMA (the row sum takes the rounded values), then O^T += V^T P^T.
-    // Lane (d, g) needs, for chunk (kb, c2), V at keys kb*32 + 16*c2 + {4g..4g+3}
-    // (elements 0..3) and kb*32 + 16*c2 + 8 + {4g..4g+3} (elements 4..7): two transpose
-    // loads of 4 keys x 16 dims each.
+    // per 32-key block: P = exp2(s*c - m), rounded to bf16 in the B-operand layout of
+    // the PV MFMA (the row sum takes the rounded values), then O^T += V^T P^T.  Lane
+    // (d, g) needs, for chunk (kb, c2), V at keys kb*32 + 16*c2 + {4g..4g+3} (elements
+    // 0..3) and kb*32 + 16*c2 + 8 + {4g..4g+3} (elements 4..7): two transpose loads of 4
+    // keys x 16 dims each.
     const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -263,7 +360,7 @@ __device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *k
         for (int db = 0; db < T::DB; ++db)
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
-                const LDS_AS char *src = vt + v_off + v_blk[db] + (kb * 32 + 16 * c2) * T::ROW_BYTES;
+                const LDS_AS char *src = vt + la.v_off + la.v_blk[db] + (kb * 32 + 16 * c2) * T::ROW_BYTES;
                 const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)src);
                 const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(src + 8 * T::ROW_BYTES));
                 const i16x4 lh[2] = {lo, hi};
@@ -275,58 +372,29 @@ __device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *k
     }
 }
 
-template <int D, bool PREFILL>
-__device__ __forceinline__ void attn_body(const AttnArgs &a) {
+
+// Runs the wave over K/V tiles 0 .. ntiles-1.  next_tile(u) makes tile u current (wait
+// for its DMA, workgroup barrier, further DMA) and returns its LDS buffer; every wave
+// calls it for every tile.  The wave computes tiles 0 .. tlast only (tlast < 0: none).
+// Tiles that reach kend (or, for the prefill, cross the causal diagonal) are masked.
+template <int D, bool PREFILL, class NextTile>
+__device__ __forceinline__ void run_tiles(WaveState<D> &ws, int ntiles, int tlast, int kend, int wq0,
+                                          const LaneAddr<D> &la, int col, int g, float c, NextTile &&next_tile) {
     using T = Tile<D>;
-    __shared__ __attribute__((aligned(1024))) char smem_raw[kBufs * T::BUF_BYTES];
-    LDS_AS char *smem = (LDS_AS char *)smem_raw;
-
-    int group, tile;
-    block_coords(a, group, tile);
-    const int b = group / a.H, h = group % a.H;
-    if (b >= a.B) return;
-    // Causal prefill: hand out the heaviest (last) query tiles first.
-    const int qtile = PREFILL ? (a.tiles - 1 - tile) : tile;
-
-    const int N = a.lens[b];
-    const int s = a.slot[b];
-    if (N < 0 || N > a.len_limit || s < 0 || s >= a.S) {
-        if (threadIdx.x == 0 && tile == 0)
-            atomicOr(a.status, (N < 0 || N > a.len_limit ? kFlagBadLen : 0u) |
-                                   (s < 0 || s >= a.S ? kFlagBadSlot : 0u));
-        return;
+    for (int t = 0; t < ntiles; ++t) {
+        const LDS_AS char *kt = next_tile(t);
+        if (t <= tlast) {
+            const bool masked = t * kTK + kTK > kend || (PREFILL && t * kTK + kTK - 1 > wq0);
+            tile_step<D, PREFILL>(ws, kt, kt + T::MAT_BYTES, t * kTK, kend, wq0, masked, la, col, g, c);
+        }
     }
+}
 
-    const int q0 = qtile * kQT;
-    const int qlimit = PREFILL ? N : a.rows;   // valid query rows are < qlimit
-    if (q0 >= qlimit) return;
-
-    const long bh = (long)b * a.H + h;
-    const bf16 *qsrc = static_cast<const bf16 *>(a.q) + bh * a.rows * D;
-    bf16 *odst = static_cast<bf16 *>(a.o) + bh * a.rows * D;
-    const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
-    bf16 *pk = static_cast<bf16 *>(a.pool_k) + slot_off;
-    bf16 *pv = static_cast<bf16 *>(a.pool_v) + slot_off;
-    // Key/value source: the history inputs (prefill) or the pool slot (decode).
-    const bf16 *ksrc = PREFILL ? static_cast<const bf16 *>(a.k) + bh * a.rows * D : pk;
-    const bf16 *vsrc = PREFILL ? static_cast<const bf16 *>(a.v) + bh * a.rows * D : pv;
-    const int kend = PREFILL ? min(q0 + kQT, N) : N;
-    const int ntiles = (kend + kTK - 1) / kTK;
-    // Rows at or past kend read as zeros.
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(ksrc, (uint32_t)kend * T::ROW_BYTES);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vsrc, (uint32_t)kend * T::ROW_BYTES);
-
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int col = lane & 31, g = lane >> 5;
-    const int wq0 = q0 + wave * kQW;
-
-    // Start the first two tiles' DMA before anything else.
-    if (ntiles > 0) dma_tile<D>(smem, rk, rv, 0, wave, lane);
-    if (ntiles > 1) dma_tile<D>(smem + T::BUF_BYTES, rk, rv, kTK, wave, lane);
-
-    WaveState<D> ws;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qsrc, (uint32_t)qlimit * T::ROW_BYTES);
+// Loads the wave's 64 query rows (rows >= qlimit read as zeros).
+template <int D>
+__device__ __forceinline__ void load_q(WaveState<D> &ws, const bf16 *qsrc, int qlimit, int wq0, int col, int g) {
+    using T = Tile<D>;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qsrc, (uint32_t)max(qlimit, 0) * T::ROW_BYTES);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         const uint32_t row = (uint32_t)(wq0 + qb * 32 + col);
@@ -334,101 +402,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a) {
         for (int cc = 0; cc < T::KC; ++cc)
             ws.qreg[qb][cc] = as_bf16x8(bload16(rq, row * T::ROW_BYTES + cc * 32 + g * 16));
     }
+}
 
-    if constexpr (PREFILL) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            ws.m[qb] = -INFINITY;
-            ws.l[qb] = 0.f;
-#pragma unroll
-            for (int db = 0; db < T::DB; ++db) ws.acc[db][qb] = f32x16{};
-        }
-    } else {
-        // The candidate's own key enters first: it sets the running max, contributes
-        // weight exp2(0) = 1 to the row sum (counted once, by the lower half) and its
-        // value vc_j to the accumulator.  An empty history therefore yields vc_j exactly.
-        const __amdgpu_buffer_rsrc_t rkc =
-            make_rsrc(static_cast<const bf16 *>(a.k) + bh * a.rows * D, (uint32_t)qlimit * T::ROW_BYTES);
-        const __amdgpu_buffer_rsrc_t rvc =
-            make_rsrc(static_cast<const bf16 *>(a.v) + bh * a.rows * D, (uint32_t)qlimit * T::ROW_BYTES);
-        const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
-        (void)ones;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const uint32_t row = (uint32_t)(wq0 + qb * 32 + col);
-            float part = 0.f;
-#pragma unroll
-            for (int cc = 0; cc < T::KC; ++cc) {
-                const bf16x8 kk = as_bf16x8(bload16(rkc, row * T::ROW_BYTES + cc * 32 + g * 16));
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const bf16x2 qa = {ws.qreg[qb][cc][e], ws.qreg[qb][cc][e + 1]};
-                    const bf16x2 ka = {kk[e], kk[e + 1]};
-                    part = __builtin_amdgcn_fdot2_f32_bf16(qa, ka, part, false);
-                }
-            }
-            const float self = part + __shfl_xor(part, 32);
-            ws.m[qb] = self * a.c;
-            ws.l[qb] = g == 0 ? 1.f : 0.f;
-#pragma unroll
-            for (int db = 0; db < T::DB; ++db) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int d0 = db * 32 + 8 * j + 4 * g;
-                    const bf16x4 vv = __builtin_bit_cast(bf16x4, bload8(rvc, row * T::ROW_BYTES + d0 * 2));
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) ws.acc[db][qb][4 * j + e] = (float)vv[e];
-                }
-            }
-        }
-    }
-
-    // Per-lane LDS offsets.  K operand: row kb*32 + col, logical block 2*cc + g.
-    const int k_off0 = col * T::ROW_BYTES;
-    int k_xor[T::KC];
-#pragma unroll
-    for (int cc = 0; cc < T::KC; ++cc) k_xor[cc] = ((2 * cc + g) ^ k_swz<D>(col)) * 16;
-    // V transpose loads: in 16-lane group (g, sub), lane i addresses key 4g + i/4 (plus the
-    // chunk's key base) and head dims db*32 + 16*sub + 4*(i%4) .. +3.
-    const int ti = lane & 15, sub = (lane >> 4) & 1;
-    const int vkey = 4 * g + (ti >> 2);
-    const int v_off = vkey * T::ROW_BYTES + (ti & 1) * 8;
-    int v_blk[T::DB];
-#pragma unroll
-    for (int db = 0; db < T::DB; ++db)
-        v_blk[db] = ((db * 4 + 2 * sub + ((ti & 3) >> 1)) ^ v_swz<D>(vkey)) * 16;
-
-    // Tiles [0, t_plain) need no mask for any wave of the block: they end before the
-    // history end and (prefill) at or before the block's first query.  The remaining
-    // tiles run the masked step; a wave skips tiles that lie wholly after its queries.
-    const int t_plain = PREFILL ? min(kend / kTK, q0 / kTK) : kend / kTK;
-    const bool wave_rows_valid = wq0 < qlimit;
-    auto pipeline = [&](int t) {
-        if (t + 1 < ntiles) wait_vmcnt<T::DMA_PER_WAVE>(); else wait_vmcnt<0>();
-        __syncthreads();
-        if (t + 2 < ntiles) dma_tile<D>(smem + ((t + 2) % kBufs) * T::BUF_BYTES, rk, rv, (t + 2) * kTK, wave, lane);
-    };
-    for (int t = 0; t < t_plain; ++t) {
-        pipeline(t);
-        const LDS_AS char *kt = smem + (t % kBufs) * T::BUF_BYTES;
-        if (wave_rows_valid)
-            tile_step<D, PREFILL, false>(ws, kt, kt + T::MAT_BYTES, t * kTK, kend, wq0, col, g,
-                                         k_off0, k_xor, v_off, v_blk, a.c);
-    }
-    for (int t = t_plain; t < ntiles; ++t) {
-        pipeline(t);
-        const int kbase = t * kTK;
-        const LDS_AS char *kt = smem + (t % kBufs) * T::BUF_BYTES;
-        if (wave_rows_valid && (!PREFILL || kbase <= wq0 + kQW - 1))
-            tile_step<D, PREFILL, true>(ws, kt, kt + T::MAT_BYTES, kbase, kend, wq0, col, g,
-                                        k_off0, k_xor, v_off, v_blk, a.c);
-    }
-
-    // ---- epilogue: combine the two halves' row sums, normalise, store bf16 rows.
+// Normalises and stores the wave's rows (< qlimit) of O^T as bf16 rows of o.
+template <int D>
+__device__ __forceinline__ void store_o(const WaveState<D> &ws, bf16 *odst, int qlimit, int wq0, int col, int g) {
+    using T = Tile<D>;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        const float lt = ws.l[qb] + __shfl_xor(ws.l[qb], 32);
-        const float inv = 1.f / lt;
+        const float inv = 1.f / half_sum(ws.l[qb]);
         const int row = wq0 + qb * 32 + col;
         if (row < qlimit) {
 #pragma unroll
@@ -443,56 +425,328 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a) {
                 }
         }
     }
+}
 
-    // ---- prefill: fused pool write of this block's own history rows, bit for bit.
-    if constexpr (PREFILL) {
-        const int r1 = min(q0 + kQT, N);
-        const int chunks = (r1 - q0) * T::R;
-        for (int i = tid; i < chunks; i += kThreads) {
-            const long off = (long)q0 * D + (long)i * 8;
-            *reinterpret_cast<u32x4 *>(pk + off) = *reinterpret_cast<const u32x4 *>(ksrc + off);
-            *reinterpret_cast<u32x4 *>(pv + off) = *reinterpret_cast<const u32x4 *>(vsrc + off);
+__device__ __forceinline__ bool user_valid(const AttnArgs &a, int N, int s, bool report) {
+    const bool bad_len = N < 0 || N > a.len_limit;
+    const bool bad_slot = s < 0 || s >= a.S;
+    if ((bad_len || bad_slot) && report && threadIdx.x == 0)
+        atomicOr(a.status, (bad_len ? kFlagBadLen : 0u) | (bad_slot ? kFlagBadSlot : 0u));
+    return !(bad_len || bad_slot);
+}
+
+// ------------------------------------------------------------------ causal prefill
+
+// Maps the linear block id to (user*H + head, query tile).  With xcd_remap, blocks are
+// dispatched round-robin over the 8 XCDs; the map makes the `tiles` consecutive blocks
+// an XCD receives belong to one (user, head), so that its K/V is fetched from HBM once
+// into that XCD's L2 and re-read from there by the other tiles.
+__device__ __forceinline__ void block_coords(const AttnArgs &a, int &group, int &tile) {
+    const int bid = blockIdx.x;
+    if (a.xcd_remap) {
+        const int xcd = bid & 7, local = bid >> 3;
+        group = (local / a.tiles) * 8 + xcd;
+        tile = local % a.tiles;
+    } else {
+        group = bid / a.tiles;
+        tile = bid % a.tiles;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *__restrict__ lens,
+                                             const int32_t *__restrict__ slots) {
+    using T = Tile<D>;
+    constexpr int W = prefill_waves<D>();
+    constexpr int QT = W * kQW;
+    constexpr int DPW = KvDma<D, W>::PER_WAVE;
+    static_assert(QT % kTK == 0, "a query tile must cover whole key tiles");
+    __shared__ __attribute__((aligned(1024))) char smem_raw[kBufs * T::BUF_BYTES];
+    LDS_AS char *smem = (LDS_AS char *)smem_raw;
+
+    int group, tile;
+    block_coords(a, group, tile);
+    const int b = group / a.H, h = group % a.H;
+    if (b >= a.B) return;
+    const int qtile = a.tiles - 1 - tile;   // heaviest (last) query tiles first
+    const int N = lens[b];
+    const int s = slots[b];
+    if (!user_valid(a, N, s, tile == 0)) return;
+    const int q0 = qtile * QT;
+    if (q0 >= N) return;
+
+    const long bh = (long)b * a.H + h;
+    const bf16 *qsrc = static_cast<const bf16 *>(a.q) + bh * a.rows * D;
+    const bf16 *ksrc = static_cast<const bf16 *>(a.k) + bh * a.rows * D;
+    const bf16 *vsrc = static_cast<const bf16 *>(a.v) + bh * a.rows * D;
+    bf16 *odst = static_cast<bf16 *>(a.o) + bh * a.rows * D;
+    const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
+    bf16 *pk = static_cast<bf16 *>(a.pool_k) + slot_off;
+    bf16 *pv = static_cast<bf16 *>(a.pool_v) + slot_off;
+    const int kend = min(q0 + QT, N);
+    const int ntiles = (kend + kTK - 1) / kTK;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int col = lane & 31, g = lane >> 5;
+    const int wq0 = q0 + wave * kQW;
+    // This wave's DMA source: the K or the V rows of the history, rows >= kend read as 0.
+    const i32x4 rsrc = rsrc_words(wave < W / 2 ? ksrc : vsrc, (uint32_t)kend * T::ROW_BYTES);
+    int voff[DPW];
+    dma_offsets<D, W>(voff, wave, lane);
+
+#pragma unroll
+    for (int t = 0; t < kAhead; ++t)
+        if (t < ntiles) dma_tile<D, W>(smem + t * T::BUF_BYTES, rsrc, t * kTK, voff, wave);
+
+    WaveState<D> ws;
+    load_q<D>(ws, qsrc, N, wq0, col, g);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        ws.m[qb] = -INFINITY;
+        ws.l[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) ws.acc[db][qb] = f32x16{};
+    }
+    const LaneAddr<D> la = lane_addr<D>(lane);
+
+    // A wave skips tiles wholly after its last query but keeps taking part in the tile
+    // barriers and DMA.
+    const int tlast = wq0 < N ? min(ntiles - 1, (wq0 + kQW - 1) / kTK) : -1;
+    auto next_tile = [&](int t) -> const LDS_AS char * {
+        wait_tiles_after<DPW>(min(ntiles - 1 - t, kAhead - 1));
+        __syncthreads();
+        if (t + kAhead < ntiles)
+            dma_tile<D, W>(smem + ((t + kAhead) % kBufs) * T::BUF_BYTES, rsrc, (t + kAhead) * kTK, voff, wave);
+        return smem + (t % kBufs) * T::BUF_BYTES;
+    };
+    run_tiles<D, true>(ws, ntiles, tlast, kend, wq0, la, col, g, a.c, next_tile);
+    store_o<D>(ws, odst, N, wq0, col, g);
+
+    // fused pool write of this block's own history rows, bit for bit
+    const int chunks = (kend - q0) * T::R;
+    for (int i = tid; i < chunks; i += W * 64) {
+        const long off = (long)q0 * D + (long)i * 8;
+        *reinterpret_cast<u32x4 *>(pk + off) = *reinterpret_cast<const u32x4 *>(ksrc + off);
+        *reinterpret_cast<u32x4 *>(pv + off) = *reinterpret_cast<const u32x4 *>(vsrc + off);
+    }
+}
+
+// ------------------------------------------------------------------ ranking decode
+
+// The item sequence of one workgroup.  Items are (user*H + head, candidate
+// tile).  With the XCD mapping (user*H divisible by 8 and the grid by 8), workgroup w
+// runs on XCD w%8 and takes groups congruent to w mod 8, so all candidate tiles of a
+// (user, head) are processed on one XCD at about the same time and share its L2 copy of
+// the slot's K/V.
+struct ItemSeq {
+    int base, stride, count, tiles, xcd, remap;
+    __device__ __forceinline__ void coords(int r, int &group, int &tile) const {
+        const int s = base + r * stride;
+        if (remap) {
+            group = (s / tiles) * 8 + xcd;
+            tile = s % tiles;
+        } else {
+            group = s / tiles;
+            tile = s % tiles;
         }
     }
+};
+
+__device__ __forceinline__ ItemSeq item_seq(const AttnArgs &a) {
+    ItemSeq q;
+    const int G = a.B * a.H;
+    const int nwg = gridDim.x, w = blockIdx.x;
+    q.tiles = a.tiles;
+    q.remap = a.xcd_remap && (G % 8 == 0) && (nwg % 8 == 0);
+    const int total = q.remap ? (G / 8) * a.tiles : G * a.tiles;
+    q.xcd = q.remap ? (w & 7) : 0;
+    q.base = q.remap ? (w >> 3) : w;
+    q.stride = q.remap ? (nwg >> 3) : nwg;
+    q.count = q.base < total ? (total - q.base + q.stride - 1) / q.stride : 0;
+    return q;
 }
 
 template <int D>
-__global__ void __launch_bounds__(kThreads, D <= 64 ? 2 : 1) prefill_bf16_kernel(AttnArgs a) {
-    attn_body<D, true>(a);
-}
+__device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__restrict__ lens,
+                                            const int32_t *__restrict__ slots) {
+    using T = Tile<D>;
+    constexpr int W = decode_waves<D>();
+    constexpr int QT = W * kQW;
+    constexpr int DPW = KvDma<D, W>::PER_WAVE;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[kBufs * T::BUF_BYTES];
+    LDS_AS char *smem = (LDS_AS char *)smem_raw;
 
-template <int D>
-__global__ void __launch_bounds__(kThreads, D <= 64 ? 2 : 1) rank_decode_bf16_kernel(AttnArgs a) {
-    attn_body<D, false>(a);
-}
+    const ItemSeq seq = item_seq(a);
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int col = lane & 31, g = lane >> 5;
+    const LaneAddr<D> la = lane_addr<D>(lane);
+    int voff[DPW];
+    dma_offsets<D, W>(voff, wave, lane);
 
-template <bool PREFILL>
-hipError_t launch_bf16(const AttnArgs &a, int D, hipStream_t stream) {
-    const long blocks = (long)a.B * a.H * a.tiles;
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)blocks), block(kThreads);
-#define UNIPIN_LAUNCH(DD)                                                                      \
-    if (PREFILL) hipLaunchKernelGGL(prefill_bf16_kernel<DD>, grid, block, 0, stream, a);       \
-    else hipLaunchKernelGGL(rank_decode_bf16_kernel<DD>, grid, block, 0, stream, a);
-    switch (D) {
-        case 32: UNIPIN_LAUNCH(32) break;
-        case 64: UNIPIN_LAUNCH(64) break;
-        case 128: UNIPIN_LAUNCH(128) break;
-        default: return hipErrorInvalidValue;
+    // DMA producer: walks the same item sequence, running up to kAhead tiles ahead of the
+    // tile in use, across item boundaries.  All its state is workgroup-uniform; the item
+    // lookup runs only when it moves to the next item.
+    int p_item = -1, p_tile = 0, p_ntiles = 0;
+    i32x4 p_rsrc = rsrc_words(a.pool_k, 0);
+    int issued = 0;
+    auto produce = [&]() -> bool {
+        while (p_tile >= p_ntiles) {
+            if (p_item + 1 >= seq.count) return false;
+            ++p_item;
+            p_tile = 0;
+            int group, ctile;
+            seq.coords(p_item, group, ctile);
+            const int b = group / a.H, h = group % a.H;
+            const int N = lens[b];
+            const int s = slots[b];
+            const bool ok = N >= 0 && N <= a.len_limit && s >= 0 && s < a.S;
+            p_ntiles = ok ? (N + kTK - 1) / kTK : 0;
+            if (ok) {
+                const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
+                const void *base = static_cast<const bf16 *>(wave < W / 2 ? a.pool_k : a.pool_v) + slot_off;
+                p_rsrc = rsrc_words(base, (uint32_t)N * T::ROW_BYTES);
+            }
+        }
+        dma_tile<D, W>(smem + (issued % kBufs) * T::BUF_BYTES, p_rsrc, p_tile * kTK, voff, wave);
+        ++p_tile;
+        ++issued;
+        return true;
+    };
+    for (int i = 0; i < kAhead; ++i) produce();
+
+    int consumed = 0;
+    for (int r = 0; r < seq.count; ++r) {
+        int group, ctile;
+        seq.coords(r, group, ctile);
+        const int b = group / a.H, h = group % a.H;
+        const int N = lens[b];
+        const int s = slots[b];
+        if (!user_valid(a, N, s, ctile == 0)) continue;   // the producer skipped it too
+
+        const long bh = (long)b * a.H + h;
+        const int wq0 = ctile * QT + wave * kQW;
+        const int qlimit = a.rows;
+        const bf16 *qsrc = static_cast<const bf16 *>(a.q) + bh * a.rows * D;
+        const bf16 *kcs = static_cast<const bf16 *>(a.k) + bh * a.rows * D;
+        const bf16 *vcs = static_cast<const bf16 *>(a.v) + bh * a.rows * D;
+        bf16 *odst = static_cast<bf16 *>(a.o) + bh * a.rows * D;
+
+        // The candidate's own key enters first: it sets the running max, contributes
+        // weight exp2(0) = 1 to the row sum (counted once, by the lower half) and its
+        // value vc_j to the accumulator.  An empty history therefore yields vc_j exactly.
+        WaveState<D> ws;
+        load_q<D>(ws, qsrc, qlimit, wq0, col, g);
+        {
+            const __amdgpu_buffer_rsrc_t rkc = make_rsrc(kcs, (uint32_t)qlimit * T::ROW_BYTES);
+            const __amdgpu_buffer_rsrc_t rvc = make_rsrc(vcs, (uint32_t)qlimit * T::ROW_BYTES);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const uint32_t row = (uint32_t)(wq0 + qb * 32 + col);
+                float part = 0.f;
+#pragma unroll
+                for (int cc = 0; cc < T::KC; ++cc) {
+                    const bf16x8 kk = as_bf16x8(bload16(rkc, row * T::ROW_BYTES + cc * 32 + g * 16));
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) {
+                        const bf16x2 qa = {ws.qreg[qb][cc][e], ws.qreg[qb][cc][e + 1]};
+                        const bf16x2 ka = {kk[e], kk[e + 1]};
+                        part = __builtin_amdgcn_fdot2_f32_bf16(qa, ka, part, false);
+                    }
+                }
+                ws.m[qb] = half_sum(part) * a.c;
+                ws.l[qb] = g == 0 ? 1.f : 0.f;
+#pragma unroll
+                for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int d0 = db * 32 + 8 * j + 4 * g;
+                        const bf16x4 vv = __builtin_bit_cast(bf16x4, bload8(rvc, row * T::ROW_BYTES + d0 * 2));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ws.acc[db][qb][4 * j + e] = (float)vv[e];
+                    }
+            }
+        }
+
+        const int ntiles = (N + kTK - 1) / kTK;
+        auto next_tile = [&](int) -> const LDS_AS char * {
+            wait_tiles_after<DPW>(issued - consumed - 1);
+            __syncthreads();
+            while (issued < consumed + kAhead + 1 && produce()) {
+            }
+            const LDS_AS char *buf = smem + (consumed % kBufs) * T::BUF_BYTES;
+            ++consumed;
+            return buf;
+        };
+        run_tiles<D, false>(ws, ntiles, wq0 < qlimit ? ntiles - 1 : -1, N, wq0, la, col, g, a.c, next_tile);
+        store_o<D>(ws, odst, qlimit, wq0, col, g);
     }
-#undef UNIPIN_LAUNCH
-    return hipGetLastError();
+}
+
+template <int D>
+__global__ void __launch_bounds__(prefill_waves<D>() * 64, D <= 64 ? 2 : 1) prefill_bf16_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
+    prefill_body<D>(a, lens, slots);
+}
+
+template <int D>
+__global__ void __launch_bounds__(decode_waves<D>() * 64, decode_min_blocks<D>()) rank_decode_bf16_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
+    decode_body<D>(a, lens, slots);
+}
+
+int g_cu_count[64];
+
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!g_cu_count[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        g_cu_count[dev] = n;
+    }
+    return g_cu_count[dev];
 }
 
 }  // namespace
 
+int bf16_prefill_rows_per_block(int D) {
+    return (D <= 32 ? prefill_waves<32>() : D <= 64 ? prefill_waves<64>() : prefill_waves<128>()) * kQW;
+}
+
+int bf16_decode_rows_per_item(int D) {
+    return (D <= 32 ? decode_waves<32>() : D <= 64 ? decode_waves<64>() : decode_waves<128>()) * kQW;
+}
+
 hipError_t launch_prefill_bf16(const AttnArgs &a, int D, hipStream_t stream) {
-    return launch_bf16<true>(a, D, stream);
+    const long blocks = (long)a.B * a.H * a.tiles;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)blocks);
+    switch (D) {
+        case 32: hipLaunchKernelGGL(prefill_bf16_kernel<32>, grid, dim3(prefill_waves<32>() * 64), 0, stream, a, a.lens, a.slot); break;
+        case 64: hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(prefill_waves<64>() * 64), 0, stream, a, a.lens, a.slot); break;
+        case 128: hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(prefill_waves<128>() * 64), 0, stream, a, a.lens, a.slot); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_bf16(const AttnArgs &a, int D, hipStream_t stream) {
-    return launch_bf16<false>(a, D, stream);
+    const long items = (long)a.B * a.H * a.tiles;
+    if (items <= 0) return hipSuccess;
+    // Persistent grid (a fixed number of workgroups per CU, never more than there are
+    // items), or one workgroup per item.
+    long grid_n = UNIPIN_DECODE_GRID_PER_CU > 0 ? (long)cu_count() * UNIPIN_DECODE_GRID_PER_CU : items;
+    if (grid_n > items) grid_n = items;
+    if (grid_n > 0x7fffffffL) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)grid_n);
+    switch (D) {
+        case 32: hipLaunchKernelGGL(rank_decode_bf16_kernel<32>, grid, dim3(decode_waves<32>() * 64), 0, stream, a, a.lens, a.slot); break;
+        case 64: hipLaunchKernelGGL(rank_decode_bf16_kernel<64>, grid, dim3(decode_waves<64>() * 64), 0, stream, a, a.lens, a.slot); break;
+        case 128: hipLaunchKernelGGL(rank_decode_bf16_kernel<128>, grid, dim3(decode_waves<128>() * 64), 0, stream, a, a.lens, a.slot); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace unipin

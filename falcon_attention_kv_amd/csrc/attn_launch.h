@@ -29,9 +29,10 @@ struct AttnArgs {
 constexpr unsigned int kFlagBadSlot = 1u;
 constexpr unsigned int kFlagBadLen = 2u;
 
-// Number of query rows one workgroup covers, per element type.
-constexpr int kBf16RowsPerBlock = 256;
+// Query rows one workgroup (prefill) or one work item (decode) covers.
 constexpr int kFp32RowsPerBlock = 64;
+int bf16_prefill_rows_per_block(int D);
+int bf16_decode_rows_per_item(int D);
 
 hipError_t launch_prefill_bf16(const AttnArgs &a, int D, hipStream_t stream);
 hipError_t launch_decode_bf16(const AttnArgs &a, int D, hipStream_t stream);

@@ -58,8 +58,9 @@ int launch(const unipin::AttnArgs &a, const unipin_pool *pool, bool prefill, voi
     return e == hipSuccess ? UNIPIN_OK : UNIPIN_EHIP;
 }
 
-int rows_per_block(const unipin_pool *pool) {
-    return pool->dtype == UNIPIN_BF16 ? unipin::kBf16RowsPerBlock : unipin::kFp32RowsPerBlock;
+int rows_per_block(const unipin_pool *pool, bool prefill) {
+    if (pool->dtype != UNIPIN_BF16) return unipin::kFp32RowsPerBlock;
+    return prefill ? unipin::bf16_prefill_rows_per_block(pool->D) : unipin::bf16_decode_rows_per_item(pool->D);
 }
 
 }  // namespace
@@ -143,7 +144,7 @@ int unipin_prefill(const void *q, const void *k, const void *v, const int32_t *l
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
         !aligned(lens, 4) || !aligned(slot, 4))
         return UNIPIN_EALIGN;
-    const int rpb = rows_per_block(pool);
+    const int rpb = rows_per_block(pool, true);
     const long long blocks = (long long)B * pool->H * ((n + rpb - 1) / rpb);
     if (blocks > 0x7fffffffLL) return UNIPIN_EINVAL;
     unipin::AttnArgs a{};
@@ -174,7 +175,7 @@ int unipin_rank_decode(const void *qc, const void *kc, const void *vc,
     if (!aligned(qc, 16) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(oc, 16) ||
         !aligned(lens, 4) || !aligned(slot, 4))
         return UNIPIN_EALIGN;
-    const int rpb = rows_per_block(pool);
+    const int rpb = rows_per_block(pool, false);
     const long long blocks = (long long)B * pool->H * ((k + rpb - 1) / rpb);
     if (blocks > 0x7fffffffLL) return UNIPIN_EINVAL;
     unipin::AttnArgs a{};
