@@ -86,6 +86,7 @@ template <int D> constexpr int decode_waves() { return D <= 64 ? UNIPIN_DECODE_W
 // Minimum resident workgroups per CU the decode is compiled for: 2 waves per SIMD at
 // D <= 64, 1 at D = 128.
 template <int D> constexpr int decode_min_blocks() { return D <= 64 ? 8 / decode_waves<D>() : 1; }
+template <int D> constexpr int prefill_min_blocks() { return D <= 64 ? 2 : 1; }
 
 constexpr uint32_t kBufferWord3 = 0x00020000u;   // gfx9 buffer descriptor, raw 32-bit access
 
@@ -142,9 +143,16 @@ __device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
 // assembly so that the compiler does not treat it as a pending write to every LDS
 // address (which makes it wait for all outstanding DMA before each LDS read and defeats
 // the prefetch); the kernels wait for it explicitly (vmcnt, then a workgroup barrier).
-// The instruction has no register results and reads its operands at issue.
+// The instruction has no register results and reads its operands at issue.  It takes
+// its LDS address from M0, and a scalar write of M0 needs one wait state before an LDS
+// DMA reads it; the compiler cannot see that hazard inside the assembly (it sets M0 in
+// the instruction just before), so the s_nop is part of the statement.
 __device__ __forceinline__ void dma16(uint32_t lds, i32x4 rsrc, int voff, int soff) {
-    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
+    // the descriptor, the scalar offset and M0 are wave-uniform by construction
+    soff = __builtin_amdgcn_readfirstlane(soff);
+    lds = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+                 "{m0}"(lds)
                  : "memory");
 }
 
@@ -257,17 +265,17 @@ __device__ __forceinline__ LaneAddr<D> lane_addr(int lane) {
     return la;
 }
 
-// One 64-key tile: S^T = K Q^T (2 key blocks x 2 query blocks), optional mask, running
-// max with lazy rescale, P in bf16, row sums, O^T += V^T P^T.
-// Masking: element i of block (kb, qb) is key kbase + kb*32 + 4g + off(i),
-// off(i) = 8*(i/4) + i%4; it is visible iff off(i) <= lim, with lim from the history end
-// and, for the prefill, the query's own position.
-template <int D, bool PREFILL>
-__device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *kt, const LDS_AS char *vt,
-                                          int kbase, int kend, int wq0, bool masked,
-                                          const LaneAddr<D> &la, int col, int g, float c) {
+// ------------------------------------------------------------------ one 64-key tile
+// Scores are held transposed, [key block kb][query block qb]: element i of lane (col, g)
+// of block (kb, qb) is the score of query wq0 + qb*32 + col against key kbase + kb*32 +
+// 4g + off(i), off(i) = 8*(i/4) + i%4.
+
+// S^T = K Q^T for one tile (its K rows in LDS at kt): 2 key blocks x 2 query blocks x
+// KC MFMAs.
+template <int D>
+__device__ __forceinline__ void tile_scores(f32x16 (&sc)[2][2], const WaveState<D> &ws, const LDS_AS char *kt,
+                                            const LaneAddr<D> &la) {
     using T = Tile<D>;
-    f32x16 sc[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -282,25 +290,32 @@ __device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *k
                 sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, ws.qreg[qb][cc], sc[kb][qb], 0, 0, 0);
         }
     }
+}
 
-    if (masked) {
+// Sets to -inf the scores of keys at or past kend and, for the prefill, of keys after
+// the query: element i is visible iff off(i) <= lim.
+template <bool PREFILL>
+__device__ __forceinline__ void tile_mask(f32x16 (&sc)[2][2], int kbase, int kend, int wq0, int col, int g) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int base = kbase + kb * 32 + 4 * g;
-                int lim = kend - 1 - base;
-                if (PREFILL) lim = min(lim, wq0 + qb * 32 + col - base);
+        for (int qb = 0; qb < 2; ++qb) {
+            const int base = kbase + kb * 32 + 4 * g;
+            int lim = kend - 1 - base;
+            if (PREFILL) lim = min(lim, wq0 + qb * 32 + col - base);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int off = 8 * (i >> 2) + (i & 3);
-                    sc[kb][qb][i] = off > lim ? -INFINITY : sc[kb][qb][i];
-                }
+            for (int i = 0; i < 16; ++i) {
+                const int off = 8 * (i >> 2) + (i & 3);
+                sc[kb][qb][i] = off > lim ? -INFINITY : sc[kb][qb][i];
             }
-    }
+        }
+}
 
-    // running max (log2 domain) with lazy rescale: the branch is wave-wide and rare
-    // (first visible tile, or a late jump of the max by more than 2^8).
+// Running max (log2 domain) with lazy rescale: the branch is wave-wide and rare (first
+// visible tile, or a late jump of the max by more than 2^8).
+template <int D>
+__device__ __forceinline__ void tile_max_rescale(const f32x16 (&sc)[2][2], WaveState<D> &ws, float c) {
+    using T = Tile<D>;
     float mt[2];
     bool grow[2];
 #pragma unroll
@@ -326,52 +341,76 @@ __device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *k
             ws.m[qb] = mn;
         }
     }
+}
 
-    // per 32-key block: P = exp2(s*c - m), rounded to bf16 in the B-operand layout of
-    // the PV MFMA (the row sum takes the rounded values), then O^T += V^T P^T.  Lane
-    // (d, g) needs, for chunk (kb, c2), V at keys kb*32 + 16*c2 + {4g..4g+3} (elements
-    // 0..3) and kb*32 + 16*c2 + 8 + {4g..4g+3} (elements 4..7): two transpose loads of 4
-    // keys x 16 dims each.
+// P = exp2(s*c - m) for key block kb, rounded to bf16 in the B-operand layout of the PV
+// MFMA, pb[chunk of 16 keys][qb]; the row sums take the rounded values.
+template <int D>
+__device__ __forceinline__ void tile_exp(bf16x8 (&pb)[2][2], const f32x16 (&sc)[2][2], int kb, WaveState<D> &ws,
+                                         float c) {
     const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 pb[2][2];  // [chunk of 16 keys][qb]
+    for (int qb = 0; qb < 2; ++qb) {
+        const float nm = -ws.m[qb];
+        float lsum = 0.f;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const float nm = -ws.m[qb];
-            float lsum = 0.f;
+        for (int c2 = 0; c2 < 2; ++c2) {
+            bf16x8 p;
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                bf16x8 p;
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][c2 * 8 + e], c, nm));
-                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][c2 * 8 + e + 1], c, nm));
-                    const bf16x2 pp = {(bf16)p0, (bf16)p1};
-                    p[e] = pp[0];
-                    p[e + 1] = pp[1];
-                    lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
-                }
-                pb[c2][qb] = p;
+            for (int e = 0; e < 8; e += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][c2 * 8 + e], c, nm));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][c2 * 8 + e + 1], c, nm));
+                const bf16x2 pp = {(bf16)p0, (bf16)p1};
+                p[e] = pp[0];
+                p[e + 1] = pp[1];
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
             }
-            ws.l[qb] += lsum;
+            pb[c2][qb] = p;
         }
-#pragma unroll
-        for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                const LDS_AS char *src = vt + la.v_off + la.v_blk[db] + (kb * 32 + 16 * c2) * T::ROW_BYTES;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)src);
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(src + 8 * T::ROW_BYTES));
-                const i16x4 lh[2] = {lo, hi};
-                const bf16x8 va = __builtin_bit_cast(bf16x8, lh);
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-                    ws.acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c2][qb], ws.acc[db][qb], 0, 0, 0);
-            }
+        ws.l[qb] += lsum;
     }
 }
 
+// O^T += V^T P^T for key block kb of the tile (its V rows in LDS at vt).  Lane (d, g)
+// needs, for chunk c2, V at keys kb*32 + 16*c2 + {4g..4g+3} (elements 0..3) and
+// kb*32 + 16*c2 + 8 + {4g..4g+3} (elements 4..7): two transpose loads of 4 keys x 16
+// dims each.
+template <int D>
+__device__ __forceinline__ void tile_pv(WaveState<D> &ws, const bf16x8 (&pb)[2][2], int kb, const LDS_AS char *vt,
+                                        const LaneAddr<D> &la) {
+    using T = Tile<D>;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+            const LDS_AS char *src = vt + la.v_off + la.v_blk[db] + (kb * 32 + 16 * c2) * T::ROW_BYTES;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)src);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(src + 8 * T::ROW_BYTES));
+            const i16x4 lh[2] = {lo, hi};
+            const bf16x8 va = __builtin_bit_cast(bf16x8, lh);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+                ws.acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c2][qb], ws.acc[db][qb], 0, 0, 0);
+        }
+}
+
+// One whole tile for one wave: scores, optional mask, max and rescale, then per key
+// block the exponentials and the PV product.
+template <int D, bool PREFILL>
+__device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *kt, const LDS_AS char *vt,
+                                          int kbase, int kend, int wq0, bool masked,
+                                          const LaneAddr<D> &la, int col, int g, float c) {
+    f32x16 sc[2][2];
+    tile_scores<D>(sc, ws, kt, la);
+    if (masked) tile_mask<PREFILL>(sc, kbase, kend, wq0, col, g);
+    tile_max_rescale<D>(sc, ws, c);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 pb[2][2];
+        tile_exp<D>(pb, sc, kb, ws, c);
+        tile_pv<D>(ws, pb, kb, vt, la);
+    }
+}
 
 // Runs the wave over K/V tiles 0 .. ntiles-1.  next_tile(u) makes tile u current (wait
 // for its DMA, workgroup barrier, further DMA) and returns its LDS buffer; every wave
@@ -424,6 +463,44 @@ __device__ __forceinline__ void store_o(const WaveState<D> &ws, bf16 *odst, int 
                     *reinterpret_cast<u32x2 *>(odst + (long)row * D + d0) = __builtin_bit_cast(u32x2, ov);
                 }
         }
+    }
+}
+
+// The candidate's own key enters first: it sets the running max, contributes weight
+// exp2(0) = 1 to the row sum (counted once, by the lower lane half) and its value vc_j
+// to the accumulator.  An empty history therefore yields vc_j exactly, and nothing in a
+// candidate's arithmetic depends on another candidate.
+template <int D>
+__device__ __forceinline__ void self_key_init(WaveState<D> &ws, const bf16 *kcs, const bf16 *vcs, int qlimit, int wq0,
+                                              int col, int g, float c) {
+    using T = Tile<D>;
+    const __amdgpu_buffer_rsrc_t rkc = make_rsrc(kcs, (uint32_t)max(qlimit, 0) * T::ROW_BYTES);
+    const __amdgpu_buffer_rsrc_t rvc = make_rsrc(vcs, (uint32_t)max(qlimit, 0) * T::ROW_BYTES);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const uint32_t row = (uint32_t)(wq0 + qb * 32 + col);
+        float part = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < T::KC; ++cc) {
+            const bf16x8 kk = as_bf16x8(bload16(rkc, row * T::ROW_BYTES + cc * 32 + g * 16));
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const bf16x2 qa = {ws.qreg[qb][cc][e], ws.qreg[qb][cc][e + 1]};
+                const bf16x2 ka = {kk[e], kk[e + 1]};
+                part = __builtin_amdgcn_fdot2_f32_bf16(qa, ka, part, false);
+            }
+        }
+        ws.m[qb] = half_sum(part) * c;
+        ws.l[qb] = g == 0 ? 1.f : 0.f;
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d0 = db * 32 + 8 * j + 4 * g;
+                const bf16x4 vv = __builtin_bit_cast(bf16x4, bload8(rvc, row * T::ROW_BYTES + d0 * 2));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ws.acc[db][qb][4 * j + e] = (float)vv[e];
+            }
     }
 }
 
@@ -633,41 +710,9 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
         const bf16 *vcs = static_cast<const bf16 *>(a.v) + bh * a.rows * D;
         bf16 *odst = static_cast<bf16 *>(a.o) + bh * a.rows * D;
 
-        // The candidate's own key enters first: it sets the running max, contributes
-        // weight exp2(0) = 1 to the row sum (counted once, by the lower half) and its
-        // value vc_j to the accumulator.  An empty history therefore yields vc_j exactly.
         WaveState<D> ws;
         load_q<D>(ws, qsrc, qlimit, wq0, col, g);
-        {
-            const __amdgpu_buffer_rsrc_t rkc = make_rsrc(kcs, (uint32_t)qlimit * T::ROW_BYTES);
-            const __amdgpu_buffer_rsrc_t rvc = make_rsrc(vcs, (uint32_t)qlimit * T::ROW_BYTES);
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const uint32_t row = (uint32_t)(wq0 + qb * 32 + col);
-                float part = 0.f;
-#pragma unroll
-                for (int cc = 0; cc < T::KC; ++cc) {
-                    const bf16x8 kk = as_bf16x8(bload16(rkc, row * T::ROW_BYTES + cc * 32 + g * 16));
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        const bf16x2 qa = {ws.qreg[qb][cc][e], ws.qreg[qb][cc][e + 1]};
-                        const bf16x2 ka = {kk[e], kk[e + 1]};
-                        part = __builtin_amdgcn_fdot2_f32_bf16(qa, ka, part, false);
-                    }
-                }
-                ws.m[qb] = half_sum(part) * a.c;
-                ws.l[qb] = g == 0 ? 1.f : 0.f;
-#pragma unroll
-                for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int d0 = db * 32 + 8 * j + 4 * g;
-                        const bf16x4 vv = __builtin_bit_cast(bf16x4, bload8(rvc, row * T::ROW_BYTES + d0 * 2));
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) ws.acc[db][qb][4 * j + e] = (float)vv[e];
-                    }
-            }
-        }
+        self_key_init<D>(ws, kcs, vcs, qlimit, wq0, col, g, a.c);
 
         const int ntiles = (N + kTK - 1) / kTK;
         auto next_tile = [&](int) -> const LDS_AS char * {
@@ -685,7 +730,7 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
 }
 
 template <int D>
-__global__ void __launch_bounds__(prefill_waves<D>() * 64, D <= 64 ? 2 : 1) prefill_bf16_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
+__global__ void __launch_bounds__(prefill_waves<D>() * 64, prefill_min_blocks<D>()) prefill_bf16_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
     prefill_body<D>(a, lens, slots);
 }
 
