@@ -6,13 +6,16 @@
 // cached history key of its user plus its own key, never to another candidate.
 //
 // Work decomposition:
-//   * a workgroup = 4 waves of 64 lanes; each wave owns 64 query rows, held in
-//     registers as the B operand of v_mfma_f32_32x32x16_bf16;
-//   * 64-key tiles of K and V are copied HBM -> LDS by the buffer-to-LDS DMA path
-//     (buffer_load_dwordx4 ... lds) into a ring of LDS buffers, up to three tiles ahead
-//     of use: no staging registers, no VALU work, and every row past the history reads
-//     as zero (the buffer's record count is the history length), so ragged histories
-//     need no branches;
+//   * a workgroup covers 256 query rows: 8 waves of 32 rows at D <= 64 (4 waves per
+//     SIMD), 4 waves of 64 rows at D = 128; a wave holds its rows in registers as the
+//     B operand of v_mfma_f32_32x32x16_bf16;
+//   * everything a workgroup reads from HBM arrives through the buffer-to-LDS DMA path
+//     (buffer_load_dwordx4 ... lds) into a ring of four LDS slots: 64-key tiles of K
+//     and V, up to three tiles ahead of use, and the 256-row blocks of queries (and, in
+//     the decode, of the candidates' own keys and values).  Each DMA instruction moves
+//     1 KB of whole rows (no VGPRs, no VALU work), and every row past the record count
+//     reads as zero, so ragged histories need no branches;
+//   * outputs go back through LDS too, so that the global stores write whole rows;
 //   * scores are computed transposed, S^T = K Q^T, so that in the MFMA result each lane
 //     holds one query and 16 keys: softmax row statistics are lane-local plus one
 //     v_permlane32_swap with the lane 32 away;
@@ -20,17 +23,15 @@
 //     very registers the score MFMA left it in; V stays in its natural [key][d] layout
 //     in LDS and ds_read_b64_tr_b16 delivers it transposed;
 //   * fp32 online softmax in the log2 domain (scale*log2(e) folded into one FMA), with a
-//     lazy rescale: the running max only moves when a tile's max exceeds it by more
-//     than 2^8, which bounds P by 256 and skips almost every rescale;
+//     lazy rescale: a tile's weights are taken against the running max as it stands,
+//     and the max only moves (and the tile is redone) when a row's weights would leave
+//     the range 2^64, so no tile computes its maximum on the common path;
 //   * the row sum is accumulated from the bf16-rounded P (v_dot2 with ones), so the
 //     normaliser matches the weights the PV product used;
 //   * masking runs only on tiles that cross the history end or the causal diagonal.
 //
-// The prefill launches one workgroup per (user, head, 256-row query tile).  The ranking
-// decode's workgroups each walk a sequence of (user, head, 256-candidate tile) items
-// with a K/V DMA ring that runs on across item boundaries; the default launch gives
-// every item its own workgroup, and a persistent grid (a few workgroups per CU) is a
-// build-time option.
+// The prefill launches one workgroup per (user, head, 256-row query tile), the ranking
+// decode one per (user, head, 256-candidate tile).
 //
 // Hardware facts relied on (checked on gfx950 with small in-bounds probes):
 //   * v_mfma_f32_32x32x16_bf16 result element i of lane l is row 8*(i/4) + 4*(l/32)
@@ -62,36 +63,23 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kQW = 64;                   // query rows per wave
 constexpr int kTK = 64;                   // keys per LDS tile
 constexpr int kBufs = 4;                  // LDS tile buffers
-// Tiles whose DMA is in flight beyond the one in use.  A tile is finished before the
-// barrier that makes the next one current, so the DMA issued at that barrier may reuse
-// the finished tile's buffer: with 4 buffers, 3 tiles ahead.
-constexpr int kAhead = 3;
 
-// Waves per workgroup: 4 (a 256-row query tile) for both kernels.  At D <= 64 two
-// workgroups share a CU (2 waves per SIMD, 256 registers per lane each); at D = 128 a
-// wave needs the whole register file.  Build-time knobs for tuning: the decode's waves
-// per workgroup, and its grid (workgroups resident per CU for a persistent grid, or 0
-// for one workgroup per work item, which measured fastest).
-#ifndef UNIPIN_DECODE_WAVES
-#define UNIPIN_DECODE_WAVES 4
+// A workgroup covers 256 query rows.  A wave holds QB blocks of 32 query rows: one at
+// D <= 64 (8 waves per workgroup, two workgroups per CU: 4 waves per SIMD with at most
+// 128 registers each), two at D = 128 (4 waves of 64 rows, one workgroup per CU).
+#ifndef UNIPIN_QB_SMALL_D
+#define UNIPIN_QB_SMALL_D 1
 #endif
-#ifndef UNIPIN_DECODE_GRID_PER_CU
-#define UNIPIN_DECODE_GRID_PER_CU 0
-#endif
-template <int D> constexpr int prefill_waves() { return 4; }
-template <int D> constexpr int decode_waves() { return D <= 64 ? UNIPIN_DECODE_WAVES : 4; }
-// Minimum resident workgroups per CU the decode is compiled for: 2 waves per SIMD at
-// D <= 64, 1 at D = 128.
-template <int D> constexpr int decode_min_blocks() { return D <= 64 ? 8 / decode_waves<D>() : 1; }
-template <int D> constexpr int prefill_min_blocks() { return D <= 64 ? 2 : 1; }
+constexpr int kBlockRows = 256;
+template <int D> constexpr int query_blocks() { return D <= 64 ? UNIPIN_QB_SMALL_D : 2; }
+template <int D> constexpr int wave_rows() { return 32 * query_blocks<D>(); }
+template <int D> constexpr int block_waves() { return kBlockRows / wave_rows<D>(); }
+template <int D> constexpr int min_blocks() { return D <= 64 ? 2 : 1; }
 
 constexpr uint32_t kBufferWord3 = 0x00020000u;   // gfx9 buffer descriptor, raw 32-bit access
 
-// Lazy-rescale threshold in log2 units: P stays below 2^8.
-constexpr float kRescaleThreshold = 8.0f;
 
 template <int D>
 struct Tile {
@@ -173,17 +161,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
-// Waits until the tile in use has landed, allowing the `tiles_after` tiles issued after
-// it (at most kAhead - 1) to stay in flight.  Other loads issued after it only make the
-// wait longer, never shorter, since loads complete in issue order.
-template <int DPW>
-__device__ __forceinline__ void wait_tiles_after(int tiles_after) {
-    static_assert(kAhead == 3, "the cases below cover up to two tiles after the one in use");
-    if (tiles_after >= 2) wait_vmcnt<2 * DPW>();
-    else if (tiles_after == 1) wait_vmcnt<DPW>();
-    else wait_vmcnt<0>();
-}
-
 // Value exchange with the lane 32 away (v_permlane32_swap: no LDS round trip).  r[0]
 // holds the lower half's value in both halves, r[1] the upper half's.
 __device__ __forceinline__ float half_max(float x) {
@@ -228,13 +205,32 @@ __device__ __forceinline__ void dma_tile(LDS_AS char *buf, i32x4 rsrc, int kbase
     for (int j = 0; j < KvDma<D, W>::PER_WAVE; ++j) dma16(dst + j * 1024, rsrc, voff[j], soff);
 }
 
+// DMA of one block of 256 query (or candidate) rows, W waves x 64, into two consecutive
+// LDS slots with the K swizzle: 16-byte block bi of the block in LDS order is row
+// bi / R, logical block (bi % R) ^ k_swz(row).  Rows past the record count read as zero.
+template <int D, int W>
+__device__ __forceinline__ void dma_rows(LDS_AS char *dst, i32x4 rsrc, int row0, int wave, int lane) {
+    using T = Tile<D>;
+    constexpr int PW = kBlockRows * T::ROW_BYTES / 1024 / W;   // 1 KB pieces per wave
+    const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(dst);
+    const int soff = row0 * T::ROW_BYTES;
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+        const int piece = wave * PW + j;
+        const int bi = piece * 64 + lane;
+        const int row = bi / T::R, blk = (bi % T::R) ^ k_swz<D>(row);
+        dma16(base + piece * 1024, rsrc, row * T::ROW_BYTES + blk * 16, soff);
+    }
+}
+
 // Per-wave attention state.
 template <int D>
 struct WaveState {
-    bf16x8 qreg[2][Tile<D>::KC];   // B operand: query rows wq0 + qb*32 + col, dims cc*16 + g*8 ..
-    f32x16 acc[Tile<D>::DB][2];    // O^T accumulators: lane = query, 16 head dims per block
-    float m[2];                    // running max (log2 domain), shared by both lane halves
-    float l[2];                    // this lane half's share of the row sum
+    static constexpr int QB = query_blocks<D>();
+    bf16x8 qreg[QB][Tile<D>::KC];   // B operand: query rows wq0 + qb*32 + col, dims cc*16 + g*8 ..
+    f32x16 acc[Tile<D>::DB][QB];    // O^T accumulators: lane = query, 16 head dims per block
+    float m[QB];                    // running max (log2 domain), shared by both lane halves
+    float l[QB];                    // this lane half's share of the row sum
 };
 
 // Per-lane LDS addressing of the operand reads, fixed for the whole kernel.
@@ -273,20 +269,20 @@ __device__ __forceinline__ LaneAddr<D> lane_addr(int lane) {
 // S^T = K Q^T for one tile (its K rows in LDS at kt): 2 key blocks x 2 query blocks x
 // KC MFMAs.
 template <int D>
-__device__ __forceinline__ void tile_scores(f32x16 (&sc)[2][2], const WaveState<D> &ws, const LDS_AS char *kt,
+__device__ __forceinline__ void tile_scores(f32x16 (&sc)[2][query_blocks<D>()], const WaveState<D> &ws, const LDS_AS char *kt,
                                             const LaneAddr<D> &la) {
     using T = Tile<D>;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) sc[kb][qb] = f32x16{};
+        for (int qb = 0; qb < query_blocks<D>(); ++qb) sc[kb][qb] = f32x16{};
 #pragma unroll
     for (int cc = 0; cc < T::KC; ++cc) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const bf16x8 ka = *reinterpret_cast<const LDS_AS bf16x8 *>(kt + la.k_off0 + kb * 32 * T::ROW_BYTES + la.k_xor[cc]);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
+            for (int qb = 0; qb < query_blocks<D>(); ++qb)
                 sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, ws.qreg[qb][cc], sc[kb][qb], 0, 0, 0);
         }
     }
@@ -294,12 +290,12 @@ __device__ __forceinline__ void tile_scores(f32x16 (&sc)[2][2], const WaveState<
 
 // Sets to -inf the scores of keys at or past kend and, for the prefill, of keys after
 // the query: element i is visible iff off(i) <= lim.
-template <bool PREFILL>
-__device__ __forceinline__ void tile_mask(f32x16 (&sc)[2][2], int kbase, int kend, int wq0, int col, int g) {
+template <int D, bool PREFILL>
+__device__ __forceinline__ void tile_mask(f32x16 (&sc)[2][query_blocks<D>()], int kbase, int kend, int wq0, int col, int g) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < query_blocks<D>(); ++qb) {
             const int base = kbase + kb * 32 + 4 * g;
             int lim = kend - 1 - base;
             if (PREFILL) lim = min(lim, wq0 + qb * 32 + col - base);
@@ -311,48 +307,17 @@ __device__ __forceinline__ void tile_mask(f32x16 (&sc)[2][2], int kbase, int ken
         }
 }
 
-// Running max (log2 domain) with lazy rescale: the branch is wave-wide and rare (first
-// visible tile, or a late jump of the max by more than 2^8).
+// P = exp2(s*c - m) for key block kb against the current running max m, rounded to bf16
+// in the B-operand layout of the PV MFMA, pb[chunk of 16 keys][qb]; lsum[qb] takes the
+// rounded values (so that the normaliser matches the weights the PV product uses).
 template <int D>
-__device__ __forceinline__ void tile_max_rescale(const f32x16 (&sc)[2][2], WaveState<D> &ws, float c) {
-    using T = Tile<D>;
-    float mt[2];
-    bool grow[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        float mx = sc[0][qb][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[0][qb][i]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[1][qb][i]);
-        mt[qb] = half_max(mx) * c;
-        grow[qb] = mt[qb] > ws.m[qb] + kRescaleThreshold;
-    }
-    if (__any(grow[0] || grow[1])) {
-        // keeps the compiler from flattening this rare path into the hot block
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const float mn = grow[qb] ? fmaxf(ws.m[qb], mt[qb]) : ws.m[qb];
-            const float alpha = grow[qb] ? __builtin_amdgcn_exp2f(ws.m[qb] - mn) : 1.f;
-            ws.l[qb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < T::DB; ++db) ws.acc[db][qb] *= alpha;
-            ws.m[qb] = mn;
-        }
-    }
-}
-
-// P = exp2(s*c - m) for key block kb, rounded to bf16 in the B-operand layout of the PV
-// MFMA, pb[chunk of 16 keys][qb]; the row sums take the rounded values.
-template <int D>
-__device__ __forceinline__ void tile_exp(bf16x8 (&pb)[2][2], const f32x16 (&sc)[2][2], int kb, WaveState<D> &ws,
+__device__ __forceinline__ void tile_exp(bf16x8 (&pb)[2][query_blocks<D>()], float (&lsum)[query_blocks<D>()],
+                                         const f32x16 (&sc)[2][query_blocks<D>()], int kb, const WaveState<D> &ws,
                                          float c) {
     const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < query_blocks<D>(); ++qb) {
         const float nm = -ws.m[qb];
-        float lsum = 0.f;
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
             bf16x8 p;
@@ -363,12 +328,64 @@ __device__ __forceinline__ void tile_exp(bf16x8 (&pb)[2][2], const f32x16 (&sc)[
                 const bf16x2 pp = {(bf16)p0, (bf16)p1};
                 p[e] = pp[0];
                 p[e + 1] = pp[1];
-                lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+                lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum[qb], false);
             }
             pb[c2][qb] = p;
         }
-        ws.l[qb] += lsum;
     }
+}
+
+// Lazy rescale.  The running max m of a row only has to keep the weights in range: the
+// tile is first evaluated against the current m, and only a row whose lane sum of
+// weights exceeds kFastSumLimit, or is not finite (m = -inf before the row's first
+// tile), moves m to max(m, tile max), scales its accumulator and row sum by
+// exp2(m_old - m_new) and re-evaluates the tile.  With the limit at 2^64 a weight never
+// exceeds 2^64, so for histories up to 2^20 keys the fp32 row sum and accumulators stay
+// below 2^84 |v|: far from overflow, and the bf16 weights keep their full relative
+// precision.  In practice only a row's first tile takes the slow path.  The decision is
+// per row (both lane halves of a row agree), so a row's arithmetic never depends on the
+// other rows of the wave; the branch is wave-wide.
+constexpr float kFastSumLimit = 18446744073709551616.0f;   // 2^64
+
+template <int D>
+__device__ __forceinline__ void tile_softmax(bf16x8 (&pb)[2][2][query_blocks<D>()], WaveState<D> &ws,
+                                             const f32x16 (&sc)[2][query_blocks<D>()], float c) {
+    using T = Tile<D>;
+    constexpr int QB = query_blocks<D>();
+    float lsum[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) lsum[qb] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) tile_exp<D>(pb[kb], lsum, sc, kb, ws, c);
+    bool slow = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) slow |= !(lsum[qb] <= kFastSumLimit);
+    if (__any(slow)) {
+        // keeps the compiler from flattening this rare path into the hot block
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float mine = !(lsum[qb] <= kFastSumLimit) ? 1.f : 0.f;
+            const bool grow = half_max(mine) > 0.f;   // either half of the row
+            float mx = sc[0][qb][0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[0][qb][i]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[1][qb][i]);
+            const float mt = half_max(mx) * c;
+            const float mn = grow ? fmaxf(ws.m[qb], mt) : ws.m[qb];
+            const float alpha = grow ? __builtin_amdgcn_exp2f(ws.m[qb] - mn) : 1.f;
+            ws.l[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db) ws.acc[db][qb] *= alpha;
+            ws.m[qb] = mn;
+            lsum[qb] = 0.f;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) tile_exp<D>(pb[kb], lsum, sc, kb, ws, c);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) ws.l[qb] += lsum[qb];
 }
 
 // O^T += V^T P^T for key block kb of the tile (its V rows in LDS at vt).  Lane (d, g)
@@ -376,7 +393,7 @@ __device__ __forceinline__ void tile_exp(bf16x8 (&pb)[2][2], const f32x16 (&sc)[
 // kb*32 + 16*c2 + 8 + {4g..4g+3} (elements 4..7): two transpose loads of 4 keys x 16
 // dims each.
 template <int D>
-__device__ __forceinline__ void tile_pv(WaveState<D> &ws, const bf16x8 (&pb)[2][2], int kb, const LDS_AS char *vt,
+__device__ __forceinline__ void tile_pv(WaveState<D> &ws, const bf16x8 (&pb)[2][query_blocks<D>()], int kb, const LDS_AS char *vt,
                                         const LaneAddr<D> &la) {
     using T = Tile<D>;
 #pragma unroll
@@ -389,27 +406,24 @@ __device__ __forceinline__ void tile_pv(WaveState<D> &ws, const bf16x8 (&pb)[2][
             const i16x4 lh[2] = {lo, hi};
             const bf16x8 va = __builtin_bit_cast(bf16x8, lh);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
+            for (int qb = 0; qb < query_blocks<D>(); ++qb)
                 ws.acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c2][qb], ws.acc[db][qb], 0, 0, 0);
         }
 }
 
-// One whole tile for one wave: scores, optional mask, max and rescale, then per key
-// block the exponentials and the PV product.
+// One whole tile for one wave: scores, optional mask, weights with the lazy rescale,
+// then the PV product.
 template <int D, bool PREFILL>
 __device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *kt, const LDS_AS char *vt,
                                           int kbase, int kend, int wq0, bool masked,
                                           const LaneAddr<D> &la, int col, int g, float c) {
-    f32x16 sc[2][2];
+    f32x16 sc[2][query_blocks<D>()];
     tile_scores<D>(sc, ws, kt, la);
-    if (masked) tile_mask<PREFILL>(sc, kbase, kend, wq0, col, g);
-    tile_max_rescale<D>(sc, ws, c);
+    if (masked) tile_mask<D, PREFILL>(sc, kbase, kend, wq0, col, g);
+    bf16x8 pb[2][2][query_blocks<D>()];
+    tile_softmax<D>(pb, ws, sc, c);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 pb[2][2];
-        tile_exp<D>(pb, sc, kb, ws, c);
-        tile_pv<D>(ws, pb, kb, vt, la);
-    }
+    for (int kb = 0; kb < 2; ++kb) tile_pv<D>(ws, pb[kb], kb, vt, la);
 }
 
 // Runs the wave over K/V tiles 0 .. ntiles-1.  next_tile(u) makes tile u current (wait
@@ -429,79 +443,96 @@ __device__ __forceinline__ void run_tiles(WaveState<D> &ws, int ntiles, int tlas
     }
 }
 
-// Loads the wave's 64 query rows (rows >= qlimit read as zeros).
+// The wave's rows of a staged row block (dma_rows), read into the B-operand layout
+// of the score MFMA: lane (col, g) gets row qb*32 + col, dims 16cc + 8g .. +7.  The
+// wave's rows start at a multiple of 32, so k_swz(row) = k_swz(col).
 template <int D>
-__device__ __forceinline__ void load_q(WaveState<D> &ws, const bf16 *qsrc, int qlimit, int wq0, int col, int g) {
-    using T = Tile<D>;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qsrc, (uint32_t)max(qlimit, 0) * T::ROW_BYTES);
+__device__ __forceinline__ void staged_operand(bf16x8 (&r)[query_blocks<D>()][Tile<D>::KC], const LDS_AS char *rows,
+                                               const LaneAddr<D> &la) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const uint32_t row = (uint32_t)(wq0 + qb * 32 + col);
+    for (int qb = 0; qb < query_blocks<D>(); ++qb)
 #pragma unroll
-        for (int cc = 0; cc < T::KC; ++cc)
-            ws.qreg[qb][cc] = as_bf16x8(bload16(rq, row * T::ROW_BYTES + cc * 32 + g * 16));
-    }
+        for (int cc = 0; cc < Tile<D>::KC; ++cc)
+            r[qb][cc] = *reinterpret_cast<const LDS_AS bf16x8 *>(rows + la.k_off0 + qb * 32 * Tile<D>::ROW_BYTES +
+                                                               la.k_xor[cc]);
 }
 
-// Normalises and stores the wave's rows (< qlimit) of O^T as bf16 rows of o.
+// Element (row qb*32 + col, dims d0 .. d0+3) of a staged row block, d0 = db*32 + 8j + 4g:
+// logical block 4db + j, bytes 8g .. 8g+7 of it.
 template <int D>
-__device__ __forceinline__ void store_o(const WaveState<D> &ws, bf16 *odst, int qlimit, int wq0, int col, int g) {
+__device__ __forceinline__ int staged_acc_off(int qb, int db, int j, int col, int g) {
+    return (qb * 32 + col) * Tile<D>::ROW_BYTES + (((db * 4 + j) ^ k_swz<D>(col)) * 16) + 8 * g;
+}
+
+// Normalises the wave's O^T and stores it as bf16 rows of o (rows < qlimit).  The rows go
+// through the wave's own region of LDS first, so that the global stores write whole
+// rows: 16 bytes per lane, 64 / R rows per instruction.
+template <int D>
+__device__ __forceinline__ void store_o(const WaveState<D> &ws, LDS_AS char *stage, bf16 *odst, int qlimit, int wq0,
+                                        int col, int g, int lane) {
     using T = Tile<D>;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < query_blocks<D>(); ++qb) {
         const float inv = 1.f / half_sum(ws.l[qb]);
-        const int row = wq0 + qb * 32 + col;
-        if (row < qlimit) {
 #pragma unroll
-            for (int db = 0; db < T::DB; ++db)
+        for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int d0 = db * 32 + 8 * j + 4 * g;
-                    bf16x4 ov;
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 ov;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) ov[e] = (bf16)(ws.acc[db][qb][4 * j + e] * inv);
-                    *reinterpret_cast<u32x2 *>(odst + (long)row * D + d0) = __builtin_bit_cast(u32x2, ov);
-                }
-        }
+                for (int e = 0; e < 4; ++e) ov[e] = (bf16)(ws.acc[db][qb][4 * j + e] * inv);
+                *reinterpret_cast<LDS_AS bf16x4 *>(stage + staged_acc_off<D>(qb, db, j, col, g)) = ov;
+            }
+    }
+    constexpr int RPI = 64 / T::R;   // rows per store instruction
+    const int blk = lane % T::R;
+#pragma unroll
+    for (int i = 0; i < wave_rows<D>() / RPI; ++i) {
+        const int row = i * RPI + lane / T::R;
+        const u32x4 v = *reinterpret_cast<const LDS_AS u32x4 *>(stage + row * T::ROW_BYTES +
+                                                                ((blk ^ k_swz<D>(row)) * 16));
+        if (wq0 + row < qlimit) *reinterpret_cast<u32x4 *>(odst + (long)(wq0 + row) * D + blk * 8) = v;
     }
 }
 
 // The candidate's own key enters first: it sets the running max, contributes weight
 // exp2(0) = 1 to the row sum (counted once, by the lower lane half) and its value vc_j
 // to the accumulator.  An empty history therefore yields vc_j exactly, and nothing in a
-// candidate's arithmetic depends on another candidate.
+// candidate's arithmetic depends on another candidate.  kc and vc are staged row blocks.
 template <int D>
-__device__ __forceinline__ void self_key_init(WaveState<D> &ws, const bf16 *kcs, const bf16 *vcs, int qlimit, int wq0,
-                                              int col, int g, float c) {
-    using T = Tile<D>;
-    const __amdgpu_buffer_rsrc_t rkc = make_rsrc(kcs, (uint32_t)max(qlimit, 0) * T::ROW_BYTES);
-    const __amdgpu_buffer_rsrc_t rvc = make_rsrc(vcs, (uint32_t)max(qlimit, 0) * T::ROW_BYTES);
+__device__ __forceinline__ void self_key_scores(WaveState<D> &ws, const LDS_AS char *kc_rows, const LaneAddr<D> &la,
+                                                int g, float c) {
+    bf16x8 kk[query_blocks<D>()][Tile<D>::KC];
+    staged_operand<D>(kk, kc_rows, la);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const uint32_t row = (uint32_t)(wq0 + qb * 32 + col);
+    for (int qb = 0; qb < query_blocks<D>(); ++qb) {
         float part = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < T::KC; ++cc) {
-            const bf16x8 kk = as_bf16x8(bload16(rkc, row * T::ROW_BYTES + cc * 32 + g * 16));
+        for (int cc = 0; cc < Tile<D>::KC; ++cc)
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
                 const bf16x2 qa = {ws.qreg[qb][cc][e], ws.qreg[qb][cc][e + 1]};
-                const bf16x2 ka = {kk[e], kk[e + 1]};
+                const bf16x2 ka = {kk[qb][cc][e], kk[qb][cc][e + 1]};
                 part = __builtin_amdgcn_fdot2_f32_bf16(qa, ka, part, false);
             }
-        }
         ws.m[qb] = half_sum(part) * c;
         ws.l[qb] = g == 0 ? 1.f : 0.f;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void self_key_values(WaveState<D> &ws, const LDS_AS char *vc_rows, int col, int g) {
+    using T = Tile<D>;
+#pragma unroll
+    for (int qb = 0; qb < query_blocks<D>(); ++qb)
 #pragma unroll
         for (int db = 0; db < T::DB; ++db)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int d0 = db * 32 + 8 * j + 4 * g;
-                const bf16x4 vv = __builtin_bit_cast(bf16x4, bload8(rvc, row * T::ROW_BYTES + d0 * 2));
+                const bf16x4 vv = *reinterpret_cast<const LDS_AS bf16x4 *>(vc_rows + staged_acc_off<D>(qb, db, j, col, g));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ws.acc[db][qb][4 * j + e] = (float)vv[e];
             }
-    }
 }
 
 __device__ __forceinline__ bool user_valid(const AttnArgs &a, int N, int s, bool report) {
@@ -530,14 +561,24 @@ __device__ __forceinline__ void block_coords(const AttnArgs &a, int &group, int 
     }
 }
 
+// Waits until the DMA issued `after` (0, 1 or 2) tiles before the most recent one has
+// landed, i.e. with after * DPW of this wave's pieces still allowed in flight.
+template <int DPW>
+__device__ __forceinline__ void wait_pieces_after(int after) {
+    if (after >= 2) wait_vmcnt<2 * DPW>();
+    else if (after == 1) wait_vmcnt<DPW>();
+    else wait_vmcnt<0>();
+}
+
 template <int D>
 __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *__restrict__ lens,
                                              const int32_t *__restrict__ slots) {
     using T = Tile<D>;
-    constexpr int W = prefill_waves<D>();
-    constexpr int QT = W * kQW;
+    constexpr int W = block_waves<D>();
+    constexpr int QT = W * wave_rows<D>();
     constexpr int DPW = KvDma<D, W>::PER_WAVE;
     static_assert(QT % kTK == 0, "a query tile must cover whole key tiles");
+    static_assert(QT * T::ROW_BYTES == 2 * T::BUF_BYTES, "a 256-row block fills two slots");
     __shared__ __attribute__((aligned(1024))) char smem_raw[kBufs * T::BUF_BYTES];
     LDS_AS char *smem = (LDS_AS char *)smem_raw;
 
@@ -566,39 +607,46 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 31, g = lane >> 5;
-    const int wq0 = q0 + wave * kQW;
-    // This wave's DMA source: the K or the V rows of the history, rows >= kend read as 0.
+    const int wq0 = q0 + wave * wave_rows<D>();
+    // This wave's K/V DMA source: the K or the V rows of the history, rows >= kend read as 0.
     const i32x4 rsrc = rsrc_words(wave < W / 2 ? ksrc : vsrc, (uint32_t)kend * T::ROW_BYTES);
     int voff[DPW];
     dma_offsets<D, W>(voff, wave, lane);
+    const LaneAddr<D> la = lane_addr<D>(lane);
 
-#pragma unroll
-    for (int t = 0; t < kAhead; ++t)
-        if (t < ntiles) dma_tile<D, W>(smem + t * T::BUF_BYTES, rsrc, t * kTK, voff, wave);
+    // The block's query rows go to slots 2-3, K/V tiles 0 and 1 to slots 0 and 1; tile t
+    // lives in slot t % 4.
+    dma_rows<D, W>(smem + 2 * T::BUF_BYTES, rsrc_words(qsrc, (uint32_t)N * T::ROW_BYTES), q0, wave, lane);
+    int issued = 0;
+    for (; issued < 2 && issued < ntiles; ++issued)
+        dma_tile<D, W>(smem + issued * T::BUF_BYTES, rsrc, issued * kTK, voff, wave);
+    wait_pieces_after<DPW>(issued);
+    __syncthreads();
 
     WaveState<D> ws;
-    load_q<D>(ws, qsrc, N, wq0, col, g);
+    staged_operand<D>(ws.qreg, smem + 2 * T::BUF_BYTES + wave * wave_rows<D>() * T::ROW_BYTES, la);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < query_blocks<D>(); ++qb) {
         ws.m[qb] = -INFINITY;
         ws.l[qb] = 0.f;
 #pragma unroll
         for (int db = 0; db < T::DB; ++db) ws.acc[db][qb] = f32x16{};
     }
-    const LaneAddr<D> la = lane_addr<D>(lane);
 
     // A wave skips tiles wholly after its last query but keeps taking part in the tile
-    // barriers and DMA.
-    const int tlast = wq0 < N ? min(ntiles - 1, (wq0 + kQW - 1) / kTK) : -1;
+    // barriers and DMA.  Making tile t current lets the DMA run up to tile t+3, into the
+    // slot of tile t-1 (or, for t = 0, the slots the query rows came from).
+    const int tlast = wq0 < N ? min(ntiles - 1, (wq0 + wave_rows<D>() - 1) / kTK) : -1;
     auto next_tile = [&](int t) -> const LDS_AS char * {
-        wait_tiles_after<DPW>(min(ntiles - 1 - t, kAhead - 1));
+        wait_pieces_after<DPW>(issued - t - 1);
         __syncthreads();
-        if (t + kAhead < ntiles)
-            dma_tile<D, W>(smem + ((t + kAhead) % kBufs) * T::BUF_BYTES, rsrc, (t + kAhead) * kTK, voff, wave);
+        for (; issued < ntiles && issued <= t + 3; ++issued)
+            dma_tile<D, W>(smem + (issued % kBufs) * T::BUF_BYTES, rsrc, issued * kTK, voff, wave);
         return smem + (t % kBufs) * T::BUF_BYTES;
     };
     run_tiles<D, true>(ws, ntiles, tlast, kend, wq0, la, col, g, a.c, next_tile);
-    store_o<D>(ws, odst, N, wq0, col, g);
+    __syncthreads();   // every wave is done with the tile slots
+    store_o<D>(ws, smem + wave * wave_rows<D>() * T::ROW_BYTES, odst, N, wq0, col, g, lane);
 
     // fused pool write of this block's own history rows, bit for bit
     const int chunks = (kend - q0) * T::R;
@@ -611,155 +659,96 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
 
 // ------------------------------------------------------------------ ranking decode
 
-// The item sequence of one workgroup.  Items are (user*H + head, candidate
-// tile).  With the XCD mapping (user*H divisible by 8 and the grid by 8), workgroup w
-// runs on XCD w%8 and takes groups congruent to w mod 8, so all candidate tiles of a
-// (user, head) are processed on one XCD at about the same time and share its L2 copy of
-// the slot's K/V.
-struct ItemSeq {
-    int base, stride, count, tiles, xcd, remap;
-    __device__ __forceinline__ void coords(int r, int &group, int &tile) const {
-        const int s = base + r * stride;
-        if (remap) {
-            group = (s / tiles) * 8 + xcd;
-            tile = s % tiles;
-        } else {
-            group = s / tiles;
-            tile = s % tiles;
-        }
-    }
-};
-
-__device__ __forceinline__ ItemSeq item_seq(const AttnArgs &a) {
-    ItemSeq q;
-    const int G = a.B * a.H;
-    const int nwg = gridDim.x, w = blockIdx.x;
-    q.tiles = a.tiles;
-    q.remap = a.xcd_remap && (G % 8 == 0) && (nwg % 8 == 0);
-    const int total = q.remap ? (G / 8) * a.tiles : G * a.tiles;
-    q.xcd = q.remap ? (w & 7) : 0;
-    q.base = q.remap ? (w >> 3) : w;
-    q.stride = q.remap ? (nwg >> 3) : nwg;
-    q.count = q.base < total ? (total - q.base + q.stride - 1) / q.stride : 0;
-    return q;
-}
-
+// One workgroup per item: (user, head, 256-candidate tile).  The candidate rows arrive
+// by DMA like the K/V tiles: q and kc first (slots 0-1 and 2-3: the queries and the own
+// key's score), then vc (slots 0-1, the own key's value) together with K/V tiles 0 and
+// 1 (slots 2 and 3); tile t lives in slot (t + 2) % 4.
 template <int D>
 __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__restrict__ lens,
                                             const int32_t *__restrict__ slots) {
     using T = Tile<D>;
-    constexpr int W = decode_waves<D>();
-    constexpr int QT = W * kQW;
+    constexpr int W = block_waves<D>();
+    constexpr int QT = W * wave_rows<D>();
     constexpr int DPW = KvDma<D, W>::PER_WAVE;
+    static_assert(QT * T::ROW_BYTES == 2 * T::BUF_BYTES, "a 256-row block fills two slots");
     __shared__ __attribute__((aligned(1024))) char smem_raw[kBufs * T::BUF_BYTES];
     LDS_AS char *smem = (LDS_AS char *)smem_raw;
 
-    const ItemSeq seq = item_seq(a);
+    int group, ctile;
+    block_coords(a, group, ctile);
+    const int b = group / a.H, h = group % a.H;
+    if (b >= a.B) return;
+    const int N = lens[b];
+    const int s = slots[b];
+    if (!user_valid(a, N, s, ctile == 0)) return;
+
+    const long bh = (long)b * a.H + h;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 31, g = lane >> 5;
-    const LaneAddr<D> la = lane_addr<D>(lane);
+    const int row0 = ctile * QT;
+    const int wq0 = row0 + wave * wave_rows<D>();
+    const int qlimit = a.rows;
+    const uint32_t rows_bytes = (uint32_t)a.rows * T::ROW_BYTES;
+    const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
+    const i32x4 rsrc = rsrc_words(static_cast<const bf16 *>(wave < W / 2 ? a.pool_k : a.pool_v) + slot_off,
+                                  (uint32_t)N * T::ROW_BYTES);
     int voff[DPW];
     dma_offsets<D, W>(voff, wave, lane);
+    const LaneAddr<D> la = lane_addr<D>(lane);
+    const int ntiles = (N + kTK - 1) / kTK;
+    const int wrows = wave * wave_rows<D>() * T::ROW_BYTES;   // this wave's rows inside a staged block
 
-    // DMA producer: walks the same item sequence, running up to kAhead tiles ahead of the
-    // tile in use, across item boundaries.  All its state is workgroup-uniform; the item
-    // lookup runs only when it moves to the next item.
-    int p_item = -1, p_tile = 0, p_ntiles = 0;
-    i32x4 p_rsrc = rsrc_words(a.pool_k, 0);
+    dma_rows<D, W>(smem, rsrc_words(static_cast<const bf16 *>(a.q) + bh * a.rows * D, rows_bytes), row0, wave, lane);
+    dma_rows<D, W>(smem + 2 * T::BUF_BYTES, rsrc_words(static_cast<const bf16 *>(a.k) + bh * a.rows * D, rows_bytes),
+                   row0, wave, lane);
+    wait_vmcnt<0>();
+    __syncthreads();
+    WaveState<D> ws;
+    staged_operand<D>(ws.qreg, smem + wrows, la);
+    self_key_scores<D>(ws, smem + 2 * T::BUF_BYTES + wrows, la, g, a.c);
+    __syncthreads();   // slots 0-3 are free again
+
+    dma_rows<D, W>(smem, rsrc_words(static_cast<const bf16 *>(a.v) + bh * a.rows * D, rows_bytes), row0, wave, lane);
     int issued = 0;
-    auto produce = [&]() -> bool {
-        while (p_tile >= p_ntiles) {
-            if (p_item + 1 >= seq.count) return false;
-            ++p_item;
-            p_tile = 0;
-            int group, ctile;
-            seq.coords(p_item, group, ctile);
-            const int b = group / a.H, h = group % a.H;
-            const int N = lens[b];
-            const int s = slots[b];
-            const bool ok = N >= 0 && N <= a.len_limit && s >= 0 && s < a.S;
-            p_ntiles = ok ? (N + kTK - 1) / kTK : 0;
-            if (ok) {
-                const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
-                const void *base = static_cast<const bf16 *>(wave < W / 2 ? a.pool_k : a.pool_v) + slot_off;
-                p_rsrc = rsrc_words(base, (uint32_t)N * T::ROW_BYTES);
-            }
-        }
-        dma_tile<D, W>(smem + (issued % kBufs) * T::BUF_BYTES, p_rsrc, p_tile * kTK, voff, wave);
-        ++p_tile;
-        ++issued;
-        return true;
+    for (; issued < 2 && issued < ntiles; ++issued)
+        dma_tile<D, W>(smem + (issued + 2) * T::BUF_BYTES, rsrc, issued * kTK, voff, wave);
+    wait_pieces_after<DPW>(issued);
+    __syncthreads();
+    self_key_values<D>(ws, smem + wrows, col, g);
+
+    auto next_tile = [&](int t) -> const LDS_AS char * {
+        wait_pieces_after<DPW>(issued - t - 1);
+        __syncthreads();
+        for (; issued < ntiles && issued <= t + 3; ++issued)
+            dma_tile<D, W>(smem + ((issued + 2) % kBufs) * T::BUF_BYTES, rsrc, issued * kTK, voff, wave);
+        return smem + ((t + 2) % kBufs) * T::BUF_BYTES;
     };
-    for (int i = 0; i < kAhead; ++i) produce();
-
-    int consumed = 0;
-    for (int r = 0; r < seq.count; ++r) {
-        int group, ctile;
-        seq.coords(r, group, ctile);
-        const int b = group / a.H, h = group % a.H;
-        const int N = lens[b];
-        const int s = slots[b];
-        if (!user_valid(a, N, s, ctile == 0)) continue;   // the producer skipped it too
-
-        const long bh = (long)b * a.H + h;
-        const int wq0 = ctile * QT + wave * kQW;
-        const int qlimit = a.rows;
-        const bf16 *qsrc = static_cast<const bf16 *>(a.q) + bh * a.rows * D;
-        const bf16 *kcs = static_cast<const bf16 *>(a.k) + bh * a.rows * D;
-        const bf16 *vcs = static_cast<const bf16 *>(a.v) + bh * a.rows * D;
-        bf16 *odst = static_cast<bf16 *>(a.o) + bh * a.rows * D;
-
-        WaveState<D> ws;
-        load_q<D>(ws, qsrc, qlimit, wq0, col, g);
-        self_key_init<D>(ws, kcs, vcs, qlimit, wq0, col, g, a.c);
-
-        const int ntiles = (N + kTK - 1) / kTK;
-        auto next_tile = [&](int) -> const LDS_AS char * {
-            wait_tiles_after<DPW>(issued - consumed - 1);
-            __syncthreads();
-            while (issued < consumed + kAhead + 1 && produce()) {
-            }
-            const LDS_AS char *buf = smem + (consumed % kBufs) * T::BUF_BYTES;
-            ++consumed;
-            return buf;
-        };
-        run_tiles<D, false>(ws, ntiles, wq0 < qlimit ? ntiles - 1 : -1, N, wq0, la, col, g, a.c, next_tile);
-        store_o<D>(ws, odst, qlimit, wq0, col, g);
-    }
+    run_tiles<D, false>(ws, ntiles, wq0 < qlimit ? ntiles - 1 : -1, N, wq0, la, col, g, a.c, next_tile);
+    __syncthreads();   // every wave is done with the tile slots
+    store_o<D>(ws, smem + wrows, static_cast<bf16 *>(a.o) + bh * a.rows * D, qlimit, wq0, col, g, lane);
 }
 
 template <int D>
-__global__ void __launch_bounds__(prefill_waves<D>() * 64, prefill_min_blocks<D>()) prefill_bf16_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
+__global__ void __launch_bounds__(block_waves<D>() * 64, min_blocks<D>()) prefill_bf16_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
     prefill_body<D>(a, lens, slots);
 }
 
 template <int D>
-__global__ void __launch_bounds__(decode_waves<D>() * 64, decode_min_blocks<D>()) rank_decode_bf16_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
+__global__ void __launch_bounds__(block_waves<D>() * 64, min_blocks<D>()) rank_decode_bf16_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
     decode_body<D>(a, lens, slots);
-}
-
-int g_cu_count[64];
-
-int cu_count() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!g_cu_count[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        g_cu_count[dev] = n;
-    }
-    return g_cu_count[dev];
 }
 
 }  // namespace
 
 int bf16_prefill_rows_per_block(int D) {
-    return (D <= 32 ? prefill_waves<32>() : D <= 64 ? prefill_waves<64>() : prefill_waves<128>()) * kQW;
+    (void)D;
+    return kBlockRows;
 }
 
 int bf16_decode_rows_per_item(int D) {
-    return (D <= 32 ? decode_waves<32>() : D <= 64 ? decode_waves<64>() : decode_waves<128>()) * kQW;
+    (void)D;
+    return kBlockRows;
 }
 
 hipError_t launch_prefill_bf16(const AttnArgs &a, int D, hipStream_t stream) {
@@ -768,9 +757,9 @@ hipError_t launch_prefill_bf16(const AttnArgs &a, int D, hipStream_t stream) {
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks);
     switch (D) {
-        case 32: hipLaunchKernelGGL(prefill_bf16_kernel<32>, grid, dim3(prefill_waves<32>() * 64), 0, stream, a, a.lens, a.slot); break;
-        case 64: hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(prefill_waves<64>() * 64), 0, stream, a, a.lens, a.slot); break;
-        case 128: hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(prefill_waves<128>() * 64), 0, stream, a, a.lens, a.slot); break;
+        case 32: hipLaunchKernelGGL(prefill_bf16_kernel<32>, grid, dim3(block_waves<32>() * 64), 0, stream, a, a.lens, a.slot); break;
+        case 64: hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(block_waves<64>() * 64), 0, stream, a, a.lens, a.slot); break;
+        case 128: hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(block_waves<128>() * 64), 0, stream, a, a.lens, a.slot); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -779,16 +768,12 @@ hipError_t launch_prefill_bf16(const AttnArgs &a, int D, hipStream_t stream) {
 hipError_t launch_decode_bf16(const AttnArgs &a, int D, hipStream_t stream) {
     const long items = (long)a.B * a.H * a.tiles;
     if (items <= 0) return hipSuccess;
-    // Persistent grid (a fixed number of workgroups per CU, never more than there are
-    // items), or one workgroup per item.
-    long grid_n = UNIPIN_DECODE_GRID_PER_CU > 0 ? (long)cu_count() * UNIPIN_DECODE_GRID_PER_CU : items;
-    if (grid_n > items) grid_n = items;
-    if (grid_n > 0x7fffffffL) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)grid_n);
+    if (items > 0x7fffffffL) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)items);
     switch (D) {
-        case 32: hipLaunchKernelGGL(rank_decode_bf16_kernel<32>, grid, dim3(decode_waves<32>() * 64), 0, stream, a, a.lens, a.slot); break;
-        case 64: hipLaunchKernelGGL(rank_decode_bf16_kernel<64>, grid, dim3(decode_waves<64>() * 64), 0, stream, a, a.lens, a.slot); break;
-        case 128: hipLaunchKernelGGL(rank_decode_bf16_kernel<128>, grid, dim3(decode_waves<128>() * 64), 0, stream, a, a.lens, a.slot); break;
+        case 32: hipLaunchKernelGGL(rank_decode_bf16_kernel<32>, grid, dim3(block_waves<32>() * 64), 0, stream, a, a.lens, a.slot); break;
+        case 64: hipLaunchKernelGGL(rank_decode_bf16_kernel<64>, grid, dim3(block_waves<64>() * 64), 0, stream, a, a.lens, a.slot); break;
+        case 128: hipLaunchKernelGGL(rank_decode_bf16_kernel<128>, grid, dim3(block_waves<128>() * 64), 0, stream, a, a.lens, a.slot); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
