@@ -205,13 +205,15 @@ __device__ __forceinline__ void dma_tile(LDS_AS char *buf, i32x4 rsrc, int kbase
     for (int j = 0; j < KvDma<D, W>::PER_WAVE; ++j) dma16(dst + j * 1024, rsrc, voff[j], soff);
 }
 
-// DMA of one block of 256 query (or candidate) rows, W waves x 64, into two consecutive
-// LDS slots with the K swizzle: 16-byte block bi of the block in LDS order is row
-// bi / R, logical block (bi % R) ^ k_swz(row).  Rows past the record count read as zero.
-template <int D, int W>
+// DMA of ROWS consecutive query (or candidate) rows from row0 into LDS with the K
+// swizzle: 16-byte block bi of the block in LDS order is row bi / R, logical block
+// (bi % R) ^ k_swz(row).  Rows past the record count read as zero.  A 256-row block
+// fills two LDS slots, a 128-row half block one.
+template <int D, int W, int ROWS>
 __device__ __forceinline__ void dma_rows(LDS_AS char *dst, i32x4 rsrc, int row0, int wave, int lane) {
     using T = Tile<D>;
-    constexpr int PW = kBlockRows * T::ROW_BYTES / 1024 / W;   // 1 KB pieces per wave
+    constexpr int PW = ROWS * T::ROW_BYTES / 1024 / W;   // 1 KB pieces per wave
+    static_assert(PW >= 1 && PW * W * 1024 == ROWS * T::ROW_BYTES, "the block must split evenly");
     const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(dst);
     const int soff = row0 * T::ROW_BYTES;
 #pragma unroll
@@ -277,9 +279,9 @@ __device__ __forceinline__ void tile_scores(f32x16 (&sc)[2][query_blocks<D>()], 
 #pragma unroll
         for (int qb = 0; qb < query_blocks<D>(); ++qb) sc[kb][qb] = f32x16{};
 #pragma unroll
-    for (int cc = 0; cc < T::KC; ++cc) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int cc = 0; cc < T::KC; ++cc) {
             const bf16x8 ka = *reinterpret_cast<const LDS_AS bf16x8 *>(kt + la.k_off0 + kb * 32 * T::ROW_BYTES + la.k_xor[cc]);
 #pragma unroll
             for (int qb = 0; qb < query_blocks<D>(); ++qb)
@@ -335,28 +337,29 @@ __device__ __forceinline__ void tile_exp(bf16x8 (&pb)[2][query_blocks<D>()], flo
     }
 }
 
-// Lazy rescale.  The running max m of a row only has to keep the weights in range: the
-// tile is first evaluated against the current m, and only a row whose lane sum of
-// weights exceeds kFastSumLimit, or is not finite (m = -inf before the row's first
-// tile), moves m to max(m, tile max), scales its accumulator and row sum by
-// exp2(m_old - m_new) and re-evaluates the tile.  With the limit at 2^64 a weight never
-// exceeds 2^64, so for histories up to 2^20 keys the fp32 row sum and accumulators stay
-// below 2^84 |v|: far from overflow, and the bf16 weights keep their full relative
-// precision.  In practice only a row's first tile takes the slow path.  The decision is
-// per row (both lane halves of a row agree), so a row's arithmetic never depends on the
-// other rows of the wave; the branch is wave-wide.
+// Lazy rescale, per 32-key block.  The running max m of a row only has to keep the
+// weights in range: a key block is first evaluated against the current m, and only a
+// row whose lane sum of weights exceeds kFastSumLimit, or is not finite (m = -inf
+// before the row's first block), moves m to max(m, block max), scales its accumulator
+// and row sum by exp2(m_old - m_new) and re-evaluates the block.  With the limit at 2^64
+// a weight never exceeds 2^64, so for histories up to 2^20 keys the fp32 row sum and
+// accumulators stay below 2^84 |v|: far from overflow, and the bf16 weights keep their
+// full relative precision.  In practice only a row's first block takes the slow path.
+// The decision is per row (both lane halves of a row agree), so a row's arithmetic
+// never depends on the other rows of the wave; the branch is wave-wide.  Working per key
+// block lets the PV product of one block run on the matrix cores while the vector ALU
+// computes the weights of the next.
 constexpr float kFastSumLimit = 18446744073709551616.0f;   // 2^64
 
 template <int D>
-__device__ __forceinline__ void tile_softmax(bf16x8 (&pb)[2][2][query_blocks<D>()], WaveState<D> &ws,
-                                             const f32x16 (&sc)[2][query_blocks<D>()], float c) {
+__device__ __forceinline__ void block_softmax(bf16x8 (&pb)[2][query_blocks<D>()], WaveState<D> &ws,
+                                              const f32x16 (&sc)[2][query_blocks<D>()], int kb, float c) {
     using T = Tile<D>;
     constexpr int QB = query_blocks<D>();
     float lsum[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) lsum[qb] = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) tile_exp<D>(pb[kb], lsum, sc, kb, ws, c);
+    tile_exp<D>(pb, lsum, sc, kb, ws, c);
     bool slow = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) slow |= !(lsum[qb] <= kFastSumLimit);
@@ -367,11 +370,9 @@ __device__ __forceinline__ void tile_softmax(bf16x8 (&pb)[2][2][query_blocks<D>(
         for (int qb = 0; qb < QB; ++qb) {
             const float mine = !(lsum[qb] <= kFastSumLimit) ? 1.f : 0.f;
             const bool grow = half_max(mine) > 0.f;   // either half of the row
-            float mx = sc[0][qb][0];
+            float mx = sc[kb][qb][0];
 #pragma unroll
-            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[0][qb][i]);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[1][qb][i]);
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[kb][qb][i]);
             const float mt = half_max(mx) * c;
             const float mn = grow ? fmaxf(ws.m[qb], mt) : ws.m[qb];
             const float alpha = grow ? __builtin_amdgcn_exp2f(ws.m[qb] - mn) : 1.f;
@@ -381,8 +382,7 @@ __device__ __forceinline__ void tile_softmax(bf16x8 (&pb)[2][2][query_blocks<D>(
             ws.m[qb] = mn;
             lsum[qb] = 0.f;
         }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) tile_exp<D>(pb[kb], lsum, sc, kb, ws, c);
+        tile_exp<D>(pb, lsum, sc, kb, ws, c);
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) ws.l[qb] += lsum[qb];
@@ -411,8 +411,8 @@ __device__ __forceinline__ void tile_pv(WaveState<D> &ws, const bf16x8 (&pb)[2][
         }
 }
 
-// One whole tile for one wave: scores, optional mask, weights with the lazy rescale,
-// then the PV product.
+// One whole tile for one wave: scores, optional mask, then per 32-key block the weights
+// with the lazy rescale and the PV product.
 template <int D, bool PREFILL>
 __device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *kt, const LDS_AS char *vt,
                                           int kbase, int kend, int wq0, bool masked,
@@ -420,10 +420,12 @@ __device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *k
     f32x16 sc[2][query_blocks<D>()];
     tile_scores<D>(sc, ws, kt, la);
     if (masked) tile_mask<D, PREFILL>(sc, kbase, kend, wq0, col, g);
-    bf16x8 pb[2][2][query_blocks<D>()];
-    tile_softmax<D>(pb, ws, sc, c);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) tile_pv<D>(ws, pb[kb], kb, vt, la);
+    for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 pb[2][query_blocks<D>()];
+        block_softmax<D>(pb, ws, sc, kb, c);
+        tile_pv<D>(ws, pb, kb, vt, la);
+    }
 }
 
 // Runs the wave over K/V tiles 0 .. ntiles-1.  next_tile(u) makes tile u current (wait
@@ -495,13 +497,14 @@ __device__ __forceinline__ void store_o(const WaveState<D> &ws, LDS_AS char *sta
     }
 }
 
-// The candidate's own key enters first: it sets the running max, contributes weight
-// exp2(0) = 1 to the row sum (counted once, by the lower lane half) and its value vc_j
-// to the accumulator.  An empty history therefore yields vc_j exactly, and nothing in a
-// candidate's arithmetic depends on another candidate.  kc and vc are staged row blocks.
+// The candidate's own key.  Its score s_j = scale*log2(e) * qc_j . kc_j starts the
+// running max (m = s_j, empty row sum and accumulator), and after the history its value
+// is merged with weight exp2(s_j - m) <= 1 (m only grows).  An empty history therefore
+// yields vc_j exactly, and nothing in a candidate's arithmetic depends on another
+// candidate.  kc and vc come from staged row blocks.
 template <int D>
-__device__ __forceinline__ void self_key_scores(WaveState<D> &ws, const LDS_AS char *kc_rows, const LaneAddr<D> &la,
-                                                int g, float c) {
+__device__ __forceinline__ void self_key_scores(WaveState<D> &ws, float (&sself)[query_blocks<D>()],
+                                                const LDS_AS char *kc_rows, const LaneAddr<D> &la, float c) {
     bf16x8 kk[query_blocks<D>()][Tile<D>::KC];
     staged_operand<D>(kk, kc_rows, la);
 #pragma unroll
@@ -515,24 +518,32 @@ __device__ __forceinline__ void self_key_scores(WaveState<D> &ws, const LDS_AS c
                 const bf16x2 ka = {kk[qb][cc][e], kk[qb][cc][e + 1]};
                 part = __builtin_amdgcn_fdot2_f32_bf16(qa, ka, part, false);
             }
-        ws.m[qb] = half_sum(part) * c;
-        ws.l[qb] = g == 0 ? 1.f : 0.f;
+        sself[qb] = half_sum(part) * c;
+        ws.m[qb] = sself[qb];
+        ws.l[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < Tile<D>::DB; ++db) ws.acc[db][qb] = f32x16{};
     }
 }
 
 template <int D>
-__device__ __forceinline__ void self_key_values(WaveState<D> &ws, const LDS_AS char *vc_rows, int col, int g) {
+__device__ __forceinline__ void self_key_merge(WaveState<D> &ws, const float (&sself)[query_blocks<D>()],
+                                               const LDS_AS char *vc_rows, int col, int g) {
     using T = Tile<D>;
 #pragma unroll
-    for (int qb = 0; qb < query_blocks<D>(); ++qb)
+    for (int qb = 0; qb < query_blocks<D>(); ++qb) {
+        const float ps = __builtin_amdgcn_exp2f(sself[qb] - ws.m[qb]);
+        ws.l[qb] += g == 0 ? ps : 0.f;   // counted once per row, by the lower lane half
 #pragma unroll
         for (int db = 0; db < T::DB; ++db)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bf16x4 vv = *reinterpret_cast<const LDS_AS bf16x4 *>(vc_rows + staged_acc_off<D>(qb, db, j, col, g));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ws.acc[db][qb][4 * j + e] = (float)vv[e];
+                for (int e = 0; e < 4; ++e)
+                    ws.acc[db][qb][4 * j + e] = __builtin_fmaf(ps, (float)vv[e], ws.acc[db][qb][4 * j + e]);
             }
+    }
 }
 
 __device__ __forceinline__ bool user_valid(const AttnArgs &a, int N, int s, bool report) {
@@ -616,7 +627,7 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
 
     // The block's query rows go to slots 2-3, K/V tiles 0 and 1 to slots 0 and 1; tile t
     // lives in slot t % 4.
-    dma_rows<D, W>(smem + 2 * T::BUF_BYTES, rsrc_words(qsrc, (uint32_t)N * T::ROW_BYTES), q0, wave, lane);
+    dma_rows<D, W, kBlockRows>(smem + 2 * T::BUF_BYTES, rsrc_words(qsrc, (uint32_t)N * T::ROW_BYTES), q0, wave, lane);
     int issued = 0;
     for (; issued < 2 && issued < ntiles; ++issued)
         dma_tile<D, W>(smem + issued * T::BUF_BYTES, rsrc, issued * kTK, voff, wave);
@@ -661,8 +672,9 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
 
 // One workgroup per item: (user, head, 256-candidate tile).  The candidate rows arrive
 // by DMA like the K/V tiles: q and kc first (slots 0-1 and 2-3: the queries and the own
-// key's score), then vc (slots 0-1, the own key's value) together with K/V tiles 0 and
-// 1 (slots 2 and 3); tile t lives in slot (t + 2) % 4.
+// key's score), then a stream of steps through the four slots, step u in slot u % 4:
+// the K/V tiles 0 .. ntiles-1, then the two 128-row halves of vc, so that the own
+// key's values load in the background while the history is processed.
 template <int D>
 __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__restrict__ lens,
                                             const int32_t *__restrict__ slots) {
@@ -670,7 +682,9 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
     constexpr int W = block_waves<D>();
     constexpr int QT = W * wave_rows<D>();
     constexpr int DPW = KvDma<D, W>::PER_WAVE;
+    constexpr int HALF = kBlockRows / 2;
     static_assert(QT * T::ROW_BYTES == 2 * T::BUF_BYTES, "a 256-row block fills two slots");
+    static_assert(HALF * T::ROW_BYTES / 1024 / W == DPW, "a vc half block moves like one K/V tile");
     __shared__ __attribute__((aligned(1024))) char smem_raw[kBufs * T::BUF_BYTES];
     LDS_AS char *smem = (LDS_AS char *)smem_raw;
 
@@ -689,43 +703,55 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
     const int row0 = ctile * QT;
     const int wq0 = row0 + wave * wave_rows<D>();
     const int qlimit = a.rows;
+    const bool active = wq0 < qlimit;
     const uint32_t rows_bytes = (uint32_t)a.rows * T::ROW_BYTES;
     const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
     const i32x4 rsrc = rsrc_words(static_cast<const bf16 *>(wave < W / 2 ? a.pool_k : a.pool_v) + slot_off,
                                   (uint32_t)N * T::ROW_BYTES);
+    const i32x4 rsrc_vc = rsrc_words(static_cast<const bf16 *>(a.v) + bh * a.rows * D, rows_bytes);
     int voff[DPW];
     dma_offsets<D, W>(voff, wave, lane);
     const LaneAddr<D> la = lane_addr<D>(lane);
     const int ntiles = (N + kTK - 1) / kTK;
+    const int nsteps = ntiles + 2;
     const int wrows = wave * wave_rows<D>() * T::ROW_BYTES;   // this wave's rows inside a staged block
 
-    dma_rows<D, W>(smem, rsrc_words(static_cast<const bf16 *>(a.q) + bh * a.rows * D, rows_bytes), row0, wave, lane);
-    dma_rows<D, W>(smem + 2 * T::BUF_BYTES, rsrc_words(static_cast<const bf16 *>(a.k) + bh * a.rows * D, rows_bytes),
-                   row0, wave, lane);
+    dma_rows<D, W, kBlockRows>(smem, rsrc_words(static_cast<const bf16 *>(a.q) + bh * a.rows * D, rows_bytes), row0,
+                               wave, lane);
+    dma_rows<D, W, kBlockRows>(smem + 2 * T::BUF_BYTES,
+                               rsrc_words(static_cast<const bf16 *>(a.k) + bh * a.rows * D, rows_bytes), row0, wave,
+                               lane);
     wait_vmcnt<0>();
     __syncthreads();
     WaveState<D> ws;
+    float sself[query_blocks<D>()];
     staged_operand<D>(ws.qreg, smem + wrows, la);
-    self_key_scores<D>(ws, smem + 2 * T::BUF_BYTES + wrows, la, g, a.c);
+    self_key_scores<D>(ws, sself, smem + 2 * T::BUF_BYTES + wrows, la, a.c);
     __syncthreads();   // slots 0-3 are free again
 
-    dma_rows<D, W>(smem, rsrc_words(static_cast<const bf16 *>(a.v) + bh * a.rows * D, rows_bytes), row0, wave, lane);
-    int issued = 0;
-    for (; issued < 2 && issued < ntiles; ++issued)
-        dma_tile<D, W>(smem + (issued + 2) * T::BUF_BYTES, rsrc, issued * kTK, voff, wave);
-    wait_pieces_after<DPW>(issued);
-    __syncthreads();
-    self_key_values<D>(ws, smem + wrows, col, g);
-
-    auto next_tile = [&](int t) -> const LDS_AS char * {
-        wait_pieces_after<DPW>(issued - t - 1);
-        __syncthreads();
-        for (; issued < ntiles && issued <= t + 3; ++issued)
-            dma_tile<D, W>(smem + ((issued + 2) % kBufs) * T::BUF_BYTES, rsrc, issued * kTK, voff, wave);
-        return smem + ((t + 2) % kBufs) * T::BUF_BYTES;
+    auto issue = [&](int u) {
+        LDS_AS char *dst = smem + (u % kBufs) * T::BUF_BYTES;
+        if (u < ntiles) dma_tile<D, W>(dst, rsrc, u * kTK, voff, wave);
+        else dma_rows<D, W, HALF>(dst, rsrc_vc, row0 + (u - ntiles) * HALF, wave, lane);
     };
-    run_tiles<D, false>(ws, ntiles, wq0 < qlimit ? ntiles - 1 : -1, N, wq0, la, col, g, a.c, next_tile);
-    __syncthreads();   // every wave is done with the tile slots
+    int issued = 0;
+    for (; issued < 3 && issued < nsteps; ++issued) issue(issued);
+    // Makes step u current: waits for its DMA, workgroup barrier (after which the slot of
+    // step u-1 is free), and lets the DMA run up to step u+3.
+    auto next_step = [&](int u) -> const LDS_AS char * {
+        wait_pieces_after<DPW>(issued - u - 1);
+        __syncthreads();
+        for (; issued < nsteps && issued <= u + 3; ++issued) issue(issued);
+        return smem + (u % kBufs) * T::BUF_BYTES;
+    };
+    run_tiles<D, false>(ws, ntiles, active ? ntiles - 1 : -1, N, wq0, la, col, g, a.c, next_step);
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv) {
+        const LDS_AS char *vc_half = next_step(ntiles + hv);
+        if (active && wave / (W / 2) == hv)
+            self_key_merge<D>(ws, sself, vc_half + (wave % (W / 2)) * wave_rows<D>() * T::ROW_BYTES, col, g);
+    }
+    __syncthreads();   // every wave is done with the slots
     store_o<D>(ws, smem + wrows, static_cast<bf16 *>(a.o) + bh * a.rows * D, qlimit, wq0, col, g, lane);
 }
 
