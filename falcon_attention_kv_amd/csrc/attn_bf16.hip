@@ -64,19 +64,21 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTK = 64;                   // keys per LDS tile
-constexpr int kBufs = 4;                  // LDS tile buffers
+// LDS slots of the DMA ring (one 64-key K/V tile or 128 query rows each): 64 KB per
+// workgroup at D = 64, so that two workgroups share a CU.
+constexpr int kBufs = 4;
 
 // A workgroup covers 256 query rows.  A wave holds QB blocks of 32 query rows: one at
 // D <= 64 (8 waves per workgroup, two workgroups per CU: 4 waves per SIMD with at most
 // 128 registers each), two at D = 128 (4 waves of 64 rows, one workgroup per CU).
-#ifndef UNIPIN_QB_SMALL_D
-#define UNIPIN_QB_SMALL_D 1
-#endif
 constexpr int kBlockRows = 256;
-template <int D> constexpr int query_blocks() { return D <= 64 ? UNIPIN_QB_SMALL_D : 2; }
+template <int D> constexpr int query_blocks() { return D <= 64 ? 1 : 2; }
 template <int D> constexpr int wave_rows() { return 32 * query_blocks<D>(); }
 template <int D> constexpr int block_waves() { return kBlockRows / wave_rows<D>(); }
-template <int D> constexpr int min_blocks() { return D <= 64 ? 2 : 1; }
+// Minimum waves per SIMD the kernels are compiled for (the second __launch_bounds__
+// argument): 4 at D <= 64 (two 8-wave workgroups per CU, at most 128 registers per
+// lane), 1 at D = 128.
+template <int D> constexpr int min_waves_per_simd() { return D <= 64 ? 4 : 1; }
 
 constexpr uint32_t kBufferWord3 = 0x00020000u;   // gfx9 buffer descriptor, raw 32-bit access
 
@@ -572,11 +574,12 @@ __device__ __forceinline__ void block_coords(const AttnArgs &a, int &group, int 
     }
 }
 
-// Waits until the DMA issued `after` (0, 1 or 2) tiles before the most recent one has
+// Waits until the DMA step issued `after` (0 .. 3) steps before the most recent one has
 // landed, i.e. with after * DPW of this wave's pieces still allowed in flight.
 template <int DPW>
 __device__ __forceinline__ void wait_pieces_after(int after) {
-    if (after >= 2) wait_vmcnt<2 * DPW>();
+    if (after >= 3) wait_vmcnt<3 * DPW>();
+    else if (after == 2) wait_vmcnt<2 * DPW>();
     else if (after == 1) wait_vmcnt<DPW>();
     else wait_vmcnt<0>();
 }
@@ -625,17 +628,18 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
     dma_offsets<D, W>(voff, wave, lane);
     const LaneAddr<D> la = lane_addr<D>(lane);
 
-    // The block's query rows go to slots 2-3, K/V tiles 0 and 1 to slots 0 and 1; tile t
-    // lives in slot t % 4.
-    dma_rows<D, W, kBlockRows>(smem + 2 * T::BUF_BYTES, rsrc_words(qsrc, (uint32_t)N * T::ROW_BYTES), q0, wave, lane);
+    // The block's query rows go to the last two slots, the first K/V tiles to the others;
+    // tile t lives in slot t % kBufs.
+    dma_rows<D, W, kBlockRows>(smem + (kBufs - 2) * T::BUF_BYTES, rsrc_words(qsrc, (uint32_t)N * T::ROW_BYTES), q0,
+                               wave, lane);
     int issued = 0;
-    for (; issued < 2 && issued < ntiles; ++issued)
+    for (; issued < kBufs - 2 && issued < ntiles; ++issued)
         dma_tile<D, W>(smem + issued * T::BUF_BYTES, rsrc, issued * kTK, voff, wave);
     wait_pieces_after<DPW>(issued);
     __syncthreads();
 
     WaveState<D> ws;
-    staged_operand<D>(ws.qreg, smem + 2 * T::BUF_BYTES + wave * wave_rows<D>() * T::ROW_BYTES, la);
+    staged_operand<D>(ws.qreg, smem + (kBufs - 2) * T::BUF_BYTES + wave * wave_rows<D>() * T::ROW_BYTES, la);
 #pragma unroll
     for (int qb = 0; qb < query_blocks<D>(); ++qb) {
         ws.m[qb] = -INFINITY;
@@ -645,13 +649,13 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
     }
 
     // A wave skips tiles wholly after its last query but keeps taking part in the tile
-    // barriers and DMA.  Making tile t current lets the DMA run up to tile t+3, into the
-    // slot of tile t-1 (or, for t = 0, the slots the query rows came from).
+    // barriers and DMA.  Making tile t current lets the DMA run up to tile t+kBufs-1,
+    // into the slot of tile t-1 (or, for t = 0, the slots the query rows came from).
     const int tlast = wq0 < N ? min(ntiles - 1, (wq0 + wave_rows<D>() - 1) / kTK) : -1;
     auto next_tile = [&](int t) -> const LDS_AS char * {
         wait_pieces_after<DPW>(issued - t - 1);
         __syncthreads();
-        for (; issued < ntiles && issued <= t + 3; ++issued)
+        for (; issued < ntiles && issued <= t + kBufs - 1; ++issued)
             dma_tile<D, W>(smem + (issued % kBufs) * T::BUF_BYTES, rsrc, issued * kTK, voff, wave);
         return smem + (t % kBufs) * T::BUF_BYTES;
     };
@@ -672,7 +676,7 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
 
 // One workgroup per item: (user, head, 256-candidate tile).  The candidate rows arrive
 // by DMA like the K/V tiles: q and kc first (slots 0-1 and 2-3: the queries and the own
-// key's score), then a stream of steps through the four slots, step u in slot u % 4:
+// key's score), then a stream of steps through the ring, step u in slot u % kBufs:
 // the K/V tiles 0 .. ntiles-1, then the two 128-row halves of vc, so that the own
 // key's values load in the background while the history is processed.
 template <int D>
@@ -727,7 +731,7 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
     float sself[query_blocks<D>()];
     staged_operand<D>(ws.qreg, smem + wrows, la);
     self_key_scores<D>(ws, sself, smem + 2 * T::BUF_BYTES + wrows, la, a.c);
-    __syncthreads();   // slots 0-3 are free again
+    __syncthreads();   // the header slots are free again
 
     auto issue = [&](int u) {
         LDS_AS char *dst = smem + (u % kBufs) * T::BUF_BYTES;
@@ -735,13 +739,13 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
         else dma_rows<D, W, HALF>(dst, rsrc_vc, row0 + (u - ntiles) * HALF, wave, lane);
     };
     int issued = 0;
-    for (; issued < 3 && issued < nsteps; ++issued) issue(issued);
+    for (; issued < kBufs - 1 && issued < nsteps; ++issued) issue(issued);
     // Makes step u current: waits for its DMA, workgroup barrier (after which the slot of
-    // step u-1 is free), and lets the DMA run up to step u+3.
+    // step u-1 is free), and lets the DMA run up to step u+kBufs-1.
     auto next_step = [&](int u) -> const LDS_AS char * {
         wait_pieces_after<DPW>(issued - u - 1);
         __syncthreads();
-        for (; issued < nsteps && issued <= u + 3; ++issued) issue(issued);
+        for (; issued < nsteps && issued <= u + kBufs - 1; ++issued) issue(issued);
         return smem + (u % kBufs) * T::BUF_BYTES;
     };
     run_tiles<D, false>(ws, ntiles, active ? ntiles - 1 : -1, N, wq0, la, col, g, a.c, next_step);
@@ -756,12 +760,12 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
 }
 
 template <int D>
-__global__ void __launch_bounds__(block_waves<D>() * 64, min_blocks<D>()) prefill_bf16_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
+__global__ void __launch_bounds__(block_waves<D>() * 64, min_waves_per_simd<D>()) prefill_bf16_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
     prefill_body<D>(a, lens, slots);
 }
 
 template <int D>
-__global__ void __launch_bounds__(block_waves<D>() * 64, min_blocks<D>()) rank_decode_bf16_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
+__global__ void __launch_bounds__(block_waves<D>() * 64, min_waves_per_simd<D>()) rank_decode_bf16_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
     decode_body<D>(a, lens, slots);
 }
 
