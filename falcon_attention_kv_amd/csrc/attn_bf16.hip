@@ -67,6 +67,9 @@ constexpr int kTK = 64;                   // keys per LDS tile
 // LDS slots of the DMA ring (one 64-key K/V tile or 128 query rows each): 64 KB per
 // workgroup at D = 64, so that two workgroups share a CU.
 constexpr int kBufs = 4;
+#ifndef UNIPIN_PREFILL_TILE_MAJOR
+#define UNIPIN_PREFILL_TILE_MAJOR 1
+#endif
 
 // A workgroup covers 256 query rows.  A wave holds QB blocks of 32 query rows: one at
 // D <= 64 (8 waves per workgroup, two workgroups per CU: 4 waves per SIMD with at most
@@ -224,6 +227,30 @@ __device__ __forceinline__ void dma_rows(LDS_AS char *dst, i32x4 rsrc, int row0,
         const int bi = piece * 64 + lane;
         const int row = bi / T::R, blk = (bi % T::R) ^ k_swz<D>(row);
         dma16(base + piece * 1024, rsrc, row * T::ROW_BYTES + blk * 16, soff);
+    }
+}
+
+// Copies keys [kbase, min(kbase + 64, kend)) of a staged K/V tile into the pool slot
+// rows (pk, pv: the slot's K and V rows 0..), undoing the LDS swizzles: whole rows, 16
+// bytes per lane, rows at or past kend untouched.
+template <int D, int W>
+__device__ __forceinline__ void tile_to_pool(const LDS_AS char *tile, bf16 *pk, bf16 *pv, int kbase, int kend,
+                                             int tid) {
+    using T = Tile<D>;
+    constexpr int BLOCKS = kTK * T::R;   // 16-byte blocks of one matrix
+#pragma unroll
+    for (int i0 = 0; i0 < BLOCKS; i0 += W * 64) {
+        const int i = i0 + tid;
+        const int key = i / T::R, blk = i % T::R;
+        if (i < BLOCKS && kbase + key < kend) {
+            const u32x4 kx = *reinterpret_cast<const LDS_AS u32x4 *>(tile + key * T::ROW_BYTES +
+                                                                     ((blk ^ k_swz<D>(key)) * 16));
+            const u32x4 vx = *reinterpret_cast<const LDS_AS u32x4 *>(tile + T::MAT_BYTES + key * T::ROW_BYTES +
+                                                                     ((blk ^ v_swz<D>(key)) * 16));
+            const long off = (long)(kbase + key) * D + blk * 8;
+            *reinterpret_cast<u32x4 *>(pk + off) = kx;
+            *reinterpret_cast<u32x4 *>(pv + off) = vx;
+        }
     }
 }
 
@@ -559,15 +586,27 @@ __device__ __forceinline__ bool user_valid(const AttnArgs &a, int N, int s, bool
 // ------------------------------------------------------------------ causal prefill
 
 // Maps the linear block id to (user*H + head, query tile).  With xcd_remap, blocks are
-// dispatched round-robin over the 8 XCDs; the map makes the `tiles` consecutive blocks
-// an XCD receives belong to one (user, head), so that its K/V is fetched from HBM once
-// into that XCD's L2 and re-read from there by the other tiles.
+// dispatched round-robin over the 8 XCDs and every (user, head) stays on one XCD, so
+// that its K/V is fetched from HBM once into that XCD's L2 and re-read from there by its
+// other tiles.  TILE_MAJOR hands out tile 0 of every (user, head) first, then tile 1,
+// and so on (the prefill's tiles differ in cost and the heaviest come first); otherwise
+// the tiles of one (user, head) are consecutive.
+template <bool TILE_MAJOR>
 __device__ __forceinline__ void block_coords(const AttnArgs &a, int &group, int &tile) {
     const int bid = blockIdx.x;
+    const int G = a.B * a.H;
     if (a.xcd_remap) {
-        const int xcd = bid & 7, local = bid >> 3;
-        group = (local / a.tiles) * 8 + xcd;
-        tile = local % a.tiles;
+        const int xcd = bid & 7, local = bid >> 3, gx = G >> 3;
+        if (TILE_MAJOR) {
+            group = (local % gx) * 8 + xcd;
+            tile = local / gx;
+        } else {
+            group = (local / a.tiles) * 8 + xcd;
+            tile = local % a.tiles;
+        }
+    } else if (TILE_MAJOR) {
+        group = bid % G;
+        tile = bid / G;
     } else {
         group = bid / a.tiles;
         tile = bid % a.tiles;
@@ -597,7 +636,7 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
     LDS_AS char *smem = (LDS_AS char *)smem_raw;
 
     int group, tile;
-    block_coords(a, group, tile);
+    block_coords<UNIPIN_PREFILL_TILE_MAJOR>(a, group, tile);
     const int b = group / a.H, h = group % a.H;
     if (b >= a.B) return;
     const int qtile = a.tiles - 1 - tile;   // heaviest (last) query tiles first
@@ -652,24 +691,21 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
     // barriers and DMA.  Making tile t current lets the DMA run up to tile t+kBufs-1,
     // into the slot of tile t-1 (or, for t = 0, the slots the query rows came from).
     const int tlast = wq0 < N ? min(ntiles - 1, (wq0 + wave_rows<D>() - 1) / kTK) : -1;
+    // Tiles from q0 on hold the block's own history rows: while such a tile is current,
+    // the workgroup also writes it into the pool slot.  (The pool stores count in vmcnt
+    // like the DMA and only make the next waits longer, never shorter.)
     auto next_tile = [&](int t) -> const LDS_AS char * {
         wait_pieces_after<DPW>(issued - t - 1);
         __syncthreads();
         for (; issued < ntiles && issued <= t + kBufs - 1; ++issued)
             dma_tile<D, W>(smem + (issued % kBufs) * T::BUF_BYTES, rsrc, issued * kTK, voff, wave);
-        return smem + (t % kBufs) * T::BUF_BYTES;
+        const LDS_AS char *cur = smem + (t % kBufs) * T::BUF_BYTES;
+        if (t * kTK >= q0) tile_to_pool<D, W>(cur, pk, pv, t * kTK, kend, tid);
+        return cur;
     };
     run_tiles<D, true>(ws, ntiles, tlast, kend, wq0, la, col, g, a.c, next_tile);
     __syncthreads();   // every wave is done with the tile slots
     store_o<D>(ws, smem + wave * wave_rows<D>() * T::ROW_BYTES, odst, N, wq0, col, g, lane);
-
-    // fused pool write of this block's own history rows, bit for bit
-    const int chunks = (kend - q0) * T::R;
-    for (int i = tid; i < chunks; i += W * 64) {
-        const long off = (long)q0 * D + (long)i * 8;
-        *reinterpret_cast<u32x4 *>(pk + off) = *reinterpret_cast<const u32x4 *>(ksrc + off);
-        *reinterpret_cast<u32x4 *>(pv + off) = *reinterpret_cast<const u32x4 *>(vsrc + off);
-    }
 }
 
 // ------------------------------------------------------------------ ranking decode
@@ -693,7 +729,7 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
     LDS_AS char *smem = (LDS_AS char *)smem_raw;
 
     int group, ctile;
-    block_coords(a, group, ctile);
+    block_coords<false>(a, group, ctile);
     const int b = group / a.H, h = group % a.H;
     if (b >= a.B) return;
     const int N = lens[b];
