@@ -10,7 +10,7 @@ synthetic draws resident in HBM before timing starts.
 Prints one JSON line.  `value` = ranked candidates per second through the whole step
 (64 x 1000 candidates per step).  The roofline object describes the dominant kernel
 (the ranking decode), its algorithmic bytes per launch over its average launch time
-(HIP events on the launch stream).  The CPU baseline is the float64 oracle timed on a
+(HIP events on the launch stream around the step's 12 decode launches, gaps included).  The CPU baseline is the float64 oracle timed on a
 bounded sample of the same work on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -142,25 +142,25 @@ def main():
     def step(events=None):
         slots = torch.tensor(pool.acquire_many(w.B), dtype=torch.int32).pin_memory()
         slots_d = slots.to(dev, non_blocking=True)
+        if events is not None:
+            events[0].record(stream)
         for l, x in enumerate(layers):
-            if events is not None:
-                events["pf"][l][0].record(stream)
             fa.prefill(x["q"], x["k"], x["v"], lens_d, pool, slots_d, l, o=outs[l])
-            if events is not None:
-                events["pf"][l][1].record(stream)
+        if events is not None:
+            events[1].record(stream)
         for l, x in enumerate(layers):
-            if events is not None:
-                events["dc"][l][0].record(stream)
             fa.rank_decode(x["qc"], x["kc"], x["vc"], pool, slots_d, lens_d, l, oc=outc[l])
-            if events is not None:
-                events["dc"][l][1].record(stream)
+        if events is not None:
+            events[2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    mk = lambda: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(w.L)]
-    all_events = [{"pf": mk(), "dc": mk()} for _ in range(args.steps)]
+    # Three HIP events per step on the launch stream: before the prefills, between the
+    # prefills and the decodes, after the decodes.  A kernel's average launch time is its
+    # span over the step divided by the 12 launches (launch gaps included).
+    all_events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -170,10 +170,8 @@ def main():
     if fa.device_status(dev) != 0:
         raise RuntimeError("a kernel flagged an invalid slot or length")
 
-    pf_ms = [s.elapsed_time(e) for ev in all_events for (s, e) in ev["pf"]]
-    dc_ms = [s.elapsed_time(e) for ev in all_events for (s, e) in ev["dc"]]
-    pf_avg = sum(pf_ms) / len(pf_ms)
-    dc_avg = sum(dc_ms) / len(dc_ms)
+    pf_avg = sum(ev[0].elapsed_time(ev[1]) for ev in all_events) / (args.steps * w.L)
+    dc_avg = sum(ev[1].elapsed_time(ev[2]) for ev in all_events) / (args.steps * w.L)
 
     pflop, pbytes, dflop, dbytes = algorithmic(w, lens)
     ms_per_step = wall * 1e3 / args.steps
