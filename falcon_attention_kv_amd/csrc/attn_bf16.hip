@@ -71,17 +71,18 @@ constexpr int kBufs = 4;
 #define UNIPIN_PREFILL_TILE_MAJOR 1
 #endif
 
-// A workgroup covers 256 query rows.  A wave holds QB blocks of 32 query rows: one at
-// D <= 64 (8 waves per workgroup, two workgroups per CU: 4 waves per SIMD with at most
-// 128 registers each), two at D = 128 (4 waves of 64 rows, one workgroup per CU).
+// A workgroup covers 256 query rows: 8 waves of one 32-row query block each (QB = 1; the
+// tile code is written for QB blocks per wave, and two blocks per wave measured slower
+// at every head dimension, since the register file then caps the CU at 4 waves).  At
+// D <= 64 two workgroups share a CU (4 waves per SIMD, at most 128 registers per lane);
+// at D = 128 the LDS ring holds one workgroup per CU (2 waves per SIMD, up to 256).
 constexpr int kBlockRows = 256;
-template <int D> constexpr int query_blocks() { return D <= 64 ? 1 : 2; }
+template <int D> constexpr int query_blocks() { return 1; }
 template <int D> constexpr int wave_rows() { return 32 * query_blocks<D>(); }
 template <int D> constexpr int block_waves() { return kBlockRows / wave_rows<D>(); }
 // Minimum waves per SIMD the kernels are compiled for (the second __launch_bounds__
-// argument): 4 at D <= 64 (two 8-wave workgroups per CU, at most 128 registers per
-// lane), 1 at D = 128.
-template <int D> constexpr int min_waves_per_simd() { return D <= 64 ? 4 : 1; }
+// argument).
+template <int D> constexpr int min_waves_per_simd() { return D <= 64 ? 4 : 2; }
 
 constexpr uint32_t kBufferWord3 = 0x00020000u;   // gfx9 buffer descriptor, raw 32-bit access
 
