@@ -84,6 +84,7 @@ template <int D> constexpr int block_waves() { return kBlockRows / wave_rows<D>(
 // argument).
 template <int D> constexpr int min_waves_per_simd() { return D <= 64 ? 4 : 2; }
 
+
 constexpr uint32_t kBufferWord3 = 0x00020000u;   // gfx9 buffer descriptor, raw 32-bit access
 
 
@@ -298,45 +299,47 @@ __device__ __forceinline__ LaneAddr<D> lane_addr(int lane) {
 // of block (kb, qb) is the score of query wq0 + qb*32 + col against key kbase + kb*32 +
 // 4g + off(i), off(i) = 8*(i/4) + i%4.
 
-// S^T = K Q^T for one tile (its K rows in LDS at kt): 2 key blocks x 2 query blocks x
-// KC MFMAs.
+// S^T = K Q^T for key block kb of one tile (the tile's K rows in LDS at kt): KC MFMAs
+// per query block.
 template <int D>
-__device__ __forceinline__ void tile_scores(f32x16 (&sc)[2][query_blocks<D>()], const WaveState<D> &ws, const LDS_AS char *kt,
-                                            const LaneAddr<D> &la) {
+__device__ __forceinline__ void block_scores(f32x16 (&sc)[query_blocks<D>()], const WaveState<D> &ws,
+                                             const LDS_AS char *kt, const LaneAddr<D> &la, int kb) {
     using T = Tile<D>;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < query_blocks<D>(); ++qb) sc[qb] = f32x16{};
+    bf16x8 ka[T::KC];
 #pragma unroll
-        for (int qb = 0; qb < query_blocks<D>(); ++qb) sc[kb][qb] = f32x16{};
+    for (int cc = 0; cc < T::KC; ++cc)
+        ka[cc] = *reinterpret_cast<const LDS_AS bf16x8 *>(kt + la.k_off0 + kb * 32 * T::ROW_BYTES + la.k_xor[cc]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int cc = 0; cc < T::KC; ++cc)
 #pragma unroll
-        for (int cc = 0; cc < T::KC; ++cc) {
-            const bf16x8 ka = *reinterpret_cast<const LDS_AS bf16x8 *>(kt + la.k_off0 + kb * 32 * T::ROW_BYTES + la.k_xor[cc]);
-#pragma unroll
-            for (int qb = 0; qb < query_blocks<D>(); ++qb)
-                sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, ws.qreg[qb][cc], sc[kb][qb], 0, 0, 0);
-        }
+        for (int qb = 0; qb < query_blocks<D>(); ++qb)
+            sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[cc], ws.qreg[qb][cc], sc[qb], 0, 0, 0);
+    if (D >= 128) {
+        // All of the block's operand reads first, then its MFMAs: left to itself the
+        // compiler keeps two operands in flight and each MFMA waits out an LDS latency.
+        __builtin_amdgcn_sched_group_barrier(0x100, T::KC, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, T::KC * query_blocks<D>(), 0);
     }
 }
 
-// Sets to -inf the scores of keys at or past kend and, for the prefill, of keys after
-// the query: element i is visible iff off(i) <= lim.
+// Sets to -inf the scores of key block kb at or past kend and, for the prefill, of keys
+// after the query: element i is visible iff off(i) <= lim.
 template <int D, bool PREFILL>
-__device__ __forceinline__ void tile_mask(f32x16 (&sc)[2][query_blocks<D>()], int kbase, int kend, int wq0, int col, int g) {
+__device__ __forceinline__ void block_mask(f32x16 (&sc)[query_blocks<D>()], int kbase, int kend, int wq0, int col,
+                                           int g, int kb) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < query_blocks<D>(); ++qb) {
+        const int base = kbase + kb * 32 + 4 * g;
+        int lim = kend - 1 - base;
+        if (PREFILL) lim = min(lim, wq0 + qb * 32 + col - base);
 #pragma unroll
-        for (int qb = 0; qb < query_blocks<D>(); ++qb) {
-            const int base = kbase + kb * 32 + 4 * g;
-            int lim = kend - 1 - base;
-            if (PREFILL) lim = min(lim, wq0 + qb * 32 + col - base);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int off = 8 * (i >> 2) + (i & 3);
-                sc[kb][qb][i] = off > lim ? -INFINITY : sc[kb][qb][i];
-            }
+        for (int i = 0; i < 16; ++i) {
+            const int off = 8 * (i >> 2) + (i & 3);
+            sc[qb][i] = off > lim ? -INFINITY : sc[qb][i];
         }
+    }
 }
 
 // P = exp2(s*c - m) for key block kb against the current running max m, rounded to bf16
@@ -448,8 +451,12 @@ __device__ __forceinline__ void tile_step(WaveState<D> &ws, const LDS_AS char *k
                                           int kbase, int kend, int wq0, bool masked,
                                           const LaneAddr<D> &la, int col, int g, float c) {
     f32x16 sc[2][query_blocks<D>()];
-    tile_scores<D>(sc, ws, kt, la);
-    if (masked) tile_mask<D, PREFILL>(sc, kbase, kend, wq0, col, g);
+    block_scores<D>(sc[0], ws, kt, la, 0);
+    block_scores<D>(sc[1], ws, kt, la, 1);
+    if (masked) {
+        block_mask<D, PREFILL>(sc[0], kbase, kend, wq0, col, g, 0);
+        block_mask<D, PREFILL>(sc[1], kbase, kend, wq0, col, g, 1);
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         bf16x8 pb[2][query_blocks<D>()];
