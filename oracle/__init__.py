@@ -3,10 +3,10 @@
 Only the tests, the smoke check and the benchmark's CPU-baseline leg use it.
 Parity of every function here is pinned by tests/test_oracle_pins.py.
 """
-from .attention import (INCLUDE_SELF, SlotRing, as_f64, bruteforce_joint, default_scale,
+from .attention import (INCLUDE_SELF, SlotRing, ar_decode, as_f64, bruteforce_joint, default_scale,
                         joint, masked_attention, mfalcon_mask, pool_write, prefill,
                         prefill_rows, rank_decode, rank_decode_rows)
 
-__all__ = ["INCLUDE_SELF", "SlotRing", "as_f64", "bruteforce_joint", "default_scale", "joint",
+__all__ = ["INCLUDE_SELF", "SlotRing", "ar_decode", "as_f64", "bruteforce_joint", "default_scale", "joint",
            "masked_attention", "mfalcon_mask", "pool_write", "prefill", "prefill_rows",
            "rank_decode", "rank_decode_rows"]

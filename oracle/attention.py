@@ -182,6 +182,37 @@ def rank_decode(qc, kc, vc, pool_k, pool_v, slot, lens, layer: int,
     return oc
 
 
+def ar_decode(q, k, v, pool_k, pool_v, slot, lens, layer: int,
+              scale: float | None = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """One autoregressive step of the retrieval model, reading and extending the slot.
+
+    The retrieval side prefills the history and then decodes query tokens one at a time
+    while the slot holds the K/V of everything so far ([review] section 2.4 and Figure 3;
+    [notes] section 2: a 12-layer causal decoder that generates several query embeddings
+    autoregressively, one token per step).  User b has N = lens[b] rows in slot[b] at
+    `layer` (its history, then the tokens generated before); the new token q, k, v
+    [B, H, 1, D] takes position N.  Its K/V are stored at row N, and it attends causally
+    to rows 0..N, itself included: the last row of the N+1 by N+1 causal mask.
+    Returns (o [B, H, 1, D], pool_k', pool_v').
+    """
+    q, k, v = (as_f64(t) for t in (q, k, v))
+    pk, pv = as_f64(pool_k).copy(), as_f64(pool_v).copy()
+    lens = [int(x) for x in np.asarray(as_f64(lens)).reshape(-1)]
+    slot = [int(x) for x in np.asarray(as_f64(slot)).reshape(-1)]
+    B, H, T, D = q.shape
+    assert T == 1, "one new token per user and call"
+    scale = default_scale(D) if scale is None else scale
+    o = np.empty((B, H, 1, D))
+    for b in range(B):
+        N, s = lens[b], slot[b]
+        pk[layer, s, :, N] = k[b, :, 0]
+        pv[layer, s, :, N] = v[b, :, 0]
+        M = mfalcon_mask(N + 1, 0)[N:N + 1]
+        for h in range(H):
+            o[b, h] = masked_attention(q[b, h], pk[layer, s, h, :N + 1], pv[layer, s, h, :N + 1], M, scale)
+    return o, pk, pv
+
+
 def rank_decode_rows(qc, kc, vc, hist_k, hist_v, rows: Sequence[int],
                      scale: float | None = None) -> np.ndarray:
     """Outputs of selected candidate rows only, for one (user, head).

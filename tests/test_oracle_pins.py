@@ -11,7 +11,9 @@ Each check below ties the oracle to something other than its own code:
   * a library routine for the textbook special cases (torch float64 causal SDPA);
   * the joint-pass invariant (prefill + pool + rank decode == one pass over
     [history || candidates]) and batch-composition independence (reading notes,
-    section 3: candidate scores do not depend on the other candidates).
+    section 3: candidate scores do not depend on the other candidates);
+  * for the autoregressive retrieval step: replaying a sequence one token at a time
+    must give the causal prefill's rows and leave the whole sequence in the slot.
 The last test plants plausible mistakes in the oracle (on the CPU) and checks that
 at least one pin catches each of them.
 """
@@ -233,9 +235,59 @@ def check_pool_write(seed=5):
     return np.array_equal(pk, ek) and np.array_equal(pv, ev)
 
 
+def check_ar_decode_replays_prefill(seed=7):
+    """Autoregressive steps reproduce the causal prefill of the same token sequence.
+
+    A history of N tokens is prefilled into a slot, then T more tokens are decoded one
+    per step: step j must give prefill row N+j of the whole sequence (each row of a
+    causal pass sees exactly the tokens before it and itself), and the slot must end up
+    holding all N+T rows.  Starting from an empty slot (N = 0) the first step must
+    return the token's own value.
+    """
+    rng = np.random.default_rng(seed)
+    L, S, H, D, layer = 2, 3, 2, 8, 1
+    for N, T, s in ((0, 5, 2), (6, 4, 0), (1, 1, 1)):
+        n = N + T
+        c = rand_case(rng, n, 0, D, B=1, H=H)
+        full = OA.prefill(c["q"], c["k"], c["v"], [n])
+        pk0, pv0 = rng.standard_normal((L, S, H, n + 2, D)), rng.standard_normal((L, S, H, n + 2, D))
+        pk, pv = OA.pool_write(pk0, pv0, c["k"], c["v"], [N], [s], layer)
+        for j in range(T):
+            t = N + j
+            o, pk, pv = OA.ar_decode(c["q"][:, :, t:t + 1], c["k"][:, :, t:t + 1], c["v"][:, :, t:t + 1],
+                                     pk, pv, [s], [t], layer)
+            if _maxerr(o[0, :, 0], full[0, :, t]) > TOL:
+                return False
+            if t == 0 and not np.array_equal(o[0, :, 0], c["v"][0, :, 0]):
+                return False
+        ek, ev = OA.pool_write(pk0, pv0, c["k"], c["v"], [n], [s], layer)
+        if not (np.array_equal(pk, ek) and np.array_equal(pv, ev)):
+            return False
+    return True
+
+
+def check_ar_decode_bruteforce(seed=8):
+    """One step against the scalar brute force, for a batch with mixed slot fill levels."""
+    rng = np.random.default_rng(seed)
+    L, S, H, nmax, D, layer = 1, 4, 2, 7, 3, 0
+    pk0, pv0 = rng.standard_normal((L, S, H, nmax, D)), rng.standard_normal((L, S, H, nmax, D))
+    lens, slot = [0, 3, 6], [3, 1, 0]
+    q, k, v = (rng.standard_normal((3, H, 1, D)) for _ in range(3))
+    scale = 0.7
+    o, pk, pv = OA.ar_decode(q, k, v, pk0, pv0, slot, lens, layer, scale=scale)
+    for b, (N, s) in enumerate(zip(lens, slot)):
+        for h in range(H):
+            keys = [list(pk0[layer, s, h, t]) for t in range(N)] + [list(k[b, h, 0])]
+            vals = [list(pv0[layer, s, h, t]) for t in range(N)] + [list(v[b, h, 0])]
+            ref = OA._softmax_average(list(q[b, h, 0]), keys, vals, scale)
+            if _maxerr(o[b, h, 0], ref) > TOL:
+                return False
+    return True
+
+
 ALL_CHECKS = [check_mask_golden, check_pair_count, check_worked_example, check_bruteforce,
               check_closed_forms, check_sdpa, check_joint_invariant, check_independence,
-              check_pool_write]
+              check_pool_write, check_ar_decode_replays_prefill, check_ar_decode_bruteforce]
 
 
 # ------------------------------------------------------------------ the pins
@@ -323,7 +375,31 @@ def _pool_write_wrong_slot(pool_k, pool_v, k, v, lens, slot, layer):
                                            [(int(s) + 1) % S for s in slot], layer)
 
 
+def _ar_without_itself(q, k, v, pool_k, pool_v, slot, lens, layer, scale=None):
+    o, pk, pv = OA.__dict__["_orig_ar"](q, k, v, pool_k, pool_v, slot, lens, layer, scale=scale)
+    pk0, pv0 = OA.as_f64(pool_k), OA.as_f64(pool_v)
+    lens = [int(x) for x in np.asarray(lens).reshape(-1)]
+    D = np.asarray(q).shape[-1]
+    sc = OA.default_scale(D) if scale is None else scale
+    for b, (N, s) in enumerate(zip(lens, [int(x) for x in np.asarray(slot).reshape(-1)])):
+        if N == 0:
+            continue
+        for h in range(np.asarray(q).shape[1]):
+            o[b, h] = OA.masked_attention(OA.as_f64(q)[b, h], pk0[layer, s, h, :N], pv0[layer, s, h, :N],
+                                          np.ones((1, N), dtype=bool), sc)
+    return o, pk, pv
+
+
+def _ar_writes_previous_row(q, k, v, pool_k, pool_v, slot, lens, layer, scale=None):
+    shifted = [max(0, int(x) - 1) for x in np.asarray(lens).reshape(-1)]
+    o, _, _ = OA.__dict__["_orig_ar"](q, k, v, pool_k, pool_v, slot, lens, layer, scale=scale)
+    _, pk, pv = OA.__dict__["_orig_ar"](q, k, v, pool_k, pool_v, slot, shifted, layer, scale=scale)
+    return o, pk, pv
+
+
 MUTANTS = {
+    "autoregressive step does not see itself": ("ar_decode", _ar_without_itself),
+    "autoregressive step stores at the previous row": ("ar_decode", _ar_writes_previous_row),
     "candidate does not see itself": ("mfalcon_mask", _mask_no_self),
     "candidates see each other": ("mfalcon_mask", _mask_candidates_see_each_other),
     "history not causal": ("mfalcon_mask", _mask_noncausal_history),
@@ -343,6 +419,7 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     monkeypatch.setitem(OA.__dict__, "_orig_mask", OA.mfalcon_mask)
     monkeypatch.setitem(OA.__dict__, "_orig_attn", OA.masked_attention)
     monkeypatch.setitem(OA.__dict__, "_orig_pool_write", OA.pool_write)
+    monkeypatch.setitem(OA.__dict__, "_orig_ar", OA.ar_decode)
     monkeypatch.setattr(OA, attr, fn)
     failed = []
     for check in ALL_CHECKS:
