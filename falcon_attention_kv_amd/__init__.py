@@ -8,9 +8,10 @@ fallback: if the library cannot be loaded, importing this package raises.
     slots = pool.acquire_many(B)                     # round-robin slot ids
     o = prefill(q, k, v, lens, pool, slots, layer)   # writes the slot's K/V rows
     oc = rank_decode(qc, kc, vc, pool, slots, lens, layer)
+    o1 = ar_decode(q1, k1, v1, pool, slots, lens, layer)  # one retrieval step, row lens[b]
 
 Functions mirror the C entry points of include/unipin.h (unipin_prefill,
-unipin_rank_decode, unipin_pool_*), with the same argument meaning.
+unipin_rank_decode, unipin_ar_decode, unipin_pool_*), with the same argument meaning.
 """
 from __future__ import annotations
 
@@ -30,13 +31,18 @@ FLAG_BAD_SLOT, FLAG_BAD_LEN = 1, 2
 # Every symbol include/unipin.h declares.
 EXPORTS = ("unipin_pool_create", "unipin_pool_destroy", "unipin_pool_acquire",
            "unipin_pool_generation", "unipin_pool_dims", "unipin_prefill",
-           "unipin_rank_decode", "unipin_device_status", "unipin_strerror", "unipin_version")
+           "unipin_rank_decode", "unipin_ar_decode", "unipin_device_status", "unipin_strerror",
+           "unipin_version")
 
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m falcon_attention_kv_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python falcon_attention_kv_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
+    missing = [name for name in EXPORTS if not hasattr(lib, name)]
+    if missing:
+        raise ImportError(f"{LIB_PATH} lacks {', '.join(missing)}: it is stale, rebuild it with "
+                          "`python falcon_attention_kv_amd/build.py`")
     vp, i32, i64p, u64p = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_uint64)
     ip = ctypes.POINTER(ctypes.c_int)
     i32p = ctypes.POINTER(ctypes.c_int32)
@@ -47,6 +53,7 @@ def _load() -> ctypes.CDLL:
     lib.unipin_pool_dims.argtypes = [vp, ip, ip, ip, ip, ip, ip]
     lib.unipin_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp]
     lib.unipin_rank_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp]
+    lib.unipin_ar_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp]
     lib.unipin_device_status.argtypes = [vp, ip]
     lib.unipin_strerror.argtypes = [i32]
     lib.unipin_strerror.restype = ctypes.c_char_p
@@ -202,6 +209,31 @@ def rank_decode(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, pool: Pool
                                   0.0 if scale is None else float(scale), oc.data_ptr(),
                                   _stream_handle(dev)), "unipin_rank_decode")
     return oc
+
+
+def ar_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pool: Pool, slot, lens,
+              layer: int, o: Optional[torch.Tensor] = None, scale: Optional[float] = None) -> torch.Tensor:
+    """unipin_ar_decode: one autoregressive retrieval step on the pool.
+
+    q, k, v [B, H, 1, D]: each user's new token; slot, lens: B ints, lens[b] = rows already
+    in the slot at this layer (the new token's position).  Stores k/v at row lens[b] and
+    returns o [B, H, 1, D].  lens is not advanced; the caller does that after the step.
+    """
+    dev = pool.k.device
+    B = q.shape[0]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(t, name, (B, pool.H, 1, pool.D), pool.dtype, dev)
+    if o is None:
+        o = torch.empty_like(q)
+    _check_tensor(o, "o", q.shape, pool.dtype, dev)
+    lens_t, slot_t = _i32_on(lens, dev), _i32_on(slot, dev)
+    if lens_t.numel() != B or slot_t.numel() != B:
+        raise UnipinError(EINVAL, "lens and slot need one entry per user")
+    _check(lib.unipin_ar_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), pool.handle,
+                                slot_t.data_ptr(), lens_t.data_ptr(), layer, B,
+                                0.0 if scale is None else float(scale), o.data_ptr(),
+                                _stream_handle(dev)), "unipin_ar_decode")
+    return o
 
 
 def device_status(device=None) -> int:

@@ -1,6 +1,7 @@
 """Builds libunipin.so (the C-ABI library and its gfx950 kernels) in place with hipcc.
 
-Usage: python -m falcon_attention_kv_amd.build   (or call build()).
+Usage: python falcon_attention_kv_amd/build.py   (or call build()).  It runs as a plain
+script: importing the package first would load the library it is about to replace.
 Always recompiles; the result is falcon_attention_kv_amd/libunipin.so.
 """
 from __future__ import annotations
@@ -16,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libunipin.so")
-SOURCES = ["unipin.cpp", "device_status.hip", "attn_bf16.hip", "attn_fp32.hip"]
+SOURCES = ["unipin.cpp", "device_status.hip", "attn_bf16.hip", "attn_fp32.hip", "attn_ar.hip"]
 ARCH = "gfx950"
 
 

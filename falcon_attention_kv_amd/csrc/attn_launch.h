@@ -38,6 +38,8 @@ hipError_t launch_prefill_bf16(const AttnArgs &a, int D, hipStream_t stream);
 hipError_t launch_decode_bf16(const AttnArgs &a, int D, hipStream_t stream);
 hipError_t launch_prefill_fp32(const AttnArgs &a, int D, hipStream_t stream);
 hipError_t launch_decode_fp32(const AttnArgs &a, int D, hipStream_t stream);
+// One autoregressive step (one new token per user and head); bf16 or fp32 elements.
+hipError_t launch_ar_decode(const AttnArgs &a, int D, bool bf16, hipStream_t stream);
 
 // Device address of the sticky status word of the current device (looked up once
 // per device with hipGetSymbolAddress).

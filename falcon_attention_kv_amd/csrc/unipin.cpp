@@ -1,7 +1,7 @@
 // C ABI of the library (include/unipin.h): pool descriptor, round-robin slot hand-out,
 // host-side argument checks, and dispatch to the HIP kernels by element type and head
 // dimension.  Nothing here allocates device memory; the only HIP calls are kernel
-// launches (prefill, rank decode) and the status read-back.
+// launches (prefill, rank decode, autoregressive step) and the status read-back.
 #include "unipin.h"
 
 #include <hip/hip_runtime.h>
@@ -195,6 +195,36 @@ int unipin_rank_decode(const void *qc, const void *kc, const void *vc,
     a.xcd_remap = pool->dtype == UNIPIN_BF16 && ((long long)B * pool->H) % 8 == 0;
     if (unipin::device_status_word(&a.status) != hipSuccess) return UNIPIN_EHIP;
     return launch(a, pool, false, stream);
+}
+
+int unipin_ar_decode(const void *q, const void *k, const void *v, unipin_pool_t *pool,
+                     const int32_t *slot, const int32_t *lens, int layer, int B, float scale,
+                     void *o, void *stream) {
+    if (!pool || !q || !k || !v || !lens || !slot || !o) return UNIPIN_EINVAL;
+    if (B < 1) return UNIPIN_EINVAL;
+    if (layer < 0 || layer >= pool->L) return UNIPIN_ERANGE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(lens, 4) || !aligned(slot, 4))
+        return UNIPIN_EALIGN;
+    if ((long long)B * pool->H > 0x7fffffffLL) return UNIPIN_EINVAL;
+    unipin::AttnArgs a{};
+    int rc = resolve_scale(scale, pool->D, &a.c);
+    if (rc) return rc;
+    fill_pool_args(a, pool, layer);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lens = lens;
+    a.slot = slot;
+    a.B = B;
+    a.rows = 1;
+    a.len_limit = pool->n_max - 1;
+    a.tiles = 1;
+    if (unipin::device_status_word(&a.status) != hipSuccess) return UNIPIN_EHIP;
+    const hipError_t e = unipin::launch_ar_decode(a, pool->D, pool->dtype == UNIPIN_BF16,
+                                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? UNIPIN_OK : UNIPIN_EHIP;
 }
 
 int unipin_device_status(void *stream, int *flags) {

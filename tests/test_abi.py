@@ -172,9 +172,28 @@ def test_decode_host_checks(kw, code):
     lib.unipin_pool_destroy(h)
 
 
+def _ar(h, q=FAKE, k=FAKE, v=FAKE, slot=FAKE, lens=FAKE, layer=0, B=1, scale=0.0, o=FAKE):
+    return lib.unipin_ar_decode(q, k, v, h, slot, lens, layer, B, scale, o, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), fa.EINVAL), (dict(k=0), fa.EINVAL), (dict(v=0), fa.EINVAL),
+    (dict(lens=0), fa.EINVAL), (dict(slot=0), fa.EINVAL), (dict(o=0), fa.EINVAL),
+    (dict(B=0), fa.EINVAL), (dict(B=-3), fa.EINVAL),
+    (dict(layer=-1), fa.ERANGE), (dict(layer=2), fa.ERANGE),
+    (dict(v=FAKE_ODD), fa.EALIGN), (dict(o=FAKE + 8), fa.EALIGN), (dict(lens=FAKE + 2), fa.EALIGN),
+    (dict(scale=float("inf")), fa.EINVAL),
+])
+def test_ar_decode_host_checks(kw, code):
+    h = make_pool(L=2, n_max=16)
+    assert _ar(h, **kw) == code
+    lib.unipin_pool_destroy(h)
+
+
 def test_null_pool_rejected():
     assert _prefill(None) == fa.EINVAL
     assert _decode(None) == fa.EINVAL
+    assert _ar(None) == fa.EINVAL
 
 
 def test_binding_rejects_mismatched_tensors():
@@ -190,4 +209,7 @@ def test_binding_rejects_mismatched_tensors():
         fa.prefill(q, q, q, [8], pool, [0], 0)
     with pytest.raises(fa.UnipinError):
         fa.Pool(k, torch.empty((1, 1, 2, 8, 32), dtype=torch.bfloat16))
+    t = torch.empty((1, 2, 2, 64), dtype=torch.bfloat16)   # two new tokens per user: not a step
+    with pytest.raises(fa.UnipinError):
+        fa.ar_decode(t, t, t, pool, [0], [3], 0)
     pool.close()

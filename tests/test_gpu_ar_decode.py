@@ -1,0 +1,164 @@
+"""GPU parity of the autoregressive retrieval step (unipin_ar_decode) against the oracle.
+
+Same tolerances as the other GPU parity tests: fp32 normwise 1e-5; bf16 max abs 2e-2
+and mean abs 2e-3.  Pool contents are compared bit for bit: the step must store the
+new token's K/V at row lens[b] of its slot and leave every other entry as it was.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import falcon_attention_kv_amd as fa
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def announce(msg: str) -> None:
+    sys.__stderr__.write(f"[gpu case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def check_close(got: torch.Tensor, ref: np.ndarray, dtype: torch.dtype, what: str):
+    g = got.detach().to("cpu").to(torch.float64).numpy()
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    diff = np.abs(g - r)
+    if dtype == torch.float32:
+        rel = diff.max() / max(np.abs(r).max(), 1e-30)
+        assert rel <= 1e-5, f"{what}: normwise relative error {rel:.3e} > 1e-5"
+        return
+    assert diff.max() <= 2e-2, f"{what}: max abs error {diff.max():.3e} > 2e-2"
+    assert diff.mean() <= 2e-3, f"{what}: mean abs error {diff.mean():.3e} > 2e-3"
+
+
+CASES = [
+    (torch.bfloat16, 64), (torch.bfloat16, 32), (torch.bfloat16, 128),
+    (torch.float32, 32), (torch.float32, 64), (torch.float32, 128),
+]
+
+
+@pytest.mark.parametrize("dtype,D", CASES, ids=lambda x: str(x))
+def test_ar_decode_one_step(dtype, D):
+    """Mixed fill levels (empty slot, partial and whole chunks, the last free row)."""
+    L, S, H, n_max, layer = 2, 9, 3, 601, 1
+    lens = [0, 1, 63, 64, 65, 200, 511, 513, n_max - 1]
+    slots = [4, 0, 8, 2, 7, 1, 3, 6, 5]
+    B = len(lens)
+    announce(f"ar_decode one step {dtype} D={D}")
+    pk, pv = W.random_pool(L, S, H, n_max, D, dtype, seed=31, device=DEV)
+    tok = W.step_tokens(B, H, D, 1, dtype, seed=32, device=DEV)
+    q, k, v = tok["q"][0], tok["k"][0], tok["v"][0]
+    before_k, before_v = pk.cpu(), pv.cpu()
+    pool = fa.Pool(pk, pv)
+    o = fa.ar_decode(q, k, v, pool, slots, lens, layer)
+    torch.cuda.synchronize()
+    assert fa.device_status() == 0
+    ref_o, ref_k, ref_v = oracle.ar_decode(q.cpu(), k.cpu(), v.cpu(), before_k, before_v, slots, lens, layer)
+    check_close(o, ref_o, dtype, f"ar_decode {dtype} D={D}")
+    exp_k, exp_v = before_k.clone(), before_v.clone()
+    for b, (N, s) in enumerate(zip(lens, slots)):
+        exp_k[layer, s, :, N] = k[b, :, 0].cpu()
+        exp_v[layer, s, :, N] = v[b, :, 0].cpu()
+    assert torch.equal(pk.cpu(), exp_k) and torch.equal(pv.cpu(), exp_v), "pool must change at row lens[b] only"
+    assert np.array_equal(oracle.as_f64(pk), ref_k)
+    pool.close()
+
+
+@pytest.mark.parametrize("scale", [None, 0.37])
+def test_ar_decode_steps_replay_the_prefill(scale):
+    """Prefill N history tokens, then decode T more one step at a time (lens advanced by
+    the caller): step j must give row N+j of a causal prefill over all N+T tokens, the
+    slot must end up holding all N+T rows, and the ranking decode still sees the history
+    it is told to see."""
+    B, H, D, N, T, k = 4, 2, 64, 130, 5, 48
+    n_max = N + T
+    announce(f"ar_decode replay scale={scale}")
+    inp = W.small_case(B, H, D, n_max, k, [n_max] * B, seed=33, device=DEV)
+    pool = fa.Pool.allocate(1, B, H, n_max, D, torch.bfloat16, DEV)
+    slots = [2, 0, 3, 1]
+    hist = [N, N - 7, 1, 0]
+    fa.prefill(inp["q"], inp["k"], inp["v"], hist, pool, slots, 0, scale=scale)
+    lens = torch.as_tensor(hist, dtype=torch.int32, device=DEV)
+    outs = []
+    for j in range(T):
+        rows = lens.long()
+        gather = lambda x: torch.stack([x[b, :, int(rows[b]):int(rows[b]) + 1] for b in range(B)])
+        outs.append(fa.ar_decode(gather(inp["q"]), gather(inp["k"]), gather(inp["v"]), pool, slots, lens, 0,
+                                 scale=scale))
+        lens = lens + 1
+    torch.cuda.synchronize()
+    assert fa.device_status() == 0
+    full = oracle.prefill(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), [n_max] * B, scale)
+    for j in range(T):
+        ref = np.stack([full[b, :, hist[b] + j] for b in range(B)])[:, :, None]
+        check_close(outs[j], ref, torch.bfloat16, f"step {j}")
+    for b, s in enumerate(slots):
+        m = hist[b] + T
+        assert torch.equal(pool.k[0, s, :, :m].cpu(), inp["k"][b, :, :m].cpu())
+        assert torch.equal(pool.v[0, s, :, :m].cpu(), inp["v"][b, :, :m].cpu())
+    # the ranking decode with the history length alone ignores the generated rows
+    oc = fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, slots, hist, 0, scale=scale)
+    torch.cuda.synchronize()
+    for b in (0, 2):
+        s = slots[b]
+        ref = oracle.rank_decode(inp["qc"][b:b + 1].cpu(), inp["kc"][b:b + 1].cpu(), inp["vc"][b:b + 1].cpu(),
+                                 oracle.as_f64(pool.k[0:1, s:s + 1].cpu()), oracle.as_f64(pool.v[0:1, s:s + 1].cpu()),
+                                 [0], [hist[b]], 0, scale)
+        check_close(oc[b:b + 1], ref, torch.bfloat16, f"rank decode after steps, user {b}")
+    pool.close()
+
+
+def test_ar_decode_invalid_users_flagged_and_skipped():
+    L, S, H, n_max, D = 1, 3, 2, 40, 64
+    announce("ar_decode invalid users")
+    pk, pv = W.random_pool(L, S, H, n_max, D, torch.bfloat16, seed=34, device=DEV)
+    tok = W.step_tokens(3, H, D, 1, torch.bfloat16, seed=35, device=DEV)
+    before_k, before_v = pk.clone(), pv.clone()
+    pool = fa.Pool(pk, pv)
+    o = torch.full_like(tok["q"][0], 7.0)
+    fa.ar_decode(tok["q"][0], tok["k"][0], tok["v"][0], pool, [0, 5, 1], [n_max, 3, -1], 0, o=o)
+    torch.cuda.synchronize()
+    flags = fa.device_status()
+    assert flags == fa.FLAG_BAD_SLOT | fa.FLAG_BAD_LEN
+    assert torch.all(o == 7.0), "skipped users' outputs must stay untouched"
+    assert torch.equal(pk, before_k) and torch.equal(pv, before_v), "skipped users must not write the pool"
+    assert fa.device_status() == 0
+    pool.close()
+
+
+def test_ar_decode_serving_shape_sampled():
+    """The retrieval step at the serving shape (64 requests x 8 heads, history 512, D=64,
+    12-layer pool), in the launch configuration the benchmark times; sampled users
+    against the oracle, every pool row written checked bit for bit."""
+    w = W.WORKLOADS[3]
+    T = 4
+    n_max = w.n + T
+    announce("ar_decode serving shape")
+    pk, pv = W.random_pool(w.L, w.S, w.H, n_max, w.D, w.dtype, seed=36, device=DEV)
+    pool = fa.Pool(pk, pv)
+    tok = W.step_tokens(w.B, w.H, w.D, 1, w.dtype, seed=37, device=DEV)
+    slots = list(range(w.B))
+    lens = [w.n + 2] * w.B
+    layer = 11
+    users = [0, 17, 63]
+    before = {b: (pk[layer, b, :, :lens[b]].cpu(), pv[layer, b, :, :lens[b]].cpu()) for b in users}
+    o = fa.ar_decode(tok["q"][0], tok["k"][0], tok["v"][0], pool, slots, lens, layer)
+    torch.cuda.synchronize()
+    assert fa.device_status() == 0
+    for b in users:
+        # the user's slot as a one-layer, one-slot pool with one free row for the new token
+        hk, hv = (np.concatenate([oracle.as_f64(x), np.zeros((w.H, 1, w.D))], axis=1)[None, None]
+                  for x in before[b])
+        ref, _, _ = oracle.ar_decode(tok["q"][0][b:b + 1].cpu(), tok["k"][0][b:b + 1].cpu(),
+                                     tok["v"][0][b:b + 1].cpu(), hk, hv, [0], [lens[b]], 0)
+        check_close(o[b:b + 1], ref, w.dtype, f"serving shape user {b}")
+    rows_k = torch.stack([pk[layer, b, :, lens[b]] for b in range(w.B)])
+    rows_v = torch.stack([pv[layer, b, :, lens[b]] for b in range(w.B)])
+    assert torch.equal(rows_k, tok["k"][0][:, :, 0]) and torch.equal(rows_v, tok["v"][0][:, :, 0])
+    pool.close()

@@ -102,6 +102,33 @@ def small_case(B: int, H: int, D: int, n: int, k: int, lens, dtype=torch.bfloat1
     return d
 
 
+def step_tokens(B: int, H: int, D: int, steps: int, dtype=torch.bfloat16, seed: int = 0,
+                std: float = 1.0, device="cpu") -> Dict[str, torch.Tensor]:
+    """q, k, v [steps, B, H, 1, D]: each user's new token for `steps` autoregressive steps.
+
+    Drawn like layer_inputs: float32 randn * std on a generator of `device` seeded with
+    `seed`, in the order q, k, v, then cast to `dtype`.
+    """
+    dev = torch.device(device)
+    g = torch.Generator(dev).manual_seed(seed)
+    out = {}
+    for name in ("q", "k", "v"):
+        t = torch.randn((steps, B, H, 1, D), generator=g, device=dev, dtype=torch.float32) * std
+        out[name] = t.to(dtype)
+    return out
+
+
+def random_pool(L: int, S: int, H: int, n_max: int, D: int, dtype=torch.bfloat16, seed: int = 0,
+                device="cpu"):
+    """K and V pool arrays [L, S, H, n_max, D] filled with seeded randn values (stand-ins for
+    rows an earlier call left in the slots)."""
+    dev = torch.device(device)
+    g = torch.Generator(dev).manual_seed(seed)
+    k = torch.randn((L, S, H, n_max, D), generator=g, device=dev, dtype=torch.float32).to(dtype)
+    v = torch.randn((L, S, H, n_max, D), generator=g, device=dev, dtype=torch.float32).to(dtype)
+    return k, v
+
+
 def poison_tail(x: torch.Tensor, lens: torch.Tensor, value=float("nan")) -> torch.Tensor:
     """Copy of a [B,H,n,D] tensor whose rows >= lens[b] hold `value` (used to prove they are never read)."""
     y = x.clone()
