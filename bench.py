@@ -13,7 +13,11 @@ Prints one JSON line.  `value` = ranked candidates per second through the whole 
 (HIP events on the launch stream around the step's 12 decode launches, gaps included).  The CPU baseline is the float64 oracle timed on a
 bounded sample of the same work on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+After the timed steps, `ar_step` reports the autoregressive retrieval step (one new
+token per user and head appended to its slot) on the serving shape and on the long
+history shape; it is a secondary figure and does not enter `value`.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ar-step]
 """
 from __future__ import annotations
 
@@ -23,6 +27,7 @@ import json
 import os
 import sys
 import time
+from dataclasses import replace
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -42,6 +47,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline sample")
+    p.add_argument("--no-ar-step", action="store_true",
+                   help="skip the secondary measurement of the autoregressive retrieval step")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run 3 plain device copies of this many MiB (a known-size "
                         "reference for the HBM byte counters of a profiler run)")
@@ -62,6 +69,47 @@ def algorithmic(w, lens):
     df = sum(4 * w.D * w.k * (N + 1) for N in lens) * w.H
     db = sum((2 * N + 4 * w.k) * w.D * e for N in lens) * w.H
     return pf, pb, df, db
+
+
+def ar_step(fa, W, torch, dev, w, lens, steps: int, warmup: int):
+    """The autoregressive retrieval step on the shape w: every user's slot holds lens[b]
+    rows in each of the w.L layers; one step appends one token per (user, head) in every
+    layer (w.L launches), the next step sees one row more.  Returns per-launch figures;
+    algorithmic bytes per (user, head) are the slot's K and V rows read once (2 N D e)
+    plus the token's q, k, v read and o and its two pool rows written (6 D e)."""
+    e = torch.tensor([], dtype=w.dtype).element_size()
+    T = warmup + steps
+    n_max = max(lens) + T
+    pk, pv = W.random_pool(w.L, w.B, w.H, n_max, w.D, w.dtype, seed=41, device=dev)
+    pool = fa.Pool(pk, pv)
+    tok = W.step_tokens(w.B, w.H, w.D, T, w.dtype, seed=42, device=dev)
+    o = torch.empty_like(tok["q"][0])
+    slots = torch.arange(w.B, dtype=torch.int32, device=dev)
+    lens_t = [torch.as_tensor(lens, dtype=torch.int32, device=dev) + j for j in range(T)]
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for j in range(T):
+        if j >= warmup:
+            ev[2 * (j - warmup)].record(stream)
+        for l in range(w.L):
+            fa.ar_decode(tok["q"][j], tok["k"][j], tok["v"][j], pool, slots, lens_t[j], l, o=o)
+        if j >= warmup:
+            ev[2 * (j - warmup) + 1].record(stream)
+    torch.cuda.synchronize()
+    if fa.device_status(dev) != 0:
+        raise RuntimeError("the autoregressive step flagged an invalid slot or length")
+    avg_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / (steps * w.L)
+    rows = sum(lens) + w.B * (warmup + (steps - 1) / 2)   # mean slot fill over the timed steps
+    nbytes = (2 * rows + 6 * w.B) * w.H * w.D * e
+    gbs = nbytes / (avg_ms / 1e3) / 1e9
+    ws_bytes = fa.ar_decode_workspace_bytes(pool, w.B)
+    pool.close()
+    del pk, pv
+    return {"avg_ms": round(avg_ms, 5), "split_workspace_bytes": ws_bytes,
+            "algorithmic_bytes_per_launch": int(nbytes), "gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "tokens_per_s": round(w.B * w.H / (avg_ms / 1e3), 1),
+            "shape": f"B={w.B} H={w.H} D={w.D} history {min(lens)}..{max(lens)}, {w.L} layer(s), "
+                     f"{steps} timed steps"}
 
 
 def kernel_source_hash() -> str:
@@ -225,6 +273,16 @@ def main():
     if not args.no_cpu_baseline:
         layers_cpu = [{k: v.cpu() for k, v in x.items()} for x in layers]
         out["cpu_baseline"] = cpu_baseline(w, layers_cpu, lens, args.cpu_seconds)
+    if not args.no_ar_step:
+        del layers, outs, outc
+        pool.close()
+        wl = W.WORKLOADS[4]
+        out["ar_step"] = {
+            "serving_shape": ar_step(fa, W, torch, dev, w, lens, steps=8, warmup=2),
+            "long_history": ar_step(fa, W, torch, dev, wl, W.history_lengths(wl).tolist(), steps=8, warmup=2),
+            "one_request_long_history": ar_step(fa, W, torch, dev, replace(wl, B=1, S=1), [4000], steps=8,
+                                                warmup=2),
+        }
     print(json.dumps(out), flush=True)
 
 

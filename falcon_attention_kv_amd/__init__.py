@@ -31,8 +31,8 @@ FLAG_BAD_SLOT, FLAG_BAD_LEN = 1, 2
 # Every symbol include/unipin.h declares.
 EXPORTS = ("unipin_pool_create", "unipin_pool_destroy", "unipin_pool_acquire",
            "unipin_pool_generation", "unipin_pool_dims", "unipin_prefill",
-           "unipin_rank_decode", "unipin_ar_decode", "unipin_device_status", "unipin_strerror",
-           "unipin_version")
+           "unipin_rank_decode", "unipin_ar_decode", "unipin_ar_decode_workspace_bytes",
+           "unipin_device_status", "unipin_strerror", "unipin_version")
 
 
 def _load() -> ctypes.CDLL:
@@ -53,14 +53,16 @@ def _load() -> ctypes.CDLL:
     lib.unipin_pool_dims.argtypes = [vp, ip, ip, ip, ip, ip, ip]
     lib.unipin_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp]
     lib.unipin_rank_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp]
-    lib.unipin_ar_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp]
+    lib.unipin_ar_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+    lib.unipin_ar_decode_workspace_bytes.argtypes = [vp, i32]
     lib.unipin_device_status.argtypes = [vp, ip]
     lib.unipin_strerror.argtypes = [i32]
     lib.unipin_strerror.restype = ctypes.c_char_p
     lib.unipin_version.argtypes = []
     for name in EXPORTS:
-        if name not in ("unipin_strerror",):
+        if name not in ("unipin_strerror", "unipin_ar_decode_workspace_bytes"):
             getattr(lib, name).restype = ctypes.c_int
+    lib.unipin_ar_decode_workspace_bytes.restype = ctypes.c_size_t
     return lib
 
 
@@ -211,13 +213,22 @@ def rank_decode(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, pool: Pool
     return oc
 
 
+def ar_decode_workspace_bytes(pool: Pool, B: int) -> int:
+    """unipin_ar_decode_workspace_bytes: scratch bytes ar_decode splits B users' rows with (0: none)."""
+    return int(lib.unipin_ar_decode_workspace_bytes(pool.handle, int(B)))
+
+
 def ar_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pool: Pool, slot, lens,
-              layer: int, o: Optional[torch.Tensor] = None, scale: Optional[float] = None) -> torch.Tensor:
+              layer: int, o: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+              workspace: Optional[torch.Tensor] = None, split: bool = True) -> torch.Tensor:
     """unipin_ar_decode: one autoregressive retrieval step on the pool.
 
     q, k, v [B, H, 1, D]: each user's new token; slot, lens: B ints, lens[b] = rows already
     in the slot at this layer (the new token's position).  Stores k/v at row lens[b] and
     returns o [B, H, 1, D].  lens is not advanced; the caller does that after the step.
+    split=True lets the library split each user's rows across workgroups, with `workspace`
+    (a device tensor of at least ar_decode_workspace_bytes(pool, B) bytes) or, when it is
+    None, a buffer from torch's caching allocator; split=False runs the one-pass kernel.
     """
     dev = pool.k.device
     B = q.shape[0]
@@ -229,10 +240,19 @@ def ar_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pool: Pool, slo
     lens_t, slot_t = _i32_on(lens, dev), _i32_on(slot, dev)
     if lens_t.numel() != B or slot_t.numel() != B:
         raise UnipinError(EINVAL, "lens and slot need one entry per user")
+    ws_ptr, ws_bytes = None, 0
+    if split:
+        need = ar_decode_workspace_bytes(pool, B)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        if workspace is not None:
+            if workspace.device != dev or not workspace.is_contiguous():
+                raise UnipinError(EINVAL, "workspace must be a contiguous tensor on the pool's device")
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _check(lib.unipin_ar_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), pool.handle,
                                 slot_t.data_ptr(), lens_t.data_ptr(), layer, B,
                                 0.0 if scale is None else float(scale), o.data_ptr(),
-                                _stream_handle(dev)), "unipin_ar_decode")
+                                ws_ptr, ws_bytes, _stream_handle(dev)), "unipin_ar_decode")
     return o
 
 

@@ -103,112 +103,120 @@ __device__ __forceinline__ float lowsum(float x) {
     return x;
 }
 
+// Geometry of one (element type, head dim): a row is R lanes of 16 bytes, a wave-wide
+// load covers RPI rows, a chunk (one wave's unit of work) is LPC loads = CH rows.
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads) ar_decode_kernel(AttnArgs a) {
-    constexpr int ROW = D * (int)sizeof(T);    // bytes per row
-    constexpr int R = ROW / 16;                // lanes per row
-    constexpr int RPI = 64 / R;                // rows per wave-wide load
-    constexpr int PER = Elem<T>::kPer16;       // elements per lane per load
-    constexpr int LPC = RPI >= 4 ? 64 / RPI : 16;   // loads per chunk and matrix
-    constexpr int CH = LPC * RPI;              // keys per chunk
+struct Geo {
+    static constexpr int ROW = D * (int)sizeof(T);
+    static constexpr int R = ROW / 16;
+    static constexpr int RPI = 64 / R;
+    static constexpr int PER = Elem<T>::kPer16;
+    static constexpr int LPC = RPI >= 4 ? 64 / RPI : 16;
+    static constexpr int CH = LPC * RPI;
     static_assert(R >= 1 && R <= 64 && 64 % R == 0, "row must split into 16-byte lanes");
-    __shared__ float part[kWaves][D + 2];      // per wave: accumulator, max, sum
+};
 
-    const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
-    const int N = a.lens[b];
-    const int s = a.slot[b];
-    const bool bad_len = N < 0 || N > a.len_limit;
-    const bool bad_slot = s < 0 || s >= a.S;
-    if (bad_len || bad_slot) {
-        if (threadIdx.x == 0 && h == 0) atomicOr(a.status, (bad_len ? kFlagBadLen : 0u) | (bad_slot ? kFlagBadSlot : 0u));
-        return;
+// Online-softmax state of one lane: running max m (log2 domain), running sum l over the
+// rows this lane's row group saw, and the weighted sum of its 16-byte piece of V.
+template <int PER>
+struct State {
+    float m, l, acc[PER];
+    __device__ void clear() {
+        m = -INFINITY;
+        l = 0.f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = 0.f;
     }
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int sub = lane % R, grp = lane / R;
-    const long bh = (long)b * a.H + h;
-    const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
-    const T *pk = static_cast<const T *>(a.pool_k) + slot_off;
-    const T *pv = static_cast<const T *>(a.pool_v) + slot_off;
-    const __amdgpu_buffer_rsrc_t rk = rsrc(pk, (uint32_t)N * ROW);   // rows >= N read as zero
-    const __amdgpu_buffer_rsrc_t rv = rsrc(pv, (uint32_t)N * ROW);
-    const u32x4 qx = load16(rsrc(static_cast<const T *>(a.q) + bh * D, ROW), sub * 16);
+};
 
-    float m = -INFINITY, l = 0.f, acc[PER];
+// The wave folds chunks c_first, c_first + stride, ... below c_end (chunk c = rows
+// [c*CH, c*CH + CH), rows >= N masked) into st.
+template <typename T, int D>
+__device__ __forceinline__ void scan_chunks(State<Geo<T, D>::PER> &st, __amdgpu_buffer_rsrc_t rk,
+                                            __amdgpu_buffer_rsrc_t rv, const u32x4 &qx, float c, int N,
+                                            int c_first, int c_end, int stride, int sub, int grp) {
+    using G = Geo<T, D>;
+    for (int ch = c_first; ch < c_end; ch += stride) {
+        const int c0 = ch * G::CH;
+        u32x4 kx[G::LPC], vx[G::LPC];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-
-    for (int c0 = wave * CH; c0 < N; c0 += kWaves * CH) {
-        u32x4 kx[LPC], vx[LPC];
-#pragma unroll
-        for (int i = 0; i < LPC; ++i) {
-            const uint32_t off = (uint32_t)(c0 + i * RPI + grp) * ROW + sub * 16;
+        for (int i = 0; i < G::LPC; ++i) {
+            const uint32_t off = (uint32_t)(c0 + i * G::RPI + grp) * G::ROW + sub * 16;
             kx[i] = load16(rk, off);
             vx[i] = load16(rv, off);
         }
-        float sc[LPC];
+        float sc[G::LPC];
         float cm = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < LPC; ++i) {
-            const float d = lowsum<R>(dot16<T>(qx, kx[i]));
-            sc[i] = c0 + i * RPI + grp < N ? d * a.c : -INFINITY;
+        for (int i = 0; i < G::LPC; ++i) {
+            const float d = lowsum<G::R>(dot16<T>(qx, kx[i]));
+            sc[i] = c0 + i * G::RPI + grp < N ? d * c : -INFINITY;
             cm = fmaxf(cm, sc[i]);
         }
-        cm = xmax<R>(cm);   // chunk max over the wave (finite: row c0 < N is valid)
-        const float mn = fmaxf(m, cm);
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        m = mn;
-        l *= alpha;
+        cm = xmax<G::R>(cm);   // chunk max over the wave (finite: row c0 < N is valid)
+        const float mn = fmaxf(st.m, cm);
+        const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
+        st.m = mn;
+        st.l *= alpha;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] *= alpha;
+        for (int e = 0; e < G::PER; ++e) st.acc[e] *= alpha;
 #pragma unroll
-        for (int i = 0; i < LPC; ++i) {
-            const float p = __builtin_amdgcn_exp2f(sc[i] - m);
-            l += p;   // the R lanes of a row hold the same weight; only rows are summed below
-            float vf[PER];
+        for (int i = 0; i < G::LPC; ++i) {
+            const float p = __builtin_amdgcn_exp2f(sc[i] - st.m);
+            st.l += p;   // the R lanes of a row hold the same weight; only rows are summed later
+            float vf[G::PER];
             widen<T>(vx[i], vf);
 #pragma unroll
-            for (int e = 0; e < PER; ++e) acc[e] = __builtin_fmaf(p, vf[e], acc[e]);
+            for (int e = 0; e < G::PER; ++e) st.acc[e] = __builtin_fmaf(p, vf[e], st.acc[e]);
         }
     }
-    // the wave's state: sum the row groups (lanes with the same sub hold the same dims)
-    l = xsum<R>(l);
+}
+
+// Sums the wave's row groups (lanes with the same sub hold the same dims) and leaves the
+// wave's state in part[wave]: accumulator [0, D), max at D, sum at D + 1.
+template <typename T, int D, int WAVES>
+__device__ __forceinline__ void publish(State<Geo<T, D>::PER> &st, float (*part)[D + 2], int wave, int sub,
+                                        int grp) {
+    using G = Geo<T, D>;
+    st.l = xsum<G::R>(st.l);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = xsum<R>(acc[e]);
+    for (int e = 0; e < G::PER; ++e) st.acc[e] = xsum<G::R>(st.acc[e]);
     if (grp == 0) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) part[wave][sub * PER + e] = acc[e];
+        for (int e = 0; e < G::PER; ++e) part[wave][sub * G::PER + e] = st.acc[e];
         if (sub == 0) {
-            part[wave][D] = m;
-            part[wave][D + 1] = l;
+            part[wave][D] = st.m;
+            part[wave][D + 1] = st.l;
         }
     }
-    __syncthreads();
-    if (wave != 0) return;
+}
 
-    // Wave 0: the new token as the last key, merge of the 8 partial states, output.
-    const u32x4 knew = load16(rsrc(static_cast<const T *>(a.k) + bh * D, ROW), sub * 16);
-    const u32x4 vnew = load16(rsrc(static_cast<const T *>(a.v) + bh * D, ROW), sub * 16);
-    const float snew = lowsum<R>(dot16<T>(qx, knew)) * a.c;
-    float mt = snew;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mt = fmaxf(mt, part[w][D]);
-    const float pnew = __builtin_amdgcn_exp2f(snew - mt);
-    float lt = pnew, out[PER];
-    float vf[PER];
+// Flags and skips an invalid user; true when (b) must be skipped.
+__device__ __forceinline__ bool invalid_user(const AttnArgs &a, int b, int N, int s, bool flag) {
+    const bool bad_len = N < 0 || N > a.len_limit;
+    const bool bad_slot = s < 0 || s >= a.S;
+    if ((bad_len || bad_slot) && flag)
+        atomicOr(a.status, (bad_len ? kFlagBadLen : 0u) | (bad_slot ? kFlagBadSlot : 0u));
+    return bad_len || bad_slot;
+}
+
+// The last step shared by both paths: the new token enters as one more key with weight
+// exp2(snew - mt); out already holds the other keys' weighted values rescaled to mt and
+// lt their weight sum.  Stores the output row and copies the token's K/V row into slot
+// row N.  Lanes with grp == 0 (one per 16-byte piece) store.
+template <typename T, int D>
+__device__ __forceinline__ void finish(const AttnArgs &a, long bh, long slot_off, int N, const u32x4 &knew,
+                                       const u32x4 &vnew, float pnew, float lt, float (&out)[Geo<T, D>::PER],
+                                       int sub, int grp) {
+    using G = Geo<T, D>;
+    float vf[G::PER];
     widen<T>(vnew, vf);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) out[e] = pnew * vf[e];
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        const float wt = __builtin_amdgcn_exp2f(part[w][D] - mt);   // 0 for a wave that saw no row
-        lt = __builtin_fmaf(wt, part[w][D + 1], lt);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) out[e] = __builtin_fmaf(wt, part[w][sub * PER + e], out[e]);
-    }
-    const float inv = 1.f / lt;
+    for (int e = 0; e < G::PER; ++e) out[e] = __builtin_fmaf(pnew, vf[e], out[e]);
+    const float inv = 1.f / (lt + pnew);
     if (grp == 0) {
         u32x4 ox;
-        if constexpr (PER == 8) {
+        if constexpr (G::PER == 8) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bf16x2 pr = {(bf16)(out[2 * i] * inv), (bf16)(out[2 * i + 1] * inv)};
@@ -227,23 +235,191 @@ __global__ void __launch_bounds__(kThreads) ar_decode_kernel(AttnArgs a) {
     }
 }
 
+// One pass per (user, head): kWaves waves take the slot's chunks in turn, then wave 0
+// merges their states with the new token.
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads) ar_decode_kernel(AttnArgs a) {
+    using G = Geo<T, D>;
+    __shared__ float part[kWaves][D + 2];
+
+    const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
+    const int N = a.lens[b];
+    const int s = a.slot[b];
+    if (invalid_user(a, b, N, s, threadIdx.x == 0 && h == 0)) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int sub = lane % G::R, grp = lane / G::R;
+    const long bh = (long)b * a.H + h;
+    const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
+    const T *pk = static_cast<const T *>(a.pool_k) + slot_off;
+    const T *pv = static_cast<const T *>(a.pool_v) + slot_off;
+    const __amdgpu_buffer_rsrc_t rk = rsrc(pk, (uint32_t)N * G::ROW);   // rows >= N read as zero
+    const __amdgpu_buffer_rsrc_t rv = rsrc(pv, (uint32_t)N * G::ROW);
+    const u32x4 qx = load16(rsrc(static_cast<const T *>(a.q) + bh * D, G::ROW), sub * 16);
+
+    State<G::PER> st;
+    st.clear();
+    scan_chunks<T, D>(st, rk, rv, qx, a.c, N, wave, (N + G::CH - 1) / G::CH, kWaves, sub, grp);
+    publish<T, D, kWaves>(st, part, wave, sub, grp);
+    __syncthreads();
+    if (wave != 0) return;
+
+    const u32x4 knew = load16(rsrc(static_cast<const T *>(a.k) + bh * D, G::ROW), sub * 16);
+    const u32x4 vnew = load16(rsrc(static_cast<const T *>(a.v) + bh * D, G::ROW), sub * 16);
+    const float snew = lowsum<G::R>(dot16<T>(qx, knew)) * a.c;
+    float mt = snew;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mt = fmaxf(mt, part[w][D]);
+    float lt = 0.f, out[G::PER];
+#pragma unroll
+    for (int e = 0; e < G::PER; ++e) out[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const float wt = __builtin_amdgcn_exp2f(part[w][D] - mt);   // 0 for a wave that saw no row
+        lt = __builtin_fmaf(wt, part[w][D + 1], lt);
+#pragma unroll
+        for (int e = 0; e < G::PER; ++e) out[e] = __builtin_fmaf(wt, part[w][sub * G::PER + e], out[e]);
+    }
+    finish<T, D>(a, bh, slot_off, N, knew, vnew, __builtin_amdgcn_exp2f(snew - mt), lt, out, sub, grp);
+}
+
+// Split-K across workgroups: a (user, head) with nc chunks cuts them into
+// ceil(nc / cps) parts of cps = ceil(nc / P) chunks; part p is one workgroup.
+__device__ __forceinline__ int split_chunks(int nc, int P) { return (nc + P - 1) / P; }
+
+// Pass 1 of the split path: workgroup (bh, p) folds its part's chunks and writes the
+// part's state (accumulator, max, sum) to ws[(bh * P + p) * (D + 4)].
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads) ar_split_kernel(AttnArgs a, float *ws, int P) {
+    using G = Geo<T, D>;
+    __shared__ float part[kWaves][D + 2];
+
+    const long bh = blockIdx.x / P;
+    const int p = blockIdx.x % P;
+    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+    const int N = a.lens[b];
+    const int s = a.slot[b];
+    if (invalid_user(a, b, N, s, threadIdx.x == 0 && h == 0 && p == 0)) return;
+    const int nc = (N + G::CH - 1) / G::CH;
+    const int cps = split_chunks(nc, P);
+    const int c_begin = p * cps, c_end = min(nc, c_begin + cps);
+    if (c_begin >= c_end) return;   // this part is empty: the merge pass skips it too
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int sub = lane % G::R, grp = lane / G::R;
+    const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
+    const __amdgpu_buffer_rsrc_t rk = rsrc(static_cast<const T *>(a.pool_k) + slot_off, (uint32_t)N * G::ROW);
+    const __amdgpu_buffer_rsrc_t rv = rsrc(static_cast<const T *>(a.pool_v) + slot_off, (uint32_t)N * G::ROW);
+    const u32x4 qx = load16(rsrc(static_cast<const T *>(a.q) + bh * D, G::ROW), sub * 16);
+
+    State<G::PER> st;
+    st.clear();
+    scan_chunks<T, D>(st, rk, rv, qx, a.c, N, c_begin + wave, c_end, kWaves, sub, grp);
+    publish<T, D, kWaves>(st, part, wave, sub, grp);
+    __syncthreads();
+    if (wave != 0) return;
+
+    float mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mt = fmaxf(mt, part[w][D]);   // finite: chunk c_begin has rows
+    float lt = 0.f, out[G::PER];
+#pragma unroll
+    for (int e = 0; e < G::PER; ++e) out[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const float wt = __builtin_amdgcn_exp2f(part[w][D] - mt);
+        lt = __builtin_fmaf(wt, part[w][D + 1], lt);
+#pragma unroll
+        for (int e = 0; e < G::PER; ++e) out[e] = __builtin_fmaf(wt, part[w][sub * G::PER + e], out[e]);
+    }
+    float *dst = ws + ((long)bh * P + p) * (D + 4);
+    if (grp == 0) {
+#pragma unroll
+        for (int e = 0; e < G::PER; ++e) dst[sub * G::PER + e] = out[e];
+        if (sub == 0) {
+            dst[D] = mt;
+            dst[D + 1] = lt;
+        }
+    }
+}
+
+// Pass 2 of the split path: one wave per (user, head) merges the non-empty parts with
+// the new token, stores the output row and the token's K/V row.
+template <typename T, int D>
+__global__ void __launch_bounds__(64) ar_merge_kernel(AttnArgs a, const float *ws, int P) {
+    using G = Geo<T, D>;
+    const long bh = blockIdx.x;
+    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+    const int N = a.lens[b];
+    const int s = a.slot[b];
+    if (invalid_user(a, b, N, s, false)) return;   // pass 1 raised the flags
+    const int lane = threadIdx.x;
+    const int sub = lane % G::R, grp = lane / G::R;
+    const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
+    const int nc = (N + G::CH - 1) / G::CH;
+    const int parts = nc == 0 ? 0 : (nc + split_chunks(nc, P) - 1) / split_chunks(nc, P);
+    const u32x4 qx = load16(rsrc(static_cast<const T *>(a.q) + bh * D, G::ROW), sub * 16);
+    const u32x4 knew = load16(rsrc(static_cast<const T *>(a.k) + bh * D, G::ROW), sub * 16);
+    const u32x4 vnew = load16(rsrc(static_cast<const T *>(a.v) + bh * D, G::ROW), sub * 16);
+    const float snew = lowsum<G::R>(dot16<T>(qx, knew)) * a.c;
+    const float *src = ws + (long)bh * P * (D + 4);
+    float mt = snew;
+    for (int p = 0; p < parts; ++p) mt = fmaxf(mt, src[p * (D + 4) + D]);
+    float lt = 0.f, out[G::PER];
+#pragma unroll
+    for (int e = 0; e < G::PER; ++e) out[e] = 0.f;
+    for (int p = 0; p < parts; ++p) {
+        const float *pp = src + p * (D + 4);
+        const float wt = __builtin_amdgcn_exp2f(pp[D] - mt);
+        lt = __builtin_fmaf(wt, pp[D + 1], lt);
+#pragma unroll
+        for (int e = 0; e < G::PER; ++e) out[e] = __builtin_fmaf(wt, pp[sub * G::PER + e], out[e]);
+    }
+    finish<T, D>(a, bh, slot_off, N, knew, vnew, __builtin_amdgcn_exp2f(snew - mt), lt, out, sub, grp);
+}
+
+template <typename T, int D>
+hipError_t launch_dim(const AttnArgs &a, float *ws, int P, hipStream_t stream) {
+    const long bh = (long)a.B * a.H;
+    if (P <= 1) {
+        hipLaunchKernelGGL((ar_decode_kernel<T, D>), dim3((unsigned)bh), dim3(kThreads), 0, stream, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((ar_split_kernel<T, D>), dim3((unsigned)(bh * P)), dim3(kThreads), 0, stream, a, ws, P);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((ar_merge_kernel<T, D>), dim3((unsigned)bh), dim3(64), 0, stream, a, ws, P);
+    return hipGetLastError();
+}
+
 template <typename T>
-hipError_t launch_typed(const AttnArgs &a, int D, hipStream_t stream) {
-    const dim3 grid((unsigned)((long)a.B * a.H)), block(kThreads);
+hipError_t launch_typed(const AttnArgs &a, int D, float *ws, int P, hipStream_t stream) {
     switch (D) {
-        case 32: hipLaunchKernelGGL((ar_decode_kernel<T, 32>), grid, block, 0, stream, a); break;
-        case 64: hipLaunchKernelGGL((ar_decode_kernel<T, 64>), grid, block, 0, stream, a); break;
-        case 128: hipLaunchKernelGGL((ar_decode_kernel<T, 128>), grid, block, 0, stream, a); break;
+        case 32: return launch_dim<T, 32>(a, ws, P, stream);
+        case 64: return launch_dim<T, 64>(a, ws, P, stream);
+        case 128: return launch_dim<T, 128>(a, ws, P, stream);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_ar_decode(const AttnArgs &a, int D, bool bf16_elems, hipStream_t stream) {
+int ar_splits(long bh, int n_max, int D, bool bf16_elems) {
+    // One workgroup streams a (user, head)'s rows at a few tens of GB/s, and the merge
+    // pass costs about one launch; so split only pairs whose K/V (at the slot's capacity)
+    // exceed 256 KiB per part, and only while the parts of all pairs stay below about
+    // 192 workgroups (a pass over more pairs than that is bound by HBM already).
+    if (bh <= 0 || n_max < 2) return 1;
+    const long pair_bytes = 2L * (n_max - 1) * D * (bf16_elems ? 2 : 4);
+    long P = pair_bytes / (256L << 10);
+    const long cap = 192 / bh;
+    if (P > cap) P = cap;
+    return P < 1 ? 1 : (int)P;
+}
+
+size_t ar_workspace_bytes(long bh, int P, int D) { return P <= 1 ? 0 : (size_t)bh * P * (D + 4) * sizeof(float); }
+
+hipError_t launch_ar_decode(const AttnArgs &a, int D, bool bf16_elems, float *ws, int P, hipStream_t stream) {
     if ((long)a.B * a.H <= 0) return hipSuccess;
-    return bf16_elems ? launch_typed<bf16>(a, D, stream) : launch_typed<float>(a, D, stream);
+    return bf16_elems ? launch_typed<bf16>(a, D, ws, P, stream) : launch_typed<float>(a, D, ws, P, stream);
 }
 
 }  // namespace unipin

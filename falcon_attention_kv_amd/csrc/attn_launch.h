@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace unipin {
@@ -39,7 +40,12 @@ hipError_t launch_decode_bf16(const AttnArgs &a, int D, hipStream_t stream);
 hipError_t launch_prefill_fp32(const AttnArgs &a, int D, hipStream_t stream);
 hipError_t launch_decode_fp32(const AttnArgs &a, int D, hipStream_t stream);
 // One autoregressive step (one new token per user and head); bf16 or fp32 elements.
-hipError_t launch_ar_decode(const AttnArgs &a, int D, bool bf16, hipStream_t stream);
+// P = 1: one pass per (user, head).  P > 1: the slot rows are split into up to P parts,
+// one workgroup each, whose states go to ws (ar_workspace_bytes(B*H, P, D) bytes, fp32)
+// and are merged by a second pass.
+int ar_splits(long bh, int n_max, int D, bool bf16);
+size_t ar_workspace_bytes(long bh, int P, int D);
+hipError_t launch_ar_decode(const AttnArgs &a, int D, bool bf16, float *ws, int P, hipStream_t stream);
 
 // Device address of the sticky status word of the current device (looked up once
 // per device with hipGetSymbolAddress).

@@ -199,7 +199,7 @@ int unipin_rank_decode(const void *qc, const void *kc, const void *vc,
 
 int unipin_ar_decode(const void *q, const void *k, const void *v, unipin_pool_t *pool,
                      const int32_t *slot, const int32_t *lens, int layer, int B, float scale,
-                     void *o, void *stream) {
+                     void *o, void *workspace, size_t workspace_bytes, void *stream) {
     if (!pool || !q || !k || !v || !lens || !slot || !o) return UNIPIN_EINVAL;
     if (B < 1) return UNIPIN_EINVAL;
     if (layer < 0 || layer >= pool->L) return UNIPIN_ERANGE;
@@ -221,10 +221,24 @@ int unipin_ar_decode(const void *q, const void *k, const void *v, unipin_pool_t 
     a.rows = 1;
     a.len_limit = pool->n_max - 1;
     a.tiles = 1;
+    const bool bf16 = pool->dtype == UNIPIN_BF16;
+    int parts = 1;
+    if (workspace) {
+        if (!aligned(workspace, 16)) return UNIPIN_EALIGN;
+        parts = unipin::ar_splits((long)B * pool->H, pool->n_max, pool->D, bf16);
+        if (workspace_bytes < unipin::ar_workspace_bytes((long)B * pool->H, parts, pool->D)) return UNIPIN_EINVAL;
+    }
     if (unipin::device_status_word(&a.status) != hipSuccess) return UNIPIN_EHIP;
-    const hipError_t e = unipin::launch_ar_decode(a, pool->D, pool->dtype == UNIPIN_BF16,
+    const hipError_t e = unipin::launch_ar_decode(a, pool->D, bf16, static_cast<float *>(workspace), parts,
                                                   static_cast<hipStream_t>(stream));
     return e == hipSuccess ? UNIPIN_OK : UNIPIN_EHIP;
+}
+
+size_t unipin_ar_decode_workspace_bytes(const unipin_pool_t *pool, int B) {
+    if (!pool || B < 1) return 0;
+    const long bh = (long)B * pool->H;
+    return unipin::ar_workspace_bytes(bh, unipin::ar_splits(bh, pool->n_max, pool->D, pool->dtype == UNIPIN_BF16),
+                                      pool->D);
 }
 
 int unipin_device_status(void *stream, int *flags) {

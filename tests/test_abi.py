@@ -172,8 +172,8 @@ def test_decode_host_checks(kw, code):
     lib.unipin_pool_destroy(h)
 
 
-def _ar(h, q=FAKE, k=FAKE, v=FAKE, slot=FAKE, lens=FAKE, layer=0, B=1, scale=0.0, o=FAKE):
-    return lib.unipin_ar_decode(q, k, v, h, slot, lens, layer, B, scale, o, None)
+def _ar(h, q=FAKE, k=FAKE, v=FAKE, slot=FAKE, lens=FAKE, layer=0, B=1, scale=0.0, o=FAKE, ws=None, ws_bytes=0):
+    return lib.unipin_ar_decode(q, k, v, h, slot, lens, layer, B, scale, o, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -187,6 +187,35 @@ def _ar(h, q=FAKE, k=FAKE, v=FAKE, slot=FAKE, lens=FAKE, layer=0, B=1, scale=0.0
 def test_ar_decode_host_checks(kw, code):
     h = make_pool(L=2, n_max=16)
     assert _ar(h, **kw) == code
+    lib.unipin_pool_destroy(h)
+
+
+def test_ar_decode_workspace_bytes():
+    """Splitting takes parts of at least 256 KiB of slot K/V (at the slot's capacity) and
+    at most about 192 workgroups over all (user, head) pairs; the buffer holds one fp32
+    state of D + 4 floats per (user, head, part)."""
+    assert lib.unipin_ar_decode_workspace_bytes(None, 4) == 0
+    h = make_pool(L=1, S=16, H=16, n_max=4106, D=128)   # 2 MiB of K/V per (user, head)
+    assert lib.unipin_ar_decode_workspace_bytes(h, 0) == 0
+    assert lib.unipin_ar_decode_workspace_bytes(h, 1) == 16 * 8 * (128 + 4) * 4    # 8 parts of 256 KiB
+    assert lib.unipin_ar_decode_workspace_bytes(h, 4) == 64 * 3 * (128 + 4) * 4    # 192 // 64 parts
+    assert lib.unipin_ar_decode_workspace_bytes(h, 16) == 0                        # 256 pairs: one pass
+    lib.unipin_pool_destroy(h)
+    h = make_pool(L=1, S=64, H=8, n_max=522, D=64)   # history 512 + a few steps: 130 KiB per pair
+    assert lib.unipin_ar_decode_workspace_bytes(h, 1) == 0
+    assert lib.unipin_ar_decode_workspace_bytes(h, 64) == 0
+    lib.unipin_pool_destroy(h)
+    h = make_pool(L=1, S=4, H=2, n_max=4097, D=64, dtype=fa.FP32)   # 2 MiB per pair in fp32
+    assert lib.unipin_ar_decode_workspace_bytes(h, 3) == 6 * 8 * (64 + 4) * 4
+    lib.unipin_pool_destroy(h)
+
+
+def test_ar_decode_workspace_checks():
+    h = make_pool(L=1, S=16, H=16, n_max=4106, D=128)
+    need = lib.unipin_ar_decode_workspace_bytes(h, 1)
+    assert need > 0
+    assert _ar(h, B=1, ws=FAKE, ws_bytes=need - 1) == fa.EINVAL
+    assert _ar(h, B=1, ws=FAKE + 4, ws_bytes=need) == fa.EALIGN
     lib.unipin_pool_destroy(h)
 
 

@@ -162,3 +162,102 @@ def test_ar_decode_serving_shape_sampled():
     rows_v = torch.stack([pv[layer, b, :, lens[b]] for b in range(w.B)])
     assert torch.equal(rows_k, tok["k"][0][:, :, 0]) and torch.equal(rows_v, tok["v"][0][:, :, 0])
     pool.close()
+
+
+SPLIT_CASES = [(torch.bfloat16, 64), (torch.bfloat16, 128), (torch.bfloat16, 32), (torch.float32, 64),
+               (torch.float32, 128)]
+
+
+@pytest.mark.parametrize("dtype,D", SPLIT_CASES, ids=lambda x: str(x))
+def test_ar_decode_split_path(dtype, D):
+    """Few (user, head) pairs on a long slot: the rows are split across workgroups and the
+    parts merged by a second pass.  Lengths cover an empty slot, fewer chunks than parts,
+    part boundaries and the last free row; the one-pass kernel must agree with the oracle
+    on the same inputs too."""
+    L, S, H, n_max, layer = 1, 12, 2, 4600, 0
+    lens = [0, 1, 64, 65, 200, 511, 513, 1024, 2047, 3000, 4100, n_max - 1]
+    slots = [3, 0, 11, 2, 7, 1, 4, 6, 5, 10, 9, 8]
+    B = len(lens)
+    announce(f"ar_decode split path {dtype} D={D}")
+    pk, pv = W.random_pool(L, S, H, n_max, D, dtype, seed=38, device=DEV)
+    tok = W.step_tokens(B, H, D, 1, dtype, seed=39, device=DEV)
+    q, k, v = tok["q"][0], tok["k"][0], tok["v"][0]
+    before_k, before_v = pk.cpu(), pv.cpu()
+    ref_o, ref_k, ref_v = oracle.ar_decode(q.cpu(), k.cpu(), v.cpu(), before_k, before_v, slots, lens, layer)
+    for split in (True, False):
+        pk.copy_(before_k.to(DEV))
+        pv.copy_(before_v.to(DEV))
+        pool = fa.Pool(pk, pv)
+        if split:
+            assert fa.ar_decode_workspace_bytes(pool, B) > 0, "this shape must take the split path"
+        o = fa.ar_decode(q, k, v, pool, slots, lens, layer, split=split)
+        torch.cuda.synchronize()
+        assert fa.device_status() == 0
+        check_close(o, ref_o, dtype, f"ar_decode split={split} {dtype} D={D}")
+        assert np.array_equal(oracle.as_f64(pk), ref_k) and np.array_equal(oracle.as_f64(pv), ref_v)
+        pool.close()
+
+
+def test_ar_decode_split_invalid_users_and_reused_workspace():
+    """Invalid users are flagged and skipped by both passes; a workspace filled with NaN
+    from an earlier call does not leak into the next one."""
+    L, S, H, n_max, D = 1, 4, 2, 3000, 64
+    announce("ar_decode split invalid users")
+    pk, pv = W.random_pool(L, S, H, n_max, D, torch.bfloat16, seed=40, device=DEV)
+    pool = fa.Pool(pk, pv)
+    tok = W.step_tokens(4, H, D, 1, torch.bfloat16, seed=41, device=DEV)
+    need = fa.ar_decode_workspace_bytes(pool, 4)
+    assert need > 0
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    before_k, before_v = pk.cpu(), pv.cpu()
+    o = torch.full_like(tok["q"][0], 7.0)
+    slots, lens = [0, 9, 1, 2], [2000, 5, n_max, 2999]
+    fa.ar_decode(tok["q"][0], tok["k"][0], tok["v"][0], pool, slots, lens, 0, o=o, workspace=ws)
+    torch.cuda.synchronize()
+    assert fa.device_status() == fa.FLAG_BAD_SLOT | fa.FLAG_BAD_LEN
+    assert torch.all(o[1:3] == 7.0), "skipped users' outputs must stay untouched"
+    ref, _, _ = oracle.ar_decode(tok["q"][0].cpu(), tok["k"][0].cpu(), tok["v"][0].cpu(), before_k, before_v,
+                                 [0, 0, 0, 2], [2000, 0, 0, 2999], 0)
+    check_close(o[[0, 3]], ref[[0, 3]], torch.bfloat16, "valid users next to invalid ones")
+    exp_k = before_k.clone()
+    exp_k[0, 0, :, 2000] = tok["k"][0][0, :, 0].cpu()
+    exp_k[0, 2, :, 2999] = tok["k"][0][3, :, 0].cpu()
+    assert torch.equal(pk.cpu(), exp_k), "only the valid users' rows may change"
+    pool.close()
+
+
+def test_ar_decode_long_history_sampled():
+    """The step at the long-history shape (16 users x 16 heads, D=128, histories drawn
+    from 1024..4096): 256 (user, head) pairs, one pass; sampled users against the oracle."""
+    w = W.WORKLOADS[4]
+    _long_history_case(w.B, w.H, w.D, W.history_lengths(w).tolist(), w.n + 1, seed=42, split_expected=False)
+
+
+def test_ar_decode_few_users_long_history_split():
+    """Two requests of 16 heads with 4000 and 2500 rows (D=128): too few pairs to fill the
+    GPU, so each pair's rows are split across workgroups."""
+    _long_history_case(2, 16, 128, [4000, 2500], 4001, seed=44, split_expected=True)
+
+
+def _long_history_case(B, H, D, lens, n_max, seed, split_expected):
+    announce(f"ar_decode long history B={B} H={H} D={D} split={split_expected}")
+    pk, pv = W.random_pool(1, B, H, n_max, D, torch.bfloat16, seed=seed, device=DEV)
+    pool = fa.Pool(pk, pv)
+    assert (fa.ar_decode_workspace_bytes(pool, B) > 0) == split_expected
+    tok = W.step_tokens(B, H, D, 1, torch.bfloat16, seed=seed + 1, device=DEV)
+    slots = list(range(B))
+    users = sorted({int(np.argmin(lens)), int(np.argmax(lens)), B // 3})
+    before = {b: (pk[0, b, :, :lens[b]].cpu(), pv[0, b, :, :lens[b]].cpu()) for b in users}
+    o = fa.ar_decode(tok["q"][0], tok["k"][0], tok["v"][0], pool, slots, lens, 0)
+    torch.cuda.synchronize()
+    assert fa.device_status() == 0
+    for b in users:
+        hk, hv = (np.concatenate([oracle.as_f64(x), np.zeros((H, 1, D))], axis=1)[None, None]
+                  for x in before[b])
+        ref, _, _ = oracle.ar_decode(tok["q"][0][b:b + 1].cpu(), tok["k"][0][b:b + 1].cpu(),
+                                     tok["v"][0][b:b + 1].cpu(), hk, hv, [0], [lens[b]], 0)
+        check_close(o[b:b + 1], ref, torch.bfloat16, f"long history user {b} (N={lens[b]})")
+    rows_k = torch.stack([pk[0, b, :, lens[b]] for b in range(B)])
+    rows_v = torch.stack([pv[0, b, :, lens[b]] for b in range(B)])
+    assert torch.equal(rows_k, tok["k"][0][:, :, 0]) and torch.equal(rows_v, tok["v"][0][:, :, 0])
+    pool.close()
