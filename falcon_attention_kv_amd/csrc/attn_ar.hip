@@ -243,18 +243,18 @@ __global__ void __launch_bounds__(kThreads) ar_decode_kernel(AttnArgs a) {
     __shared__ float part[kWaves][D + 2];
 
     const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
-    const int N = a.lens[b];
-    const int s = a.slot[b];
-    if (invalid_user(a, b, N, s, threadIdx.x == 0 && h == 0)) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int sub = lane % G::R, grp = lane / G::R;
     const long bh = (long)b * a.H + h;
+    const u32x4 qx = load16(rsrc(static_cast<const T *>(a.q) + bh * D, G::ROW), sub * 16);   // slot-independent
+    const int N = a.lens[b];
+    const int s = a.slot[b];
+    if (invalid_user(a, b, N, s, threadIdx.x == 0 && h == 0)) return;
     const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
     const T *pk = static_cast<const T *>(a.pool_k) + slot_off;
     const T *pv = static_cast<const T *>(a.pool_v) + slot_off;
     const __amdgpu_buffer_rsrc_t rk = rsrc(pk, (uint32_t)N * G::ROW);   // rows >= N read as zero
     const __amdgpu_buffer_rsrc_t rv = rsrc(pv, (uint32_t)N * G::ROW);
-    const u32x4 qx = load16(rsrc(static_cast<const T *>(a.q) + bh * D, G::ROW), sub * 16);
 
     State<G::PER> st;
     st.clear();
@@ -296,6 +296,9 @@ __global__ void __launch_bounds__(kThreads) ar_split_kernel(AttnArgs a, float *w
     const long bh = blockIdx.x / P;
     const int p = blockIdx.x % P;
     const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int sub = lane % G::R, grp = lane / G::R;
+    const u32x4 qx = load16(rsrc(static_cast<const T *>(a.q) + bh * D, G::ROW), sub * 16);   // slot-independent
     const int N = a.lens[b];
     const int s = a.slot[b];
     if (invalid_user(a, b, N, s, threadIdx.x == 0 && h == 0 && p == 0)) return;
@@ -303,12 +306,9 @@ __global__ void __launch_bounds__(kThreads) ar_split_kernel(AttnArgs a, float *w
     const int cps = split_chunks(nc, P);
     const int c_begin = p * cps, c_end = min(nc, c_begin + cps);
     if (c_begin >= c_end) return;   // this part is empty: the merge pass skips it too
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int sub = lane % G::R, grp = lane / G::R;
     const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
     const __amdgpu_buffer_rsrc_t rk = rsrc(static_cast<const T *>(a.pool_k) + slot_off, (uint32_t)N * G::ROW);
     const __amdgpu_buffer_rsrc_t rv = rsrc(static_cast<const T *>(a.pool_v) + slot_off, (uint32_t)N * G::ROW);
-    const u32x4 qx = load16(rsrc(static_cast<const T *>(a.q) + bh * D, G::ROW), sub * 16);
 
     State<G::PER> st;
     st.clear();
@@ -342,38 +342,54 @@ __global__ void __launch_bounds__(kThreads) ar_split_kernel(AttnArgs a, float *w
 }
 
 // Pass 2 of the split path: one wave per (user, head) merges the non-empty parts with
-// the new token, stores the output row and the token's K/V row.
+// the new token, stores the output row and the token's K/V row.  Lane p holds part p's
+// max and sum (at most 64 parts); the accumulators are read four parts at a time so
+// that their loads overlap.
 template <typename T, int D>
 __global__ void __launch_bounds__(64) ar_merge_kernel(AttnArgs a, const float *ws, int P) {
     using G = Geo<T, D>;
+    constexpr int SD = D + 4;   // floats per part state
     const long bh = blockIdx.x;
     const int b = (int)(bh / a.H), h = (int)(bh % a.H);
-    const int N = a.lens[b];
-    const int s = a.slot[b];
-    if (invalid_user(a, b, N, s, false)) return;   // pass 1 raised the flags
     const int lane = threadIdx.x;
     const int sub = lane % G::R, grp = lane / G::R;
-    const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
-    const int nc = (N + G::CH - 1) / G::CH;
-    const int parts = nc == 0 ? 0 : (nc + split_chunks(nc, P) - 1) / split_chunks(nc, P);
+    // the token's rows do not depend on the slot: their loads go out first
     const u32x4 qx = load16(rsrc(static_cast<const T *>(a.q) + bh * D, G::ROW), sub * 16);
     const u32x4 knew = load16(rsrc(static_cast<const T *>(a.k) + bh * D, G::ROW), sub * 16);
     const u32x4 vnew = load16(rsrc(static_cast<const T *>(a.v) + bh * D, G::ROW), sub * 16);
+    // an invalid user (flagged by pass 1) merges nothing and stores nothing; no early
+    // exit, so that the loads above are not held back behind the check
+    const bool ok = !invalid_user(a, b, a.lens[b], a.slot[b], false);
+    const int N = ok ? a.lens[b] : 0;
+    const long slot_off = ok ? ((long)a.slot[b] * a.H + h) * (long)a.n_max * D : 0;
+    const int nc = (N + G::CH - 1) / G::CH;
+    const int parts = nc == 0 ? 0 : (nc + split_chunks(nc, P) - 1) / split_chunks(nc, P);
+    const float *src = ws + (long)bh * P * SD;
+    const float mp = lane < parts ? src[lane * SD + D] : -INFINITY;
+    const float lp = lane < parts ? src[lane * SD + D + 1] : 0.f;
     const float snew = lowsum<G::R>(dot16<T>(qx, knew)) * a.c;
-    const float *src = ws + (long)bh * P * (D + 4);
-    float mt = snew;
-    for (int p = 0; p < parts; ++p) mt = fmaxf(mt, src[p * (D + 4) + D]);
-    float lt = 0.f, out[G::PER];
+    const float mt = fmaxf(snew, xmax<1>(mp));
+    const float wp = __builtin_amdgcn_exp2f(mp - mt);   // 0 past the last part
+    const float lt = xsum<1>(wp * lp);
+    float out[G::PER];
 #pragma unroll
     for (int e = 0; e < G::PER; ++e) out[e] = 0.f;
-    for (int p = 0; p < parts; ++p) {
-        const float *pp = src + p * (D + 4);
-        const float wt = __builtin_amdgcn_exp2f(pp[D] - mt);
-        lt = __builtin_fmaf(wt, pp[D + 1], lt);
+    for (int p0 = 0; p0 < parts; p0 += 4) {
+        float x[4][G::PER];
 #pragma unroll
-        for (int e = 0; e < G::PER; ++e) out[e] = __builtin_fmaf(wt, pp[sub * G::PER + e], out[e]);
+        for (int j = 0; j < 4; ++j) {
+            const float *pp = src + (long)min(p0 + j, parts - 1) * SD + sub * G::PER;
+#pragma unroll
+            for (int e = 0; e < G::PER; ++e) x[j][e] = pp[e];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float w = p0 + j < parts ? __shfl(wp, p0 + j) : 0.f;
+#pragma unroll
+            for (int e = 0; e < G::PER; ++e) out[e] = __builtin_fmaf(w, x[j][e], out[e]);
+        }
     }
-    finish<T, D>(a, bh, slot_off, N, knew, vnew, __builtin_amdgcn_exp2f(snew - mt), lt, out, sub, grp);
+    if (ok) finish<T, D>(a, bh, slot_off, N, knew, vnew, __builtin_amdgcn_exp2f(snew - mt), lt, out, sub, grp);
 }
 
 template <typename T, int D>
@@ -400,18 +416,33 @@ hipError_t launch_typed(const AttnArgs &a, int D, float *ws, int P, hipStream_t 
     }
 }
 
+template <typename T>
+int chunk_rows(int D) {
+    switch (D) {
+        case 32: return Geo<T, 32>::CH;
+        case 64: return Geo<T, 64>::CH;
+        case 128: return Geo<T, 128>::CH;
+        default: return 0;
+    }
+}
+
 }  // namespace
 
 int ar_splits(long bh, int n_max, int D, bool bf16_elems) {
-    // One workgroup streams a (user, head)'s rows at a few tens of GB/s, and the merge
-    // pass costs about one launch; so split only pairs whose K/V (at the slot's capacity)
-    // exceed 256 KiB per part, and only while the parts of all pairs stay below about
-    // 192 workgroups (a pass over more pairs than that is bound by HBM already).
+    // A pair whose K/V (at the slot's capacity) fit in 256 KiB costs the one-pass kernel
+    // about two memory round trips, less than the merge pass: no split.  Otherwise cut
+    // the rows into parts of at least 4 chunks, up to about 256 workgroups over all
+    // pairs (more only add merge work; HBM is busy by then) and 64 parts per pair (one
+    // per lane of the merge wave).
     if (bh <= 0 || n_max < 2) return 1;
-    const long pair_bytes = 2L * (n_max - 1) * D * (bf16_elems ? 2 : 4);
-    long P = pair_bytes / (256L << 10);
-    const long cap = 192 / bh;
-    if (P > cap) P = cap;
+    const long rows = n_max - 1;
+    if (2L * rows * D * (bf16_elems ? 2 : 4) <= (256L << 10)) return 1;
+    const int ch = bf16_elems ? chunk_rows<bf16>(D) : chunk_rows<float>(D);
+    if (ch == 0) return 1;
+    const long nc = (rows + ch - 1) / ch;
+    long P = (nc + 3) / 4;
+    if (P > 256 / bh) P = 256 / bh;
+    if (P > 64) P = 64;
     return P < 1 ? 1 : (int)P;
 }
 

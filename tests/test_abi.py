@@ -191,22 +191,28 @@ def test_ar_decode_host_checks(kw, code):
 
 
 def test_ar_decode_workspace_bytes():
-    """Splitting takes parts of at least 256 KiB of slot K/V (at the slot's capacity) and
-    at most about 192 workgroups over all (user, head) pairs; the buffer holds one fp32
-    state of D + 4 floats per (user, head, part)."""
+    """A pair is split only when its slot K/V (at capacity) exceed 256 KiB; then into
+    parts of at least 4 chunks (64 rows each here), at most 256 // (B*H) parts and 64;
+    the buffer holds one fp32 state of D + 4 floats per (user, head, part)."""
     assert lib.unipin_ar_decode_workspace_bytes(None, 4) == 0
-    h = make_pool(L=1, S=16, H=16, n_max=4106, D=128)   # 2 MiB of K/V per (user, head)
+    h = make_pool(L=1, S=16, H=16, n_max=4106, D=128)   # 2 MiB of K/V per pair, 65 chunks
     assert lib.unipin_ar_decode_workspace_bytes(h, 0) == 0
-    assert lib.unipin_ar_decode_workspace_bytes(h, 1) == 16 * 8 * (128 + 4) * 4    # 8 parts of 256 KiB
-    assert lib.unipin_ar_decode_workspace_bytes(h, 4) == 64 * 3 * (128 + 4) * 4    # 192 // 64 parts
+    assert lib.unipin_ar_decode_workspace_bytes(h, 1) == 16 * 16 * (128 + 4) * 4   # 256 // 16 parts
+    assert lib.unipin_ar_decode_workspace_bytes(h, 4) == 64 * 4 * (128 + 4) * 4    # 256 // 64 parts
     assert lib.unipin_ar_decode_workspace_bytes(h, 16) == 0                        # 256 pairs: one pass
     lib.unipin_pool_destroy(h)
     h = make_pool(L=1, S=64, H=8, n_max=522, D=64)   # history 512 + a few steps: 130 KiB per pair
     assert lib.unipin_ar_decode_workspace_bytes(h, 1) == 0
     assert lib.unipin_ar_decode_workspace_bytes(h, 64) == 0
     lib.unipin_pool_destroy(h)
-    h = make_pool(L=1, S=4, H=2, n_max=4097, D=64, dtype=fa.FP32)   # 2 MiB per pair in fp32
-    assert lib.unipin_ar_decode_workspace_bytes(h, 3) == 6 * 8 * (64 + 4) * 4
+    h = make_pool(L=1, S=4, H=1, n_max=4097, D=128)   # 64 chunks: 16 parts of 4
+    assert lib.unipin_ar_decode_workspace_bytes(h, 1) == 1 * 16 * (128 + 4) * 4
+    lib.unipin_pool_destroy(h)
+    h = make_pool(L=1, S=4, H=1, n_max=40001, D=128)   # 625 chunks: capped at 64 parts
+    assert lib.unipin_ar_decode_workspace_bytes(h, 1) == 64 * (128 + 4) * 4
+    lib.unipin_pool_destroy(h)
+    h = make_pool(L=1, S=4, H=2, n_max=4097, D=64, dtype=fa.FP32)   # 2 MiB per pair, 64 chunks
+    assert lib.unipin_ar_decode_workspace_bytes(h, 3) == 6 * 16 * (64 + 4) * 4
     lib.unipin_pool_destroy(h)
 
 
