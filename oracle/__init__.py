@@ -7,6 +7,8 @@ from .attention import (INCLUDE_SELF, SlotRing, ar_decode, as_f64, bruteforce_jo
                         joint, masked_attention, mfalcon_mask, pool_write, prefill,
                         prefill_rows, rank_decode, rank_decode_rows)
 
-__all__ = ["INCLUDE_SELF", "SlotRing", "ar_decode", "as_f64", "bruteforce_joint", "default_scale", "joint",
+from .block import LN_EPS, WEIGHT_KEYS, block_candidates, block_history, block_joint, gelu, layer_norm
+
+__all__ = ["LN_EPS", "WEIGHT_KEYS", "block_candidates", "block_history", "block_joint", "gelu", "layer_norm", "INCLUDE_SELF", "SlotRing", "ar_decode", "as_f64", "bruteforce_joint", "default_scale", "joint",
            "masked_attention", "mfalcon_mask", "pool_write", "prefill", "prefill_rows",
            "rank_decode", "rank_decode_rows"]

@@ -23,6 +23,7 @@ Recipe (stated once, used everywhere):
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass, replace
 from typing import Dict, Optional
 
@@ -135,3 +136,38 @@ def poison_tail(x: torch.Tensor, lens: torch.Tensor, value=float("nan")) -> torc
     for b, nb in enumerate(lens.tolist()):
         y[b, :, nb:, :] = value
     return y
+
+
+BLOCK_WEIGHT_SHAPES = (("ln1_w", (1,)), ("ln1_b", (1,)), ("w_qkv", (1, 3)), ("b_qkv", (3,)), ("w_o", (1, 1)),
+                       ("b_o", (1,)), ("ln2_w", (1,)), ("ln2_b", (1,)), ("w_fc", (1, 4)), ("b_fc", (4,)),
+                       ("w_proj", (4, 1)), ("b_proj", (1,)))
+
+
+def block_weights(C: int, dtype=torch.bfloat16, seed: int = 0, device="cpu") -> Dict[str, torch.Tensor]:
+    """Random weights of one transformer block of width C, drawn in the order of
+    BLOCK_WEIGHT_SHAPES on a generator of `device` seeded with `seed` (shapes in units of
+    C): matrices N(0, 1/fan_in) so projected values stay O(1), biases N(0, 0.02^2),
+    LayerNorm gains 1 + N(0, 0.1^2) and shifts N(0, 0.02^2); then cast to `dtype`.
+    Matrices are row-major "x @ W": [fan_in, fan_out]."""
+    dev = torch.device(device)
+    g = torch.Generator(dev).manual_seed(seed)
+    out = {}
+    for name, units in BLOCK_WEIGHT_SHAPES:
+        shape = tuple(u * C for u in units)
+        t = torch.randn(shape, generator=g, device=dev, dtype=torch.float32)
+        if name.startswith("w_"):
+            t = t / math.sqrt(shape[0])
+        elif name.endswith("_w"):
+            t = 1.0 + 0.1 * t
+        else:
+            t = 0.02 * t
+        out[name] = t.to(dtype)
+    return out
+
+
+def block_inputs(B: int, rows: int, C: int, dtype=torch.bfloat16, seed: int = 0, device="cpu") -> torch.Tensor:
+    """Hidden states [B, rows, C] entering a block: float32 N(0, 1) on a generator of
+    `device` seeded with `seed`, cast to `dtype`."""
+    dev = torch.device(device)
+    g = torch.Generator(dev).manual_seed(seed)
+    return torch.randn((B, rows, C), generator=g, device=dev, dtype=torch.float32).to(dtype)
