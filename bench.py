@@ -13,11 +13,12 @@ Prints one JSON line.  `value` = ranked candidates per second through the whole 
 (HIP events on the launch stream around the step's 12 decode launches, gaps included).  The CPU baseline is the float64 oracle timed on a
 bounded sample of the same work on the host cores.
 
-After the timed steps, `ar_step` reports the autoregressive retrieval step (one new
+After the timed steps, `block_table2` reports the 12-layer transformer around the
+attention (projections, LayerNorm, MLP) at the pages' Table 2 shape, and `ar_step` reports the autoregressive retrieval step (one new
 token per user and head appended to its slot) on the serving shape and on the long
 history shape; it is a secondary figure and does not enter `value`.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ar-step]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ar-step] [--no-block]
 """
 from __future__ import annotations
 
@@ -49,6 +50,8 @@ def parse_args():
                    help="approximate CPU time budget of the oracle baseline sample")
     p.add_argument("--no-ar-step", action="store_true",
                    help="skip the secondary measurement of the autoregressive retrieval step")
+    p.add_argument("--no-block", action="store_true",
+                   help="skip the secondary measurement of the 12-layer transformer at the Table 2 shape")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run 3 plain device copies of this many MiB (a known-size "
                         "reference for the HBM byte counters of a profiler run)")
@@ -110,6 +113,57 @@ def ar_step(fa, W, torch, dev, w, lens, steps: int, warmup: int):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "tokens_per_s": round(w.B * w.H / (avg_ms / 1e3), 1),
             "shape": f"B={w.B} H={w.H} D={w.D} history {min(lens)}..{max(lens)}, {w.L} layer(s), "
                      f"{steps} timed steps"}
+
+
+def block_table2(fa, W, torch, dev, steps: int, warmup: int):
+    """The 12-layer transformer around the attention at the Table 2 shape of the pages
+    (B=8 requests, history 992, 656 candidates, 12 layers), width 512 = 8 heads x 64:
+    the history forward that fills the pool and the ranking stage's candidate-only
+    forward (the pages' "decode with KV reuse"), each timed over its 12 layers with HIP
+    events.  FLOPs per layer: 24 M C^2 in the four projections (M hidden rows) plus the
+    attention's 2 D N (N + 1) per (user, head) for the history, 4 D k (N + 1) for the
+    candidates."""
+    L, B, n, K, H, D = 12, 8, 992, 656, 8, 64
+    C = H * D
+    ws = [W.block_weights(C, torch.bfloat16, seed=300 + l, device=dev) for l in range(L)]
+    xh0 = W.block_inputs(B, n, C, torch.bfloat16, seed=298, device=dev)
+    xc0 = W.block_inputs(B, K, C, torch.bfloat16, seed=299, device=dev)
+    xh, xc = xh0.clone(), xc0.clone()
+    pool = fa.Pool.allocate(L, B, H, n, D, torch.bfloat16, dev)
+    slots = torch.arange(B, dtype=torch.int32, device=dev)
+    lens = torch.full((B,), n, dtype=torch.int32, device=dev)
+    ctx = fa.BlockContext()
+    work = torch.empty(max(fa.block_workspace_bytes(pool, B, n), fa.block_workspace_bytes(pool, B, K)),
+                       dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(warmup + steps):
+        xh.copy_(xh0)
+        xc.copy_(xc0)
+        e = ev[i - warmup] if i >= warmup else None
+        if e:
+            e[0].record(stream)
+        for l in range(L):
+            fa.block_forward(ctx, ws[l], fa.BLOCK_HISTORY, xh, pool, slots, lens, l, workspace=work)
+        if e:
+            e[1].record(stream)
+        for l in range(L):
+            fa.block_forward(ctx, ws[l], fa.BLOCK_CANDIDATES, xc, pool, slots, lens, l, workspace=work)
+        if e:
+            e[2].record(stream)
+    torch.cuda.synchronize()
+    if fa.device_status(dev) != 0:
+        raise RuntimeError("a block flagged an invalid slot or length")
+    hist_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    cand_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    hist_flop = L * (24 * B * n * C * C + 2 * D * n * (n + 1) * B * H)
+    cand_flop = L * (24 * B * K * C * C + 4 * D * K * (n + 1) * B * H)
+    pool.close()
+    ctx.close()
+    return {"shape": "B=8 history 992 candidates 656, 12 layers, C=512 (H=8, D=64), bf16",
+            "history_forward_ms": round(hist_ms, 4), "history_tflops": round(hist_flop / hist_ms / 1e9, 1),
+            "candidate_forward_ms": round(cand_ms, 4), "candidate_tflops": round(cand_flop / cand_ms / 1e9, 1),
+            "candidate_mfma_frac": round(cand_flop / cand_ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
 
 
 def kernel_source_hash() -> str:
@@ -262,6 +316,8 @@ def main():
                             "decode_candidates_per_s": round(cand_per_step / (w.L * dc_avg / 1e3), 1)},
         },
     }
+    if not args.no_block:
+        out["block_table2"] = block_table2(fa, W, torch, dev, steps=5, warmup=2)
     if args.copy_calib_mib:
         n = args.copy_calib_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

@@ -32,7 +32,19 @@ FLAG_BAD_SLOT, FLAG_BAD_LEN = 1, 2
 EXPORTS = ("unipin_pool_create", "unipin_pool_destroy", "unipin_pool_acquire",
            "unipin_pool_generation", "unipin_pool_dims", "unipin_prefill",
            "unipin_rank_decode", "unipin_ar_decode", "unipin_ar_decode_workspace_bytes",
-           "unipin_device_status", "unipin_strerror", "unipin_version")
+           "unipin_device_status", "unipin_strerror", "unipin_version",
+           "unipin_block_ctx_create", "unipin_block_ctx_destroy", "unipin_block_workspace_bytes",
+           "unipin_block_forward")
+
+
+# Weights of one transformer block, in the order of unipin_block_weights_t.
+BLOCK_WEIGHT_NAMES = ("ln1_w", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_w", "ln2_b", "w_fc", "b_fc",
+                      "w_proj", "b_proj")
+BLOCK_HISTORY, BLOCK_CANDIDATES = 0, 1
+
+
+class BlockWeights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in BLOCK_WEIGHT_NAMES]
 
 
 def _load() -> ctypes.CDLL:
@@ -55,14 +67,20 @@ def _load() -> ctypes.CDLL:
     lib.unipin_rank_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp]
     lib.unipin_ar_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
     lib.unipin_ar_decode_workspace_bytes.argtypes = [vp, i32]
+    lib.unipin_block_ctx_create.argtypes = [ctypes.POINTER(vp)]
+    lib.unipin_block_ctx_destroy.argtypes = [vp]
+    lib.unipin_block_workspace_bytes.argtypes = [vp, i32, i32]
+    lib.unipin_block_forward.argtypes = [vp, ctypes.POINTER(BlockWeights), i32, vp, vp, vp, vp, i32, i32, i32,
+                                         ctypes.c_float, vp, ctypes.c_size_t, vp]
     lib.unipin_device_status.argtypes = [vp, ip]
     lib.unipin_strerror.argtypes = [i32]
     lib.unipin_strerror.restype = ctypes.c_char_p
     lib.unipin_version.argtypes = []
     for name in EXPORTS:
-        if name not in ("unipin_strerror", "unipin_ar_decode_workspace_bytes"):
+        if name not in ("unipin_strerror", "unipin_ar_decode_workspace_bytes", "unipin_block_workspace_bytes"):
             getattr(lib, name).restype = ctypes.c_int
     lib.unipin_ar_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.unipin_block_workspace_bytes.restype = ctypes.c_size_t
     return lib
 
 
@@ -254,6 +272,78 @@ def ar_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pool: Pool, slo
                                 0.0 if scale is None else float(scale), o.data_ptr(),
                                 ws_ptr, ws_bytes, _stream_handle(dev)), "unipin_ar_decode")
     return o
+
+
+class BlockContext:
+    """unipin_block_ctx_create/destroy: GEMM plans for the current device."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check(lib.unipin_block_ctx_create(ctypes.byref(h)), "unipin_block_ctx_create")
+        self._h = h
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise UnipinError(EINVAL, "block context is closed")
+        return self._h
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            lib.unipin_block_ctx_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def block_workspace_bytes(pool: Pool, B: int, rows: int) -> int:
+    """unipin_block_workspace_bytes."""
+    return int(lib.unipin_block_workspace_bytes(pool.handle, int(B), int(rows)))
+
+
+def block_forward(ctx: BlockContext, weights, mode: int, x: torch.Tensor, pool: Pool, slot, lens, layer: int,
+                  scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """unipin_block_forward: one transformer block, in place on x [B, rows, C] (bf16).
+
+    weights: a dict with the BLOCK_WEIGHT_NAMES keys (bf16 device tensors; matrices
+    row-major [fan_in, fan_out]).  mode: BLOCK_HISTORY (causal over each user's lens[b]
+    rows; their k, v go to the pool) or BLOCK_CANDIDATES (the candidates attend to the
+    pool's lens[b] rows and themselves).  workspace: a device tensor of at least
+    block_workspace_bytes(pool, B, rows) bytes, or None for one from torch's allocator.
+    """
+    dev = pool.k.device
+    if x.dim() != 3:
+        raise UnipinError(EINVAL, "x must be [B, rows, C]")
+    B, rows, C = x.shape
+    if C != pool.H * pool.D:
+        raise UnipinError(EINVAL, f"x has width {C}, the pool's heads give {pool.H * pool.D}")
+    _check_tensor(x, "x", (B, rows, C), torch.bfloat16, dev)
+    shapes = {"ln1_w": (C,), "ln1_b": (C,), "w_qkv": (C, 3 * C), "b_qkv": (3 * C,), "w_o": (C, C), "b_o": (C,),
+              "ln2_w": (C,), "ln2_b": (C,), "w_fc": (C, 4 * C), "b_fc": (4 * C,), "w_proj": (4 * C, C),
+              "b_proj": (C,)}
+    for name in BLOCK_WEIGHT_NAMES:
+        if name not in weights:
+            raise UnipinError(EINVAL, f"weights lack {name}")
+        _check_tensor(weights[name], name, shapes[name], torch.bfloat16, dev)
+    bw = BlockWeights(*(weights[name].data_ptr() for name in BLOCK_WEIGHT_NAMES))
+    lens_t, slot_t = _i32_on(lens, dev), _i32_on(slot, dev)
+    if lens_t.numel() != B or slot_t.numel() != B:
+        raise UnipinError(EINVAL, "lens and slot need one entry per user")
+    need = block_workspace_bytes(pool, B, rows)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise UnipinError(EINVAL, "workspace must be a contiguous tensor on the pool's device")
+    _check(lib.unipin_block_forward(ctx.handle, ctypes.byref(bw), int(mode), x.data_ptr(), pool.handle,
+                                    slot_t.data_ptr(), lens_t.data_ptr(), layer, B, rows,
+                                    0.0 if scale is None else float(scale), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream_handle(dev)),
+           "unipin_block_forward")
+    return x
 
 
 def device_status(device=None) -> int:

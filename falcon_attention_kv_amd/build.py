@@ -17,7 +17,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libunipin.so")
-SOURCES = ["unipin.cpp", "device_status.hip", "attn_bf16.hip", "attn_fp32.hip", "attn_ar.hip"]
+SOURCES = ["unipin.cpp", "device_status.hip", "attn_bf16.hip", "attn_fp32.hip", "attn_ar.hip",
+           "block.cpp", "block_kernels.hip"]
+# hipBLASLt runs the block's plain GEMMs; found at run time through the ROCm library path
+LINK = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 ARCH = "gfx950"
 
 
@@ -53,7 +56,7 @@ def build(verbose: bool = False, extra=()) -> str:
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs + LINK
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,0 +1,223 @@
+// C ABI of the transformer block around the masked attention (include/unipin.h): one
+// GPT2-style pre-LayerNorm block, run either as the history forward (causal attention,
+// K/V stored in the pool) or as the ranking stage's candidate-only forward (attention
+// to the pool's history plus the candidate's own key).
+//
+// The four projections are plain bf16 GEMMs with fp32 accumulation and go to hipBLASLt,
+// with its epilogues doing the bias, the tanh-form GELU and (through beta = 1 on the
+// hidden state itself) the residual adds.  LayerNorm and the head layout changes are
+// this library's kernels (block_kernels.hip), and the attention is the library's own
+// prefill and rank-decode kernels.  Host code here allocates nothing on the device:
+// every intermediate lives in the caller's workspace.
+#include <hip/hip_runtime.h>
+#include <hipblaslt/hipblaslt.h>
+
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <tuple>
+
+#include "block_launch.h"
+#include "unipin.h"
+
+namespace {
+
+constexpr float kLnEps = 1e-5f;
+constexpr size_t kGemmWorkspace = 32u << 20;   // hipBLASLt's share of the workspace
+constexpr size_t kAlign = 256;
+
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// out[M, N] (row-major) = in[M, K] (row-major) @ W[K, N] (row-major), seen by the
+// column-major library as D[N x M] = W[N x K] * in[K x M]: the bias runs along D's rows.
+struct GemmPlan {
+    hipblasLtMatmulDesc_t desc = nullptr;
+    hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
+    hipblasLtMatmulAlgo_t algo{};
+};
+
+using PlanKey = std::tuple<long, int, int, int, bool>;   // M, N, K, epilogue, residual
+
+}  // namespace
+
+struct unipin_block_ctx {
+    hipblasLtHandle_t handle = nullptr;
+    int device = -1;
+    std::mutex mu;                       // plans and their descriptors are shared by calls
+    std::map<PlanKey, GemmPlan> plans;
+};
+
+namespace {
+
+void destroy_plan(GemmPlan &p) {
+    if (p.la) hipblasLtMatrixLayoutDestroy(p.la);
+    if (p.lb) hipblasLtMatrixLayoutDestroy(p.lb);
+    if (p.lc) hipblasLtMatrixLayoutDestroy(p.lc);
+    if (p.desc) hipblasLtMatmulDescDestroy(p.desc);
+}
+
+// The plan for one GEMM shape and epilogue, made on first use (descriptors and the
+// library's first heuristic choice).  Called with ctx->mu held.
+GemmPlan *plan_for(unipin_block_ctx *ctx, long M, int N, int K, hipblasLtEpilogue_t ep, bool residual) {
+    const PlanKey key{M, N, K, (int)ep, residual};
+    auto it = ctx->plans.find(key);
+    if (it != ctx->plans.end()) return &it->second;
+    GemmPlan p;
+    const hipblasOperation_t op = HIPBLAS_OP_N;
+    const hipDataType bias_type = HIP_R_16BF;
+    hipblasLtMatmulPreference_t pref = nullptr;
+    const uint64_t ws = kGemmWorkspace;
+    hipblasLtMatmulHeuristicResult_t res[1];
+    int found = 0;
+    bool ok = hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &op, sizeof(op)) == 0 &&
+              hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &op, sizeof(op)) == 0 &&
+              hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_EPILOGUE, &ep, sizeof(ep)) == 0 &&
+              hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_BIAS_DATA_TYPE, &bias_type,
+                                              sizeof(bias_type)) == 0 &&
+              hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, N, K, N) == 0 &&
+              hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16BF, K, M, K) == 0 &&
+              hipblasLtMatrixLayoutCreate(&p.lc, HIP_R_16BF, N, M, N) == 0 &&
+              hipblasLtMatmulPreferenceCreate(&pref) == 0 &&
+              hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &ws,
+                                                    sizeof(ws)) == 0 &&
+              hipblasLtMatmulAlgoGetHeuristic(ctx->handle, p.desc, p.la, p.lb, p.lc, p.lc, pref, 1, res, &found) ==
+                  0 &&
+              found > 0;
+    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+    if (!ok) {
+        destroy_plan(p);
+        return nullptr;
+    }
+    p.algo = res[0].algo;
+    return &ctx->plans.emplace(key, p).first->second;
+}
+
+// out = in @ W + bias (then GELU, with ep = GELU_BIAS); residual: out += the old out.
+int gemm(unipin_block_ctx *ctx, const void *in, const void *W, const void *bias, void *out, long M, int N, int K,
+         hipblasLtEpilogue_t ep, bool residual, void *ws, hipStream_t stream) {
+    std::lock_guard<std::mutex> lock(ctx->mu);
+    GemmPlan *p = plan_for(ctx, M, N, K, ep, residual);
+    if (!p) return UNIPIN_EHIP;
+    if (hipblasLtMatmulDescSetAttribute(p->desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof(bias)) != 0)
+        return UNIPIN_EHIP;
+    const float alpha = 1.f, beta = residual ? 1.f : 0.f;
+    const hipblasStatus_t s = hipblasLtMatmul(ctx->handle, p->desc, &alpha, W, p->la, in, p->lb, &beta, out, p->lc,
+                                              out, p->lc, &p->algo, ws, kGemmWorkspace, stream);
+    return s == HIPBLAS_STATUS_SUCCESS ? UNIPIN_OK : UNIPIN_EHIP;
+}
+
+// Workspace layout for M = B * rows hidden rows of width C (bytes, 256-aligned):
+//   [gemm]  hipBLASLt workspace
+//   [big]   M x 4C: the fused QKV output (M x 3C), later the MLP's hidden layer
+//   [heads] M x 3C: q, k, v in per-head layout [B, H, rows, D]
+//   [ln]    M x C:  LayerNorm output, later the merged attention output
+//   [attn]  M x C:  attention output [B, H, rows, D]
+struct Layout {
+    size_t gemm, big, heads, ln, attn, total;
+};
+
+Layout layout(long M, int C) {
+    Layout l;
+    const size_t e = 2;
+    l.gemm = 0;
+    l.big = up(kGemmWorkspace);
+    l.heads = l.big + up((size_t)M * 4 * C * e);
+    l.ln = l.heads + up((size_t)M * 3 * C * e);
+    l.attn = l.ln + up((size_t)M * C * e);
+    l.total = l.attn + up((size_t)M * C * e);
+    return l;
+}
+
+bool weights_present(const unipin_block_weights_t *w) {
+    const void *p[] = {w->ln1_w, w->ln1_b, w->w_qkv, w->b_qkv, w->w_o, w->b_o,
+                       w->ln2_w, w->ln2_b, w->w_fc, w->b_fc, w->w_proj, w->b_proj};
+    for (const void *q : p)
+        if (!q || !aligned16(q)) return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int unipin_block_ctx_create(unipin_block_ctx_t **out) {
+    if (!out) return UNIPIN_EINVAL;
+    *out = nullptr;
+    auto *ctx = new (std::nothrow) unipin_block_ctx;
+    if (!ctx) return UNIPIN_ENOMEM;
+    if (hipGetDevice(&ctx->device) != hipSuccess || hipblasLtCreate(&ctx->handle) != HIPBLAS_STATUS_SUCCESS) {
+        delete ctx;
+        return UNIPIN_EHIP;
+    }
+    *out = ctx;
+    return UNIPIN_OK;
+}
+
+int unipin_block_ctx_destroy(unipin_block_ctx_t *ctx) {
+    if (!ctx) return UNIPIN_EINVAL;
+    for (auto &kv : ctx->plans) destroy_plan(kv.second);
+    hipblasLtDestroy(ctx->handle);
+    delete ctx;
+    return UNIPIN_OK;
+}
+
+size_t unipin_block_workspace_bytes(const unipin_pool_t *pool, int B, int rows) {
+    int L, S, H, n_max, D, dt;
+    if (!pool || B < 1 || rows < 1 || unipin_pool_dims(pool, &L, &S, &H, &n_max, &D, &dt) != UNIPIN_OK) return 0;
+    return layout((long)B * rows, H * D).total;
+}
+
+int unipin_block_forward(unipin_block_ctx_t *ctx, const unipin_block_weights_t *w, int mode, void *x,
+                         unipin_pool_t *pool, const int32_t *slot, const int32_t *lens, int layer, int B, int rows,
+                         float scale, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!ctx || !w || !x || !pool || !slot || !lens || !workspace) return UNIPIN_EINVAL;
+    if (mode != UNIPIN_BLOCK_HISTORY && mode != UNIPIN_BLOCK_CANDIDATES) return UNIPIN_EINVAL;
+    if (B < 1 || rows < 1) return UNIPIN_EINVAL;
+    int L, S, H, n_max, D, dt;
+    if (unipin_pool_dims(pool, &L, &S, &H, &n_max, &D, &dt) != UNIPIN_OK) return UNIPIN_EINVAL;
+    if (dt != UNIPIN_BF16) return UNIPIN_EDTYPE;
+    if (layer < 0 || layer >= L) return UNIPIN_ERANGE;
+    if (mode == UNIPIN_BLOCK_HISTORY && rows > n_max) return UNIPIN_EINVAL;
+    const int C = H * D;
+    if (C > 2048) return UNIPIN_EINVAL;
+    if (!weights_present(w)) return w->ln1_w && w->ln1_b && w->w_qkv && w->b_qkv && w->w_o && w->b_o &&
+                                           w->ln2_w && w->ln2_b && w->w_fc && w->b_fc && w->w_proj && w->b_proj
+                                       ? UNIPIN_EALIGN
+                                       : UNIPIN_EINVAL;
+    if (!aligned16(x) || !aligned16(workspace) || !aligned16(slot) || !aligned16(lens)) return UNIPIN_EALIGN;
+    const long M = (long)B * rows;
+    const Layout lo = layout(M, C);
+    if (workspace_bytes < lo.total) return UNIPIN_EINVAL;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != ctx->device) return UNIPIN_EINVAL;
+
+    char *ws = static_cast<char *>(workspace);
+    void *gws = ws + lo.gemm, *big = ws + lo.big, *ln = ws + lo.ln, *attn = ws + lo.attn;
+    char *heads = ws + lo.heads;
+    void *q = heads, *k = heads + (size_t)M * C * 2, *v = heads + (size_t)M * C * 4;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    int rc;
+
+    // attention half: x += (attention of LN1(x)) @ W_o + b_o
+    if (unipin::launch_layernorm(x, w->ln1_w, w->ln1_b, ln, M, C, kLnEps, st) != hipSuccess) return UNIPIN_EHIP;
+    if ((rc = gemm(ctx, ln, w->w_qkv, w->b_qkv, big, M, 3 * C, C, HIPBLASLT_EPILOGUE_BIAS, false, gws, st))) return rc;
+    if (unipin::launch_split_heads(big, q, k, v, B, rows, H, D, st) != hipSuccess) return UNIPIN_EHIP;
+    rc = mode == UNIPIN_BLOCK_HISTORY
+             ? unipin_prefill(q, k, v, lens, pool, slot, layer, B, rows, scale, attn, stream)
+             : unipin_rank_decode(q, k, v, pool, slot, lens, layer, B, rows, scale, attn, stream);
+    if (rc) return rc;
+    if (unipin::launch_merge_heads(attn, ln, B, rows, H, D, st) != hipSuccess) return UNIPIN_EHIP;
+    if ((rc = gemm(ctx, ln, w->w_o, w->b_o, x, M, C, C, HIPBLASLT_EPILOGUE_BIAS, true, gws, st))) return rc;
+    // MLP half: x += GELU(LN2(x) @ W_fc + b_fc) @ W_proj + b_proj
+    if (unipin::launch_layernorm(x, w->ln2_w, w->ln2_b, ln, M, C, kLnEps, st) != hipSuccess) return UNIPIN_EHIP;
+    if ((rc = gemm(ctx, ln, w->w_fc, w->b_fc, big, M, 4 * C, C, HIPBLASLT_EPILOGUE_GELU_BIAS, false, gws, st)))
+        return rc;
+    return gemm(ctx, big, w->w_proj, w->b_proj, x, M, C, 4 * C, HIPBLASLT_EPILOGUE_BIAS, true, gws, st);
+}
+
+}  // extern "C"

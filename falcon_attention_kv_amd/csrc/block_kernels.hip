@@ -1,0 +1,170 @@
+// Element-wise and row kernels of the transformer block around the masked attention, for
+// gfx950: LayerNorm over rows of the hidden state, and the two layout changes between
+// the fused QKV projection's rows [B, T, 3, H, D] and the attention kernels' per-head
+// rows [B, H, T, D].  All three are HBM-bound copies with a little arithmetic; each
+// lane moves 16 bytes per access, and a wave reads or writes whole contiguous rows.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "block_launch.h"
+
+namespace unipin {
+namespace {
+
+typedef __bf16 bf16;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void unpack8(const u32x4 &x, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(x[i] << 16);
+        f[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf16 lo = (bf16)f[2 * i], hi = (bf16)f[2 * i + 1];   // round to nearest even
+        r[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    return r;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+// y = (x - mean) / sqrt(var + eps) * w + b over each row of C values (population
+// variance, fp32 statistics, bf16 out).  One wave per row; lane l holds 16-byte pieces
+// l, l + 64, ... (P of them, C <= 512 P).
+template <int P>
+__global__ void __launch_bounds__(256) layernorm_kernel(const bf16 *__restrict__ x, const bf16 *__restrict__ w,
+                                                        const bf16 *__restrict__ b, bf16 *__restrict__ y, long M,
+                                                        int C, float eps) {
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= M) return;
+    const int pieces = C / 8;
+    const u32x4 *xr = reinterpret_cast<const u32x4 *>(x + row * C);
+    float v[P][8];
+    float s = 0.f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const int i = lane + 64 * p;
+        if (i < pieces) {
+            unpack8(xr[i], v[p]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[p][e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += v[p][e];
+    }
+    const float mean = wave_sum(s) / (float)C;
+    float q = 0.f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        if (lane + 64 * p < pieces) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float d = v[p][e] - mean;
+                q = __builtin_fmaf(d, d, q);
+            }
+        }
+    }
+    const float rstd = 1.f / sqrtf(wave_sum(q) / (float)C + eps);
+    u32x4 *yr = reinterpret_cast<u32x4 *>(y + row * C);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const int i = lane + 64 * p;
+        if (i < pieces) {
+            float wf[8], bf[8], o[8];
+            unpack8(reinterpret_cast<const u32x4 *>(w)[i], wf);
+            unpack8(reinterpret_cast<const u32x4 *>(b)[i], bf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf((v[p][e] - mean) * rstd, wf[e], bf[e]);
+            yr[i] = pack8(o);
+        }
+    }
+}
+
+// qkv rows [B, T, 3, H, D] -> q, k, v [B, H, T, D]; one 16-byte piece per thread, in
+// source order (contiguous reads; each group of D/8 lanes writes one whole row).
+__global__ void __launch_bounds__(256) split_heads_kernel(const bf16 *__restrict__ qkv, bf16 *__restrict__ q,
+                                                          bf16 *__restrict__ k, bf16 *__restrict__ v, int B, int T,
+                                                          int H, int D) {
+    const long per_row = 3L * H * D / 8;   // pieces per source row
+    const long total = (long)B * T * per_row;
+    const long p = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= total) return;
+    const int d8 = (int)(p % (D / 8));
+    long r = p / (D / 8);
+    const int h = (int)(r % H);
+    r /= H;
+    const int part = (int)(r % 3);
+    r /= 3;
+    const int t = (int)(r % T);
+    const int b = (int)(r / T);
+    bf16 *dst = part == 0 ? q : part == 1 ? k : v;
+    reinterpret_cast<u32x4 *>(dst + (((long)b * H + h) * T + t) * D)[d8] = reinterpret_cast<const u32x4 *>(qkv)[p];
+}
+
+// o [B, H, T, D] -> y [B, T, H * D]; one 16-byte piece per thread, in destination order.
+__global__ void __launch_bounds__(256) merge_heads_kernel(const bf16 *__restrict__ o, bf16 *__restrict__ y, int B,
+                                                          int T, int H, int D) {
+    const long total = (long)B * T * H * D / 8;
+    const long p = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= total) return;
+    const int d8 = (int)(p % (D / 8));
+    long r = p / (D / 8);
+    const int h = (int)(r % H);
+    r /= H;
+    const int t = (int)(r % T);
+    const int b = (int)(r / T);
+    reinterpret_cast<u32x4 *>(y)[p] = reinterpret_cast<const u32x4 *>(o + (((long)b * H + h) * T + t) * D)[d8];
+}
+
+unsigned blocks_for(long threads) { return (unsigned)((threads + 255) / 256); }
+
+}  // namespace
+
+hipError_t launch_layernorm(const void *x, const void *w, const void *b, void *y, long M, int C, float eps,
+                            hipStream_t stream) {
+    if (M <= 0) return hipSuccess;
+    if (C % 8 != 0 || C > 2048) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((M + 3) / 4)), block(256);
+    const bf16 *xs = static_cast<const bf16 *>(x), *ws = static_cast<const bf16 *>(w),
+               *bs = static_cast<const bf16 *>(b);
+    bf16 *ys = static_cast<bf16 *>(y);
+    if (C <= 512)
+        hipLaunchKernelGGL(layernorm_kernel<1>, grid, block, 0, stream, xs, ws, bs, ys, M, C, eps);
+    else if (C <= 1024)
+        hipLaunchKernelGGL(layernorm_kernel<2>, grid, block, 0, stream, xs, ws, bs, ys, M, C, eps);
+    else
+        hipLaunchKernelGGL(layernorm_kernel<4>, grid, block, 0, stream, xs, ws, bs, ys, M, C, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_heads(const void *qkv, void *q, void *k, void *v, int B, int T, int H, int D,
+                              hipStream_t stream) {
+    const long threads = (long)B * T * 3 * H * D / 8;
+    if (threads <= 0) return hipSuccess;
+    hipLaunchKernelGGL(split_heads_kernel, dim3(blocks_for(threads)), dim3(256), 0, stream,
+                       static_cast<const bf16 *>(qkv), static_cast<bf16 *>(q), static_cast<bf16 *>(k),
+                       static_cast<bf16 *>(v), B, T, H, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge_heads(const void *o, void *y, int B, int T, int H, int D, hipStream_t stream) {
+    const long threads = (long)B * T * H * D / 8;
+    if (threads <= 0) return hipSuccess;
+    hipLaunchKernelGGL(merge_heads_kernel, dim3(blocks_for(threads)), dim3(256), 0, stream,
+                       static_cast<const bf16 *>(o), static_cast<bf16 *>(y), B, T, H, D);
+    return hipGetLastError();
+}
+
+}  // namespace unipin

@@ -1,0 +1,19 @@
+// Internal interface between the block's host code (block.cpp) and its kernels
+// (block_kernels.hip).  Not installed; the public interface is include/unipin.h.
+// All tensors are bf16, contiguous, 16-byte aligned device memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace unipin {
+
+// y[M, C] = LayerNorm(x[M, C]) * w + b, eps as given; C % 8 == 0, C <= 2048.
+hipError_t launch_layernorm(const void *x, const void *w, const void *b, void *y, long M, int C, float eps,
+                            hipStream_t stream);
+// qkv [B, T, 3, H, D] -> q, k, v [B, H, T, D].
+hipError_t launch_split_heads(const void *qkv, void *q, void *k, void *v, int B, int T, int H, int D,
+                              hipStream_t stream);
+// o [B, H, T, D] -> y [B, T, H*D].
+hipError_t launch_merge_heads(const void *o, void *y, int B, int T, int H, int D, hipStream_t stream);
+
+}  // namespace unipin

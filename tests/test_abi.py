@@ -225,6 +225,30 @@ def test_ar_decode_workspace_checks():
     lib.unipin_pool_destroy(h)
 
 
+def test_block_workspace_bytes():
+    """The block's workspace: 32 MiB for the GEMM library, then M x 4C, M x 3C and two
+    M x C bf16 regions (M = B * rows), each rounded up to 256 bytes."""
+    up = lambda x: (x + 255) // 256 * 256
+    h = make_pool(L=1, S=8, H=8, n_max=992, D=64)
+    M, C = 8 * 656, 512
+    assert lib.unipin_block_workspace_bytes(h, 8, 656) == (32 << 20) + up(M * 4 * C * 2) + up(M * 3 * C * 2) \
+        + 2 * up(M * C * 2)
+    assert lib.unipin_block_workspace_bytes(h, 0, 656) == 0
+    assert lib.unipin_block_workspace_bytes(None, 8, 656) == 0
+    lib.unipin_pool_destroy(h)
+
+
+def test_block_host_checks():
+    h = make_pool(L=1, S=2, H=2, n_max=16, D=32)
+    w = fa.BlockWeights(*([FAKE] * len(fa.BLOCK_WEIGHT_NAMES)))
+    args = lambda ctx, wp, mode=fa.BLOCK_CANDIDATES: lib.unipin_block_forward(
+        ctx, wp, mode, FAKE, h, FAKE, FAKE, 0, 1, 4, 0.0, FAKE, 1 << 30, None)
+    assert args(None, ctypes.byref(w)) == fa.EINVAL          # no context
+    assert lib.unipin_block_ctx_destroy(None) == fa.EINVAL
+    assert lib.unipin_block_ctx_create(None) == fa.EINVAL
+    lib.unipin_pool_destroy(h)
+
+
 def test_null_pool_rejected():
     assert _prefill(None) == fa.EINVAL
     assert _decode(None) == fa.EINVAL
