@@ -34,7 +34,7 @@ EXPORTS = ("unipin_pool_create", "unipin_pool_destroy", "unipin_pool_acquire",
            "unipin_rank_decode", "unipin_ar_decode", "unipin_ar_decode_workspace_bytes",
            "unipin_device_status", "unipin_strerror", "unipin_version",
            "unipin_block_ctx_create", "unipin_block_ctx_destroy", "unipin_block_workspace_bytes",
-           "unipin_block_forward")
+           "unipin_block_ctx_tune", "unipin_block_forward")
 
 
 # Weights of one transformer block, in the order of unipin_block_weights_t.
@@ -70,6 +70,7 @@ def _load() -> ctypes.CDLL:
     lib.unipin_block_ctx_create.argtypes = [ctypes.POINTER(vp)]
     lib.unipin_block_ctx_destroy.argtypes = [vp]
     lib.unipin_block_workspace_bytes.argtypes = [vp, i32, i32]
+    lib.unipin_block_ctx_tune.argtypes = [vp, vp, i32, i32, vp, ctypes.c_size_t, vp]
     lib.unipin_block_forward.argtypes = [vp, ctypes.POINTER(BlockWeights), i32, vp, vp, vp, vp, i32, i32, i32,
                                          ctypes.c_float, vp, ctypes.c_size_t, vp]
     lib.unipin_device_status.argtypes = [vp, ip]
@@ -287,6 +288,16 @@ class BlockContext:
         if self._h is None:
             raise UnipinError(EINVAL, "block context is closed")
         return self._h
+
+    def tune(self, pool: "Pool", B: int, rows: int, workspace: Optional[torch.Tensor] = None) -> None:
+        """unipin_block_ctx_tune: time hipBLASLt's candidate kernels for the block's GEMMs
+        at B users x rows rows and keep the fastest (blocks until done)."""
+        dev = pool.k.device
+        if workspace is None:
+            workspace = torch.empty(block_workspace_bytes(pool, B, rows), dtype=torch.uint8, device=dev)
+        _check(lib.unipin_block_ctx_tune(self.handle, pool.handle, int(B), int(rows), workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(), _stream_handle(dev)),
+               "unipin_block_ctx_tune")
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None:

@@ -133,6 +133,21 @@ Layout layout(long M, int C) {
     return l;
 }
 
+// The block's four GEMMs for M hidden rows of width C: QKV, output projection (plus
+// residual), MLP up (bias and GELU), MLP down (plus residual).
+struct GemmShape {
+    int N, K;
+    hipblasLtEpilogue_t ep;
+    bool residual;
+};
+
+void block_gemms(int C, GemmShape (&g)[4]) {
+    g[0] = {3 * C, C, HIPBLASLT_EPILOGUE_BIAS, false};
+    g[1] = {C, C, HIPBLASLT_EPILOGUE_BIAS, true};
+    g[2] = {4 * C, C, HIPBLASLT_EPILOGUE_GELU_BIAS, false};
+    g[3] = {C, 4 * C, HIPBLASLT_EPILOGUE_BIAS, true};
+}
+
 bool weights_present(const unipin_block_weights_t *w) {
     const void *p[] = {w->ln1_w, w->ln1_b, w->w_qkv, w->b_qkv, w->w_o, w->b_o,
                        w->ln2_w, w->ln2_b, w->w_fc, w->b_fc, w->w_proj, w->b_proj};
@@ -170,6 +185,103 @@ size_t unipin_block_workspace_bytes(const unipin_pool_t *pool, int B, int rows) 
     int L, S, H, n_max, D, dt;
     if (!pool || B < 1 || rows < 1 || unipin_pool_dims(pool, &L, &S, &H, &n_max, &D, &dt) != UNIPIN_OK) return 0;
     return layout((long)B * rows, H * D).total;
+}
+
+int unipin_block_ctx_tune(unipin_block_ctx_t *ctx, const unipin_pool_t *pool, int B, int rows, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    if (!ctx || !pool || !workspace || B < 1 || rows < 1) return UNIPIN_EINVAL;
+    int L, S, H, n_max, D, dt;
+    if (unipin_pool_dims(pool, &L, &S, &H, &n_max, &D, &dt) != UNIPIN_OK) return UNIPIN_EINVAL;
+    if (dt != UNIPIN_BF16) return UNIPIN_EDTYPE;
+    const int C = H * D;
+    const long M = (long)B * rows;
+    const Layout lo = layout(M, C);
+    if (!aligned16(workspace)) return UNIPIN_EALIGN;
+    if (workspace_bytes < lo.total || (size_t)4 * C * C * 2 > lo.ln - lo.heads || (size_t)4 * C * 2 > lo.total - lo.attn)
+        return UNIPIN_EINVAL;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != ctx->device) return UNIPIN_EINVAL;
+    char *ws = static_cast<char *>(workspace);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    // operands: activations in [ln] / [big], weights in [heads], bias in [attn]; values
+    // of the size the block sees (a GEMM's speed can depend on the data through power)
+    if (unipin::launch_fill_random(ws + lo.big, (size_t)M * 4 * C, 1u, 1.f, st) != hipSuccess ||
+        unipin::launch_fill_random(ws + lo.heads, (size_t)4 * C * C, 2u, 0.05f, st) != hipSuccess ||
+        unipin::launch_fill_random(ws + lo.ln, (size_t)M * C, 3u, 1.f, st) != hipSuccess ||
+        unipin::launch_fill_random(ws + lo.attn, (size_t)M * C, 4u, 1.f, st) != hipSuccess)
+        return UNIPIN_EHIP;
+    GemmShape g[4];
+    block_gemms(C, g);
+    void *in_of[4] = {ws + lo.ln, ws + lo.attn, ws + lo.ln, ws + lo.big};
+    void *out_of[4] = {ws + lo.big, ws + lo.ln, ws + lo.big, ws + lo.ln};
+    const void *W = ws + lo.heads, *bias = ws + lo.attn;
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return UNIPIN_EHIP;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        hipEventDestroy(e0);
+        return UNIPIN_EHIP;
+    }
+    int rc = UNIPIN_OK;
+    std::lock_guard<std::mutex> lock(ctx->mu);
+    for (int i = 0; i < 4 && rc == UNIPIN_OK; ++i) {
+        GemmPlan *p = plan_for(ctx, M, g[i].N, g[i].K, g[i].ep, g[i].residual);
+        if (!p) {
+            rc = UNIPIN_EHIP;
+            break;
+        }
+        hipblasLtMatmulPreference_t pref = nullptr;
+        const uint64_t wsz = kGemmWorkspace;
+        constexpr int kMaxAlgos = 32;
+        hipblasLtMatmulHeuristicResult_t res[kMaxAlgos];
+        int found = 0;
+        if (hipblasLtMatmulPreferenceCreate(&pref) != 0 ||
+            hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsz,
+                                                  sizeof(wsz)) != 0 ||
+            hipblasLtMatmulDescSetAttribute(p->desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof(bias)) != 0 ||
+            hipblasLtMatmulAlgoGetHeuristic(ctx->handle, p->desc, p->la, p->lb, p->lc, p->lc, pref, kMaxAlgos, res,
+                                            &found) != 0) {
+            if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+            rc = UNIPIN_EHIP;
+            break;
+        }
+        hipblasLtMatmulPreferenceDestroy(pref);
+        const float alpha = 1.f, beta = g[i].residual ? 1.f : 0.f;
+        float best = 1e30f;
+        for (int a = 0; a < found; ++a) {
+            if (res[a].state != HIPBLAS_STATUS_SUCCESS || res[a].workspaceSize > kGemmWorkspace) continue;
+            auto run = [&]() {
+                return hipblasLtMatmul(ctx->handle, p->desc, &alpha, W, p->la, in_of[i], p->lb, &beta, out_of[i],
+                                       p->lc, out_of[i], p->lc, &res[a].algo, ws + lo.gemm, kGemmWorkspace, st);
+            };
+            if (run() != HIPBLAS_STATUS_SUCCESS || run() != HIPBLAS_STATUS_SUCCESS) continue;
+            if (hipEventRecord(e0, st) != hipSuccess) {
+                rc = UNIPIN_EHIP;
+                break;
+            }
+            bool ok = true;
+            for (int r = 0; r < 5 && ok; ++r) ok = run() == HIPBLAS_STATUS_SUCCESS;
+            float ms = 0.f;
+            if (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+                rc = UNIPIN_EHIP;
+                break;
+            }
+            if (ok && ms < best) {
+                best = ms;
+                p->algo = res[a].algo;
+            }
+            // the residual GEMMs add into their output each run; start the next from
+            // the same values as the first so that no candidate sees overflowing data
+            if (g[i].residual &&
+                unipin::launch_fill_random(out_of[i], (size_t)M * g[i].N, 5u, 1.f, st) != hipSuccess) {
+                rc = UNIPIN_EHIP;
+                break;
+            }
+        }
+    }
+    hipEventDestroy(e0);
+    hipEventDestroy(e1);
+    return rc;
 }
 
 int unipin_block_forward(unipin_block_ctx_t *ctx, const unipin_block_weights_t *w, int mode, void *x,

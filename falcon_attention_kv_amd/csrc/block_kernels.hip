@@ -128,6 +128,21 @@ __global__ void __launch_bounds__(256) merge_heads_kernel(const bf16 *__restrict
     reinterpret_cast<u32x4 *>(y)[p] = reinterpret_cast<const u32x4 *>(o + (((long)b * H + h) * T + t) * D)[d8];
 }
 
+// Fills n bf16 values with a hash of (seed, index) mapped to [-amp, amp): operands for
+// timing GEMM kernels on data of realistic size and spread.
+__global__ void __launch_bounds__(256) fill_random_kernel(bf16 *__restrict__ dst, size_t n, unsigned seed,
+                                                          float amp) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    uint32_t h = (uint32_t)i * 0x9e3779b1u ^ seed * 0x85ebca77u;
+    h ^= h >> 15;
+    h *= 0x2c1b3c6du;
+    h ^= h >> 12;
+    h *= 0x297a2d39u;
+    h ^= h >> 15;
+    dst[i] = (bf16)(amp * ((float)(h >> 8) * (1.f / 8388608.f) - 1.f));
+}
+
 unsigned blocks_for(long threads) { return (unsigned)((threads + 255) / 256); }
 
 }  // namespace
@@ -156,6 +171,13 @@ hipError_t launch_split_heads(const void *qkv, void *q, void *k, void *v, int B,
     hipLaunchKernelGGL(split_heads_kernel, dim3(blocks_for(threads)), dim3(256), 0, stream,
                        static_cast<const bf16 *>(qkv), static_cast<bf16 *>(q), static_cast<bf16 *>(k),
                        static_cast<bf16 *>(v), B, T, H, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_random(void *dst, size_t n, unsigned seed, float amp, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_random_kernel, dim3(blocks_for((long)n)), dim3(256), 0, stream, static_cast<bf16 *>(dst),
+                       n, seed, amp);
     return hipGetLastError();
 }
 
