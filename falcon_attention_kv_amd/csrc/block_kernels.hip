@@ -39,55 +39,72 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // y = (x - mean) / sqrt(var + eps) * w + b over each row of C values (population
-// variance, fp32 statistics, bf16 out).  One wave per row; lane l holds 16-byte pieces
-// l, l + 64, ... (P of them, C <= 512 P).
+// variance, fp32 statistics, bf16 out).  One wave per RPW rows, whose loads all go out
+// before any arithmetic; lane l holds 16-byte pieces l, l + 64, ... of a row (P of
+// them, C <= 512 P).
+constexpr int kLnRowsPerWave = 1;
+
 template <int P>
 __global__ void __launch_bounds__(256) layernorm_kernel(const bf16 *__restrict__ x, const bf16 *__restrict__ w,
                                                         const bf16 *__restrict__ b, bf16 *__restrict__ y, long M,
                                                         int C, float eps) {
-    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    constexpr int RPW = kLnRowsPerWave;
+    const long row0 = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW;
     const int lane = threadIdx.x & 63;
-    if (row >= M) return;
+    if (row0 >= M) return;
     const int pieces = C / 8;
-    const u32x4 *xr = reinterpret_cast<const u32x4 *>(x + row * C);
-    float v[P][8];
-    float s = 0.f;
+    u32x4 raw[RPW][P];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int i = lane + 64 * p;
+            raw[r][p] = row0 + r < M && i < pieces ? reinterpret_cast<const u32x4 *>(x + (row0 + r) * C)[i]
+                                                   : u32x4{0u, 0u, 0u, 0u};
+        }
+    float wf[P][8], bf[P][8];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         const int i = lane + 64 * p;
-        if (i < pieces) {
-            unpack8(xr[i], v[p]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[p][e] = 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s += v[p][e];
+        const u32x4 wz = i < pieces ? reinterpret_cast<const u32x4 *>(w)[i] : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 bz = i < pieces ? reinterpret_cast<const u32x4 *>(b)[i] : u32x4{0u, 0u, 0u, 0u};
+        unpack8(wz, wf[p]);
+        unpack8(bz, bf[p]);
     }
-    const float mean = wave_sum(s) / (float)C;
-    float q = 0.f;
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-        if (lane + 64 * p < pieces) {
+    for (int r = 0; r < RPW; ++r) {
+        if (row0 + r >= M) break;
+        float v[P][8];
+        float s = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float d = v[p][e] - mean;
-                q = __builtin_fmaf(d, d, q);
+        for (int p = 0; p < P; ++p) {
+            unpack8(raw[r][p], v[p]);   // pieces past C are zero and add nothing
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += v[p][e];
+        }
+        const float mean = wave_sum(s) / (float)C;
+        float q = 0.f;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            if (lane + 64 * p < pieces) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float d = v[p][e] - mean;
+                    q = __builtin_fmaf(d, d, q);
+                }
             }
         }
-    }
-    const float rstd = 1.f / sqrtf(wave_sum(q) / (float)C + eps);
-    u32x4 *yr = reinterpret_cast<u32x4 *>(y + row * C);
+        const float rstd = 1.f / sqrtf(wave_sum(q) / (float)C + eps);
+        u32x4 *yr = reinterpret_cast<u32x4 *>(y + (row0 + r) * C);
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-        const int i = lane + 64 * p;
-        if (i < pieces) {
-            float wf[8], bf[8], o[8];
-            unpack8(reinterpret_cast<const u32x4 *>(w)[i], wf);
-            unpack8(reinterpret_cast<const u32x4 *>(b)[i], bf);
+        for (int p = 0; p < P; ++p) {
+            const int i = lane + 64 * p;
+            if (i < pieces) {
+                float o[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf((v[p][e] - mean) * rstd, wf[e], bf[e]);
-            yr[i] = pack8(o);
+                for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf((v[p][e] - mean) * rstd, wf[p][e], bf[p][e]);
+                yr[i] = pack8(o);
+            }
         }
     }
 }
@@ -151,7 +168,8 @@ hipError_t launch_layernorm(const void *x, const void *w, const void *b, void *y
                             hipStream_t stream) {
     if (M <= 0) return hipSuccess;
     if (C % 8 != 0 || C > 2048) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((M + 3) / 4)), block(256);
+    const long waves = (M + kLnRowsPerWave - 1) / kLnRowsPerWave;
+    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
     const bf16 *xs = static_cast<const bf16 *>(x), *ws = static_cast<const bf16 *>(w),
                *bs = static_cast<const bf16 *>(b);
     bf16 *ys = static_cast<bf16 *>(y);
