@@ -184,7 +184,8 @@ __device__ __forceinline__ float half_sum(float x) {
 // within that matrix), i.e. key row (64*pj + l) / R at swizzled block (64*pj + l) % R,
 // taken from the matching unswizzled 16-byte block of that row.
 template <int D, int W>
-__device__ __forceinline__ void dma_offsets(int (&voff)[(KvDma<D, W>::PER_WAVE)], int wave, int lane) {
+__device__ __forceinline__ void dma_offsets(int (&voff)[(KvDma<D, W>::PER_WAVE)], int wave, int lane,
+                                            int row_stride) {
     using T = Tile<D>;
 #pragma unroll
     for (int j = 0; j < KvDma<D, W>::PER_WAVE; ++j) {
@@ -194,7 +195,7 @@ __device__ __forceinline__ void dma_offsets(int (&voff)[(KvDma<D, W>::PER_WAVE)]
         const int p = pj * 64 + lane;
         const int key = p / T::R, blks = p % T::R;
         const int blk = blks ^ (is_v ? v_swz<D>(key) : k_swz<D>(key));
-        voff[j] = key * T::ROW_BYTES + blk * 16;
+        voff[j] = key * row_stride + blk * 16;
     }
 }
 
@@ -202,12 +203,12 @@ __device__ __forceinline__ void dma_offsets(int (&voff)[(KvDma<D, W>::PER_WAVE)]
 // `buf`; `rsrc` is the K or V buffer of the wave's half.
 template <int D, int W>
 __device__ __forceinline__ void dma_tile(LDS_AS char *buf, i32x4 rsrc, int kbase,
-                                         const int (&voff)[(KvDma<D, W>::PER_WAVE)], int wave) {
+                                         const int (&voff)[(KvDma<D, W>::PER_WAVE)], int wave, int row_stride) {
     using T = Tile<D>;
     const bool is_v = wave >= W / 2;
     const int first = wave * KvDma<D, W>::PER_WAVE - (is_v ? T::DMA_PER_MAT : 0);
     const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(buf) + (is_v ? T::MAT_BYTES : 0) + first * 1024;
-    const int soff = kbase * T::ROW_BYTES;
+    const int soff = kbase * row_stride;
 #pragma unroll
     for (int j = 0; j < KvDma<D, W>::PER_WAVE; ++j) dma16(dst + j * 1024, rsrc, voff[j], soff);
 }
@@ -217,18 +218,19 @@ __device__ __forceinline__ void dma_tile(LDS_AS char *buf, i32x4 rsrc, int kbase
 // (bi % R) ^ k_swz(row).  Rows past the record count read as zero.  A 256-row block
 // fills two LDS slots, a 128-row half block one.
 template <int D, int W, int ROWS>
-__device__ __forceinline__ void dma_rows(LDS_AS char *dst, i32x4 rsrc, int row0, int wave, int lane) {
+__device__ __forceinline__ void dma_rows(LDS_AS char *dst, i32x4 rsrc, int row0, int wave, int lane,
+                                         int row_stride) {
     using T = Tile<D>;
     constexpr int PW = ROWS * T::ROW_BYTES / 1024 / W;   // 1 KB pieces per wave
     static_assert(PW >= 1 && PW * W * 1024 == ROWS * T::ROW_BYTES, "the block must split evenly");
     const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(dst);
-    const int soff = row0 * T::ROW_BYTES;
+    const int soff = row0 * row_stride;
 #pragma unroll
     for (int j = 0; j < PW; ++j) {
         const int piece = wave * PW + j;
         const int bi = piece * 64 + lane;
         const int row = bi / T::R, blk = (bi % T::R) ^ k_swz<D>(row);
-        dma16(base + piece * 1024, rsrc, row * T::ROW_BYTES + blk * 16, soff);
+        dma16(base + piece * 1024, rsrc, row * row_stride + blk * 16, soff);
     }
 }
 
@@ -508,7 +510,7 @@ __device__ __forceinline__ int staged_acc_off(int qb, int db, int j, int col, in
 // rows: 16 bytes per lane, 64 / R rows per instruction.
 template <int D>
 __device__ __forceinline__ void store_o(const WaveState<D> &ws, LDS_AS char *stage, bf16 *odst, int qlimit, int wq0,
-                                        int col, int g, int lane) {
+                                        int col, int g, int lane, int row_stride) {
     using T = Tile<D>;
 #pragma unroll
     for (int qb = 0; qb < query_blocks<D>(); ++qb) {
@@ -530,7 +532,7 @@ __device__ __forceinline__ void store_o(const WaveState<D> &ws, LDS_AS char *sta
         const int row = i * RPI + lane / T::R;
         const u32x4 v = *reinterpret_cast<const LDS_AS u32x4 *>(stage + row * T::ROW_BYTES +
                                                                 ((blk ^ k_swz<D>(row)) * 16));
-        if (wq0 + row < qlimit) *reinterpret_cast<u32x4 *>(odst + (long)(wq0 + row) * D + blk * 8) = v;
+        if (wq0 + row < qlimit) *reinterpret_cast<u32x4 *>(odst + (long)(wq0 + row) * row_stride + blk * 8) = v;
     }
 }
 
@@ -654,11 +656,12 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
     const int q0 = qtile * QT;
     if (q0 >= N) return;
 
-    const long bh = (long)b * a.H + h;
-    const bf16 *qsrc = static_cast<const bf16 *>(a.q) + bh * a.rows * D;
-    const bf16 *ksrc = static_cast<const bf16 *>(a.k) + bh * a.rows * D;
-    const bf16 *vsrc = static_cast<const bf16 *>(a.v) + bh * a.rows * D;
-    bf16 *odst = static_cast<bf16 *>(a.o) + bh * a.rows * D;
+    const long in_off = (long)b * a.in_bstride + (long)h * a.in_hstride;
+    const int in_rs = a.in_rstride * (int)sizeof(bf16);   // bytes between rows of q, k, v
+    const bf16 *qsrc = static_cast<const bf16 *>(a.q) + in_off;
+    const bf16 *ksrc = static_cast<const bf16 *>(a.k) + in_off;
+    const bf16 *vsrc = static_cast<const bf16 *>(a.v) + in_off;
+    bf16 *odst = static_cast<bf16 *>(a.o) + (long)b * a.out_bstride + (long)h * a.out_hstride;
     const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
     bf16 *pk = static_cast<bf16 *>(a.pool_k) + slot_off;
     bf16 *pv = static_cast<bf16 *>(a.pool_v) + slot_off;
@@ -670,18 +673,18 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
     const int col = lane & 31, g = lane >> 5;
     const int wq0 = q0 + wave * wave_rows<D>();
     // This wave's K/V DMA source: the K or the V rows of the history, rows >= kend read as 0.
-    const i32x4 rsrc = rsrc_words(wave < W / 2 ? ksrc : vsrc, (uint32_t)kend * T::ROW_BYTES);
+    const i32x4 rsrc = rsrc_words(wave < W / 2 ? ksrc : vsrc, (uint32_t)kend * in_rs);
     int voff[DPW];
-    dma_offsets<D, W>(voff, wave, lane);
+    dma_offsets<D, W>(voff, wave, lane, in_rs);
     const LaneAddr<D> la = lane_addr<D>(lane);
 
     // The block's query rows go to the last two slots, the first K/V tiles to the others;
     // tile t lives in slot t % kBufs.
-    dma_rows<D, W, kBlockRows>(smem + (kBufs - 2) * T::BUF_BYTES, rsrc_words(qsrc, (uint32_t)N * T::ROW_BYTES), q0,
-                               wave, lane);
+    dma_rows<D, W, kBlockRows>(smem + (kBufs - 2) * T::BUF_BYTES, rsrc_words(qsrc, (uint32_t)N * in_rs), q0, wave,
+                               lane, in_rs);
     int issued = 0;
     for (; issued < kBufs - 2 && issued < ntiles; ++issued)
-        dma_tile<D, W>(smem + issued * T::BUF_BYTES, rsrc, issued * kTK, voff, wave);
+        dma_tile<D, W>(smem + issued * T::BUF_BYTES, rsrc, issued * kTK, voff, wave, in_rs);
     wait_pieces_after<DPW>(issued);
     __syncthreads();
 
@@ -706,14 +709,14 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
         wait_pieces_after<DPW>(issued - t - 1);
         __syncthreads();
         for (; issued < ntiles && issued <= t + kBufs - 1; ++issued)
-            dma_tile<D, W>(smem + (issued % kBufs) * T::BUF_BYTES, rsrc, issued * kTK, voff, wave);
+            dma_tile<D, W>(smem + (issued % kBufs) * T::BUF_BYTES, rsrc, issued * kTK, voff, wave, in_rs);
         const LDS_AS char *cur = smem + (t % kBufs) * T::BUF_BYTES;
         if (t * kTK >= q0) tile_to_pool<D, W>(cur, pk, pv, t * kTK, kend, tid);
         return cur;
     };
     run_tiles<D, true>(ws, ntiles, tlast, kend, wq0, la, col, g, a.c, next_tile);
     __syncthreads();   // every wave is done with the tile slots
-    store_o<D>(ws, smem + wave * wave_rows<D>() * T::ROW_BYTES, odst, N, wq0, col, g, lane);
+    store_o<D>(ws, smem + wave * wave_rows<D>() * T::ROW_BYTES, odst, N, wq0, col, g, lane, a.out_rstride);
 }
 
 // ------------------------------------------------------------------ ranking decode
@@ -744,7 +747,6 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
     const int s = slots[b];
     if (!user_valid(a, N, s, ctile == 0)) return;
 
-    const long bh = (long)b * a.H + h;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 31, g = lane >> 5;
@@ -752,23 +754,24 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
     const int wq0 = row0 + wave * wave_rows<D>();
     const int qlimit = a.rows;
     const bool active = wq0 < qlimit;
-    const uint32_t rows_bytes = (uint32_t)a.rows * T::ROW_BYTES;
+    const long in_off = (long)b * a.in_bstride + (long)h * a.in_hstride;
+    const int in_rs = a.in_rstride * (int)sizeof(bf16);   // bytes between candidate rows
+    const uint32_t rows_bytes = (uint32_t)a.rows * in_rs;
     const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
     const i32x4 rsrc = rsrc_words(static_cast<const bf16 *>(wave < W / 2 ? a.pool_k : a.pool_v) + slot_off,
                                   (uint32_t)N * T::ROW_BYTES);
-    const i32x4 rsrc_vc = rsrc_words(static_cast<const bf16 *>(a.v) + bh * a.rows * D, rows_bytes);
+    const i32x4 rsrc_vc = rsrc_words(static_cast<const bf16 *>(a.v) + in_off, rows_bytes);
     int voff[DPW];
-    dma_offsets<D, W>(voff, wave, lane);
+    dma_offsets<D, W>(voff, wave, lane, T::ROW_BYTES);   // the pool's K/V rows
     const LaneAddr<D> la = lane_addr<D>(lane);
     const int ntiles = (N + kTK - 1) / kTK;
     const int nsteps = ntiles + 2;
     const int wrows = wave * wave_rows<D>() * T::ROW_BYTES;   // this wave's rows inside a staged block
 
-    dma_rows<D, W, kBlockRows>(smem, rsrc_words(static_cast<const bf16 *>(a.q) + bh * a.rows * D, rows_bytes), row0,
-                               wave, lane);
-    dma_rows<D, W, kBlockRows>(smem + 2 * T::BUF_BYTES,
-                               rsrc_words(static_cast<const bf16 *>(a.k) + bh * a.rows * D, rows_bytes), row0, wave,
-                               lane);
+    dma_rows<D, W, kBlockRows>(smem, rsrc_words(static_cast<const bf16 *>(a.q) + in_off, rows_bytes), row0, wave,
+                               lane, in_rs);
+    dma_rows<D, W, kBlockRows>(smem + 2 * T::BUF_BYTES, rsrc_words(static_cast<const bf16 *>(a.k) + in_off, rows_bytes),
+                               row0, wave, lane, in_rs);
     wait_vmcnt<0>();
     __syncthreads();
     WaveState<D> ws;
@@ -779,8 +782,8 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
 
     auto issue = [&](int u) {
         LDS_AS char *dst = smem + (u % kBufs) * T::BUF_BYTES;
-        if (u < ntiles) dma_tile<D, W>(dst, rsrc, u * kTK, voff, wave);
-        else dma_rows<D, W, HALF>(dst, rsrc_vc, row0 + (u - ntiles) * HALF, wave, lane);
+        if (u < ntiles) dma_tile<D, W>(dst, rsrc, u * kTK, voff, wave, T::ROW_BYTES);
+        else dma_rows<D, W, HALF>(dst, rsrc_vc, row0 + (u - ntiles) * HALF, wave, lane, in_rs);
     };
     int issued = 0;
     for (; issued < kBufs - 1 && issued < nsteps; ++issued) issue(issued);
@@ -800,7 +803,8 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
             self_key_merge<D>(ws, sself, vc_half + (wave % (W / 2)) * wave_rows<D>() * T::ROW_BYTES, col, g);
     }
     __syncthreads();   // every wave is done with the slots
-    store_o<D>(ws, smem + wrows, static_cast<bf16 *>(a.o) + bh * a.rows * D, qlimit, wq0, col, g, lane);
+    store_o<D>(ws, smem + wrows, static_cast<bf16 *>(a.o) + (long)b * a.out_bstride + (long)h * a.out_hstride, qlimit,
+               wq0, col, g, lane, a.out_rstride);
 }
 
 template <int D>

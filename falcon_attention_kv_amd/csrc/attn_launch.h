@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct unipin_pool;   // the pool descriptor of the C ABI (unipin.cpp)
+
 namespace unipin {
 
 // Arguments of one attention launch.  Both kernels of the library take this struct by
@@ -24,7 +26,28 @@ struct AttnArgs {
     int xcd_remap;                // 1: map blocks so all tiles of a (user, head) share an XCD
     float c;                      // scale * log2(e)
     unsigned int *status;         // sticky per-device flags
+    // Row addressing of q, k, v (in) and o (out), in elements: row t of (user b, head h)
+    // starts at b * bstride + h * hstride + t * rstride.  The contiguous [B, H, rows, D]
+    // layout is bstride = H * rows * D, hstride = rows * D, rstride = D; the bf16 kernels
+    // take any layout whose rows and bases are 16-byte aligned (the fp32 kernels and the
+    // autoregressive step only the contiguous one).
+    long in_bstride, in_hstride, out_bstride, out_hstride;
+    int in_rstride, out_rstride;
 };
+
+// Row layout of one attention operand, in elements (see AttnArgs).
+struct RowLayout {
+    long bstride, hstride;
+    int rstride;
+};
+
+// The prefill (prefill = true) or the ranking decode over the pool, with q, k, v read
+// and o written in the given layouts: the public entry points' shared body, after
+// their argument checks.  bf16 pools only for a non-contiguous layout.  Returns a
+// UNIPIN_* status.
+int attention_call(bool prefill, const void *q, const void *k, const void *v, RowLayout in, void *o, RowLayout out,
+                   ::unipin_pool *pool, const int32_t *slot, const int32_t *lens, int layer, int B, int rows,
+                   float scale, void *stream);
 
 // Flags raised on the device (mirrors UNIPIN_FLAG_* of the public header).
 constexpr unsigned int kFlagBadSlot = 1u;

@@ -5,10 +5,12 @@
 //
 // The four projections are plain bf16 GEMMs with fp32 accumulation and go to hipBLASLt,
 // with its epilogues doing the bias, the tanh-form GELU and (through beta = 1 on the
-// hidden state itself) the residual adds.  LayerNorm and the head layout changes are
-// this library's kernels (block_kernels.hip), and the attention is the library's own
-// prefill and rank-decode kernels.  Host code here allocates nothing on the device:
-// every intermediate lives in the caller's workspace.
+// hidden state itself) the residual adds.  LayerNorm is this library's kernel
+// (block_kernels.hip), and the attention is the library's own prefill and rank-decode
+// kernels, which read q, k and v straight from the fused projection's rows
+// [B, rows, 3, H, D] and write the heads' outputs straight into the merged rows
+// [B, rows, H, D] that the output projection reads.  Host code here allocates nothing on
+// the device: every intermediate lives in the caller's workspace.
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 
@@ -19,6 +21,7 @@
 #include <new>
 #include <tuple>
 
+#include "attn_launch.h"
 #include "block_launch.h"
 #include "unipin.h"
 
@@ -114,11 +117,10 @@ int gemm(unipin_block_ctx *ctx, const void *in, const void *W, const void *bias,
 // Workspace layout for M = B * rows hidden rows of width C (bytes, 256-aligned):
 //   [gemm]  hipBLASLt workspace
 //   [big]   M x 4C: the fused QKV output (M x 3C), later the MLP's hidden layer
-//   [heads] M x 3C: q, k, v in per-head layout [B, H, rows, D]
-//   [ln]    M x C:  LayerNorm output, later the merged attention output
-//   [attn]  M x C:  attention output [B, H, rows, D]
+//   [ln]    M x C:  LayerNorm output, then the attention output, then LayerNorm again
+//   [tune]  4C x C + 4C: weights and bias for timing the GEMM kernels (tuning only)
 struct Layout {
-    size_t gemm, big, heads, ln, attn, total;
+    size_t gemm, big, ln, tune, total;
 };
 
 Layout layout(long M, int C) {
@@ -126,10 +128,9 @@ Layout layout(long M, int C) {
     const size_t e = 2;
     l.gemm = 0;
     l.big = up(kGemmWorkspace);
-    l.heads = l.big + up((size_t)M * 4 * C * e);
-    l.ln = l.heads + up((size_t)M * 3 * C * e);
-    l.attn = l.ln + up((size_t)M * C * e);
-    l.total = l.attn + up((size_t)M * C * e);
+    l.ln = l.big + up((size_t)M * 4 * C * e);
+    l.tune = l.ln + up((size_t)M * C * e);
+    l.total = l.tune + up(((size_t)4 * C * C + 4 * C) * e);
     return l;
 }
 
@@ -197,24 +198,24 @@ int unipin_block_ctx_tune(unipin_block_ctx_t *ctx, const unipin_pool_t *pool, in
     const long M = (long)B * rows;
     const Layout lo = layout(M, C);
     if (!aligned16(workspace)) return UNIPIN_EALIGN;
-    if (workspace_bytes < lo.total || (size_t)4 * C * C * 2 > lo.ln - lo.heads || (size_t)4 * C * 2 > lo.total - lo.attn)
-        return UNIPIN_EINVAL;
+    if (workspace_bytes < lo.total) return UNIPIN_EINVAL;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev != ctx->device) return UNIPIN_EINVAL;
     char *ws = static_cast<char *>(workspace);
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    // operands: activations in [ln] / [big], weights in [heads], bias in [attn]; values
-    // of the size the block sees (a GEMM's speed can depend on the data through power)
+    // operands: activations in [ln] and [big], weights and bias in [tune]; values of the
+    // size the block sees (a GEMM's speed can depend on the data through power)
     if (unipin::launch_fill_random(ws + lo.big, (size_t)M * 4 * C, 1u, 1.f, st) != hipSuccess ||
-        unipin::launch_fill_random(ws + lo.heads, (size_t)4 * C * C, 2u, 0.05f, st) != hipSuccess ||
-        unipin::launch_fill_random(ws + lo.ln, (size_t)M * C, 3u, 1.f, st) != hipSuccess ||
-        unipin::launch_fill_random(ws + lo.attn, (size_t)M * C, 4u, 1.f, st) != hipSuccess)
+        unipin::launch_fill_random(ws + lo.tune, (size_t)4 * C * C + 4 * C, 2u, 0.05f, st) != hipSuccess ||
+        unipin::launch_fill_random(ws + lo.ln, (size_t)M * C, 3u, 1.f, st) != hipSuccess)
         return UNIPIN_EHIP;
     GemmShape g[4];
     block_gemms(C, g);
-    void *in_of[4] = {ws + lo.ln, ws + lo.attn, ws + lo.ln, ws + lo.big};
-    void *out_of[4] = {ws + lo.big, ws + lo.ln, ws + lo.big, ws + lo.ln};
-    const void *W = ws + lo.heads, *bias = ws + lo.attn;
+    // QKV: ln -> big; output projection: ln -> big (M x C of it); MLP up: ln -> big;
+    // MLP down: big -> ln
+    void *in_of[4] = {ws + lo.ln, ws + lo.ln, ws + lo.ln, ws + lo.big};
+    void *out_of[4] = {ws + lo.big, ws + lo.big, ws + lo.big, ws + lo.ln};
+    const void *W = ws + lo.tune, *bias = ws + lo.tune + (size_t)4 * C * C * 2;
     hipEvent_t e0, e1;
     if (hipEventCreate(&e0) != hipSuccess) return UNIPIN_EHIP;
     if (hipEventCreate(&e1) != hipSuccess) {
@@ -309,21 +310,20 @@ int unipin_block_forward(unipin_block_ctx_t *ctx, const unipin_block_weights_t *
     if (hipGetDevice(&dev) != hipSuccess || dev != ctx->device) return UNIPIN_EINVAL;
 
     char *ws = static_cast<char *>(workspace);
-    void *gws = ws + lo.gemm, *big = ws + lo.big, *ln = ws + lo.ln, *attn = ws + lo.attn;
-    char *heads = ws + lo.heads;
-    void *q = heads, *k = heads + (size_t)M * C * 2, *v = heads + (size_t)M * C * 4;
+    void *gws = ws + lo.gemm, *ln = ws + lo.ln;
+    char *big = ws + lo.big;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     int rc;
 
-    // attention half: x += (attention of LN1(x)) @ W_o + b_o
+    // attention half: x += (attention of LN1(x)) @ W_o + b_o.  The QKV rows are
+    // [B, rows, 3, H, D]: q, k, v of head h start at columns h*D, C + h*D, 2C + h*D of a
+    // row; the heads' outputs land at columns h*D of the merged rows [B, rows, C].
     if (unipin::launch_layernorm(x, w->ln1_w, w->ln1_b, ln, M, C, kLnEps, st) != hipSuccess) return UNIPIN_EHIP;
     if ((rc = gemm(ctx, ln, w->w_qkv, w->b_qkv, big, M, 3 * C, C, HIPBLASLT_EPILOGUE_BIAS, false, gws, st))) return rc;
-    if (unipin::launch_split_heads(big, q, k, v, B, rows, H, D, st) != hipSuccess) return UNIPIN_EHIP;
-    rc = mode == UNIPIN_BLOCK_HISTORY
-             ? unipin_prefill(q, k, v, lens, pool, slot, layer, B, rows, scale, attn, stream)
-             : unipin_rank_decode(q, k, v, pool, slot, lens, layer, B, rows, scale, attn, stream);
+    const unipin::RowLayout qkv_rows{(long)rows * 3 * C, D, 3 * C}, merged_rows{(long)rows * C, D, C};
+    rc = unipin::attention_call(mode == UNIPIN_BLOCK_HISTORY, big, big + (size_t)C * 2, big + (size_t)2 * C * 2,
+                                qkv_rows, ln, merged_rows, pool, slot, lens, layer, B, rows, scale, stream);
     if (rc) return rc;
-    if (unipin::launch_merge_heads(attn, ln, B, rows, H, D, st) != hipSuccess) return UNIPIN_EHIP;
     if ((rc = gemm(ctx, ln, w->w_o, w->b_o, x, M, C, C, HIPBLASLT_EPILOGUE_BIAS, true, gws, st))) return rc;
     // MLP half: x += GELU(LN2(x) @ W_fc + b_fc) @ W_proj + b_proj
     if (unipin::launch_layernorm(x, w->ln2_w, w->ln2_b, ln, M, C, kLnEps, st) != hipSuccess) return UNIPIN_EHIP;

@@ -1,8 +1,7 @@
-// Element-wise and row kernels of the transformer block around the masked attention, for
-// gfx950: LayerNorm over rows of the hidden state, and the two layout changes between
-// the fused QKV projection's rows [B, T, 3, H, D] and the attention kernels' per-head
-// rows [B, H, T, D].  All three are HBM-bound copies with a little arithmetic; each
-// lane moves 16 bytes per access, and a wave reads or writes whole contiguous rows.
+// Row kernels of the transformer block around the masked attention, for gfx950:
+// LayerNorm over rows of the hidden state (HBM-bound: each lane moves 16 bytes per
+// access and a wave reads and writes whole rows), and a pseudo-random fill that gives
+// the GEMM tuner operands of realistic size.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -109,42 +108,6 @@ __global__ void __launch_bounds__(256) layernorm_kernel(const bf16 *__restrict__
     }
 }
 
-// qkv rows [B, T, 3, H, D] -> q, k, v [B, H, T, D]; one 16-byte piece per thread, in
-// source order (contiguous reads; each group of D/8 lanes writes one whole row).
-__global__ void __launch_bounds__(256) split_heads_kernel(const bf16 *__restrict__ qkv, bf16 *__restrict__ q,
-                                                          bf16 *__restrict__ k, bf16 *__restrict__ v, int B, int T,
-                                                          int H, int D) {
-    const long per_row = 3L * H * D / 8;   // pieces per source row
-    const long total = (long)B * T * per_row;
-    const long p = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (p >= total) return;
-    const int d8 = (int)(p % (D / 8));
-    long r = p / (D / 8);
-    const int h = (int)(r % H);
-    r /= H;
-    const int part = (int)(r % 3);
-    r /= 3;
-    const int t = (int)(r % T);
-    const int b = (int)(r / T);
-    bf16 *dst = part == 0 ? q : part == 1 ? k : v;
-    reinterpret_cast<u32x4 *>(dst + (((long)b * H + h) * T + t) * D)[d8] = reinterpret_cast<const u32x4 *>(qkv)[p];
-}
-
-// o [B, H, T, D] -> y [B, T, H * D]; one 16-byte piece per thread, in destination order.
-__global__ void __launch_bounds__(256) merge_heads_kernel(const bf16 *__restrict__ o, bf16 *__restrict__ y, int B,
-                                                          int T, int H, int D) {
-    const long total = (long)B * T * H * D / 8;
-    const long p = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (p >= total) return;
-    const int d8 = (int)(p % (D / 8));
-    long r = p / (D / 8);
-    const int h = (int)(r % H);
-    r /= H;
-    const int t = (int)(r % T);
-    const int b = (int)(r / T);
-    reinterpret_cast<u32x4 *>(y)[p] = reinterpret_cast<const u32x4 *>(o + (((long)b * H + h) * T + t) * D)[d8];
-}
-
 // Fills n bf16 values with a hash of (seed, index) mapped to [-amp, amp): operands for
 // timing GEMM kernels on data of realistic size and spread.
 __global__ void __launch_bounds__(256) fill_random_kernel(bf16 *__restrict__ dst, size_t n, unsigned seed,
@@ -182,28 +145,10 @@ hipError_t launch_layernorm(const void *x, const void *w, const void *b, void *y
     return hipGetLastError();
 }
 
-hipError_t launch_split_heads(const void *qkv, void *q, void *k, void *v, int B, int T, int H, int D,
-                              hipStream_t stream) {
-    const long threads = (long)B * T * 3 * H * D / 8;
-    if (threads <= 0) return hipSuccess;
-    hipLaunchKernelGGL(split_heads_kernel, dim3(blocks_for(threads)), dim3(256), 0, stream,
-                       static_cast<const bf16 *>(qkv), static_cast<bf16 *>(q), static_cast<bf16 *>(k),
-                       static_cast<bf16 *>(v), B, T, H, D);
-    return hipGetLastError();
-}
-
 hipError_t launch_fill_random(void *dst, size_t n, unsigned seed, float amp, hipStream_t stream) {
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(fill_random_kernel, dim3(blocks_for((long)n)), dim3(256), 0, stream, static_cast<bf16 *>(dst),
                        n, seed, amp);
-    return hipGetLastError();
-}
-
-hipError_t launch_merge_heads(const void *o, void *y, int B, int T, int H, int D, hipStream_t stream) {
-    const long threads = (long)B * T * H * D / 8;
-    if (threads <= 0) return hipSuccess;
-    hipLaunchKernelGGL(merge_heads_kernel, dim3(blocks_for(threads)), dim3(256), 0, stream,
-                       static_cast<const bf16 *>(o), static_cast<bf16 *>(y), B, T, H, D);
     return hipGetLastError();
 }
 

@@ -10,12 +10,7 @@ namespace unipin {
 // y[M, C] = LayerNorm(x[M, C]) * w + b, eps as given; C % 8 == 0, C <= 2048.
 hipError_t launch_layernorm(const void *x, const void *w, const void *b, void *y, long M, int C, float eps,
                             hipStream_t stream);
-// qkv [B, T, 3, H, D] -> q, k, v [B, H, T, D].
-hipError_t launch_split_heads(const void *qkv, void *q, void *k, void *v, int B, int T, int H, int D,
-                              hipStream_t stream);
 // n bf16 values of a fixed pseudo-random sequence (seed), uniform in [-amp, amp).
 hipError_t launch_fill_random(void *dst, size_t n, unsigned seed, float amp, hipStream_t stream);
-// o [B, H, T, D] -> y [B, T, H*D].
-hipError_t launch_merge_heads(const void *o, void *y, int B, int T, int H, int D, hipStream_t stream);
 
 }  // namespace unipin

@@ -65,6 +65,62 @@ int rows_per_block(const unipin_pool *pool, bool prefill) {
 
 }  // namespace
 
+namespace unipin {
+
+int attention_call(bool prefill, const void *q, const void *k, const void *v, RowLayout in, void *o, RowLayout out,
+                   ::unipin_pool *pool, const int32_t *slot, const int32_t *lens, int layer, int B, int rows,
+                   float scale, void *stream) {
+    if (!pool || !q || !k || !v || !lens || !slot || !o) return UNIPIN_EINVAL;
+    if (B < 1 || rows < 1 || (prefill && rows > pool->n_max)) return UNIPIN_EINVAL;
+    if (layer < 0 || layer >= pool->L) return UNIPIN_ERANGE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lens, 4) ||
+        !aligned(slot, 4))
+        return UNIPIN_EALIGN;
+    const int D = pool->D, H = pool->H;
+    const bool dense = in.rstride == D && in.hstride == (long)rows * D && in.bstride == (long)H * rows * D &&
+                       out.rstride == D && out.hstride == (long)rows * D && out.bstride == (long)H * rows * D;
+    if (!dense) {
+        // other layouts: bf16 only, rows at least D elements apart, every row 16-byte aligned
+        // and every byte offset within 32 bits
+        if (pool->dtype != UNIPIN_BF16) return UNIPIN_EDTYPE;
+        const RowLayout *ls[2] = {&in, &out};
+        for (const RowLayout *l : ls) {
+            if (l->rstride < D || l->rstride % 8 || l->hstride % 8 || l->bstride % 8 || l->hstride < 0 ||
+                l->bstride < 0)
+                return UNIPIN_EINVAL;
+            if ((long long)rows * l->rstride * pool->elem >= 0x7fffffffLL) return UNIPIN_EINVAL;
+        }
+    }
+    const int rpb = rows_per_block(pool, prefill);
+    const long long blocks = (long long)B * H * ((rows + rpb - 1) / rpb);
+    if (blocks > 0x7fffffffLL) return UNIPIN_EINVAL;
+    unipin::AttnArgs a{};
+    int rc = resolve_scale(scale, D, &a.c);
+    if (rc) return rc;
+    fill_pool_args(a, pool, layer);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lens = lens;
+    a.slot = slot;
+    a.B = B;
+    a.rows = rows;
+    a.len_limit = prefill ? rows : pool->n_max;
+    a.tiles = (rows + rpb - 1) / rpb;
+    a.xcd_remap = pool->dtype == UNIPIN_BF16 && ((long long)B * H) % 8 == 0;
+    a.in_bstride = in.bstride;
+    a.in_hstride = in.hstride;
+    a.in_rstride = in.rstride;
+    a.out_bstride = out.bstride;
+    a.out_hstride = out.hstride;
+    a.out_rstride = out.rstride;
+    if (unipin::device_status_word(&a.status) != hipSuccess) return UNIPIN_EHIP;
+    return launch(a, pool, prefill, stream);
+}
+
+}  // namespace unipin
+
 extern "C" {
 
 int unipin_pool_create(unipin_pool_t **out, void *k_pool, void *v_pool, int L, int S, int H,
@@ -140,30 +196,8 @@ int unipin_prefill(const void *q, const void *k, const void *v, const int32_t *l
                    float scale, void *o, void *stream) {
     if (!pool || !q || !k || !v || !lens || !slot || !o) return UNIPIN_EINVAL;
     if (B < 1 || n < 1 || n > pool->n_max) return UNIPIN_EINVAL;
-    if (layer < 0 || layer >= pool->L) return UNIPIN_ERANGE;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-        !aligned(lens, 4) || !aligned(slot, 4))
-        return UNIPIN_EALIGN;
-    const int rpb = rows_per_block(pool, true);
-    const long long blocks = (long long)B * pool->H * ((n + rpb - 1) / rpb);
-    if (blocks > 0x7fffffffLL) return UNIPIN_EINVAL;
-    unipin::AttnArgs a{};
-    int rc = resolve_scale(scale, pool->D, &a.c);
-    if (rc) return rc;
-    fill_pool_args(a, pool, layer);
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.o = o;
-    a.lens = lens;
-    a.slot = slot;
-    a.B = B;
-    a.rows = n;
-    a.len_limit = n;
-    a.tiles = (n + rpb - 1) / rpb;
-    a.xcd_remap = pool->dtype == UNIPIN_BF16 && ((long long)B * pool->H) % 8 == 0;
-    if (unipin::device_status_word(&a.status) != hipSuccess) return UNIPIN_EHIP;
-    return launch(a, pool, true, stream);
+    const unipin::RowLayout dense{(long)pool->H * n * pool->D, (long)n * pool->D, pool->D};
+    return unipin::attention_call(true, q, k, v, dense, o, dense, pool, slot, lens, layer, B, n, scale, stream);
 }
 
 int unipin_rank_decode(const void *qc, const void *kc, const void *vc,
@@ -171,30 +205,9 @@ int unipin_rank_decode(const void *qc, const void *kc, const void *vc,
                        int layer, int B, int k, float scale, void *oc, void *stream) {
     if (!pool || !qc || !kc || !vc || !lens || !slot || !oc) return UNIPIN_EINVAL;
     if (B < 1 || k < 1) return UNIPIN_EINVAL;
-    if (layer < 0 || layer >= pool->L) return UNIPIN_ERANGE;
-    if (!aligned(qc, 16) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(oc, 16) ||
-        !aligned(lens, 4) || !aligned(slot, 4))
-        return UNIPIN_EALIGN;
-    const int rpb = rows_per_block(pool, false);
-    const long long blocks = (long long)B * pool->H * ((k + rpb - 1) / rpb);
-    if (blocks > 0x7fffffffLL) return UNIPIN_EINVAL;
-    unipin::AttnArgs a{};
-    int rc = resolve_scale(scale, pool->D, &a.c);
-    if (rc) return rc;
-    fill_pool_args(a, pool, layer);
-    a.q = qc;
-    a.k = kc;
-    a.v = vc;
-    a.o = oc;
-    a.lens = lens;
-    a.slot = slot;
-    a.B = B;
-    a.rows = k;
-    a.len_limit = pool->n_max;
-    a.tiles = (k + rpb - 1) / rpb;
-    a.xcd_remap = pool->dtype == UNIPIN_BF16 && ((long long)B * pool->H) % 8 == 0;
-    if (unipin::device_status_word(&a.status) != hipSuccess) return UNIPIN_EHIP;
-    return launch(a, pool, false, stream);
+    const unipin::RowLayout dense{(long)pool->H * k * pool->D, (long)k * pool->D, pool->D};
+    return unipin::attention_call(false, qc, kc, vc, dense, oc, dense, const_cast<unipin_pool_t *>(pool), slot, lens,
+                                  layer, B, k, scale, stream);
 }
 
 int unipin_ar_decode(const void *q, const void *k, const void *v, unipin_pool_t *pool,

@@ -226,13 +226,14 @@ def test_ar_decode_workspace_checks():
 
 
 def test_block_workspace_bytes():
-    """The block's workspace: 32 MiB for the GEMM library, then M x 4C, M x 3C and two
-    M x C bf16 regions (M = B * rows), each rounded up to 256 bytes."""
+    """The block's workspace: 32 MiB for the GEMM library, then M x 4C and M x C bf16
+    regions (M = B * rows) and 4C x C + 4C values for the GEMM tuner, each rounded up
+    to 256 bytes."""
     up = lambda x: (x + 255) // 256 * 256
     h = make_pool(L=1, S=8, H=8, n_max=992, D=64)
     M, C = 8 * 656, 512
-    assert lib.unipin_block_workspace_bytes(h, 8, 656) == (32 << 20) + up(M * 4 * C * 2) + up(M * 3 * C * 2) \
-        + 2 * up(M * C * 2)
+    assert lib.unipin_block_workspace_bytes(h, 8, 656) == (32 << 20) + up(M * 4 * C * 2) + up(M * C * 2) \
+        + up((4 * C * C + 4 * C) * 2)
     assert lib.unipin_block_workspace_bytes(h, 0, 656) == 0
     assert lib.unipin_block_workspace_bytes(None, 8, 656) == 0
     lib.unipin_pool_destroy(h)
