@@ -24,7 +24,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libunipin.so")
 
-FP32, BF16 = 0, 1
+FP32, BF16, FP8_E4M3 = 0, 1, 2
 OK, EINVAL, ERANGE, EDTYPE, EALIGN, EDEVICE, EHIP, ENOMEM = 0, -1, -2, -3, -4, -5, -6, -7
 FLAG_BAD_SLOT, FLAG_BAD_LEN = 1, 2
 
@@ -105,6 +105,8 @@ def _dtype_code(dtype: torch.dtype) -> int:
         return BF16
     if dtype == torch.float32:
         return FP32
+    if dtype == torch.float8_e4m3fn:
+        return FP8_E4M3
     raise UnipinError(EDTYPE, f"unsupported dtype {dtype}")
 
 
@@ -113,7 +115,10 @@ def _stream_handle(device: torch.device) -> int:
 
 
 class Pool:
-    """KV pool: K and V device tensors [L, S, H, n_max, D] plus the library descriptor."""
+    """KV pool: K and V device tensors [L, S, H, n_max, D] plus the library descriptor.
+
+    The tensors are float32, bfloat16 or float8_e4m3fn; calls on a float8_e4m3fn pool
+    take bfloat16 activations (act_dtype)."""
 
     def __init__(self, k_pool: torch.Tensor, v_pool: torch.Tensor):
         if k_pool.shape != v_pool.shape or k_pool.dim() != 5:
@@ -123,6 +128,8 @@ class Pool:
         self.k, self.v = k_pool, v_pool
         self.L, self.S, self.H, self.n_max, self.D = k_pool.shape
         self.dtype = k_pool.dtype
+        # the element type of the tensors a call takes: an E4M3 pool works on bf16
+        self.act_dtype = torch.bfloat16 if k_pool.dtype == torch.float8_e4m3fn else k_pool.dtype
         h = ctypes.c_void_p()
         _check(lib.unipin_pool_create(ctypes.byref(h), k_pool.data_ptr(), v_pool.data_ptr(),
                                       self.L, self.S, self.H, self.n_max, self.D,
@@ -195,10 +202,10 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lens, pool: Pool,
     dev = pool.k.device
     B, H, n, D = q.shape
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_tensor(t, name, (B, pool.H, n, pool.D), pool.dtype, dev)
+        _check_tensor(t, name, (B, pool.H, n, pool.D), pool.act_dtype, dev)
     if o is None:
         o = torch.empty_like(q)
-    _check_tensor(o, "o", q.shape, pool.dtype, dev)
+    _check_tensor(o, "o", q.shape, pool.act_dtype, dev)
     lens_t, slot_t = _i32_on(lens, dev), _i32_on(slot, dev)
     if lens_t.numel() != B or slot_t.numel() != B:
         raise UnipinError(EINVAL, "lens and slot need one entry per user")
@@ -218,10 +225,10 @@ def rank_decode(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, pool: Pool
     dev = pool.k.device
     B, H, kk, D = qc.shape
     for name, t in (("qc", qc), ("kc", kc), ("vc", vc)):
-        _check_tensor(t, name, (B, pool.H, kk, pool.D), pool.dtype, dev)
+        _check_tensor(t, name, (B, pool.H, kk, pool.D), pool.act_dtype, dev)
     if oc is None:
         oc = torch.empty_like(qc)
-    _check_tensor(oc, "oc", qc.shape, pool.dtype, dev)
+    _check_tensor(oc, "oc", qc.shape, pool.act_dtype, dev)
     lens_t, slot_t = _i32_on(lens, dev), _i32_on(slot, dev)
     if lens_t.numel() != B or slot_t.numel() != B:
         raise UnipinError(EINVAL, "lens and slot need one entry per user")
@@ -252,10 +259,10 @@ def ar_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pool: Pool, slo
     dev = pool.k.device
     B = q.shape[0]
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_tensor(t, name, (B, pool.H, 1, pool.D), pool.dtype, dev)
+        _check_tensor(t, name, (B, pool.H, 1, pool.D), pool.act_dtype, dev)
     if o is None:
         o = torch.empty_like(q)
-    _check_tensor(o, "o", q.shape, pool.dtype, dev)
+    _check_tensor(o, "o", q.shape, pool.act_dtype, dev)
     lens_t, slot_t = _i32_on(lens, dev), _i32_on(slot, dev)
     if lens_t.numel() != B or slot_t.numel() != B:
         raise UnipinError(EINVAL, "lens and slot need one entry per user")

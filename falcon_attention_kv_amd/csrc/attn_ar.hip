@@ -14,10 +14,16 @@
 // weighted in fp32.  At the end the waves' partial states (running max, sum and
 // accumulator) are merged through LDS, the new token enters as the last key, and the
 // output row is normalised and stored; the new K/V row is copied into the slot.
+//
+// An E4M3 pool (bf16 activations) halves the row bytes: a lane's 16-byte load then
+// holds 16 codes, which it decodes to fp32 and dots with the matching 32 bytes of the
+// bf16 query; the new token's K/V row is stored as codes (clamped to +-448, rounded to
+// nearest with ties to even).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "attn_launch.h"
+#include "e4m3.h"
 
 namespace unipin {
 namespace {
@@ -103,14 +109,98 @@ __device__ __forceinline__ float lowsum(float x) {
     return x;
 }
 
-// Geometry of one (element type, head dim): a row is R lanes of 16 bytes, a wave-wide
-// load covers RPI rows, a chunk (one wave's unit of work) is LPC loads = CH rows.
-template <typename T, int D>
+// Element kind: activations (q, k, v, o) of type T; the pool holds T as well, or E4M3
+// codes (P8).  A lane's 16-byte pool load holds PER elements; the matching activation
+// piece is AB = PER * sizeof(T) bytes (16, or 32 for an E4M3 pool).
+template <typename T, bool P8>
+struct Kind {
+    using Act = T;
+    static constexpr bool kP8 = P8;
+    static constexpr int PB = P8 ? 1 : (int)sizeof(T);   // pool bytes per element
+    static constexpr int PER = 16 / PB;
+    static constexpr int AB = PER * (int)sizeof(T);
+    static_assert(!P8 || sizeof(T) == 2, "an E4M3 pool pairs with bf16 activations");
+};
+
+// One lane's piece of an activation row (a query, key or value of the new token).
+template <typename K>
+struct ActPiece {
+    u32x4 x[K::AB / 16];
+};
+
+template <typename K, int D>
+__device__ __forceinline__ ActPiece<K> load_act(const typename K::Act *row, int sub) {
+    const __amdgpu_buffer_rsrc_t r = rsrc(row, (uint32_t)(D * sizeof(typename K::Act)));
+    ActPiece<K> a;
+#pragma unroll
+    for (int j = 0; j < K::AB / 16; ++j) a.x[j] = load16(r, sub * K::AB + 16 * j);
+    return a;
+}
+
+// The lane's query piece dotted with its 16 bytes of a pool row.
+template <typename K>
+__device__ __forceinline__ float dot_pool(const ActPiece<K> &q, const u32x4 &kx) {
+    if constexpr (!K::kP8) {
+        return dot16<typename K::Act>(q.x[0], kx);
+    } else {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            float kf[4], qf[8];
+            e4m3x4_to_f32(kx[w], kf);
+            widen<bf16>(q.x[w / 2], qf);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s = __builtin_fmaf(qf[(w % 2) * 4 + e], kf[e], s);
+        }
+        return s;
+    }
+}
+
+// The lane's query piece dotted with the same piece of another activation row.
+template <typename K>
+__device__ __forceinline__ float dot_act(const ActPiece<K> &q, const ActPiece<K> &k) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < K::AB / 16; ++j) s += dot16<typename K::Act>(q.x[j], k.x[j]);
+    return s;
+}
+
+template <typename K>
+__device__ __forceinline__ void widen_pool(const u32x4 &x, float (&f)[K::PER]) {
+    if constexpr (!K::kP8) {
+        widen<typename K::Act>(x, f);
+    } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            float g[4];
+            e4m3x4_to_f32(x[w], g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[4 * w + e] = g[e];
+        }
+    }
+}
+
+template <typename K>
+__device__ __forceinline__ void widen_act(const ActPiece<K> &a, float (&f)[K::PER]) {
+    constexpr int E = 16 / (int)sizeof(typename K::Act);   // elements per 16 bytes
+#pragma unroll
+    for (int j = 0; j < K::AB / 16; ++j) {
+        float g[E];
+        widen<typename K::Act>(a.x[j], g);
+#pragma unroll
+        for (int e = 0; e < E; ++e) f[j * E + e] = g[e];
+    }
+}
+
+// Geometry of one (element kind, head dim): a pool row is R lanes of 16 bytes, a
+// wave-wide load covers RPI rows, a chunk (one wave's unit of work) is LPC loads = CH
+// rows.
+template <typename K, int D>
 struct Geo {
-    static constexpr int ROW = D * (int)sizeof(T);
+    static constexpr int ROW = D * K::PB;
     static constexpr int R = ROW / 16;
     static constexpr int RPI = 64 / R;
-    static constexpr int PER = Elem<T>::kPer16;
+    static constexpr int PER = K::PER;
     static constexpr int LPC = RPI >= 4 ? 64 / RPI : 16;
     static constexpr int CH = LPC * RPI;
     static_assert(R >= 1 && R <= 64 && 64 % R == 0, "row must split into 16-byte lanes");
@@ -131,11 +221,11 @@ struct State {
 
 // The wave folds chunks c_first, c_first + stride, ... below c_end (chunk c = rows
 // [c*CH, c*CH + CH), rows >= N masked) into st.
-template <typename T, int D>
-__device__ __forceinline__ void scan_chunks(State<Geo<T, D>::PER> &st, __amdgpu_buffer_rsrc_t rk,
-                                            __amdgpu_buffer_rsrc_t rv, const u32x4 &qx, float c, int N,
+template <typename K, int D>
+__device__ __forceinline__ void scan_chunks(State<Geo<K, D>::PER> &st, __amdgpu_buffer_rsrc_t rk,
+                                            __amdgpu_buffer_rsrc_t rv, const ActPiece<K> &qx, float c, int N,
                                             int c_first, int c_end, int stride, int sub, int grp) {
-    using G = Geo<T, D>;
+    using G = Geo<K, D>;
     for (int ch = c_first; ch < c_end; ch += stride) {
         const int c0 = ch * G::CH;
         u32x4 kx[G::LPC], vx[G::LPC];
@@ -149,7 +239,7 @@ __device__ __forceinline__ void scan_chunks(State<Geo<T, D>::PER> &st, __amdgpu_
         float cm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < G::LPC; ++i) {
-            const float d = lowsum<G::R>(dot16<T>(qx, kx[i]));
+            const float d = lowsum<G::R>(dot_pool<K>(qx, kx[i]));
             sc[i] = c0 + i * G::RPI + grp < N ? d * c : -INFINITY;
             cm = fmaxf(cm, sc[i]);
         }
@@ -165,7 +255,7 @@ __device__ __forceinline__ void scan_chunks(State<Geo<T, D>::PER> &st, __amdgpu_
             const float p = __builtin_amdgcn_exp2f(sc[i] - st.m);
             st.l += p;   // the R lanes of a row hold the same weight; only rows are summed later
             float vf[G::PER];
-            widen<T>(vx[i], vf);
+            widen_pool<K>(vx[i], vf);
 #pragma unroll
             for (int e = 0; e < G::PER; ++e) st.acc[e] = __builtin_fmaf(p, vf[e], st.acc[e]);
         }
@@ -174,10 +264,10 @@ __device__ __forceinline__ void scan_chunks(State<Geo<T, D>::PER> &st, __amdgpu_
 
 // Sums the wave's row groups (lanes with the same sub hold the same dims) and leaves the
 // wave's state in part[wave]: accumulator [0, D), max at D, sum at D + 1.
-template <typename T, int D, int WAVES>
-__device__ __forceinline__ void publish(State<Geo<T, D>::PER> &st, float (*part)[D + 2], int wave, int sub,
+template <typename K, int D, int WAVES>
+__device__ __forceinline__ void publish(State<Geo<K, D>::PER> &st, float (*part)[D + 2], int wave, int sub,
                                         int grp) {
-    using G = Geo<T, D>;
+    using G = Geo<K, D>;
     st.l = xsum<G::R>(st.l);
 #pragma unroll
     for (int e = 0; e < G::PER; ++e) st.acc[e] = xsum<G::R>(st.acc[e]);
@@ -202,70 +292,83 @@ __device__ __forceinline__ bool invalid_user(const AttnArgs &a, int b, int N, in
 
 // The last step shared by both paths: the new token enters as one more key with weight
 // exp2(snew - mt); out already holds the other keys' weighted values rescaled to mt and
-// lt their weight sum.  Stores the output row and copies the token's K/V row into slot
-// row N.  Lanes with grp == 0 (one per 16-byte piece) store.
-template <typename T, int D>
-__device__ __forceinline__ void finish(const AttnArgs &a, long bh, long slot_off, int N, const u32x4 &knew,
-                                       const u32x4 &vnew, float pnew, float lt, float (&out)[Geo<T, D>::PER],
+// lt their weight sum.  Stores the output row and the token's K/V row into slot row N
+// (as it is, or as E4M3 codes).  Lanes with grp == 0 (one per pool piece) store.
+template <typename K, int D>
+__device__ __forceinline__ void finish(const AttnArgs &a, long bh, long slot_off, int N, const ActPiece<K> &knew,
+                                       const ActPiece<K> &vnew, float pnew, float lt, float (&out)[Geo<K, D>::PER],
                                        int sub, int grp) {
-    using G = Geo<T, D>;
+    using G = Geo<K, D>;
+    using T = typename K::Act;
     float vf[G::PER];
-    widen<T>(vnew, vf);
+    widen_act<K>(vnew, vf);
 #pragma unroll
     for (int e = 0; e < G::PER; ++e) out[e] = __builtin_fmaf(pnew, vf[e], out[e]);
     const float inv = 1.f / (lt + pnew);
     if (grp == 0) {
-        u32x4 ox;
-        if constexpr (G::PER == 8) {
+        char *orow = reinterpret_cast<char *>(static_cast<T *>(a.o) + bh * D) + sub * K::AB;
+        if constexpr (sizeof(T) == 2) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bf16x2 pr = {(bf16)(out[2 * i] * inv), (bf16)(out[2 * i + 1] * inv)};
-                ox[i] = __builtin_bit_cast(uint32_t, pr);
+            for (int j = 0; j < K::AB / 16; ++j) {
+                u32x4 ox;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bf16x2 pr = {(bf16)(out[8 * j + 2 * i] * inv), (bf16)(out[8 * j + 2 * i + 1] * inv)};
+                    ox[i] = __builtin_bit_cast(uint32_t, pr);
+                }
+                *reinterpret_cast<u32x4 *>(orow + 16 * j) = ox;
             }
         } else {
+            u32x4 ox;
 #pragma unroll
             for (int i = 0; i < 4; ++i) ox[i] = __float_as_uint(out[i] * inv);
+            *reinterpret_cast<u32x4 *>(orow) = ox;
         }
-        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(static_cast<T *>(a.o) + bh * D) + sub * 16) = ox;
-        // the new token's K/V row goes to slot row N, bit for bit
-        T *dk = static_cast<T *>(a.pool_k) + slot_off + (long)N * D;
-        T *dv = static_cast<T *>(a.pool_v) + slot_off + (long)N * D;
-        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(dk) + sub * 16) = knew;
-        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(dv) + sub * 16) = vnew;
+        char *dk = static_cast<char *>(a.pool_k) + (slot_off + (long)N * D) * K::PB + sub * 16;
+        char *dv = static_cast<char *>(a.pool_v) + (slot_off + (long)N * D) * K::PB + sub * 16;
+        if constexpr (K::kP8) {
+            *reinterpret_cast<u32x4 *>(dk) = e4m3x16_from_bf16x16(knew.x[0], knew.x[1]);
+            *reinterpret_cast<u32x4 *>(dv) = e4m3x16_from_bf16x16(vnew.x[0], vnew.x[1]);
+        } else {
+            // bit for bit
+            *reinterpret_cast<u32x4 *>(dk) = knew.x[0];
+            *reinterpret_cast<u32x4 *>(dv) = vnew.x[0];
+        }
     }
 }
 
 // One pass per (user, head): kWaves waves take the slot's chunks in turn, then wave 0
 // merges their states with the new token.
-template <typename T, int D>
+template <typename K, int D>
 __global__ void __launch_bounds__(kThreads) ar_decode_kernel(AttnArgs a) {
-    using G = Geo<T, D>;
+    using G = Geo<K, D>;
+    using T = typename K::Act;
     __shared__ float part[kWaves][D + 2];
 
     const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int sub = lane % G::R, grp = lane / G::R;
     const long bh = (long)b * a.H + h;
-    const u32x4 qx = load16(rsrc(static_cast<const T *>(a.q) + bh * D, G::ROW), sub * 16);   // slot-independent
+    const ActPiece<K> qx = load_act<K, D>(static_cast<const T *>(a.q) + bh * D, sub);   // slot-independent
     const int N = a.lens[b];
     const int s = a.slot[b];
     if (invalid_user(a, b, N, s, threadIdx.x == 0 && h == 0)) return;
-    const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
-    const T *pk = static_cast<const T *>(a.pool_k) + slot_off;
-    const T *pv = static_cast<const T *>(a.pool_v) + slot_off;
+    const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;   // in elements
+    const char *pk = static_cast<const char *>(a.pool_k) + slot_off * K::PB;
+    const char *pv = static_cast<const char *>(a.pool_v) + slot_off * K::PB;
     const __amdgpu_buffer_rsrc_t rk = rsrc(pk, (uint32_t)N * G::ROW);   // rows >= N read as zero
     const __amdgpu_buffer_rsrc_t rv = rsrc(pv, (uint32_t)N * G::ROW);
 
     State<G::PER> st;
     st.clear();
-    scan_chunks<T, D>(st, rk, rv, qx, a.c, N, wave, (N + G::CH - 1) / G::CH, kWaves, sub, grp);
-    publish<T, D, kWaves>(st, part, wave, sub, grp);
+    scan_chunks<K, D>(st, rk, rv, qx, a.c, N, wave, (N + G::CH - 1) / G::CH, kWaves, sub, grp);
+    publish<K, D, kWaves>(st, part, wave, sub, grp);
     __syncthreads();
     if (wave != 0) return;
 
-    const u32x4 knew = load16(rsrc(static_cast<const T *>(a.k) + bh * D, G::ROW), sub * 16);
-    const u32x4 vnew = load16(rsrc(static_cast<const T *>(a.v) + bh * D, G::ROW), sub * 16);
-    const float snew = lowsum<G::R>(dot16<T>(qx, knew)) * a.c;
+    const ActPiece<K> knew = load_act<K, D>(static_cast<const T *>(a.k) + bh * D, sub);
+    const ActPiece<K> vnew = load_act<K, D>(static_cast<const T *>(a.v) + bh * D, sub);
+    const float snew = lowsum<G::R>(dot_act<K>(qx, knew)) * a.c;
     float mt = snew;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mt = fmaxf(mt, part[w][D]);
@@ -279,7 +382,7 @@ __global__ void __launch_bounds__(kThreads) ar_decode_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < G::PER; ++e) out[e] = __builtin_fmaf(wt, part[w][sub * G::PER + e], out[e]);
     }
-    finish<T, D>(a, bh, slot_off, N, knew, vnew, __builtin_amdgcn_exp2f(snew - mt), lt, out, sub, grp);
+    finish<K, D>(a, bh, slot_off, N, knew, vnew, __builtin_amdgcn_exp2f(snew - mt), lt, out, sub, grp);
 }
 
 // Split-K across workgroups: a (user, head) with nc chunks cuts them into
@@ -288,9 +391,10 @@ __device__ __forceinline__ int split_chunks(int nc, int P) { return (nc + P - 1)
 
 // Pass 1 of the split path: workgroup (bh, p) folds its part's chunks and writes the
 // part's state (accumulator, max, sum) to ws[(bh * P + p) * (D + 4)].
-template <typename T, int D>
+template <typename K, int D>
 __global__ void __launch_bounds__(kThreads) ar_split_kernel(AttnArgs a, float *ws, int P) {
-    using G = Geo<T, D>;
+    using G = Geo<K, D>;
+    using T = typename K::Act;
     __shared__ float part[kWaves][D + 2];
 
     const long bh = blockIdx.x / P;
@@ -298,7 +402,7 @@ __global__ void __launch_bounds__(kThreads) ar_split_kernel(AttnArgs a, float *w
     const int b = (int)(bh / a.H), h = (int)(bh % a.H);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int sub = lane % G::R, grp = lane / G::R;
-    const u32x4 qx = load16(rsrc(static_cast<const T *>(a.q) + bh * D, G::ROW), sub * 16);   // slot-independent
+    const ActPiece<K> qx = load_act<K, D>(static_cast<const T *>(a.q) + bh * D, sub);   // slot-independent
     const int N = a.lens[b];
     const int s = a.slot[b];
     if (invalid_user(a, b, N, s, threadIdx.x == 0 && h == 0 && p == 0)) return;
@@ -307,13 +411,15 @@ __global__ void __launch_bounds__(kThreads) ar_split_kernel(AttnArgs a, float *w
     const int c_begin = p * cps, c_end = min(nc, c_begin + cps);
     if (c_begin >= c_end) return;   // this part is empty: the merge pass skips it too
     const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
-    const __amdgpu_buffer_rsrc_t rk = rsrc(static_cast<const T *>(a.pool_k) + slot_off, (uint32_t)N * G::ROW);
-    const __amdgpu_buffer_rsrc_t rv = rsrc(static_cast<const T *>(a.pool_v) + slot_off, (uint32_t)N * G::ROW);
+    const __amdgpu_buffer_rsrc_t rk =
+        rsrc(static_cast<const char *>(a.pool_k) + slot_off * K::PB, (uint32_t)N * G::ROW);
+    const __amdgpu_buffer_rsrc_t rv =
+        rsrc(static_cast<const char *>(a.pool_v) + slot_off * K::PB, (uint32_t)N * G::ROW);
 
     State<G::PER> st;
     st.clear();
-    scan_chunks<T, D>(st, rk, rv, qx, a.c, N, c_begin + wave, c_end, kWaves, sub, grp);
-    publish<T, D, kWaves>(st, part, wave, sub, grp);
+    scan_chunks<K, D>(st, rk, rv, qx, a.c, N, c_begin + wave, c_end, kWaves, sub, grp);
+    publish<K, D, kWaves>(st, part, wave, sub, grp);
     __syncthreads();
     if (wave != 0) return;
 
@@ -345,18 +451,19 @@ __global__ void __launch_bounds__(kThreads) ar_split_kernel(AttnArgs a, float *w
 // the new token, stores the output row and the token's K/V row.  Lane p holds part p's
 // max and sum (at most 64 parts); the accumulators are read four parts at a time so
 // that their loads overlap.
-template <typename T, int D>
+template <typename K, int D>
 __global__ void __launch_bounds__(64) ar_merge_kernel(AttnArgs a, const float *ws, int P) {
-    using G = Geo<T, D>;
+    using G = Geo<K, D>;
+    using T = typename K::Act;
     constexpr int SD = D + 4;   // floats per part state
     const long bh = blockIdx.x;
     const int b = (int)(bh / a.H), h = (int)(bh % a.H);
     const int lane = threadIdx.x;
     const int sub = lane % G::R, grp = lane / G::R;
     // the token's rows do not depend on the slot: their loads go out first
-    const u32x4 qx = load16(rsrc(static_cast<const T *>(a.q) + bh * D, G::ROW), sub * 16);
-    const u32x4 knew = load16(rsrc(static_cast<const T *>(a.k) + bh * D, G::ROW), sub * 16);
-    const u32x4 vnew = load16(rsrc(static_cast<const T *>(a.v) + bh * D, G::ROW), sub * 16);
+    const ActPiece<K> qx = load_act<K, D>(static_cast<const T *>(a.q) + bh * D, sub);
+    const ActPiece<K> knew = load_act<K, D>(static_cast<const T *>(a.k) + bh * D, sub);
+    const ActPiece<K> vnew = load_act<K, D>(static_cast<const T *>(a.v) + bh * D, sub);
     // an invalid user (flagged by pass 1) merges nothing and stores nothing; no early
     // exit, so that the loads above are not held back behind the check
     const bool ok = !invalid_user(a, b, a.lens[b], a.slot[b], false);
@@ -367,7 +474,7 @@ __global__ void __launch_bounds__(64) ar_merge_kernel(AttnArgs a, const float *w
     const float *src = ws + (long)bh * P * SD;
     const float mp = lane < parts ? src[lane * SD + D] : -INFINITY;
     const float lp = lane < parts ? src[lane * SD + D + 1] : 0.f;
-    const float snew = lowsum<G::R>(dot16<T>(qx, knew)) * a.c;
+    const float snew = lowsum<G::R>(dot_act<K>(qx, knew)) * a.c;
     const float mt = fmaxf(snew, xmax<1>(mp));
     const float wp = __builtin_amdgcn_exp2f(mp - mt);   // 0 past the last part
     const float lt = xsum<1>(wp * lp);
@@ -389,46 +496,52 @@ __global__ void __launch_bounds__(64) ar_merge_kernel(AttnArgs a, const float *w
             for (int e = 0; e < G::PER; ++e) out[e] = __builtin_fmaf(w, x[j][e], out[e]);
         }
     }
-    if (ok) finish<T, D>(a, bh, slot_off, N, knew, vnew, __builtin_amdgcn_exp2f(snew - mt), lt, out, sub, grp);
+    if (ok) finish<K, D>(a, bh, slot_off, N, knew, vnew, __builtin_amdgcn_exp2f(snew - mt), lt, out, sub, grp);
 }
 
-template <typename T, int D>
+template <typename K, int D>
 hipError_t launch_dim(const AttnArgs &a, float *ws, int P, hipStream_t stream) {
     const long bh = (long)a.B * a.H;
     if (P <= 1) {
-        hipLaunchKernelGGL((ar_decode_kernel<T, D>), dim3((unsigned)bh), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((ar_decode_kernel<K, D>), dim3((unsigned)bh), dim3(kThreads), 0, stream, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((ar_split_kernel<T, D>), dim3((unsigned)(bh * P)), dim3(kThreads), 0, stream, a, ws, P);
+    hipLaunchKernelGGL((ar_split_kernel<K, D>), dim3((unsigned)(bh * P)), dim3(kThreads), 0, stream, a, ws, P);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((ar_merge_kernel<T, D>), dim3((unsigned)bh), dim3(64), 0, stream, a, ws, P);
+    hipLaunchKernelGGL((ar_merge_kernel<K, D>), dim3((unsigned)bh), dim3(64), 0, stream, a, ws, P);
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_typed(const AttnArgs &a, int D, float *ws, int P, hipStream_t stream) {
+template <typename K>
+hipError_t launch_kind(const AttnArgs &a, int D, float *ws, int P, hipStream_t stream) {
     switch (D) {
-        case 32: return launch_dim<T, 32>(a, ws, P, stream);
-        case 64: return launch_dim<T, 64>(a, ws, P, stream);
-        case 128: return launch_dim<T, 128>(a, ws, P, stream);
+        case 32:
+            if constexpr (K::kP8) return hipErrorInvalidValue;   // a 32-byte E4M3 row is below one 16-byte lane pair
+            else return launch_dim<K, 32>(a, ws, P, stream);
+        case 64: return launch_dim<K, 64>(a, ws, P, stream);
+        case 128: return launch_dim<K, 128>(a, ws, P, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T>
+template <typename K>
 int chunk_rows(int D) {
     switch (D) {
-        case 32: return Geo<T, 32>::CH;
-        case 64: return Geo<T, 64>::CH;
-        case 128: return Geo<T, 128>::CH;
+        case 32: return Geo<K, 32>::CH;
+        case 64: return Geo<K, 64>::CH;
+        case 128: return Geo<K, 128>::CH;
         default: return 0;
     }
 }
 
+using KindF32 = Kind<float, false>;
+using KindBf16 = Kind<bf16, false>;
+using KindBf16P8 = Kind<bf16, true>;
+
 }  // namespace
 
-int ar_splits(long bh, int n_max, int D, bool bf16_elems) {
+int ar_splits(long bh, int n_max, int D, int kind) {
     // A pair whose K/V (at the slot's capacity) fit in 256 KiB costs the one-pass kernel
     // about two memory round trips, less than the merge pass: no split.  Otherwise cut
     // the rows into parts of at least 4 chunks, up to about 256 workgroups over all
@@ -436,8 +549,9 @@ int ar_splits(long bh, int n_max, int D, bool bf16_elems) {
     // per lane of the merge wave).
     if (bh <= 0 || n_max < 2) return 1;
     const long rows = n_max - 1;
-    if (2L * rows * D * (bf16_elems ? 2 : 4) <= (256L << 10)) return 1;
-    const int ch = bf16_elems ? chunk_rows<bf16>(D) : chunk_rows<float>(D);
+    const int pool_bytes = kind == 0 ? 4 : kind == 1 ? 2 : 1;
+    if (2L * rows * D * pool_bytes <= (256L << 10)) return 1;
+    const int ch = kind == 0 ? chunk_rows<KindF32>(D) : kind == 1 ? chunk_rows<KindBf16>(D) : chunk_rows<KindBf16P8>(D);
     if (ch == 0) return 1;
     const long nc = (rows + ch - 1) / ch;
     long P = (nc + 3) / 4;
@@ -448,9 +562,14 @@ int ar_splits(long bh, int n_max, int D, bool bf16_elems) {
 
 size_t ar_workspace_bytes(long bh, int P, int D) { return P <= 1 ? 0 : (size_t)bh * P * (D + 4) * sizeof(float); }
 
-hipError_t launch_ar_decode(const AttnArgs &a, int D, bool bf16_elems, float *ws, int P, hipStream_t stream) {
+hipError_t launch_ar_decode(const AttnArgs &a, int D, int kind, float *ws, int P, hipStream_t stream) {
     if ((long)a.B * a.H <= 0) return hipSuccess;
-    return bf16_elems ? launch_typed<bf16>(a, D, ws, P, stream) : launch_typed<float>(a, D, ws, P, stream);
+    switch (kind) {
+        case 0: return launch_kind<KindF32>(a, D, ws, P, stream);
+        case 1: return launch_kind<KindBf16>(a, D, ws, P, stream);
+        case 2: return launch_kind<KindBf16P8>(a, D, ws, P, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace unipin

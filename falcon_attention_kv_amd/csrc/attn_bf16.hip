@@ -48,6 +48,7 @@
 #include <stdint.h>
 
 #include "attn_launch.h"
+#include "e4m3.h"
 
 namespace unipin {
 namespace {
@@ -235,10 +236,11 @@ __device__ __forceinline__ void dma_rows(LDS_AS char *dst, i32x4 rsrc, int row0,
 }
 
 // Copies keys [kbase, min(kbase + 64, kend)) of a staged K/V tile into the pool slot
-// rows (pk, pv: the slot's K and V rows 0..), undoing the LDS swizzles: whole rows, 16
-// bytes per lane, rows at or past kend untouched.
-template <int D, int W>
-__device__ __forceinline__ void tile_to_pool(const LDS_AS char *tile, bf16 *pk, bf16 *pv, int kbase, int kend,
+// rows (pk, pv: the slot's K and V rows 0.., of P8 ? 1 : 2 bytes per element), undoing
+// the LDS swizzles: whole rows, 16 bytes of the tile per lane (as E4M3 codes, 8 bytes),
+// rows at or past kend untouched.
+template <int D, int W, bool P8>
+__device__ __forceinline__ void tile_to_pool(const LDS_AS char *tile, void *pk, void *pv, int kbase, int kend,
                                              int tid) {
     using T = Tile<D>;
     constexpr int BLOCKS = kTK * T::R;   // 16-byte blocks of one matrix
@@ -251,9 +253,14 @@ __device__ __forceinline__ void tile_to_pool(const LDS_AS char *tile, bf16 *pk, 
                                                                      ((blk ^ k_swz<D>(key)) * 16));
             const u32x4 vx = *reinterpret_cast<const LDS_AS u32x4 *>(tile + T::MAT_BYTES + key * T::ROW_BYTES +
                                                                      ((blk ^ v_swz<D>(key)) * 16));
-            const long off = (long)(kbase + key) * D + blk * 8;
-            *reinterpret_cast<u32x4 *>(pk + off) = kx;
-            *reinterpret_cast<u32x4 *>(pv + off) = vx;
+            const long off = (long)(kbase + key) * D + blk * 8;   // in elements
+            if constexpr (P8) {
+                *reinterpret_cast<u32x2 *>(static_cast<uint8_t *>(pk) + off) = e4m3x8_from_bf16x8(kx);
+                *reinterpret_cast<u32x2 *>(static_cast<uint8_t *>(pv) + off) = e4m3x8_from_bf16x8(vx);
+            } else {
+                *reinterpret_cast<u32x4 *>(static_cast<bf16 *>(pk) + off) = kx;
+                *reinterpret_cast<u32x4 *>(static_cast<bf16 *>(pv) + off) = vx;
+            }
         }
     }
 }
@@ -633,7 +640,7 @@ __device__ __forceinline__ void wait_pieces_after(int after) {
     else wait_vmcnt<0>();
 }
 
-template <int D>
+template <int D, bool P8>
 __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *__restrict__ lens,
                                              const int32_t *__restrict__ slots) {
     using T = Tile<D>;
@@ -663,8 +670,8 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
     const bf16 *vsrc = static_cast<const bf16 *>(a.v) + in_off;
     bf16 *odst = static_cast<bf16 *>(a.o) + (long)b * a.out_bstride + (long)h * a.out_hstride;
     const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
-    bf16 *pk = static_cast<bf16 *>(a.pool_k) + slot_off;
-    bf16 *pv = static_cast<bf16 *>(a.pool_v) + slot_off;
+    void *pk = static_cast<char *>(a.pool_k) + slot_off * (P8 ? 1 : (long)sizeof(bf16));
+    void *pv = static_cast<char *>(a.pool_v) + slot_off * (P8 ? 1 : (long)sizeof(bf16));
     const int kend = min(q0 + QT, N);
     const int ntiles = (kend + kTK - 1) / kTK;
 
@@ -711,7 +718,7 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
         for (; issued < ntiles && issued <= t + kBufs - 1; ++issued)
             dma_tile<D, W>(smem + (issued % kBufs) * T::BUF_BYTES, rsrc, issued * kTK, voff, wave, in_rs);
         const LDS_AS char *cur = smem + (t % kBufs) * T::BUF_BYTES;
-        if (t * kTK >= q0) tile_to_pool<D, W>(cur, pk, pv, t * kTK, kend, tid);
+        if (t * kTK >= q0) tile_to_pool<D, W, P8>(cur, pk, pv, t * kTK, kend, tid);
         return cur;
     };
     run_tiles<D, true>(ws, ntiles, tlast, kend, wq0, la, col, g, a.c, next_tile);
@@ -807,9 +814,9 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
                wq0, col, g, lane, a.out_rstride);
 }
 
-template <int D>
+template <int D, bool P8>
 __global__ void __launch_bounds__(block_waves<D>() * 64, min_waves_per_simd<D>()) prefill_bf16_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
-    prefill_body<D>(a, lens, slots);
+    prefill_body<D, P8>(a, lens, slots);
 }
 
 template <int D>
@@ -829,24 +836,28 @@ int bf16_decode_rows_per_item(int D) {
     return kBlockRows;
 }
 
-hipError_t launch_prefill_bf16(const AttnArgs &a, int D, hipStream_t stream) {
+hipError_t launch_prefill_bf16(const AttnArgs &a, int D, bool pool8, hipStream_t stream) {
     const long blocks = (long)a.B * a.H * a.tiles;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks);
+#define UNIPIN_PREFILL(DD, P8) \
+    hipLaunchKernelGGL((prefill_bf16_kernel<DD, P8>), grid, dim3(block_waves<DD>() * 64), 0, stream, a, a.lens, a.slot)
     switch (D) {
-        case 32: hipLaunchKernelGGL(prefill_bf16_kernel<32>, grid, dim3(block_waves<32>() * 64), 0, stream, a, a.lens, a.slot); break;
-        case 64: hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(block_waves<64>() * 64), 0, stream, a, a.lens, a.slot); break;
-        case 128: hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(block_waves<128>() * 64), 0, stream, a, a.lens, a.slot); break;
+        case 32: if (pool8) return hipErrorInvalidValue; UNIPIN_PREFILL(32, false); break;
+        case 64: if (pool8) UNIPIN_PREFILL(64, true); else UNIPIN_PREFILL(64, false); break;
+        case 128: if (pool8) UNIPIN_PREFILL(128, true); else UNIPIN_PREFILL(128, false); break;
         default: return hipErrorInvalidValue;
     }
+#undef UNIPIN_PREFILL
     return hipGetLastError();
 }
 
-hipError_t launch_decode_bf16(const AttnArgs &a, int D, hipStream_t stream) {
+hipError_t launch_decode_bf16(const AttnArgs &a, int D, bool pool8, hipStream_t stream) {
     const long items = (long)a.B * a.H * a.tiles;
     if (items <= 0) return hipSuccess;
     if (items > 0x7fffffffL) return hipErrorInvalidValue;
+    if (pool8) return hipErrorInvalidValue;
     const dim3 grid((unsigned)items);
     switch (D) {
         case 32: hipLaunchKernelGGL(rank_decode_bf16_kernel<32>, grid, dim3(block_waves<32>() * 64), 0, stream, a, a.lens, a.slot); break;

@@ -58,17 +58,20 @@ constexpr int kFp32RowsPerBlock = 64;
 int bf16_prefill_rows_per_block(int D);
 int bf16_decode_rows_per_item(int D);
 
-hipError_t launch_prefill_bf16(const AttnArgs &a, int D, hipStream_t stream);
-hipError_t launch_decode_bf16(const AttnArgs &a, int D, hipStream_t stream);
+// bf16 activations; pool8: the pool holds E4M3 codes (written by the prefill's fused
+// pool write, decoded by the ranking decode as its tiles arrive), else bf16.
+hipError_t launch_prefill_bf16(const AttnArgs &a, int D, bool pool8, hipStream_t stream);
+hipError_t launch_decode_bf16(const AttnArgs &a, int D, bool pool8, hipStream_t stream);
 hipError_t launch_prefill_fp32(const AttnArgs &a, int D, hipStream_t stream);
 hipError_t launch_decode_fp32(const AttnArgs &a, int D, hipStream_t stream);
-// One autoregressive step (one new token per user and head); bf16 or fp32 elements.
-// P = 1: one pass per (user, head).  P > 1: the slot rows are split into up to P parts,
-// one workgroup each, whose states go to ws (ar_workspace_bytes(B*H, P, D) bytes, fp32)
-// and are merged by a second pass.
-int ar_splits(long bh, int n_max, int D, bool bf16);
+// One autoregressive step (one new token per user and head).  kind: 0 fp32 activations
+// and pool, 1 bf16 activations and pool, 2 bf16 activations with an E4M3 pool (the
+// unipin_dtype_t codes).  P = 1: one pass per (user, head).  P > 1: the slot rows are
+// split into up to P parts, one workgroup each, whose states go to ws
+// (ar_workspace_bytes(B*H, P, D) bytes, fp32) and are merged by a second pass.
+int ar_splits(long bh, int n_max, int D, int kind);
 size_t ar_workspace_bytes(long bh, int P, int D);
-hipError_t launch_ar_decode(const AttnArgs &a, int D, bool bf16, float *ws, int P, hipStream_t stream);
+hipError_t launch_ar_decode(const AttnArgs &a, int D, int kind, float *ws, int P, hipStream_t stream);
 
 // Device address of the sticky status word of the current device (looked up once
 // per device with hipGetSymbolAddress).

@@ -193,7 +193,7 @@ int unipin_block_ctx_tune(unipin_block_ctx_t *ctx, const unipin_pool_t *pool, in
     if (!ctx || !pool || !workspace || B < 1 || rows < 1) return UNIPIN_EINVAL;
     int L, S, H, n_max, D, dt;
     if (unipin_pool_dims(pool, &L, &S, &H, &n_max, &D, &dt) != UNIPIN_OK) return UNIPIN_EINVAL;
-    if (dt != UNIPIN_BF16) return UNIPIN_EDTYPE;
+    if (dt == UNIPIN_FP32) return UNIPIN_EDTYPE;   // bf16 activations (bf16 or E4M3 pool)
     const int C = H * D;
     const long M = (long)B * rows;
     const Layout lo = layout(M, C);
@@ -293,7 +293,7 @@ int unipin_block_forward(unipin_block_ctx_t *ctx, const unipin_block_weights_t *
     if (B < 1 || rows < 1) return UNIPIN_EINVAL;
     int L, S, H, n_max, D, dt;
     if (unipin_pool_dims(pool, &L, &S, &H, &n_max, &D, &dt) != UNIPIN_OK) return UNIPIN_EINVAL;
-    if (dt != UNIPIN_BF16) return UNIPIN_EDTYPE;
+    if (dt == UNIPIN_FP32) return UNIPIN_EDTYPE;   // bf16 activations (bf16 or E4M3 pool)
     if (layer < 0 || layer >= L) return UNIPIN_ERANGE;
     if (mode == UNIPIN_BLOCK_HISTORY && rows > n_max) return UNIPIN_EINVAL;
     const int C = H * D;

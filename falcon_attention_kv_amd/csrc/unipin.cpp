@@ -38,6 +38,12 @@ int resolve_scale(float scale, int D, float *c) {
     return UNIPIN_OK;
 }
 
+// bf16 kernels serve bf16 and E4M3 pools (bf16 activations); fp32 pools the fp32 ones.
+bool bf16_kernels(const unipin_pool *pool) { return pool->dtype != UNIPIN_FP32; }
+
+// bytes of one activation element (q, k, v, o) for this pool
+int act_bytes(const unipin_pool *pool) { return pool->dtype == UNIPIN_FP32 ? 4 : 2; }
+
 int fill_pool_args(unipin::AttnArgs &a, const unipin_pool *pool, int layer) {
     const long long per_layer = (long long)pool->S * pool->H * pool->n_max * pool->D;
     a.pool_k = static_cast<char *>(pool->k) + (long long)layer * per_layer * pool->elem;
@@ -51,15 +57,18 @@ int fill_pool_args(unipin::AttnArgs &a, const unipin_pool *pool, int layer) {
 int launch(const unipin::AttnArgs &a, const unipin_pool *pool, bool prefill, void *stream) {
     const hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (pool->dtype == UNIPIN_BF16)
-        e = prefill ? unipin::launch_prefill_bf16(a, pool->D, st) : unipin::launch_decode_bf16(a, pool->D, st);
+    if (bf16_kernels(pool)) {
+        const bool pool8 = pool->dtype == UNIPIN_FP8_E4M3;
+        e = prefill ? unipin::launch_prefill_bf16(a, pool->D, pool8, st)
+                    : unipin::launch_decode_bf16(a, pool->D, pool8, st);
+    }
     else
         e = prefill ? unipin::launch_prefill_fp32(a, pool->D, st) : unipin::launch_decode_fp32(a, pool->D, st);
     return e == hipSuccess ? UNIPIN_OK : UNIPIN_EHIP;
 }
 
 int rows_per_block(const unipin_pool *pool, bool prefill) {
-    if (pool->dtype != UNIPIN_BF16) return unipin::kFp32RowsPerBlock;
+    if (!bf16_kernels(pool)) return unipin::kFp32RowsPerBlock;
     return prefill ? unipin::bf16_prefill_rows_per_block(pool->D) : unipin::bf16_decode_rows_per_item(pool->D);
 }
 
@@ -82,13 +91,13 @@ int attention_call(bool prefill, const void *q, const void *k, const void *v, Ro
     if (!dense) {
         // other layouts: bf16 only, rows at least D elements apart, every row 16-byte aligned
         // and every byte offset within 32 bits
-        if (pool->dtype != UNIPIN_BF16) return UNIPIN_EDTYPE;
+        if (!bf16_kernels(pool)) return UNIPIN_EDTYPE;
         const RowLayout *ls[2] = {&in, &out};
         for (const RowLayout *l : ls) {
             if (l->rstride < D || l->rstride % 8 || l->hstride % 8 || l->bstride % 8 || l->hstride < 0 ||
                 l->bstride < 0)
                 return UNIPIN_EINVAL;
-            if ((long long)rows * l->rstride * pool->elem >= 0x7fffffffLL) return UNIPIN_EINVAL;
+            if ((long long)rows * l->rstride * act_bytes(pool) >= 0x7fffffffLL) return UNIPIN_EINVAL;
         }
     }
     const int rpb = rows_per_block(pool, prefill);
@@ -108,7 +117,7 @@ int attention_call(bool prefill, const void *q, const void *k, const void *v, Ro
     a.rows = rows;
     a.len_limit = prefill ? rows : pool->n_max;
     a.tiles = (rows + rpb - 1) / rpb;
-    a.xcd_remap = pool->dtype == UNIPIN_BF16 && ((long long)B * H) % 8 == 0;
+    a.xcd_remap = bf16_kernels(pool) && ((long long)B * H) % 8 == 0;
     a.in_bstride = in.bstride;
     a.in_hstride = in.hstride;
     a.in_rstride = in.rstride;
@@ -129,7 +138,8 @@ int unipin_pool_create(unipin_pool_t **out, void *k_pool, void *v_pool, int L, i
     *out = nullptr;
     if (!k_pool || !v_pool) return UNIPIN_EINVAL;
     if (L < 1 || S < 1 || H < 1 || n_max < 1 || !supported_d(D)) return UNIPIN_EINVAL;
-    if (dtype != UNIPIN_FP32 && dtype != UNIPIN_BF16) return UNIPIN_EDTYPE;
+    if (dtype != UNIPIN_FP32 && dtype != UNIPIN_BF16 && dtype != UNIPIN_FP8_E4M3) return UNIPIN_EDTYPE;
+    if (dtype == UNIPIN_FP8_E4M3 && D != 64 && D != 128) return UNIPIN_EINVAL;
     if (!aligned(k_pool, 16) || !aligned(v_pool, 16)) return UNIPIN_EALIGN;
     const long long elems = (long long)L * S * H * n_max * D;
     if (elems / L / S / H / n_max != D || elems > (1LL << 46)) return UNIPIN_EINVAL;
@@ -150,7 +160,7 @@ int unipin_pool_create(unipin_pool_t **out, void *k_pool, void *v_pool, int L, i
     p->n_max = n_max;
     p->D = D;
     p->dtype = dtype;
-    p->elem = dtype == UNIPIN_BF16 ? 2 : 4;
+    p->elem = dtype == UNIPIN_FP32 ? 4 : dtype == UNIPIN_BF16 ? 2 : 1;
     *out = p;
     return UNIPIN_OK;
 }
@@ -234,15 +244,15 @@ int unipin_ar_decode(const void *q, const void *k, const void *v, unipin_pool_t 
     a.rows = 1;
     a.len_limit = pool->n_max - 1;
     a.tiles = 1;
-    const bool bf16 = pool->dtype == UNIPIN_BF16;
+    const int kind = pool->dtype;
     int parts = 1;
     if (workspace) {
         if (!aligned(workspace, 16)) return UNIPIN_EALIGN;
-        parts = unipin::ar_splits((long)B * pool->H, pool->n_max, pool->D, bf16);
+        parts = unipin::ar_splits((long)B * pool->H, pool->n_max, pool->D, kind);
         if (workspace_bytes < unipin::ar_workspace_bytes((long)B * pool->H, parts, pool->D)) return UNIPIN_EINVAL;
     }
     if (unipin::device_status_word(&a.status) != hipSuccess) return UNIPIN_EHIP;
-    const hipError_t e = unipin::launch_ar_decode(a, pool->D, bf16, static_cast<float *>(workspace), parts,
+    const hipError_t e = unipin::launch_ar_decode(a, pool->D, kind, static_cast<float *>(workspace), parts,
                                                   static_cast<hipStream_t>(stream));
     return e == hipSuccess ? UNIPIN_OK : UNIPIN_EHIP;
 }
@@ -250,7 +260,7 @@ int unipin_ar_decode(const void *q, const void *k, const void *v, unipin_pool_t 
 size_t unipin_ar_decode_workspace_bytes(const unipin_pool_t *pool, int B) {
     if (!pool || B < 1) return 0;
     const long bh = (long)B * pool->H;
-    return unipin::ar_workspace_bytes(bh, unipin::ar_splits(bh, pool->n_max, pool->D, pool->dtype == UNIPIN_BF16),
+    return unipin::ar_workspace_bytes(bh, unipin::ar_splits(bh, pool->n_max, pool->D, pool->dtype),
                                       pool->D);
 }
 

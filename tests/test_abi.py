@@ -250,6 +250,16 @@ def test_block_host_checks():
     lib.unipin_pool_destroy(h)
 
 
+def test_e4m3_pool_dims():
+    """E4M3 pools take D = 64 or 128; other element types keep D = 32 too."""
+    h = vp()
+    assert lib.unipin_pool_create(ctypes.byref(h), FAKE, FAKE * 2, 1, 1, 1, 8, 32, fa.FP8_E4M3) == fa.EINVAL
+    assert lib.unipin_pool_create(ctypes.byref(h), FAKE, FAKE * 2, 1, 1, 1, 8, 64, 3) == fa.EDTYPE
+    for D in (64, 128):
+        assert lib.unipin_pool_create(ctypes.byref(h), FAKE, FAKE * 2, 1, 1, 1, 8, D, fa.FP8_E4M3) == fa.OK
+        lib.unipin_pool_destroy(h)
+
+
 def test_null_pool_rejected():
     assert _prefill(None) == fa.EINVAL
     assert _decode(None) == fa.EINVAL
