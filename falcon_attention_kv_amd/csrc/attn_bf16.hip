@@ -728,12 +728,64 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
 
 // ------------------------------------------------------------------ ranking decode
 
+// E4M3 K/V tiles.  A tile of codes (K: kTK rows of D bytes, then V) is DMA'd as it is,
+// 1 KB per wave-wide piece in plain row order, into a staging area; the workgroup then
+// decodes it into the bf16 tile layout (rows of 16-byte blocks at the K and V
+// swizzles) that the tile step reads.  An E4M3 value is exact in bf16, and its fp32
+// form has 16 zero low bits, so the bf16 bits are its fp32 bits shifted down.
+template <int D, int W>
+struct F8Tile {
+    static constexpr int MAT = kTK * D;                 // bytes of one staged matrix
+    static constexpr int BYTES = 2 * MAT;               // K then V
+    static constexpr int PER_WAVE = BYTES / 1024 / W;   // DMA pieces per wave
+    static_assert(PER_WAVE >= 1 && PER_WAVE * W * 1024 == BYTES, "an E4M3 tile must split evenly over the waves");
+    static_assert(2 * BYTES == Tile<D>::BUF_BYTES, "two staged E4M3 tiles fill one LDS slot");
+};
+
+// DMA of this wave's share of E4M3 tile keys kbase .. kbase+63 (plain row order) into
+// `stage`; waves 0 .. W/2-1 move K, the others V, from `rsrc`.
+template <int D, int W>
+__device__ __forceinline__ void dma_tile8(LDS_AS char *stage, i32x4 rsrc, int kbase, int wave, int lane) {
+    using F = F8Tile<D, W>;
+    const bool is_v = wave >= W / 2;
+    const int first = (wave % (W / 2)) * F::PER_WAVE;   // piece index inside the matrix
+    const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(stage) + (is_v ? F::MAT : 0) + first * 1024;
+#pragma unroll
+    for (int j = 0; j < F::PER_WAVE; ++j) dma16(dst + j * 1024, rsrc, ((first + j) * 64 + lane) * 16, kbase * D);
+}
+
+// Decodes a staged E4M3 tile into the bf16 tile at `tile`: 16-byte output blocks (8
+// values), one per thread per pass.
+template <int D, int W>
+__device__ __forceinline__ void decode_tile8(const LDS_AS char *stage, LDS_AS char *tile, int tid) {
+    using T = Tile<D>;
+    using F = F8Tile<D, W>;
+    constexpr int BLOCKS = 2 * kTK * T::R;
+    static_assert(BLOCKS % (W * 64) == 0, "blocks must split evenly over the threads");
+#pragma unroll
+    for (int i0 = 0; i0 < BLOCKS; i0 += W * 64) {
+        const int i = i0 + tid;
+        const int mat = i / (kTK * T::R), key = (i / T::R) % kTK, blk = i % T::R;
+        const u32x2 raw = *reinterpret_cast<const LDS_AS u32x2 *>(stage + mat * F::MAT + key * D + blk * 8);
+        u32x4 out;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            float f[4];
+            e4m3x4_to_f32(raw[w], f);
+            out[2 * w] = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+            out[2 * w + 1] = (__float_as_uint(f[2]) >> 16) | (__float_as_uint(f[3]) & 0xffff0000u);
+        }
+        const int swz = mat ? v_swz<D>(key) : k_swz<D>(key);
+        *reinterpret_cast<LDS_AS u32x4 *>(tile + mat * T::MAT_BYTES + key * T::ROW_BYTES + (blk ^ swz) * 16) = out;
+    }
+}
+
 // One workgroup per item: (user, head, 256-candidate tile).  The candidate rows arrive
 // by DMA like the K/V tiles: q and kc first (slots 0-1 and 2-3: the queries and the own
 // key's score), then a stream of steps through the ring, step u in slot u % kBufs:
 // the K/V tiles 0 .. ntiles-1, then the two 128-row halves of vc, so that the own
 // key's values load in the background while the history is processed.
-template <int D>
+template <int D, bool P8>
 __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__restrict__ lens,
                                             const int32_t *__restrict__ slots) {
     using T = Tile<D>;
@@ -764,9 +816,10 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
     const long in_off = (long)b * a.in_bstride + (long)h * a.in_hstride;
     const int in_rs = a.in_rstride * (int)sizeof(bf16);   // bytes between candidate rows
     const uint32_t rows_bytes = (uint32_t)a.rows * in_rs;
-    const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
-    const i32x4 rsrc = rsrc_words(static_cast<const bf16 *>(wave < W / 2 ? a.pool_k : a.pool_v) + slot_off,
-                                  (uint32_t)N * T::ROW_BYTES);
+    const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;   // in elements
+    constexpr int PROW = P8 ? D : T::ROW_BYTES;                      // bytes of one pool row
+    const i32x4 rsrc = rsrc_words(static_cast<const char *>(wave < W / 2 ? a.pool_k : a.pool_v) + slot_off * (PROW / D),
+                                  (uint32_t)N * PROW);
     const i32x4 rsrc_vc = rsrc_words(static_cast<const bf16 *>(a.v) + in_off, rows_bytes);
     int voff[DPW];
     dma_offsets<D, W>(voff, wave, lane, T::ROW_BYTES);   // the pool's K/V rows
@@ -787,27 +840,68 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
     self_key_scores<D>(ws, sself, smem + 2 * T::BUF_BYTES + wrows, la, a.c);
     __syncthreads();   // the header slots are free again
 
-    auto issue = [&](int u) {
-        LDS_AS char *dst = smem + (u % kBufs) * T::BUF_BYTES;
-        if (u < ntiles) dma_tile<D, W>(dst, rsrc, u * kTK, voff, wave, T::ROW_BYTES);
-        else dma_rows<D, W, HALF>(dst, rsrc_vc, row0 + (u - ntiles) * HALF, wave, lane, in_rs);
-    };
-    int issued = 0;
-    for (; issued < kBufs - 1 && issued < nsteps; ++issued) issue(issued);
-    // Makes step u current: waits for its DMA, workgroup barrier (after which the slot of
-    // step u-1 is free), and lets the DMA run up to step u+kBufs-1.
-    auto next_step = [&](int u) -> const LDS_AS char * {
-        wait_pieces_after<DPW>(issued - u - 1);
-        __syncthreads();
-        for (; issued < nsteps && issued <= u + kBufs - 1; ++issued) issue(issued);
-        return smem + (u % kBufs) * T::BUF_BYTES;
-    };
-    run_tiles<D, false>(ws, ntiles, active ? ntiles - 1 : -1, N, wq0, la, col, g, a.c, next_step);
+    if constexpr (!P8) {
+        auto issue = [&](int u) {
+            LDS_AS char *dst = smem + (u % kBufs) * T::BUF_BYTES;
+            if (u < ntiles) dma_tile<D, W>(dst, rsrc, u * kTK, voff, wave, T::ROW_BYTES);
+            else dma_rows<D, W, HALF>(dst, rsrc_vc, row0 + (u - ntiles) * HALF, wave, lane, in_rs);
+        };
+        int issued = 0;
+        for (; issued < kBufs - 1 && issued < nsteps; ++issued) issue(issued);
+        // Makes step u current: waits for its DMA, workgroup barrier (after which the slot
+        // of step u-1 is free), and lets the DMA run up to step u+kBufs-1.
+        auto next_step = [&](int u) -> const LDS_AS char * {
+            wait_pieces_after<DPW>(issued - u - 1);
+            __syncthreads();
+            for (; issued < nsteps && issued <= u + kBufs - 1; ++issued) issue(issued);
+            return smem + (u % kBufs) * T::BUF_BYTES;
+        };
+        run_tiles<D, false>(ws, ntiles, active ? ntiles - 1 : -1, N, wq0, la, col, g, a.c, next_step);
 #pragma unroll
-    for (int hv = 0; hv < 2; ++hv) {
-        const LDS_AS char *vc_half = next_step(ntiles + hv);
-        if (active && wave / (W / 2) == hv)
-            self_key_merge<D>(ws, sself, vc_half + (wave % (W / 2)) * wave_rows<D>() * T::ROW_BYTES, col, g);
+        for (int hv = 0; hv < 2; ++hv) {
+            const LDS_AS char *vc_half = next_step(ntiles + hv);
+            if (active && wave / (W / 2) == hv)
+                self_key_merge<D>(ws, sself, vc_half + (wave % (W / 2)) * wave_rows<D>() * T::ROW_BYTES, col, g);
+        }
+    } else {
+        // E4M3 pool.  LDS: slot 0 the current tile decoded to bf16, slot 1 two staged
+        // E4M3 tiles (tile t at half t % 2), slots 2 and 3 the two vc halves.  DMA order
+        // per wave: tiles 0 and 1, then one tile per step (tile t + 2 after tile t is
+        // decoded), then both vc halves once no tile is left to issue.
+        using F = F8Tile<D, W>;
+        constexpr int FP = F::PER_WAVE;   // this wave's pieces per staged tile
+        LDS_AS char *stage = smem + T::BUF_BYTES;
+        LDS_AS char *cur = smem;
+        auto issue_vc = [&]() {
+            dma_rows<D, W, HALF>(smem + 2 * T::BUF_BYTES, rsrc_vc, row0, wave, lane, in_rs);
+            dma_rows<D, W, HALF>(smem + 3 * T::BUF_BYTES, rsrc_vc, row0 + HALF, wave, lane, in_rs);
+        };
+        if (ntiles > 0) dma_tile8<D, W>(stage, rsrc, 0, wave, lane);
+        if (ntiles > 1) dma_tile8<D, W>(stage + F::BYTES, rsrc, kTK, wave, lane);
+        if (ntiles == 0) issue_vc();
+        auto next_tile8 = [&](int t) -> const LDS_AS char * {
+            // pieces of this wave issued after tile t: tile t + 1 while it exists; at the
+            // last tile of two or more, the vc halves (issued one step earlier)
+            if (t + 1 < ntiles) wait_vmcnt<FP>();
+            else if (ntiles >= 2) wait_vmcnt<2 * DPW>();
+            else wait_vmcnt<0>();
+            __syncthreads();   // tile t has landed; every wave is done with slot 0
+            decode_tile8<D, W>(stage + (t % 2) * F::BYTES, cur, tid);
+            __syncthreads();   // slot 0 holds tile t; its staging half is free
+            if (t + 2 < ntiles) dma_tile8<D, W>(stage + (t % 2) * F::BYTES, rsrc, (t + 2) * kTK, wave, lane);
+            else if (t + 2 == ntiles || (ntiles == 1 && t == 0)) issue_vc();
+            return cur;
+        };
+        run_tiles<D, false>(ws, ntiles, active ? ntiles - 1 : -1, N, wq0, la, col, g, a.c, next_tile8);
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv) {
+            if (hv == 0) wait_vmcnt<DPW>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+            const LDS_AS char *vc_half = smem + (2 + hv) * T::BUF_BYTES;
+            if (active && wave / (W / 2) == hv)
+                self_key_merge<D>(ws, sself, vc_half + (wave % (W / 2)) * wave_rows<D>() * T::ROW_BYTES, col, g);
+        }
     }
     __syncthreads();   // every wave is done with the slots
     store_o<D>(ws, smem + wrows, static_cast<bf16 *>(a.o) + (long)b * a.out_bstride + (long)h * a.out_hstride, qlimit,
@@ -819,9 +913,9 @@ __global__ void __launch_bounds__(block_waves<D>() * 64, min_waves_per_simd<D>()
     prefill_body<D, P8>(a, lens, slots);
 }
 
-template <int D>
+template <int D, bool P8>
 __global__ void __launch_bounds__(block_waves<D>() * 64, min_waves_per_simd<D>()) rank_decode_bf16_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
-    decode_body<D>(a, lens, slots);
+    decode_body<D, P8>(a, lens, slots);
 }
 
 }  // namespace
@@ -857,14 +951,16 @@ hipError_t launch_decode_bf16(const AttnArgs &a, int D, bool pool8, hipStream_t 
     const long items = (long)a.B * a.H * a.tiles;
     if (items <= 0) return hipSuccess;
     if (items > 0x7fffffffL) return hipErrorInvalidValue;
-    if (pool8) return hipErrorInvalidValue;
     const dim3 grid((unsigned)items);
+#define UNIPIN_DECODE(DD, P8) \
+    hipLaunchKernelGGL((rank_decode_bf16_kernel<DD, P8>), grid, dim3(block_waves<DD>() * 64), 0, stream, a, a.lens, a.slot)
     switch (D) {
-        case 32: hipLaunchKernelGGL(rank_decode_bf16_kernel<32>, grid, dim3(block_waves<32>() * 64), 0, stream, a, a.lens, a.slot); break;
-        case 64: hipLaunchKernelGGL(rank_decode_bf16_kernel<64>, grid, dim3(block_waves<64>() * 64), 0, stream, a, a.lens, a.slot); break;
-        case 128: hipLaunchKernelGGL(rank_decode_bf16_kernel<128>, grid, dim3(block_waves<128>() * 64), 0, stream, a, a.lens, a.slot); break;
+        case 32: if (pool8) return hipErrorInvalidValue; UNIPIN_DECODE(32, false); break;
+        case 64: if (pool8) UNIPIN_DECODE(64, true); else UNIPIN_DECODE(64, false); break;
+        case 128: if (pool8) UNIPIN_DECODE(128, true); else UNIPIN_DECODE(128, false); break;
         default: return hipErrorInvalidValue;
     }
+#undef UNIPIN_DECODE
     return hipGetLastError();
 }
 

@@ -134,3 +134,101 @@ def test_prefill_on_e4m3_pool(D):
     rk, rv = oracle.pool_write_e4m3(before_k, before_v, inp["k"].cpu(), inp["v"].cpu(), lens, slots, 0)
     assert np.array_equal(codes(pool.k), rk) and np.array_equal(codes(pool.v), rv), "pool codes"
     pool.close()
+
+
+def test_rank_decode_reads_every_code_exactly():
+    """User c's slot holds one row of code c; its one candidate has q = k = v = 0, so the
+    output is decode(c) / 2 exactly, for every non-NaN code."""
+    announce("e4m3 ranking decode of every code")
+    D = 64
+    cs = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    B = len(cs)
+    kp = torch.zeros((1, B, 1, 4, D), dtype=torch.uint8)
+    for b, c in enumerate(cs):
+        kp[0, b, 0, 0] = c
+    pool = fa.Pool(kp.to(DEV).view(F8), kp.to(DEV).view(F8).clone())
+    z = torch.zeros((B, 1, 1, D), dtype=torch.bfloat16, device=DEV)
+    oc = fa.rank_decode(z, z, z, pool, list(range(B)), [1] * B, 0)
+    torch.cuda.synchronize()
+    assert fa.device_status() == 0
+    exp = oracle.e4m3_decode(np.array(cs, dtype=np.uint8)) / 2
+    assert np.array_equal(oc[:, 0, 0].double().cpu().numpy(), np.repeat(exp[:, None], D, axis=1))
+    pool.close()
+
+
+@pytest.mark.parametrize("D,k", [(64, 1), (64, 300), (64, 600), (128, 100), (128, 513)], ids=str)
+def test_rank_decode_on_e4m3_pool(D, k):
+    """Histories of 0 to n_max rows (0, 1 and 2 tiles, partial tiles) and 1 to 3
+    candidate tiles, against the oracle on the decoded pool."""
+    announce(f"e4m3 ranking decode D={D} k={k}")
+    L, S, H, n_max, layer = 2, 9, 2, 700, 1
+    lens = [0, 1, 63, 64, 65, 128, 200, 511, n_max][: 9]
+    slots = [4, 0, 8, 2, 7, 1, 3, 6, 5]
+    B = len(lens)
+    pool = e4m3_pool(L, S, H, n_max, D, seed=55)
+    inp = W.small_case(B, H, D, 8, k, [1] * B, seed=56, device=DEV)
+    oc = fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, slots, lens, layer)
+    torch.cuda.synchronize()
+    assert fa.device_status() == 0
+    pk, pv = oracle.e4m3_decode(codes(pool.k)), oracle.e4m3_decode(codes(pool.v))
+    ref = oracle.rank_decode(inp["qc"].cpu(), inp["kc"].cpu(), inp["vc"].cpu(), pk, pv, slots, lens, layer)
+    check_close(oc, ref, f"e4m3 ranking decode D={D} k={k}")
+    pool.close()
+
+
+def test_serving_shape_on_e4m3_pool_sampled():
+    """The 12-layer serving shape (64 requests x 8 heads, history 512, 1000 candidates)
+    prefilled into an E4M3 pool and decoded, sampled (layer, user) against the oracle."""
+    w = W.WORKLOADS[3]
+    announce("e4m3 serving shape")
+    lens = W.history_lengths(w).tolist()
+    pool = fa.Pool(torch.zeros((w.L, w.S, w.H, w.n, w.D), dtype=F8, device=DEV),
+                   torch.zeros((w.L, w.S, w.H, w.n, w.D), dtype=F8, device=DEV))
+    slots = pool.acquire_many(w.B)
+    checks = [(0, 3), (11, 60)]
+    outs = {}
+    for l in range(w.L):
+        x = W.layer_inputs(w, l, DEV)
+        fa.prefill(x["q"], x["k"], x["v"], lens, pool, slots, l)
+        oc = fa.rank_decode(x["qc"], x["kc"], x["vc"], pool, slots, lens, l)
+        for (cl, b) in checks:
+            if cl == l:
+                outs[(l, b)] = (oc[b:b + 1].cpu(), {kk: vv[b:b + 1].cpu() for kk, vv in x.items()})
+    torch.cuda.synchronize()
+    assert fa.device_status() == 0
+    for (l, b), (got, x) in outs.items():
+        s = slots[b]
+        pk = oracle.e4m3_decode(codes(pool.k[l:l + 1, s:s + 1]))
+        pv = oracle.e4m3_decode(codes(pool.v[l:l + 1, s:s + 1]))
+        assert np.array_equal(codes(pool.k[l, s, :, :lens[b]]), oracle.e4m3_encode(x["k"][0, :, :lens[b]]))
+        ref = oracle.rank_decode(x["qc"], x["kc"], x["vc"], pk, pv, [0], [lens[b]], 0)
+        check_close(got, ref, f"e4m3 serving shape layer {l} user {b}")
+    pool.close()
+
+
+def test_block_on_e4m3_pool():
+    """The transformer block with an E4M3 pool: the history forward stores codes, the
+    candidate forward reads them; against the oracle's candidate forward on the decoded
+    pool the GPU wrote (bf16 bounds relative to the output's size)."""
+    announce("block on an e4m3 pool")
+    B, n, K, H, D = 2, 130, 65, 8, 64
+    C = H * D
+    w = W.block_weights(C, torch.bfloat16, seed=57, device=DEV)
+    xh = W.block_inputs(B, n, C, torch.bfloat16, seed=58, device=DEV)
+    xc = W.block_inputs(B, K, C, torch.bfloat16, seed=59, device=DEV)
+    pool = fa.Pool(torch.zeros((1, B, H, n, D), dtype=F8, device=DEV), torch.zeros((1, B, H, n, D), dtype=F8, device=DEV))
+    lens, slots = [n, 71], [1, 0]
+    ctx = fa.BlockContext()
+    xc0 = xc.cpu()
+    fa.block_forward(ctx, w, fa.BLOCK_HISTORY, xh, pool, slots, lens, 0)
+    fa.block_forward(ctx, w, fa.BLOCK_CANDIDATES, xc, pool, slots, lens, 0)
+    torch.cuda.synchronize()
+    assert fa.device_status() == 0
+    pk, pv = oracle.e4m3_decode(codes(pool.k)), oracle.e4m3_decode(codes(pool.v))
+    ref = oracle.block_candidates(xc0, {kk: vv.cpu() for kk, vv in w.items()}, H, pk, pv, slots, lens, 0)
+    g = oracle.as_f64(xc)
+    u = 2.0 ** -8
+    assert np.abs(g - ref).max() <= 4 * u * np.abs(ref).max()
+    assert np.abs(g - ref).mean() <= 1 * u * np.abs(ref).mean()
+    ctx.close()
+    pool.close()
