@@ -14,11 +14,12 @@ Prints one JSON line.  `value` = ranked candidates per second through the whole 
 bounded sample of the same work on the host cores.
 
 After the timed steps, `block_table2` reports the 12-layer transformer around the
-attention (projections, LayerNorm, MLP) at the pages' Table 2 shape, and `ar_step` reports the autoregressive retrieval step (one new
+attention (projections, LayerNorm, MLP) at the pages' Table 2 shape, `e4m3_pool` the
+serving step and the retrieval step with the pool stored as E4M3 codes, and `ar_step` reports the autoregressive retrieval step (one new
 token per user and head appended to its slot) on the serving shape and on the long
 history shape; it is a secondary figure and does not enter `value`.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ar-step] [--no-block]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ar-step] [--no-block] [--no-e4m3]
 """
 from __future__ import annotations
 
@@ -52,6 +53,8 @@ def parse_args():
                    help="skip the secondary measurement of the autoregressive retrieval step")
     p.add_argument("--no-block", action="store_true",
                    help="skip the secondary measurement of the 12-layer transformer at the Table 2 shape")
+    p.add_argument("--no-e4m3", action="store_true",
+                   help="skip the secondary measurements on an E4M3 pool")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run 3 plain device copies of this many MiB (a known-size "
                         "reference for the HBM byte counters of a profiler run)")
@@ -74,16 +77,21 @@ def algorithmic(w, lens):
     return pf, pb, df, db
 
 
-def ar_step(fa, W, torch, dev, w, lens, steps: int, warmup: int):
+def ar_step(fa, W, torch, dev, w, lens, steps: int, warmup: int, pool_dtype=None):
     """The autoregressive retrieval step on the shape w: every user's slot holds lens[b]
     rows in each of the w.L layers; one step appends one token per (user, head) in every
     layer (w.L launches), the next step sees one row more.  Returns per-launch figures;
-    algorithmic bytes per (user, head) are the slot's K and V rows read once (2 N D e)
-    plus the token's q, k, v read and o and its two pool rows written (6 D e)."""
-    e = torch.tensor([], dtype=w.dtype).element_size()
+    algorithmic bytes per (user, head) are the slot's K and V rows read once (2 N D e,
+    e the pool's element size) plus the token's q, k, v read and o and its two pool rows
+    written (6 D e_act, counted at the activation size)."""
+    pool_dtype = pool_dtype or w.dtype
+    e = torch.tensor([], dtype=pool_dtype).element_size()   # bytes of one pool element
+    ea = torch.tensor([], dtype=w.dtype).element_size()     # bytes of one activation element
     T = warmup + steps
     n_max = max(lens) + T
-    pk, pv = W.random_pool(w.L, w.B, w.H, n_max, w.D, w.dtype, seed=41, device=dev)
+    pk, pv = W.random_pool(w.L, w.B, w.H, n_max, w.D, torch.float32 if pool_dtype != w.dtype else w.dtype,
+                           seed=41, device=dev)
+    pk, pv = pk.to(pool_dtype), pv.to(pool_dtype)
     pool = fa.Pool(pk, pv)
     tok = W.step_tokens(w.B, w.H, w.D, T, w.dtype, seed=42, device=dev)
     o = torch.empty_like(tok["q"][0])
@@ -103,7 +111,7 @@ def ar_step(fa, W, torch, dev, w, lens, steps: int, warmup: int):
         raise RuntimeError("the autoregressive step flagged an invalid slot or length")
     avg_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / (steps * w.L)
     rows = sum(lens) + w.B * (warmup + (steps - 1) / 2)   # mean slot fill over the timed steps
-    nbytes = (2 * rows + 6 * w.B) * w.H * w.D * e
+    nbytes = (2 * rows * e + 6 * w.B * ea) * w.H * w.D
     gbs = nbytes / (avg_ms / 1e3) / 1e9
     ws_bytes = fa.ar_decode_workspace_bytes(pool, w.B)
     pool.close()
@@ -113,6 +121,44 @@ def ar_step(fa, W, torch, dev, w, lens, steps: int, warmup: int):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "tokens_per_s": round(w.B * w.H / (avg_ms / 1e3), 1),
             "shape": f"B={w.B} H={w.H} D={w.D} history {min(lens)}..{max(lens)}, {w.L} layer(s), "
                      f"{steps} timed steps"}
+
+
+def serving_step_e4m3(fa, torch, dev, w, layers, lens, steps: int, warmup: int):
+    """The serving-shape step of the headline (12 prefills, then 12 ranking decodes over
+    the same layer inputs) with the pool stored as E4M3 codes.  Decode bytes per (user,
+    head): the slot's K and V codes (2 N D) plus the candidates' bf16 q, k, v, o
+    (4 k D 2)."""
+    pool = fa.Pool.allocate(w.L, w.S, w.H, w.n, w.D, torch.float8_e4m3fn, dev)
+    lens_d = torch.as_tensor(lens, dtype=torch.int32, device=dev)
+    outs = [torch.empty_like(x["q"]) for x in layers]
+    outc = [torch.empty_like(x["qc"]) for x in layers]
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(warmup + steps):
+        slots = torch.tensor(pool.acquire_many(w.B), dtype=torch.int32).pin_memory().to(dev, non_blocking=True)
+        e = ev[i - warmup] if i >= warmup else None
+        if e:
+            e[0].record(stream)
+        for l, x in enumerate(layers):
+            fa.prefill(x["q"], x["k"], x["v"], lens_d, pool, slots, l, o=outs[l])
+        if e:
+            e[1].record(stream)
+        for l, x in enumerate(layers):
+            fa.rank_decode(x["qc"], x["kc"], x["vc"], pool, slots, lens_d, l, oc=outc[l])
+        if e:
+            e[2].record(stream)
+    torch.cuda.synchronize()
+    if fa.device_status(dev) != 0:
+        raise RuntimeError("a kernel flagged an invalid slot or length")
+    pf = sum(e[0].elapsed_time(e[1]) for e in ev) / (steps * w.L)
+    dc = sum(e[1].elapsed_time(e[2]) for e in ev) / (steps * w.L)
+    step_ms = sum(e[0].elapsed_time(e[2]) for e in ev) / steps
+    dbytes = sum((2 * N * 1 + 4 * w.k * 2) * w.D for N in lens) * w.H
+    pool.close()
+    return {"candidates_per_s": round(w.B * w.k / (step_ms / 1e3), 1), "step_ms": round(step_ms, 4),
+            "prefill_avg_ms": round(pf, 5), "rank_decode_avg_ms": round(dc, 5),
+            "rank_decode_bytes_per_launch": int(dbytes),
+            "rank_decode_hbm_frac": round(dbytes / (dc / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def block_table2(fa, W, torch, dev, steps: int, warmup: int):
@@ -331,6 +377,15 @@ def main():
     if not args.no_cpu_baseline:
         layers_cpu = [{k: v.cpu() for k, v in x.items()} for x in layers]
         out["cpu_baseline"] = cpu_baseline(w, layers_cpu, lens, args.cpu_seconds)
+    if not args.no_e4m3:
+        pool.close()
+        e8 = {"serving_step": serving_step_e4m3(fa, torch, dev, w, layers, lens, steps=10, warmup=3)}
+        wl4 = W.WORKLOADS[4]
+        e8["ar_step_serving_shape"] = ar_step(fa, W, torch, dev, w, lens, steps=8, warmup=2,
+                                             pool_dtype=torch.float8_e4m3fn)
+        e8["ar_step_long_history"] = ar_step(fa, W, torch, dev, wl4, W.history_lengths(wl4).tolist(), steps=8,
+                                            warmup=2, pool_dtype=torch.float8_e4m3fn)
+        out["e4m3_pool"] = e8
     if not args.no_ar_step:
         del layers, outs, outc
         pool.close()

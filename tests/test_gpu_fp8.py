@@ -91,6 +91,26 @@ def test_ar_step_reads_every_code_exactly():
     pool.close()
 
 
+def test_ar_step_stores_nan_and_extreme_tokens_as_the_oracle_does():
+    """The new token's K/V row goes to the pool as codes: NaN stays NaN (sign kept),
+    infinities and huge values saturate, subnormal-range values round as specified."""
+    announce("e4m3 codes of NaN and extreme token values")
+    D = 64
+    special = torch.tensor([float("nan"), -float("nan"), float("inf"), -float("inf"), 1e30, -500.0, 464.0, 2.0 ** -10,
+                            3 * 2.0 ** -10, -2.0 ** -12, 0.0, -0.0, 447.9, 1.0625, 1.1875, -1.8125], dtype=torch.float32)
+    k = special.repeat(D // special.numel()).to(torch.bfloat16).reshape(1, 1, 1, D).to(DEV)
+    pool = fa.Pool(torch.zeros((1, 1, 1, 4, D), dtype=F8, device=DEV), torch.zeros((1, 1, 1, 4, D), dtype=F8, device=DEV))
+    z = torch.zeros_like(k)
+    fa.ar_decode(z, k, k, pool, [0], [2], 0)
+    torch.cuda.synchronize()
+    got = codes(pool.k)[0, 0, 0, 2]
+    ref = oracle.e4m3_encode(k.cpu().reshape(-1))
+    assert np.array_equal(got, ref), (got.tolist()[:16], ref.tolist()[:16])
+    assert np.array_equal(codes(pool.v)[0, 0, 0, 2], ref)
+    fa.device_status()   # NaN attention output is expected; clear nothing else
+    pool.close()
+
+
 @pytest.mark.parametrize("D,n_max", [(64, 601), (128, 601), (64, 4600), (128, 4600)], ids=str)
 def test_ar_step_on_e4m3_pool(D, n_max):
     """Mixed fill levels, one pass (n_max 601) and the split path (n_max 4600)."""
