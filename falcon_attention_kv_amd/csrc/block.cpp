@@ -12,6 +12,7 @@
 // [B, rows, H, D] that the output projection reads.  Host code here allocates nothing on
 // the device: every intermediate lives in the caller's workspace.
 #include <hip/hip_runtime.h>
+#include <hipblaslt/hipblaslt-ext.hpp>
 #include <hipblaslt/hipblaslt.h>
 
 #include <cstdint>
@@ -20,6 +21,7 @@
 #include <mutex>
 #include <new>
 #include <tuple>
+#include <vector>
 
 #include "attn_launch.h"
 #include "block_launch.h"
@@ -29,6 +31,7 @@ namespace {
 
 constexpr float kLnEps = 1e-5f;
 constexpr size_t kGemmWorkspace = 32u << 20;   // hipBLASLt's share of the workspace
+constexpr size_t kMaxTuneCandidates = 1500;    // GEMM kernels timed per shape by the tuner
 constexpr size_t kAlign = 256;
 
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -230,29 +233,50 @@ int unipin_block_ctx_tune(unipin_block_ctx_t *ctx, const unipin_pool_t *pool, in
             rc = UNIPIN_EHIP;
             break;
         }
+        // candidates: the library's heuristic choices, then every kernel it has for a
+        // bf16 GEMM that accepts this problem (shape, layouts, epilogue) within the workspace
         hipblasLtMatmulPreference_t pref = nullptr;
         const uint64_t wsz = kGemmWorkspace;
-        constexpr int kMaxAlgos = 32;
-        hipblasLtMatmulHeuristicResult_t res[kMaxAlgos];
+        constexpr int kHeuristic = 32;
+        hipblasLtMatmulHeuristicResult_t heur[kHeuristic];
         int found = 0;
         if (hipblasLtMatmulPreferenceCreate(&pref) != 0 ||
             hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsz,
                                                   sizeof(wsz)) != 0 ||
             hipblasLtMatmulDescSetAttribute(p->desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof(bias)) != 0 ||
-            hipblasLtMatmulAlgoGetHeuristic(ctx->handle, p->desc, p->la, p->lb, p->lc, p->lc, pref, kMaxAlgos, res,
+            hipblasLtMatmulAlgoGetHeuristic(ctx->handle, p->desc, p->la, p->lb, p->lc, p->lc, pref, kHeuristic, heur,
                                             &found) != 0) {
             if (pref) hipblasLtMatmulPreferenceDestroy(pref);
             rc = UNIPIN_EHIP;
             break;
         }
         hipblasLtMatmulPreferenceDestroy(pref);
+        std::vector<hipblasLtMatmulAlgo_t> cands;
+        for (int a = 0; a < found; ++a)
+            if (heur[a].state == HIPBLAS_STATUS_SUCCESS && heur[a].workspaceSize <= kGemmWorkspace)
+                cands.push_back(heur[a].algo);
+        {
+            const float al = 1.f, be = g[i].residual ? 1.f : 0.f;
+            std::vector<hipblasLtMatmulHeuristicResult_t> all;
+            if (hipblaslt_ext::getAllAlgos(ctx->handle, hipblaslt_ext::GemmType::HIPBLASLT_GEMM, HIPBLAS_OP_N,
+                                           HIPBLAS_OP_N, HIP_R_16BF, HIP_R_16BF, HIP_R_16BF, HIP_R_16BF,
+                                           HIPBLAS_COMPUTE_32F, all) == HIPBLAS_STATUS_SUCCESS) {
+                for (auto &r : all) {
+                    if (cands.size() >= kMaxTuneCandidates) break;
+                    size_t need = 0;
+                    if (hipblaslt_ext::matmulIsAlgoSupported(ctx->handle, p->desc, &al, p->la, p->lb, &be, p->lc,
+                                                             p->lc, r.algo, need) == HIPBLAS_STATUS_SUCCESS &&
+                        need <= kGemmWorkspace)
+                        cands.push_back(r.algo);
+                }
+            }
+        }
         const float alpha = 1.f, beta = g[i].residual ? 1.f : 0.f;
         float best = 1e30f;
-        for (int a = 0; a < found; ++a) {
-            if (res[a].state != HIPBLAS_STATUS_SUCCESS || res[a].workspaceSize > kGemmWorkspace) continue;
+        for (auto &algo : cands) {
             auto run = [&]() {
                 return hipblasLtMatmul(ctx->handle, p->desc, &alpha, W, p->la, in_of[i], p->lb, &beta, out_of[i],
-                                       p->lc, out_of[i], p->lc, &res[a].algo, ws + lo.gemm, kGemmWorkspace, st);
+                                       p->lc, out_of[i], p->lc, &algo, ws + lo.gemm, kGemmWorkspace, st);
             };
             if (run() != HIPBLAS_STATUS_SUCCESS || run() != HIPBLAS_STATUS_SUCCESS) continue;
             if (hipEventRecord(e0, st) != hipSuccess) {
@@ -269,7 +293,7 @@ int unipin_block_ctx_tune(unipin_block_ctx_t *ctx, const unipin_pool_t *pool, in
             }
             if (ok && ms < best) {
                 best = ms;
-                p->algo = res[a].algo;
+                p->algo = algo;
             }
             // the residual GEMMs add into their output each run; start the next from
             // the same values as the first so that no candidate sees overflowing data
