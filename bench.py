@@ -19,7 +19,11 @@ serving step and the retrieval step with the pool stored as E4M3 codes, and `ar_
 token per user and head appended to its slot) on the serving shape and on the long
 history shape; it is a secondary figure and does not enter `value`.
 
+`--workloads` replaces all of this with a per-kernel table over every bf16 workload
+(one layer each, cold and back to back).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ar-step] [--no-block] [--no-e4m3]
+                       [--workloads]
 """
 from __future__ import annotations
 
@@ -55,6 +59,9 @@ def parse_args():
                    help="skip the secondary measurement of the 12-layer transformer at the Table 2 shape")
     p.add_argument("--no-e4m3", action="store_true",
                    help="skip the secondary measurements on an E4M3 pool")
+    p.add_argument("--workloads", action="store_true",
+                   help="instead of the serving step, time one layer's prefill and decode on every bf16 "
+                        "workload, cold (a 512 MiB overwrite before each launch) and back to back")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run 3 plain device copies of this many MiB (a known-size "
                         "reference for the HBM byte counters of a profiler run)")
@@ -214,6 +221,77 @@ def block_table2(fa, W, torch, dev, steps: int, warmup: int):
             "candidate_mfma_frac": round(cand_flop / cand_ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
 
 
+def workload_kernels(fa, W, torch, dev, launches: int = 10, warmup: int = 3):
+    """One layer's prefill and rank decode on each bf16 workload (the parity shapes and
+    the serving shape's first layer).  Cold: before each launch a 512 MiB buffer is
+    overwritten, so inputs and pool come from HBM, and HIP events bracket the launch
+    alone (median reported).  Warm: `launches` back-to-back launches on the same inputs
+    between two events (mean reported)."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for w in W.WORKLOADS[1:]:
+        lens = W.history_lengths(w).tolist()
+        lens_d = torch.as_tensor(lens, dtype=torch.int32, device=dev)
+        x = W.layer_inputs(w, 0, dev)
+        pool = fa.Pool.allocate(1, w.S, w.H, w.n, w.D, w.dtype, dev)
+        slots = torch.tensor(pool.acquire_many(w.B), dtype=torch.int32, device=dev)
+        o, oc = torch.empty_like(x["q"]), torch.empty_like(x["qc"])
+        calls = {
+            "prefill": lambda: fa.prefill(x["q"], x["k"], x["v"], lens_d, pool, slots, 0, o=o),
+            "rank_decode": lambda: fa.rank_decode(x["qc"], x["kc"], x["vc"], pool, slots, lens_d, 0, oc=oc),
+        }
+        pf, pb, df, db = algorithmic(w, lens)
+        work = {"prefill": (pf, pb), "rank_decode": (df, db)}
+        entry = {}
+        for name, call in calls.items():
+            for _ in range(warmup):
+                call()
+            cold = []
+            for _ in range(launches):
+                flush.fill_(1)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                call()
+                e1.record(stream)
+                e1.synchronize()
+                cold.append(e0.elapsed_time(e1))
+            cold.sort()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(launches):
+                call()
+            e1.record(stream)
+            e1.synchronize()
+            warm = e0.elapsed_time(e1) / launches
+            flop, byts = work[name]
+            t = cold[len(cold) // 2]
+            entry[name] = {"cold_median_ms": round(t, 5), "warm_mean_ms": round(warm, 5),
+                           "algorithmic_gflop": round(flop / 1e9, 3), "algorithmic_mb": round(byts / 1e6, 2),
+                           "cold_tflops": round(flop / (t / 1e3) / 1e12, 1),
+                           "cold_mfma_frac": round(flop / (t / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                           "cold_gbs": round(byts / (t / 1e3) / 1e9, 1),
+                           "cold_hbm_frac": round(byts / (t / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if fa.device_status(dev) != 0:
+            raise RuntimeError("a kernel flagged an invalid slot or length")
+        pool.close()
+        res[w.name] = entry
+        del x, o, oc
+    return res
+
+
+def copy_calibration(torch, dev, mib: int) -> int:
+    """Three plain device copies of `mib` MiB: a known-size reference for the HBM byte
+    counters of a profiler run.  Returns the bytes one copy reads."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return n * 4
+
+
 def kernel_source_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -281,6 +359,12 @@ def main():
     w = W.WORKLOADS[3]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workloads:
+        out = {"workload_kernels": workload_kernels(fa, W, torch, dev)}
+        if args.copy_calib_mib:
+            out["copy_calibration_bytes"] = copy_calibration(torch, dev, args.copy_calib_mib)
+        print(json.dumps(out), flush=True)
+        return
     lens = W.history_lengths(w).tolist()
     lens_d = torch.as_tensor(lens, dtype=torch.int32, device=dev)
     layers = [W.layer_inputs(w, l, dev) for l in range(w.L)]
@@ -367,13 +451,7 @@ def main():
     if not args.no_block:
         out["block_table2"] = block_table2(fa, W, torch, dev, steps=5, warmup=2)
     if args.copy_calib_mib:
-        n = args.copy_calib_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        out["copy_calibration_bytes"] = n * 4
+        out["copy_calibration_bytes"] = copy_calibration(torch, dev, args.copy_calib_mib)
     if not args.no_cpu_baseline:
         layers_cpu = [{k: v.cpu() for k, v in x.items()} for x in layers]
         out["cpu_baseline"] = cpu_baseline(w, layers_cpu, lens, args.cpu_seconds)
