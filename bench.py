@@ -19,11 +19,12 @@ serving step and the retrieval step with the pool stored as E4M3 codes, and `ar_
 token per user and head appended to its slot) on the serving shape and on the long
 history shape; it is a secondary figure and does not enter `value`.
 
+`--block-only` runs only the Table 2 transformer measurement (3 timed passes).
 `--workloads` replaces all of this with a per-kernel table over every bf16 workload
 (one layer each, cold and back to back).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ar-step] [--no-block] [--no-e4m3]
-                       [--workloads]
+                       [--workloads] [--block-only]
 """
 from __future__ import annotations
 
@@ -62,6 +63,9 @@ def parse_args():
     p.add_argument("--workloads", action="store_true",
                    help="instead of the serving step, time one layer's prefill and decode on every bf16 "
                         "workload, cold (a 512 MiB overwrite before each launch) and back to back")
+    p.add_argument("--block-only", action="store_true",
+                   help="instead of the serving step, run only the Table 2 transformer measurement "
+                        "(3 timed passes after 1 warm-up; a short program for a kernel trace)")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run 3 plain device copies of this many MiB (a known-size "
                         "reference for the HBM byte counters of a profiler run)")
@@ -359,6 +363,9 @@ def main():
     w = W.WORKLOADS[3]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.block_only:
+        print(json.dumps({"block_table2": block_table2(fa, W, torch, dev, steps=3, warmup=1)}), flush=True)
+        return
     if args.workloads:
         out = {"workload_kernels": workload_kernels(fa, W, torch, dev)}
         if args.copy_calib_mib:
