@@ -34,13 +34,15 @@ EXPORTS = ("unipin_pool_create", "unipin_pool_destroy", "unipin_pool_acquire",
            "unipin_rank_decode", "unipin_ar_decode", "unipin_ar_decode_workspace_bytes",
            "unipin_device_status", "unipin_strerror", "unipin_version",
            "unipin_block_ctx_create", "unipin_block_ctx_destroy", "unipin_block_workspace_bytes",
-           "unipin_block_ctx_tune", "unipin_block_forward")
+           "unipin_block_ctx_tune", "unipin_block_ctx_set_gemm", "unipin_block_forward")
 
 
 # Weights of one transformer block, in the order of unipin_block_weights_t.
 BLOCK_WEIGHT_NAMES = ("ln1_w", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_w", "ln2_b", "w_fc", "b_fc",
                       "w_proj", "b_proj")
 BLOCK_HISTORY, BLOCK_CANDIDATES = 0, 1
+# unipin_block_ctx_set_gemm: AUTO, hipBLASLt only, or the library's kernel with tile 0, 1, 2
+GEMM_AUTO, GEMM_LIBRARY = -2, -1
 
 
 class BlockWeights(ctypes.Structure):
@@ -71,6 +73,7 @@ def _load() -> ctypes.CDLL:
     lib.unipin_block_ctx_destroy.argtypes = [vp]
     lib.unipin_block_workspace_bytes.argtypes = [vp, i32, i32]
     lib.unipin_block_ctx_tune.argtypes = [vp, vp, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.unipin_block_ctx_set_gemm.argtypes = [vp, i32]
     lib.unipin_block_forward.argtypes = [vp, ctypes.POINTER(BlockWeights), i32, vp, vp, vp, vp, i32, i32, i32,
                                          ctypes.c_float, vp, ctypes.c_size_t, vp]
     lib.unipin_device_status.argtypes = [vp, ip]
@@ -296,9 +299,15 @@ class BlockContext:
             raise UnipinError(EINVAL, "block context is closed")
         return self._h
 
+    def set_gemm(self, kernel: int) -> None:
+        """unipin_block_ctx_set_gemm: GEMM_AUTO, GEMM_LIBRARY (hipBLASLt) or the library's
+        kernel with tile configuration 0, 1 or 2; drops the plans made so far."""
+        _check(lib.unipin_block_ctx_set_gemm(self.handle, int(kernel)), "unipin_block_ctx_set_gemm")
+
     def tune(self, pool: "Pool", B: int, rows: int, workspace: Optional[torch.Tensor] = None) -> None:
-        """unipin_block_ctx_tune: time hipBLASLt's candidate kernels for the block's GEMMs
-        at B users x rows rows and keep the fastest (blocks until done)."""
+        """unipin_block_ctx_tune: time the candidate GEMM kernels (the library's own in each
+        tile size, hipBLASLt's) for the block at B users x rows rows and keep the fastest
+        (blocks until done)."""
         dev = pool.k.device
         if workspace is None:
             workspace = torch.empty(block_workspace_bytes(pool, B, rows), dtype=torch.uint8, device=dev)

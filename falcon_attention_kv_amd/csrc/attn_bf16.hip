@@ -49,20 +49,10 @@
 
 #include "attn_launch.h"
 #include "e4m3.h"
+#include "lds_dma.h"
 
 namespace unipin {
 namespace {
-
-#define LDS_AS __attribute__((address_space(3)))
-
-typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTK = 64;                   // keys per LDS tile
 // LDS slots of the DMA ring (one 64-key K/V tile or 128 query rows each): 64 KB per
@@ -84,9 +74,6 @@ template <int D> constexpr int block_waves() { return kBlockRows / wave_rows<D>(
 // Minimum waves per SIMD the kernels are compiled for (the second __launch_bounds__
 // argument).
 template <int D> constexpr int min_waves_per_simd() { return D <= 64 ? 4 : 2; }
-
-
-constexpr uint32_t kBufferWord3 = 0x00020000u;   // gfx9 buffer descriptor, raw 32-bit access
 
 
 template <int D>
@@ -121,52 +108,6 @@ template <int D>
 __device__ __forceinline__ int v_swz(int key) {
     constexpr int R = Tile<D>::R;
     return R >= 16 ? ((key & 3) << 2) : R == 8 ? (((key >> 1) & 1) << 2) : 0;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, (int)kBufferWord3);
-}
-
-// Buffer descriptor as four scalar words, for the DMA issued from inline assembly.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
-    const uint64_t addr = reinterpret_cast<uint64_t>(base);
-    return i32x4{(int)(uint32_t)addr, (int)((uint32_t)(addr >> 32) & 0xffffu), (int)bytes, (int)kBufferWord3};
-}
-
-// One 16-byte-per-lane buffer-to-LDS DMA: lane l writes LDS bytes [lds + 16 l, +16) from
-// buffer offset voff + soff (zeros past the record count).  It is issued from inline
-// assembly so that the compiler does not treat it as a pending write to every LDS
-// address (which makes it wait for all outstanding DMA before each LDS read and defeats
-// the prefetch); the kernels wait for it explicitly (vmcnt, then a workgroup barrier).
-// The instruction has no register results and reads its operands at issue.  It takes
-// its LDS address from M0, and a scalar write of M0 needs one wait state before an LDS
-// DMA reads it; the compiler cannot see that hazard inside the assembly (it sets M0 in
-// the instruction just before), so the s_nop is part of the statement.
-__device__ __forceinline__ void dma16(uint32_t lds, i32x4 rsrc, int voff, int soff) {
-    // the descriptor, the scalar offset and M0 are wave-uniform by construction
-    soff = __builtin_amdgcn_readfirstlane(soff);
-    lds = __builtin_amdgcn_readfirstlane(lds);
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
-                 "{m0}"(lds)
-                 : "memory");
-}
-
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-}
-
-__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
 // Value exchange with the lane 32 away (v_permlane32_swap: no LDS round trip).  r[0]

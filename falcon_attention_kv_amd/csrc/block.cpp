@@ -3,10 +3,12 @@
 // K/V stored in the pool) or as the ranking stage's candidate-only forward (attention
 // to the pool's history plus the candidate's own key).
 //
-// The four projections are plain bf16 GEMMs with fp32 accumulation and go to hipBLASLt,
-// with its epilogues doing the bias, the tanh-form GELU and (through beta = 1 on the
-// hidden state itself) the residual adds.  LayerNorm is this library's kernel
-// (block_kernels.hip), and the attention is the library's own prefill and rank-decode
+// The four projections are bf16 GEMMs with fp32 accumulation and fused epilogues (bias,
+// tanh-form GELU, residual add into the hidden state).  They run on hipBLASLt (its
+// epilogues, beta = 1 on the hidden state for the residual) or on this library's MFMA
+// kernel (gemm_bf16.hip, three workgroup tile sizes), whichever the tuner timed fastest
+// for the shape; untuned, on hipBLASLt's first heuristic choice.  LayerNorm is this library's
+// kernel (block_kernels.hip), and the attention is the library's own prefill and rank-decode
 // kernels, which read q, k and v straight from the fused projection's rows
 // [B, rows, 3, H, D] and write the heads' outputs straight into the merged rows
 // [B, rows, H, D] that the output projection reads.  Host code here allocates nothing on
@@ -44,6 +46,7 @@ struct GemmPlan {
     hipblasLtMatmulDesc_t desc = nullptr;
     hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
     hipblasLtMatmulAlgo_t algo{};
+    int own = -1;   // >= 0: this library's kernel with that tile configuration; -1: hipBLASLt
 };
 
 using PlanKey = std::tuple<long, int, int, int, bool>;   // M, N, K, epilogue, residual
@@ -53,6 +56,7 @@ using PlanKey = std::tuple<long, int, int, int, bool>;   // M, N, K, epilogue, r
 struct unipin_block_ctx {
     hipblasLtHandle_t handle = nullptr;
     int device = -1;
+    int kernel = UNIPIN_GEMM_AUTO;       // unipin_block_ctx_set_gemm
     std::mutex mu;                       // plans and their descriptors are shared by calls
     std::map<PlanKey, GemmPlan> plans;
 };
@@ -66,13 +70,20 @@ void destroy_plan(GemmPlan &p) {
     if (p.desc) hipblasLtMatmulDescDestroy(p.desc);
 }
 
-// The plan for one GEMM shape and epilogue, made on first use (descriptors and the
-// library's first heuristic choice).  Called with ctx->mu held.
+// This library's GEMM epilogue for a hipBLASLt one.
+int own_epilogue(hipblasLtEpilogue_t ep, bool residual) {
+    if (ep == HIPBLASLT_EPILOGUE_GELU_BIAS) return unipin::kGemmBiasGelu;
+    return residual ? unipin::kGemmBiasResidual : unipin::kGemmBias;
+}
+
+// The plan for one GEMM shape and epilogue, made on first use (descriptors, the
+// library's first heuristic choice and the kernel selection).  Called with ctx->mu held.
 GemmPlan *plan_for(unipin_block_ctx *ctx, long M, int N, int K, hipblasLtEpilogue_t ep, bool residual) {
     const PlanKey key{M, N, K, (int)ep, residual};
     auto it = ctx->plans.find(key);
     if (it != ctx->plans.end()) return &it->second;
     GemmPlan p;
+    if (ctx->kernel >= 0 && unipin::gemm_bf16_supported(M, N, K)) p.own = ctx->kernel;
     const hipblasOperation_t op = HIPBLAS_OP_N;
     const hipDataType bias_type = HIP_R_16BF;
     hipblasLtMatmulPreference_t pref = nullptr;
@@ -103,18 +114,29 @@ GemmPlan *plan_for(unipin_block_ctx *ctx, long M, int N, int K, hipblasLtEpilogu
     return &ctx->plans.emplace(key, p).first->second;
 }
 
-// out = in @ W + bias (then GELU, with ep = GELU_BIAS); residual: out += the old out.
-int gemm(unipin_block_ctx *ctx, const void *in, const void *W, const void *bias, void *out, long M, int N, int K,
-         hipblasLtEpilogue_t ep, bool residual, void *ws, hipStream_t stream) {
-    std::lock_guard<std::mutex> lock(ctx->mu);
-    GemmPlan *p = plan_for(ctx, M, N, K, ep, residual);
-    if (!p) return UNIPIN_EHIP;
+// One run of a planned GEMM: out = in @ W + bias (then GELU, with ep = GELU_BIAS);
+// residual: out += the old out.  Called with ctx->mu held.
+int run_plan(unipin_block_ctx *ctx, GemmPlan *p, const void *in, const void *W, const void *bias, void *out, long M,
+             int N, int K, hipblasLtEpilogue_t ep, bool residual, void *ws, hipStream_t stream) {
+    if (p->own >= 0)
+        return unipin::launch_gemm_bf16(in, W, bias, out, M, N, K, own_epilogue(ep, residual), p->own, stream) ==
+                       hipSuccess
+                   ? UNIPIN_OK
+                   : UNIPIN_EHIP;
     if (hipblasLtMatmulDescSetAttribute(p->desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof(bias)) != 0)
         return UNIPIN_EHIP;
     const float alpha = 1.f, beta = residual ? 1.f : 0.f;
     const hipblasStatus_t s = hipblasLtMatmul(ctx->handle, p->desc, &alpha, W, p->la, in, p->lb, &beta, out, p->lc,
                                               out, p->lc, &p->algo, ws, kGemmWorkspace, stream);
     return s == HIPBLAS_STATUS_SUCCESS ? UNIPIN_OK : UNIPIN_EHIP;
+}
+
+int gemm(unipin_block_ctx *ctx, const void *in, const void *W, const void *bias, void *out, long M, int N, int K,
+         hipblasLtEpilogue_t ep, bool residual, void *ws, hipStream_t stream) {
+    std::lock_guard<std::mutex> lock(ctx->mu);
+    GemmPlan *p = plan_for(ctx, M, N, K, ep, residual);
+    if (!p) return UNIPIN_EHIP;
+    return run_plan(ctx, p, in, W, bias, out, M, N, K, ep, residual, ws, stream);
 }
 
 // Workspace layout for M = B * rows hidden rows of width C (bytes, 256-aligned):
@@ -185,6 +207,15 @@ int unipin_block_ctx_destroy(unipin_block_ctx_t *ctx) {
     return UNIPIN_OK;
 }
 
+int unipin_block_ctx_set_gemm(unipin_block_ctx_t *ctx, int kernel) {
+    if (!ctx || kernel < UNIPIN_GEMM_AUTO || kernel >= unipin::kGemmConfigs) return UNIPIN_EINVAL;
+    std::lock_guard<std::mutex> lock(ctx->mu);
+    for (auto &kv : ctx->plans) destroy_plan(kv.second);
+    ctx->plans.clear();
+    ctx->kernel = kernel;
+    return UNIPIN_OK;
+}
+
 size_t unipin_block_workspace_bytes(const unipin_pool_t *pool, int B, int rows) {
     int L, S, H, n_max, D, dt;
     if (!pool || B < 1 || rows < 1 || unipin_pool_dims(pool, &L, &S, &H, &n_max, &D, &dt) != UNIPIN_OK) return 0;
@@ -233,8 +264,20 @@ int unipin_block_ctx_tune(unipin_block_ctx_t *ctx, const unipin_pool_t *pool, in
             rc = UNIPIN_EHIP;
             break;
         }
-        // candidates: the library's heuristic choices, then every kernel it has for a
-        // bf16 GEMM that accepts this problem (shape, layouts, epilogue) within the workspace
+        // candidates: this library's kernel in each tile configuration, hipBLASLt's
+        // heuristic choices, then every kernel hipBLASLt has for a bf16 GEMM that accepts
+        // this problem (shape, layouts, epilogue) within the workspace; restricted to one
+        // kernel or to hipBLASLt by unipin_block_ctx_set_gemm
+        struct Cand {
+            int own;
+            hipblasLtMatmulAlgo_t algo;
+        };
+        std::vector<Cand> cands;
+        const bool own_ok = unipin::gemm_bf16_supported(M, g[i].N, g[i].K);
+        if (own_ok && ctx->kernel >= 0) cands.push_back({ctx->kernel, {}});
+        if (own_ok && ctx->kernel == UNIPIN_GEMM_AUTO)
+            for (int c = 0; c < unipin::kGemmConfigs; ++c) cands.push_back({c, {}});
+        const bool lib = ctx->kernel == UNIPIN_GEMM_LIBRARY || (ctx->kernel == UNIPIN_GEMM_AUTO) || !own_ok;
         hipblasLtMatmulPreference_t pref = nullptr;
         const uint64_t wsz = kGemmWorkspace;
         constexpr int kHeuristic = 32;
@@ -251,11 +294,10 @@ int unipin_block_ctx_tune(unipin_block_ctx_t *ctx, const unipin_pool_t *pool, in
             break;
         }
         hipblasLtMatmulPreferenceDestroy(pref);
-        std::vector<hipblasLtMatmulAlgo_t> cands;
-        for (int a = 0; a < found; ++a)
+        for (int a = 0; lib && a < found; ++a)
             if (heur[a].state == HIPBLAS_STATUS_SUCCESS && heur[a].workspaceSize <= kGemmWorkspace)
-                cands.push_back(heur[a].algo);
-        {
+                cands.push_back({-1, heur[a].algo});
+        if (lib) {
             const float al = 1.f, be = g[i].residual ? 1.f : 0.f;
             std::vector<hipblasLtMatmulHeuristicResult_t> all;
             if (hipblaslt_ext::getAllAlgos(ctx->handle, hipblaslt_ext::GemmType::HIPBLASLT_GEMM, HIPBLAS_OP_N,
@@ -267,24 +309,26 @@ int unipin_block_ctx_tune(unipin_block_ctx_t *ctx, const unipin_pool_t *pool, in
                     if (hipblaslt_ext::matmulIsAlgoSupported(ctx->handle, p->desc, &al, p->la, p->lb, &be, p->lc,
                                                              p->lc, r.algo, need) == HIPBLAS_STATUS_SUCCESS &&
                         need <= kGemmWorkspace)
-                        cands.push_back(r.algo);
+                        cands.push_back({-1, r.algo});
                 }
             }
         }
-        const float alpha = 1.f, beta = g[i].residual ? 1.f : 0.f;
         float best = 1e30f;
-        for (auto &algo : cands) {
+        GemmPlan trial = *p;
+        for (auto &c : cands) {
+            trial.own = c.own;
+            trial.algo = c.algo;
             auto run = [&]() {
-                return hipblasLtMatmul(ctx->handle, p->desc, &alpha, W, p->la, in_of[i], p->lb, &beta, out_of[i],
-                                       p->lc, out_of[i], p->lc, &algo, ws + lo.gemm, kGemmWorkspace, st);
+                return run_plan(ctx, &trial, in_of[i], W, bias, out_of[i], M, g[i].N, g[i].K, g[i].ep, g[i].residual,
+                                ws + lo.gemm, st);
             };
-            if (run() != HIPBLAS_STATUS_SUCCESS || run() != HIPBLAS_STATUS_SUCCESS) continue;
+            if (run() != UNIPIN_OK || run() != UNIPIN_OK) continue;
             if (hipEventRecord(e0, st) != hipSuccess) {
                 rc = UNIPIN_EHIP;
                 break;
             }
             bool ok = true;
-            for (int r = 0; r < 5 && ok; ++r) ok = run() == HIPBLAS_STATUS_SUCCESS;
+            for (int r = 0; r < 5 && ok; ++r) ok = run() == UNIPIN_OK;
             float ms = 0.f;
             if (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
                 hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
@@ -293,7 +337,8 @@ int unipin_block_ctx_tune(unipin_block_ctx_t *ctx, const unipin_pool_t *pool, in
             }
             if (ok && ms < best) {
                 best = ms;
-                p->algo = algo;
+                p->own = c.own;
+                p->algo = c.algo;
             }
             // the residual GEMMs add into their output each run; start the next from
             // the same values as the first so that no candidate sees overflowing data

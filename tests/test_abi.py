@@ -247,6 +247,7 @@ def test_block_host_checks():
     assert args(None, ctypes.byref(w)) == fa.EINVAL          # no context
     assert lib.unipin_block_ctx_destroy(None) == fa.EINVAL
     assert lib.unipin_block_ctx_create(None) == fa.EINVAL
+    assert lib.unipin_block_ctx_set_gemm(None, fa.GEMM_AUTO) == fa.EINVAL
     lib.unipin_pool_destroy(h)
 
 

@@ -57,16 +57,23 @@ def make(B, n, K, H, D, L=2, S=None, seed=0):
 SHAPES = [(3, 70, 33, 4, 32), (2, 130, 65, 8, 64), (2, 64, 20, 2, 128)]
 
 
+# the block's GEMMs: hipBLASLt, or the library's kernel with each workgroup tile
+GEMM_KERNELS = [fa.GEMM_LIBRARY, 0, 1, 2]
+
+
+@pytest.mark.parametrize("gemm", GEMM_KERNELS, ids=lambda k: "hipblaslt" if k == fa.GEMM_LIBRARY else f"tile{k}")
 @pytest.mark.parametrize("B,n,K,H,D", SHAPES, ids=lambda x: str(x))
-def test_block_history_then_candidates(B, n, K, H, D):
+def test_block_history_then_candidates(B, n, K, H, D, gemm):
     """History forward (fills the pool), then the candidate-only forward, against the
-    oracle's two forwards and its joint pass; the pool rows against the oracle's."""
-    announce(f"block history+candidates B={B} n={n} K={K} H={H} D={D}")
+    oracle's two forwards and its joint pass; the pool rows against the oracle's.  Every
+    shape is run with each GEMM kernel (rows B*n and B*K leave ragged row tiles)."""
+    announce(f"block history+candidates B={B} n={n} K={K} H={H} D={D} gemm={gemm}")
     w, xh, xc, pool = make(B, n, K, H, D, seed=50)
     lens = [n, n // 2, 0][:B]
     slots = [B - 1 - b for b in range(B)]
     layer = 1
     ctx = fa.BlockContext()
+    ctx.set_gemm(gemm)
     xh0, xc0 = xh.clone(), xc.clone()
     fa.block_forward(ctx, w, fa.BLOCK_HISTORY, xh, pool, slots, lens, layer)
     fa.block_forward(ctx, w, fa.BLOCK_CANDIDATES, xc, pool, slots, lens, layer)
