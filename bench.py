@@ -42,7 +42,9 @@ sys.path.insert(0, ROOT)
 METRIC = "ranked candidates/sec + TFLOP/s (frac of MFMA/HBM roofline), 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published (no sparsity)
-KERNEL_SRC = os.path.join(ROOT, "falcon_attention_kv_amd", "csrc", "attn_bf16.hip")
+# the sources compiled into the bf16 attention kernels (the counters' validity check)
+KERNEL_SRC = [os.path.join(ROOT, "falcon_attention_kv_amd", "csrc", f)
+              for f in ("attn_bf16.hip", "lds_dma.h", "e4m3.h", "attn_launch.h")]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "rank_decode_serving_shape_pmc.txt")
 
 
@@ -297,8 +299,11 @@ def copy_calibration(torch, dev, mib: int) -> int:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
