@@ -349,9 +349,20 @@ def cpu_baseline(w, layers_cpu, lens, budget_s):
         units += 1
     per_unit = t_total / units
     step_s = per_unit * w.L * w.B * w.H
+    # algorithmic FLOPs of one (layer, user, head) unit: prefill N(N+1)/2 pairs, decode
+    # k(N+1) pairs, 4D FLOPs each (all lens are equal at this shape)
+    N = lens[0]
+    unit_flop = 4 * w.D * (N * (N + 1) // 2 + w.k * (N + 1))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
     return {"value": w.B * w.k / step_s, "unit": "candidates/s", "cores": threads, "kind": "oracle",
             "sample": f"{units} (layer, user, head) units of prefill + rank decode "
-                      f"(float64 numpy, {t_total:.1f} s), scaled x{w.L * w.B * w.H} to one step"}
+                      f"(float64 numpy, {t_total:.1f} s), scaled x{w.L * w.B * w.H} to one step",
+            "algorithmic_gflops": round(unit_flop / per_unit / 1e9, 2), "cpu_model": model}
 
 
 def main():
@@ -416,8 +427,15 @@ def main():
     if fa.device_status(dev) != 0:
         raise RuntimeError("a kernel flagged an invalid slot or length")
 
-    pf_avg = sum(ev[0].elapsed_time(ev[1]) for ev in all_events) / (args.steps * w.L)
-    dc_avg = sum(ev[1].elapsed_time(ev[2]) for ev in all_events) / (args.steps * w.L)
+    pf_per_step = sorted(ev[0].elapsed_time(ev[1]) / w.L for ev in all_events)
+    dc_per_step = sorted(ev[1].elapsed_time(ev[2]) / w.L for ev in all_events)
+    pf_avg = sum(pf_per_step) / args.steps
+    dc_avg = sum(dc_per_step) / args.steps
+
+    def spread(xs):
+        # per-launch time of the steps (each step's span / its 12 launches): median, p10, p90
+        q = lambda f: xs[min(len(xs) - 1, int(round(f * (len(xs) - 1))))]
+        return {"median_ms": round(q(0.5), 5), "p10_ms": round(q(0.1), 5), "p90_ms": round(q(0.9), 5)}
 
     pflop, pbytes, dflop, dbytes = algorithmic(w, lens)
     ms_per_step = wall * 1e3 / args.steps
@@ -450,11 +468,13 @@ def main():
                      "algorithmic_bytes_per_launch": dbytes,
                      "avg_launch_ms": round(dc_avg, 5)},
         "kernels": {
-            "prefill": {"avg_ms": round(pf_avg, 5), "tflops": round(pflop / (pf_avg / 1e3) / 1e12, 2),
+            "prefill": {"avg_ms": round(pf_avg, 5), "per_step": spread(pf_per_step),
+                        "tflops": round(pflop / (pf_avg / 1e3) / 1e12, 2),
                         "gbs": round(pbytes / (pf_avg / 1e3) / 1e9, 1),
                         "hbm_frac": round(pbytes / (pf_avg / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                         "mfma_frac": round(pflop / (pf_avg / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
-            "rank_decode": {"avg_ms": round(dc_avg, 5), "tflops": round(dflop / (dc_avg / 1e3) / 1e12, 2),
+            "rank_decode": {"avg_ms": round(dc_avg, 5), "per_step": spread(dc_per_step),
+                            "tflops": round(dflop / (dc_avg / 1e3) / 1e12, 2),
                             "gbs": round(dc_gbs, 1), "hbm_frac": round(dc_gbs / HBM_PEAK_GBS, 4),
                             "mfma_frac": round(dflop / (dc_avg / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                             "decode_candidates_per_s": round(cand_per_step / (w.L * dc_avg / 1e3), 1)},

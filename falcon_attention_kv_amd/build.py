@@ -19,7 +19,8 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libunipin.so")
 SOURCES = ["unipin.cpp", "device_status.hip", "attn_bf16.hip", "attn_fp32.hip", "attn_ar.hip",
            "block.cpp", "block_kernels.hip", "gemm_bf16.hip"]
-# hipBLASLt runs the block's plain GEMMs; found at run time through the ROCm library path
+# hipBLASLt is one of the two GEMM kernel families of the block; found at run time through
+# the ROCm library path
 LINK = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 ARCH = "gfx950"
 
