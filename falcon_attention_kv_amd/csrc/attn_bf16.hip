@@ -672,8 +672,8 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
 // E4M3 K/V tiles.  A tile of codes (K: kTK rows of D bytes, then V) is DMA'd as it is,
 // 1 KB per wave-wide piece in plain row order, into a staging area; the workgroup then
 // decodes it into the bf16 tile layout (rows of 16-byte blocks at the K and V
-// swizzles) that the tile step reads.  An E4M3 value is exact in bf16, and its fp32
-// form has 16 zero low bits, so the bf16 bits are its fp32 bits shifted down.
+// swizzles) that the tile step reads.  An E4M3 value is exact in bf16: one conversion
+// instruction turns two codes into two bf16 values.
 template <int D, int W>
 struct F8Tile {
     static constexpr int MAT = kTK * D;                 // bytes of one staged matrix
@@ -708,14 +708,8 @@ __device__ __forceinline__ void decode_tile8(const LDS_AS char *stage, LDS_AS ch
         const int i = i0 + tid;
         const int mat = i / (kTK * T::R), key = (i / T::R) % kTK, blk = i % T::R;
         const u32x2 raw = *reinterpret_cast<const LDS_AS u32x2 *>(stage + mat * F::MAT + key * D + blk * 8);
-        u32x4 out;
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-            float f[4];
-            e4m3x4_to_f32(raw[w], f);
-            out[2 * w] = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
-            out[2 * w + 1] = (__float_as_uint(f[2]) >> 16) | (__float_as_uint(f[3]) & 0xffff0000u);
-        }
+        const u32x2 a = e4m3x4_to_bf16x4(raw[0]), b = e4m3x4_to_bf16x4(raw[1]);
+        const u32x4 out = {a[0], a[1], b[0], b[1]};
         const int swz = mat ? v_swz<D>(key) : k_swz<D>(key);
         *reinterpret_cast<LDS_AS u32x4 *>(tile + mat * T::MAT_BYTES + key * T::ROW_BYTES + (blk ^ swz) * 16) = out;
     }

@@ -48,4 +48,15 @@ __device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float (&f)[4]) {
     f[3] = hi[1];
 }
 
+// The four E4M3 codes of a 32-bit word (byte 0 first) as four bf16 values in two 32-bit
+// words, element order kept; exact, since every E4M3 value is a bf16 value.  One gfx950
+// instruction per pair (the scaled conversion, with scale 1), which reads the OCP E4M3
+// format like the fp32 one.
+__device__ __forceinline__ e4m3_u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+    typedef __bf16 pair_t __attribute__((ext_vector_type(2)));
+    const pair_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const pair_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    return e4m3_u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
 }  // namespace unipin
