@@ -176,31 +176,45 @@ __global__ void __launch_bounds__(gemm_threads<WM>(), WPS)
     // then stores them as whole 16-byte pieces of rows.
     __syncthreads();   // every wave is done with the ring
     LDS_AS char *stg = smem + wave * G::STAGE_OUT;
+    // The epilogue's global loads go out together, one round trip per column block: the
+    // bias of the wave's columns, and for the residual the old outputs (a row past M
+    // reads row M-1 instead, and its result is never stored).
+    bf16x4 bv[2][4];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            bv[nb][jj] = *reinterpret_cast<const bf16x4 *>(bias + n0 + (wn * 2 + nb) * 32 + 8 * jj + 4 * g);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        bf16x4 rv[4][MB];
+        if (EPI == kGemmBiasResidual) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const int m = min(m0 + wm * 32 * MB + mb * 32 + col, M - 1);
+                    rv[jj][mb] = *reinterpret_cast<const bf16x4 *>(y + (long)m * N + n0 + (wn * 2 + nb) * 32 + 8 * jj +
+                                                                   4 * g);
+                }
+        }
+#pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const int n = n0 + (wn * 2 + nb) * 32 + 8 * jj + 4 * g;
-            const bf16x4 bv = *reinterpret_cast<const bf16x4 *>(bias + n);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int r = mb * 32 + col;
-                const int m = m0 + wm * 32 * MB + r;
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    v[e] = acc[nb][mb][4 * jj + e] + (float)bv[e];
+                    v[e] = acc[nb][mb][4 * jj + e] + (float)bv[nb][jj][e];
                     if (EPI == kGemmBiasGelu) v[e] = gelu_tanh(v[e]);
-                }
-                if (EPI == kGemmBiasResidual && m < M) {
-                    const bf16x4 rv = *reinterpret_cast<const bf16x4 *>(y + (long)m * N + n);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] += (float)rv[e];
+                    if (EPI == kGemmBiasResidual) v[e] += (float)rv[jj][mb][e];
                 }
                 const bf16x4 o = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};   // round to nearest even
                 *reinterpret_cast<LDS_AS bf16x4 *>(stg + r * 128 + (((nb * 4 + jj) ^ (r & 7)) * 16) + g * 8) = o;
             }
         }
+    }
     asm volatile("" ::: "memory");   // a wave's LDS operations run in order: the reads see the writes
 #pragma unroll
     for (int i = lane; i < 32 * MB * 8; i += 64) {
