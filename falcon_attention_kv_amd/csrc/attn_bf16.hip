@@ -737,9 +737,6 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
     block_coords<false>(a, group, ctile);
     const int b = group / a.H, h = group % a.H;
     if (b >= a.B) return;
-    const int N = lens[b];
-    const int s = slots[b];
-    if (!user_valid(a, N, s, ctile == 0)) return;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -751,6 +748,20 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
     const long in_off = (long)b * a.in_bstride + (long)h * a.in_hstride;
     const int in_rs = a.in_rstride * (int)sizeof(bf16);   // bytes between candidate rows
     const uint32_t rows_bytes = (uint32_t)a.rows * in_rs;
+    // The candidates' q and own keys do not depend on the user's slot or history length:
+    // their DMA goes out before those are read, so the two loads overlap.  A user with an
+    // invalid slot or length waits for that DMA before it leaves (no LDS write may
+    // outlive the workgroup).
+    dma_rows<D, W, kBlockRows>(smem, rsrc_words(static_cast<const bf16 *>(a.q) + in_off, rows_bytes), row0, wave,
+                               lane, in_rs);
+    dma_rows<D, W, kBlockRows>(smem + 2 * T::BUF_BYTES, rsrc_words(static_cast<const bf16 *>(a.k) + in_off, rows_bytes),
+                               row0, wave, lane, in_rs);
+    const int N = lens[b];
+    const int s = slots[b];
+    if (!user_valid(a, N, s, ctile == 0)) {
+        wait_vmcnt<0>();
+        return;
+    }
     const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;   // in elements
     constexpr int PROW = P8 ? D : T::ROW_BYTES;                      // bytes of one pool row
     const i32x4 rsrc = rsrc_words(static_cast<const char *>(wave < W / 2 ? a.pool_k : a.pool_v) + slot_off * (PROW / D),
@@ -763,10 +774,6 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
     const int nsteps = ntiles + 2;
     const int wrows = wave * wave_rows<D>() * T::ROW_BYTES;   // this wave's rows inside a staged block
 
-    dma_rows<D, W, kBlockRows>(smem, rsrc_words(static_cast<const bf16 *>(a.q) + in_off, rows_bytes), row0, wave,
-                               lane, in_rs);
-    dma_rows<D, W, kBlockRows>(smem + 2 * T::BUF_BYTES, rsrc_words(static_cast<const bf16 *>(a.k) + in_off, rows_bytes),
-                               row0, wave, lane, in_rs);
     wait_vmcnt<0>();
     __syncthreads();
     WaveState<D> ws;
