@@ -349,7 +349,14 @@ __global__ void __launch_bounds__(kThreads) ar_decode_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int sub = lane % G::R, grp = lane / G::R;
     const long bh = (long)b * a.H + h;
-    const ActPiece<K> qx = load_act<K, D>(static_cast<const T *>(a.q) + bh * D, sub);   // slot-independent
+    // the token's own rows do not depend on the slot: q for every wave, and k, v for wave
+    // 0 (which merges at the end), all in the first round trip
+    const ActPiece<K> qx = load_act<K, D>(static_cast<const T *>(a.q) + bh * D, sub);
+    ActPiece<K> knew{}, vnew{};
+    if (wave == 0) {
+        knew = load_act<K, D>(static_cast<const T *>(a.k) + bh * D, sub);
+        vnew = load_act<K, D>(static_cast<const T *>(a.v) + bh * D, sub);
+    }
     const int N = a.lens[b];
     const int s = a.slot[b];
     if (invalid_user(a, b, N, s, threadIdx.x == 0 && h == 0)) return;
@@ -366,8 +373,6 @@ __global__ void __launch_bounds__(kThreads) ar_decode_kernel(AttnArgs a) {
     __syncthreads();
     if (wave != 0) return;
 
-    const ActPiece<K> knew = load_act<K, D>(static_cast<const T *>(a.k) + bh * D, sub);
-    const ActPiece<K> vnew = load_act<K, D>(static_cast<const T *>(a.v) + bh * D, sub);
     const float snew = lowsum<G::R>(dot_act<K>(qx, knew)) * a.c;
     float mt = snew;
 #pragma unroll
