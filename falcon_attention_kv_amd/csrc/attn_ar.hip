@@ -454,8 +454,8 @@ __global__ void __launch_bounds__(kThreads) ar_split_kernel(AttnArgs a, float *w
 
 // Pass 2 of the split path: one wave per (user, head) merges the non-empty parts with
 // the new token, stores the output row and the token's K/V row.  Lane p holds part p's
-// max and sum (at most 64 parts); the accumulators are read four parts at a time so
-// that their loads overlap.
+// max and sum (at most 64 parts); the accumulators are read by the lane groups in
+// rounds of 4 RPI parts, whose loads overlap.
 template <typename K, int D>
 __global__ void __launch_bounds__(64) ar_merge_kernel(AttnArgs a, const float *ws, int P) {
     using G = Geo<K, D>;
@@ -483,24 +483,32 @@ __global__ void __launch_bounds__(64) ar_merge_kernel(AttnArgs a, const float *w
     const float mt = fmaxf(snew, xmax<1>(mp));
     const float wp = __builtin_amdgcn_exp2f(mp - mt);   // 0 past the last part
     const float lt = xsum<1>(wp * lp);
+    // The parts' accumulators are spread over the wave's RPI lane groups (the lanes of a
+    // group cover one row's dims), four parts per group per round, so that up to 4 RPI
+    // parts cost one round trip; the groups' sums are added at the end.
     float out[G::PER];
 #pragma unroll
     for (int e = 0; e < G::PER; ++e) out[e] = 0.f;
-    for (int p0 = 0; p0 < parts; p0 += 4) {
+    for (int p0 = 0; p0 < parts; p0 += 4 * G::RPI) {
         float x[4][G::PER];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float *pp = src + (long)min(p0 + j, parts - 1) * SD + sub * G::PER;
+            const int pi = p0 + j * G::RPI + grp;
+            const float *pp = src + (long)min(pi, parts - 1) * SD + sub * G::PER;
 #pragma unroll
             for (int e = 0; e < G::PER; ++e) x[j][e] = pp[e];
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float w = p0 + j < parts ? __shfl(wp, p0 + j) : 0.f;
+            const int pi = p0 + j * G::RPI + grp;
+            const float w = __shfl(wp, min(pi, 63));   // part pi's weight sits in lane pi
+            const float wv = pi < parts ? w : 0.f;
 #pragma unroll
-            for (int e = 0; e < G::PER; ++e) out[e] = __builtin_fmaf(w, x[j][e], out[e]);
+            for (int e = 0; e < G::PER; ++e) out[e] = __builtin_fmaf(wv, x[j][e], out[e]);
         }
     }
+#pragma unroll
+    for (int e = 0; e < G::PER; ++e) out[e] = xsum<G::R>(out[e]);
     if (ok) finish<K, D>(a, bh, slot_off, N, knew, vnew, __builtin_amdgcn_exp2f(snew - mt), lt, out, sub, grp);
 }
 
