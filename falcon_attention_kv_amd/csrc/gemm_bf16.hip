@@ -12,8 +12,11 @@
 //     layout and ds_read_b64_tr_b16 delivers W^T as the A operand;
 //   * the epilogue adds the bias and applies the tanh-form GELU or adds the residual (the
 //     output's old value) in fp32, rounds once to bf16 and stores whole rows through LDS;
-//   * workgroup b runs on XCD b % 8, and the column tiles of one row tile are given to
-//     consecutive workgroups of one XCD, so that they share its L2 copy of the X rows.
+//   * workgroup b runs on XCD b % 8.  The column tiles of one row tile go to consecutive
+//     workgroups of one XCD, so that they share its L2 copy of the X rows, for the first
+//     8 floor(mtiles / 8) row tiles; the workgroups of the rest are spread over all XCDs,
+//     so that no XCD holds a whole extra row tile (with 64 workgroup slots per XCD, one
+//     row tile too many can cost a second round).
 //
 // The contraction index of an MFMA is spread over (lane / 32, element) the same way in
 // A and B: a lane of half g holds k = 8g .. 8g + 7 of its 16-deep chunk.  The X read
@@ -83,8 +86,17 @@ __global__ void __launch_bounds__(gemm_threads<WM>(), WPS)
     LDS_AS char *smem = (LDS_AS char *)smem_raw;
 
     const int ntn = N / kBN;
-    const int bid = blockIdx.x, j = bid >> 3;
-    const int mt = (bid & 7) + 8 * (j / ntn), nt = j % ntn;
+    const int bid = blockIdx.x, xcd = bid & 7, j = bid >> 3;
+    const int whole = (mtiles >> 3) * ntn;   // per XCD: workgroups of its whole row tiles
+    int mt, nt;
+    if (j < whole) {
+        mt = xcd + 8 * (j / ntn);
+        nt = j % ntn;
+    } else {
+        const int r = (j - whole) * 8 + xcd;   // the remaining row tiles' workgroups, in turn
+        mt = (mtiles & ~7) + r / ntn;
+        nt = r % ntn;
+    }
     if (mt >= mtiles) return;
     const int m0 = mt * G::BM, n0 = nt * kBN;
     const int tid = threadIdx.x;
@@ -230,7 +242,8 @@ hipError_t launch_cfg(const void *x, const void *w, const void *bias, void *y, i
                       hipStream_t stream) {
     using G = GemmCfg<WM, MB, NS>;
     const int mtiles = (M + G::BM - 1) / G::BM;
-    const long blocks = 8L * ((mtiles + 7) / 8) * (N / kBN);
+    const long ntn = N / kBN;
+    const long blocks = 8L * ((mtiles / 8) * ntn + ((mtiles % 8) * ntn + 7) / 8);
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks), block(G::W * 64);
     const bf16 *xs = static_cast<const bf16 *>(x), *ws = static_cast<const bf16 *>(w),
