@@ -20,11 +20,12 @@ token per user and head appended to its slot) on the serving shape and on the lo
 history shape; it is a secondary figure and does not enter `value`.
 
 `--block-only` runs only the Table 2 transformer measurement (3 timed passes).
+`--sdpa-reference` times torch's fused attention beside this library at one layer.
 `--workloads` replaces all of this with a per-kernel table over every bf16 workload
 (one layer each, cold and back to back).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ar-step] [--no-block] [--no-e4m3]
-                       [--workloads] [--block-only]
+                       [--workloads] [--block-only] [--sdpa-reference]
 """
 from __future__ import annotations
 
@@ -65,6 +66,10 @@ def parse_args():
     p.add_argument("--workloads", action="store_true",
                    help="instead of the serving step, time one layer's prefill and decode on every bf16 "
                         "workload, cold (a 512 MiB overwrite before each launch) and back to back")
+    p.add_argument("--sdpa-reference", action="store_true",
+                   help="instead of the serving step, time torch's scaled-dot-product attention (the "
+                        "platform's fused attention, the pages' own baseline) at one layer of the serving "
+                        "shape, beside this library's kernels on the same inputs")
     p.add_argument("--block-only", action="store_true",
                    help="instead of the serving step, run only the Table 2 transformer measurement "
                         "(3 timed passes after 1 warm-up; a short program for a kernel trace)")
@@ -286,6 +291,53 @@ def workload_kernels(fa, W, torch, dev, launches: int = 10, warmup: int = 3):
     return res
 
 
+def sdpa_reference(fa, W, torch, dev, launches: int = 20):
+    """One layer of the serving shape through torch's scaled-dot-product attention (ROCm's
+    fused attention kernels) and through this library, back to back on the same inputs:
+    the decode-shaped product (1000 queries over the 512 history keys, without the
+    candidate's own key) and the causal prefill over 512 rows (without the pool write)."""
+    import torch.nn.functional as F
+    w = W.WORKLOADS[3]
+    x = W.layer_inputs(w, 0, dev)
+    lens = W.history_lengths(w).tolist()
+    lens_d = torch.as_tensor(lens, dtype=torch.int32, device=dev)
+    pool = fa.Pool.allocate(1, w.S, w.H, w.n, w.D, w.dtype, dev)
+    slots = torch.tensor(pool.acquire_many(w.B), dtype=torch.int32, device=dev)
+    fa.prefill(x["q"], x["k"], x["v"], lens_d, pool, slots, 0)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / launches
+
+    pf, _, df, _ = algorithmic(w, lens)
+    res = {}
+    for name, backend in (("flash", torch.nn.attention.SDPBackend.FLASH_ATTENTION),
+                          ("efficient", torch.nn.attention.SDPBackend.EFFICIENT_ATTENTION)):
+        try:
+            with torch.nn.attention.sdpa_kernel(backend):
+                d_ms = timed(lambda: F.scaled_dot_product_attention(x["qc"], x["k"], x["v"]))
+                p_ms = timed(lambda: F.scaled_dot_product_attention(x["q"], x["k"], x["v"], is_causal=True))
+            res["torch_sdpa_" + name] = {"decode_shaped_ms": round(d_ms, 5), "causal_prefill_ms": round(p_ms, 5)}
+        except RuntimeError as e:  # a backend the build does not have
+            res["torch_sdpa_" + name] = {"unavailable": str(e)[:200]}
+    d_ms = timed(lambda: fa.rank_decode(x["qc"], x["kc"], x["vc"], pool, slots, lens_d, 0))
+    p_ms = timed(lambda: fa.prefill(x["q"], x["k"], x["v"], lens_d, pool, slots, 0))
+    res["this_library"] = {"rank_decode_ms": round(d_ms, 5), "prefill_ms": round(p_ms, 5),
+                           "rank_decode_tflops": round(df / (d_ms / 1e3) / 1e12, 1),
+                           "prefill_tflops": round(pf / (p_ms / 1e3) / 1e12, 1)}
+    res["note"] = ("one layer of the serving shape, warm (the same inputs back to back); torch's "
+                   "decode-shaped call omits the candidate's own key and its prefill the pool write")
+    pool.close()
+    return res
+
+
 def copy_calibration(torch, dev, mib: int) -> int:
     """Three plain device copies of `mib` MiB: a known-size reference for the HBM byte
     counters of a profiler run.  Returns the bytes one copy reads."""
@@ -379,6 +431,9 @@ def main():
     w = W.WORKLOADS[3]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sdpa_reference:
+        print(json.dumps({"sdpa_reference": sdpa_reference(fa, W, torch, dev)}), flush=True)
+        return
     if args.block_only:
         print(json.dumps({"block_table2": block_table2(fa, W, torch, dev, steps=3, warmup=1)}), flush=True)
         return
