@@ -295,7 +295,9 @@ def sdpa_reference(fa, W, torch, dev, launches: int = 20):
     """One layer of the serving shape through torch's scaled-dot-product attention (ROCm's
     fused attention kernels) and through this library, back to back on the same inputs:
     the decode-shaped product (1000 queries over the 512 history keys, without the
-    candidate's own key) and the causal prefill over 512 rows (without the pool write)."""
+    candidate's own key), the causal prefill over 512 rows (without the pool write) and
+    one new token per user and head over the 512 rows (without its own key and the
+    append)."""
     import torch.nn.functional as F
     w = W.WORKLOADS[3]
     x = W.layer_inputs(w, 0, dev)
@@ -317,6 +319,11 @@ def sdpa_reference(fa, W, torch, dev, launches: int = 20):
         return e0.elapsed_time(e1) / launches
 
     pf, _, df, _ = algorithmic(w, lens)
+    q1, k1, v1 = (x[n][:, :, :1].contiguous() for n in ("qc", "kc", "vc"))   # one new token per (user, head)
+    # the library's step appends at row lens[b]: a pool one row longer, lens kept at 512
+    pool1 = fa.Pool.allocate(1, w.S, w.H, w.n + 1, w.D, w.dtype, dev)
+    slots1 = torch.tensor(pool1.acquire_many(w.B), dtype=torch.int32, device=dev)
+    fa.prefill(x["q"], x["k"], x["v"], lens_d, pool1, slots1, 0)
     res = {}
     for name, backend in (("flash", torch.nn.attention.SDPBackend.FLASH_ATTENTION),
                           ("efficient", torch.nn.attention.SDPBackend.EFFICIENT_ATTENTION)):
@@ -324,17 +331,21 @@ def sdpa_reference(fa, W, torch, dev, launches: int = 20):
             with torch.nn.attention.sdpa_kernel(backend):
                 d_ms = timed(lambda: F.scaled_dot_product_attention(x["qc"], x["k"], x["v"]))
                 p_ms = timed(lambda: F.scaled_dot_product_attention(x["q"], x["k"], x["v"], is_causal=True))
-            res["torch_sdpa_" + name] = {"decode_shaped_ms": round(d_ms, 5), "causal_prefill_ms": round(p_ms, 5)}
+                t_ms = timed(lambda: F.scaled_dot_product_attention(q1, x["k"], x["v"]))
+            res["torch_sdpa_" + name] = {"decode_shaped_ms": round(d_ms, 5), "causal_prefill_ms": round(p_ms, 5),
+                                         "one_token_ms": round(t_ms, 5)}
         except RuntimeError as e:  # a backend the build does not have
             res["torch_sdpa_" + name] = {"unavailable": str(e)[:200]}
     d_ms = timed(lambda: fa.rank_decode(x["qc"], x["kc"], x["vc"], pool, slots, lens_d, 0))
     p_ms = timed(lambda: fa.prefill(x["q"], x["k"], x["v"], lens_d, pool, slots, 0))
-    res["this_library"] = {"rank_decode_ms": round(d_ms, 5), "prefill_ms": round(p_ms, 5),
+    t_ms = timed(lambda: fa.ar_decode(q1, k1, v1, pool1, slots1, lens_d, 0))
+    res["this_library"] = {"rank_decode_ms": round(d_ms, 5), "prefill_ms": round(p_ms, 5), "ar_step_ms": round(t_ms, 5),
                            "rank_decode_tflops": round(df / (d_ms / 1e3) / 1e12, 1),
                            "prefill_tflops": round(pf / (p_ms / 1e3) / 1e12, 1)}
     res["note"] = ("one layer of the serving shape, warm (the same inputs back to back); torch's "
                    "decode-shaped call omits the candidate's own key and its prefill the pool write")
     pool.close()
+    pool1.close()
     return res
 
 
