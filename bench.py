@@ -361,6 +361,28 @@ def copy_calibration(torch, dev, mib: int) -> int:
     return n * 4
 
 
+def hbm_copy_reference(torch, dev, mib: int = 1024, launches: int = 10) -> dict:
+    """What a plain device copy reaches on this GPU: `launches` copies of `mib` MiB, timed
+    with events, (bytes read + bytes written) / time.  Context for the roofline fractions,
+    which are taken against the published 8 TB/s."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(launches):
+        dst.copy_(src)
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / launches
+    gbs = 2 * n * 4 / (ms / 1e3) / 1e9
+    del src, dst
+    return {"bytes_read_plus_written": 2 * n * 4, "avg_ms": round(ms, 4), "gbs": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for path in KERNEL_SRC:
@@ -550,6 +572,8 @@ def main():
         out["block_table2"] = block_table2(fa, W, torch, dev, steps=5, warmup=2)
     if args.copy_calib_mib:
         out["copy_calibration_bytes"] = copy_calibration(torch, dev, args.copy_calib_mib)
+    else:  # kept out of the counter runs, whose calibration picks the run's largest copies
+        out["hbm_copy_reference"] = hbm_copy_reference(torch, dev)
     if not args.no_cpu_baseline:
         layers_cpu = [{k: v.cpu() for k, v in x.items()} for x in layers]
         out["cpu_baseline"] = cpu_baseline(w, layers_cpu, lens, args.cpu_seconds)
