@@ -453,7 +453,7 @@ def cpu_baseline(w, layers_cpu, lens, budget_s):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "one process drives one GPU here; --gpus must be 1 (sharding over GPUs is a design, not code)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

@@ -31,3 +31,18 @@ def test_kernel_source_hash_covers_the_kernel_sources():
     names = {os.path.basename(p) for p in bench.KERNEL_SRC}
     assert {"attn_bf16.hip", "lds_dma.h", "e4m3.h", "attn_launch.h"} <= names
     assert len(bench.kernel_source_hash()) == 16
+
+
+def test_more_than_one_gpu_is_refused():
+    # the bench measures one GPU; asking for more ends with a message and status 2,
+    # before any device is touched
+    import json
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], cwd=root,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "--gpus must be 1" in line["error"]
