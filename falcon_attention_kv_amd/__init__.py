@@ -25,14 +25,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libunipin.so")
 
 FP32, BF16, FP8_E4M3 = 0, 1, 2
-OK, EINVAL, ERANGE, EDTYPE, EALIGN, EDEVICE, EHIP, ENOMEM = 0, -1, -2, -3, -4, -5, -6, -7
+OK, EINVAL, ERANGE, EDTYPE, EALIGN, EDEVICE, EHIP, ENOMEM, EPERM, EIO = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 FLAG_BAD_SLOT, FLAG_BAD_LEN = 1, 2
 
 # Every symbol include/unipin.h declares.
 EXPORTS = ("unipin_pool_create", "unipin_pool_destroy", "unipin_pool_acquire",
-           "unipin_pool_generation", "unipin_pool_dims", "unipin_prefill",
+           "unipin_pool_generation", "unipin_pool_dims", "unipin_pool_export",
+           "unipin_pool_import", "unipin_prefill",
            "unipin_rank_decode", "unipin_ar_decode", "unipin_ar_decode_workspace_bytes",
-           "unipin_device_status", "unipin_strerror", "unipin_version",
+           "unipin_pool_status", "unipin_strerror", "unipin_version",
            "unipin_block_ctx_create", "unipin_block_ctx_destroy", "unipin_block_workspace_bytes",
            "unipin_block_ctx_tune", "unipin_block_ctx_set_gemm", "unipin_block_forward")
 
@@ -63,8 +64,10 @@ def _load() -> ctypes.CDLL:
     lib.unipin_pool_create.argtypes = [ctypes.POINTER(vp), vp, vp, i32, i32, i32, i32, i32, i32]
     lib.unipin_pool_destroy.argtypes = [vp]
     lib.unipin_pool_acquire.argtypes = [vp, i32p, u64p]
-    lib.unipin_pool_generation.argtypes = [vp, ctypes.c_int32, u64p]
+    lib.unipin_pool_generation.argtypes = [vp, ctypes.c_int32]
     lib.unipin_pool_dims.argtypes = [vp, ip, ip, ip, ip, ip, ip]
+    lib.unipin_pool_export.argtypes = [vp, ctypes.c_char_p]
+    lib.unipin_pool_import.argtypes = [ctypes.POINTER(vp), ctypes.c_char_p]
     lib.unipin_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp]
     lib.unipin_rank_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp]
     lib.unipin_ar_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
@@ -76,13 +79,15 @@ def _load() -> ctypes.CDLL:
     lib.unipin_block_ctx_set_gemm.argtypes = [vp, i32]
     lib.unipin_block_forward.argtypes = [vp, ctypes.POINTER(BlockWeights), i32, vp, vp, vp, vp, i32, i32, i32,
                                          ctypes.c_float, vp, ctypes.c_size_t, vp]
-    lib.unipin_device_status.argtypes = [vp, ip]
+    lib.unipin_pool_status.argtypes = [vp, vp, ip]
     lib.unipin_strerror.argtypes = [i32]
     lib.unipin_strerror.restype = ctypes.c_char_p
     lib.unipin_version.argtypes = []
     for name in EXPORTS:
-        if name not in ("unipin_strerror", "unipin_ar_decode_workspace_bytes", "unipin_block_workspace_bytes"):
+        if name not in ("unipin_strerror", "unipin_ar_decode_workspace_bytes", "unipin_block_workspace_bytes",
+                        "unipin_pool_generation"):
             getattr(lib, name).restype = ctypes.c_int
+    lib.unipin_pool_generation.restype = ctypes.c_uint64
     lib.unipin_ar_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.unipin_block_workspace_bytes.restype = ctypes.c_size_t
     return lib
@@ -121,7 +126,10 @@ class Pool:
     """KV pool: K and V device tensors [L, S, H, n_max, D] plus the library descriptor.
 
     The tensors are float32, bfloat16 or float8_e4m3fn; calls on a float8_e4m3fn pool
-    take bfloat16 activations (act_dtype)."""
+    take bfloat16 activations (act_dtype).  A pool opened with Pool.import_shared has no
+    tensors here (k and v are None): its memory belongs to the process that exported it."""
+
+    _DTYPES = {FP32: torch.float32, BF16: torch.bfloat16, FP8_E4M3: torch.float8_e4m3fn}
 
     def __init__(self, k_pool: torch.Tensor, v_pool: torch.Tensor):
         if k_pool.shape != v_pool.shape or k_pool.dim() != 5:
@@ -129,21 +137,48 @@ class Pool:
         if k_pool.dtype != v_pool.dtype or not k_pool.is_contiguous() or not v_pool.is_contiguous():
             raise UnipinError(EINVAL, "pool tensors must be contiguous and of one dtype")
         self.k, self.v = k_pool, v_pool
-        self.L, self.S, self.H, self.n_max, self.D = k_pool.shape
-        self.dtype = k_pool.dtype
-        # the element type of the tensors a call takes: an E4M3 pool works on bf16
-        self.act_dtype = torch.bfloat16 if k_pool.dtype == torch.float8_e4m3fn else k_pool.dtype
+        self.device = k_pool.device
         h = ctypes.c_void_p()
+        L, S, H, n_max, D = k_pool.shape
         _check(lib.unipin_pool_create(ctypes.byref(h), k_pool.data_ptr(), v_pool.data_ptr(),
-                                      self.L, self.S, self.H, self.n_max, self.D,
-                                      _dtype_code(k_pool.dtype)), "unipin_pool_create")
+                                      L, S, H, n_max, D, _dtype_code(k_pool.dtype)), "unipin_pool_create")
         self._h = h
+        self._read_dims()
+
+    def _read_dims(self) -> None:
+        d = [ctypes.c_int() for _ in range(6)]
+        _check(lib.unipin_pool_dims(self._h, *[ctypes.byref(x) for x in d]), "unipin_pool_dims")
+        self.L, self.S, self.H, self.n_max, self.D, code = (x.value for x in d)
+        self.dtype = self._DTYPES[code]
+        # the element type of the tensors a call takes: an E4M3 pool works on bf16
+        self.act_dtype = torch.bfloat16 if self.dtype == torch.float8_e4m3fn else self.dtype
 
     @classmethod
     def allocate(cls, L, S, H, n_max, D, dtype=torch.bfloat16, device="cuda") -> "Pool":
         shape = (L, S, H, n_max, D)
         return cls(torch.empty(shape, dtype=dtype, device=device),
                    torch.empty(shape, dtype=dtype, device=device))
+
+    @classmethod
+    def import_shared(cls, path: str, device=None) -> "Pool":
+        """unipin_pool_import: a read-only view, in this process, of a pool that another
+        process exported to `path` (rank_decode only)."""
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        self = cls.__new__(cls)
+        self.k = self.v = None
+        self.device = dev
+        h = ctypes.c_void_p()
+        with torch.cuda.device(dev):
+            _check(lib.unipin_pool_import(ctypes.byref(h), os.fsencode(path)), "unipin_pool_import")
+        self._h = h
+        self._read_dims()
+        return self
+
+    def export(self, path: str) -> None:
+        """unipin_pool_export: writes the share file other processes import (IPC handles of
+        the two arrays, the shared page of the slot generations)."""
+        with torch.cuda.device(self.device):
+            _check(lib.unipin_pool_export(self.handle, os.fsencode(path)), "unipin_pool_export")
 
     @property
     def handle(self) -> ctypes.c_void_p:
@@ -161,9 +196,20 @@ class Pool:
         return [self.acquire()[0] for _ in range(count)]
 
     def generation(self, slot: int) -> int:
-        g = ctypes.c_uint64()
-        _check(lib.unipin_pool_generation(self.handle, slot, ctypes.byref(g)), "unipin_pool_generation")
-        return g.value
+        """unipin_pool_generation: hand-outs of `slot` so far (0 also for a slot outside [0, S))."""
+        return int(lib.unipin_pool_generation(self.handle, int(slot)))
+
+    def status(self, stream: Optional[torch.cuda.Stream] = None) -> int:
+        """unipin_pool_status: the sticky flags (FLAG_BAD_SLOT | FLAG_BAD_LEN) that kernels of
+        calls on this pool raised since the last call; clears them.  Synchronises `stream`
+        (default: the current stream of the pool's device)."""
+        st = stream.cuda_stream if stream is not None else _stream_handle(self.device)
+        flags = ctypes.c_int()
+        with torch.cuda.device(self.device):
+            rc = lib.unipin_pool_status(self.handle, st, ctypes.byref(flags))
+        if rc not in (OK, EDEVICE):
+            raise UnipinError(rc, "unipin_pool_status")
+        return flags.value
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None:
@@ -202,7 +248,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lens, pool: Pool,
     q, k, v [B, H, n, D]; lens, slot: B ints (device tensor or anything torch.as_tensor takes).
     Returns o [B, H, n, D] (rows >= lens[b] are left as they were).
     """
-    dev = pool.k.device
+    dev = pool.device
     B, H, n, D = q.shape
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_tensor(t, name, (B, pool.H, n, pool.D), pool.act_dtype, dev)
@@ -225,7 +271,7 @@ def rank_decode(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, pool: Pool
 
     qc, kc, vc [B, H, k, D]; slot, lens: B ints.  Returns oc [B, H, k, D].
     """
-    dev = pool.k.device
+    dev = pool.device
     B, H, kk, D = qc.shape
     for name, t in (("qc", qc), ("kc", kc), ("vc", vc)):
         _check_tensor(t, name, (B, pool.H, kk, pool.D), pool.act_dtype, dev)
@@ -259,7 +305,7 @@ def ar_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pool: Pool, slo
     (a device tensor of at least ar_decode_workspace_bytes(pool, B) bytes) or, when it is
     None, a buffer from torch's caching allocator; split=False runs the one-pass kernel.
     """
-    dev = pool.k.device
+    dev = pool.device
     B = q.shape[0]
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_tensor(t, name, (B, pool.H, 1, pool.D), pool.act_dtype, dev)
@@ -308,7 +354,7 @@ class BlockContext:
         """unipin_block_ctx_tune: time the candidate GEMM kernels (the library's own in each
         tile size, hipBLASLt's) for the block at B users x rows rows and keep the fastest
         (blocks until done)."""
-        dev = pool.k.device
+        dev = pool.device
         if workspace is None:
             workspace = torch.empty(block_workspace_bytes(pool, B, rows), dtype=torch.uint8, device=dev)
         _check(lib.unipin_block_ctx_tune(self.handle, pool.handle, int(B), int(rows), workspace.data_ptr(),
@@ -342,7 +388,7 @@ def block_forward(ctx: BlockContext, weights, mode: int, x: torch.Tensor, pool: 
     pool's lens[b] rows and themselves).  workspace: a device tensor of at least
     block_workspace_bytes(pool, B, rows) bytes, or None for one from torch's allocator.
     """
-    dev = pool.k.device
+    dev = pool.device
     if x.dim() != 3:
         raise UnipinError(EINVAL, "x must be [B, rows, C]")
     B, rows, C = x.shape
@@ -371,19 +417,6 @@ def block_forward(ctx: BlockContext, weights, mode: int, x: torch.Tensor, pool: 
                                     workspace.numel() * workspace.element_size(), _stream_handle(dev)),
            "unipin_block_forward")
     return x
-
-
-def device_status(device=None) -> int:
-    """Sticky device flags (FLAG_BAD_SLOT | FLAG_BAD_LEN) raised since the last call; clears them.
-
-    Synchronises the current stream.
-    """
-    dev = torch.device("cuda") if device is None else torch.device(device)
-    flags = ctypes.c_int()
-    st = lib.unipin_device_status(_stream_handle(dev), ctypes.byref(flags))
-    if st not in (OK, EDEVICE):
-        raise UnipinError(st, "unipin_device_status")
-    return flags.value
 
 
 def version() -> int:

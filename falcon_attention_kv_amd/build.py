@@ -17,11 +17,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libunipin.so")
-SOURCES = ["unipin.cpp", "device_status.hip", "attn_bf16.hip", "attn_fp32.hip", "attn_ar.hip",
+SOURCES = ["unipin.cpp", "pool_share.cpp", "pool_status.hip", "attn_bf16.hip", "attn_fp32.hip", "attn_ar.hip",
            "block.cpp", "block_kernels.hip", "gemm_bf16.hip"]
 # hipBLASLt is one of the two GEMM kernel families of the block; found at run time through
-# the ROCm library path
-LINK = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
+# the ROCm library path.  librt: the shared pages of pools shared between processes.
+LINK = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib", "-lrt"]
 ARCH = "gfx950"
 
 

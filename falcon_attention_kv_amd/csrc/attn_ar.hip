@@ -548,7 +548,6 @@ int chunk_rows(int D) {
     }
 }
 
-using KindF32 = Kind<float, false>;
 using KindBf16 = Kind<bf16, false>;
 using KindBf16P8 = Kind<bf16, true>;
 
@@ -560,11 +559,12 @@ int ar_splits(long bh, int n_max, int D, int kind) {
     // the rows into parts of at least 4 chunks, up to about 256 workgroups over all
     // pairs (more only add merge work; HBM is busy by then) and 64 parts per pair (one
     // per lane of the merge wave).
-    if (bh <= 0 || n_max < 2) return 1;
+    // fp32 pools (kind 0) run the fp64 one-pass kernel and never split.
+    if (bh <= 0 || n_max < 2 || kind == 0) return 1;
     const long rows = n_max - 1;
-    const int pool_bytes = kind == 0 ? 4 : kind == 1 ? 2 : 1;
+    const int pool_bytes = kind == 1 ? 2 : 1;
     if (2L * rows * D * pool_bytes <= (256L << 10)) return 1;
-    const int ch = kind == 0 ? chunk_rows<KindF32>(D) : kind == 1 ? chunk_rows<KindBf16>(D) : chunk_rows<KindBf16P8>(D);
+    const int ch = kind == 1 ? chunk_rows<KindBf16>(D) : chunk_rows<KindBf16P8>(D);
     if (ch == 0) return 1;
     const long nc = (rows + ch - 1) / ch;
     long P = (nc + 3) / 4;
@@ -578,7 +578,6 @@ size_t ar_workspace_bytes(long bh, int P, int D) { return P <= 1 ? 0 : (size_t)b
 hipError_t launch_ar_decode(const AttnArgs &a, int D, int kind, float *ws, int P, hipStream_t stream) {
     if ((long)a.B * a.H <= 0) return hipSuccess;
     switch (kind) {
-        case 0: return launch_kind<KindF32>(a, D, ws, P, stream);
         case 1: return launch_kind<KindBf16>(a, D, ws, P, stream);
         case 2: return launch_kind<KindBf16P8>(a, D, ws, P, stream);
         default: return hipErrorInvalidValue;

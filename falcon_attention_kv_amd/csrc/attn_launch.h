@@ -25,7 +25,8 @@ struct AttnArgs {
     int tiles;                    // query tiles per (user, head)
     int xcd_remap;                // 1: map blocks so all tiles of a (user, head) share an XCD
     float c;                      // scale * log2(e)
-    unsigned int *status;         // sticky per-device flags
+    double scale64;               // the score scale itself, in fp64 (fp32 kernels)
+    unsigned int *status;         // the pool's sticky flag word on this device
     // Row addressing of q, k, v (in) and o (out), in elements: row t of (user b, head h)
     // starts at b * bstride + h * hstride + t * rstride.  The contiguous [B, H, rows, D]
     // layout is bstride = H * rows * D, hstride = rows * D, rstride = D; the bf16 kernels
@@ -62,19 +63,27 @@ int bf16_decode_rows_per_item(int D);
 // pool write, decoded by the ranking decode as its tiles arrive), else bf16.
 hipError_t launch_prefill_bf16(const AttnArgs &a, int D, bool pool8, hipStream_t stream);
 hipError_t launch_decode_bf16(const AttnArgs &a, int D, bool pool8, hipStream_t stream);
+// fp32 pools: fp32 in and out, fp64 arithmetic inside.
 hipError_t launch_prefill_fp32(const AttnArgs &a, int D, hipStream_t stream);
 hipError_t launch_decode_fp32(const AttnArgs &a, int D, hipStream_t stream);
-// One autoregressive step (one new token per user and head).  kind: 0 fp32 activations
-// and pool, 1 bf16 activations and pool, 2 bf16 activations with an E4M3 pool (the
-// unipin_dtype_t codes).  P = 1: one pass per (user, head).  P > 1: the slot rows are
+hipError_t launch_ar_decode_fp32(const AttnArgs &a, int D, hipStream_t stream);
+// One autoregressive step (one new token per user and head) on a bf16 pool (kind 1) or
+// with bf16 activations over an E4M3 pool (kind 2) (the unipin_dtype_t codes; fp32
+// pools take launch_ar_decode_fp32 and never split).  P = 1: one pass per (user, head).  P > 1: the slot rows are
 // split into up to P parts, one workgroup each, whose states go to ws
 // (ar_workspace_bytes(B*H, P, D) bytes, fp32) and are merged by a second pass.
 int ar_splits(long bh, int n_max, int D, int kind);
 size_t ar_workspace_bytes(long bh, int P, int D);
 hipError_t launch_ar_decode(const AttnArgs &a, int D, int kind, float *ws, int P, hipStream_t stream);
 
-// Device address of the sticky status word of the current device (looked up once
-// per device with hipGetSymbolAddress).
-hipError_t device_status_word(unsigned int **out);
+// Per-pool sticky flag words: one entry per live pool descriptor, in file-scope device
+// arrays on every device (addresses looked up once per device with hipGetSymbolAddress).
+constexpr int kMaxPools = 4096;
+// Device address, on the current device, of pool entry `index`'s flag word.
+hipError_t pool_flag_word(int index, unsigned int **out);
+// Enqueues on `stream` a one-thread kernel that exchanges entry `index`'s flags for 0.
+hipError_t clear_pool_flags(int index, hipStream_t stream);
+// The same exchange, then a copy of the old value to *host and a wait for `stream`.
+hipError_t take_pool_flags(int index, hipStream_t stream, unsigned int *host);
 
 }  // namespace unipin

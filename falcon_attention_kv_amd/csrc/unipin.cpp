@@ -1,7 +1,8 @@
 // C ABI of the library (include/unipin.h): pool descriptor, round-robin slot hand-out,
 // host-side argument checks, and dispatch to the HIP kernels by element type and head
 // dimension.  Nothing here allocates device memory; the only HIP calls are kernel
-// launches (prefill, rank decode, autoregressive step) and the status read-back.
+// launches (prefill, rank decode, autoregressive step, the flag exchange) and the
+// status read-back.
 #include "unipin.h"
 
 #include <hip/hip_runtime.h>
@@ -9,18 +10,11 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <new>
 
 #include "attn_launch.h"
-
-struct unipin_pool {
-    void *k;
-    void *v;
-    int L, S, H, n_max, D, dtype;
-    int elem;                              // bytes per element
-    std::atomic<uint64_t> cursor;          // hand-outs so far
-    std::atomic<uint64_t> *gen;            // [S] hand-outs per slot
-};
+#include "pool_internal.h"
 
 namespace {
 
@@ -28,13 +22,42 @@ constexpr int kVersion = 10000;  // 1.0.0
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Byte offsets inside one (user, head)'s rows and inside one pool slot row block are
+// 32-bit in the kernels (buffer record counts, scalar offsets).
+constexpr long long kMaxOffset = 0x7fffffffLL;
+
+// Entries of the per-device flag arrays, one per live descriptor; an entry that served
+// an earlier descriptor may still hold that descriptor's flags, so its new owner clears
+// it before its first kernel.
+std::mutex g_index_mu;
+bool g_index_used[unipin::kMaxPools];
+bool g_index_dirty[unipin::kMaxPools];
+
+int take_flag_index(bool *dirty) {
+    std::lock_guard<std::mutex> lock(g_index_mu);
+    for (int i = 0; i < unipin::kMaxPools; ++i)
+        if (!g_index_used[i]) {
+            g_index_used[i] = true;
+            *dirty = g_index_dirty[i];
+            g_index_dirty[i] = true;
+            return i;
+        }
+    return -1;
+}
+
+void release_flag_index(int i) {
+    std::lock_guard<std::mutex> lock(g_index_mu);
+    if (i >= 0 && i < unipin::kMaxPools) g_index_used[i] = false;
+}
+
 bool supported_d(int D) { return D == 32 || D == 64 || D == 128; }
 
 // Resolves the score scale: non-positive or NaN means 1/sqrt(D); infinity is rejected.
-int resolve_scale(float scale, int D, float *c) {
+int resolve_scale(float scale, int D, unipin::AttnArgs &a) {
     if (std::isinf(scale)) return UNIPIN_EINVAL;
     const double s = (std::isnan(scale) || scale <= 0.f) ? 1.0 / std::sqrt((double)D) : (double)scale;
-    *c = (float)(s * 1.4426950408889634);  // scale * log2(e)
+    a.c = (float)(s * 1.4426950408889634);  // scale * log2(e)
+    a.scale64 = s;
     return UNIPIN_OK;
 }
 
@@ -43,6 +66,24 @@ bool bf16_kernels(const unipin_pool *pool) { return pool->dtype != UNIPIN_FP32; 
 
 // bytes of one activation element (q, k, v, o) for this pool
 int act_bytes(const unipin_pool *pool) { return pool->dtype == UNIPIN_FP32 ? 4 : 2; }
+
+}  // namespace
+
+namespace unipin {
+
+int pool_kernel_prologue(unipin_pool *pool, hipStream_t stream, unsigned int **flag_word) {
+    if (pool->clear_flags.load(std::memory_order_acquire) && pool->clear_flags.exchange(false)) {
+        if (clear_pool_flags(pool->flag_index, stream) != hipSuccess) {
+            pool->clear_flags.store(true);
+            return UNIPIN_EHIP;
+        }
+    }
+    return pool_flag_word(pool->flag_index, flag_word) == hipSuccess ? UNIPIN_OK : UNIPIN_EHIP;
+}
+
+}  // namespace unipin
+
+namespace {
 
 int fill_pool_args(unipin::AttnArgs &a, const unipin_pool *pool, int layer) {
     const long long per_layer = (long long)pool->S * pool->H * pool->n_max * pool->D;
@@ -82,6 +123,7 @@ int attention_call(bool prefill, const void *q, const void *k, const void *v, Ro
     if (!pool || !q || !k || !v || !lens || !slot || !o) return UNIPIN_EINVAL;
     if (B < 1 || rows < 1 || (prefill && rows > pool->n_max)) return UNIPIN_EINVAL;
     if (layer < 0 || layer >= pool->L) return UNIPIN_ERANGE;
+    if (prefill && pool->readonly) return UNIPIN_EPERM;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lens, 4) ||
         !aligned(slot, 4))
         return UNIPIN_EALIGN;
@@ -97,14 +139,17 @@ int attention_call(bool prefill, const void *q, const void *k, const void *v, Ro
             if (l->rstride < D || l->rstride % 8 || l->hstride % 8 || l->bstride % 8 || l->hstride < 0 ||
                 l->bstride < 0)
                 return UNIPIN_EINVAL;
-            if ((long long)rows * l->rstride * act_bytes(pool) >= 0x7fffffffLL) return UNIPIN_EINVAL;
         }
     }
+    // one (user, head)'s rows of every operand within 32-bit byte offsets
+    const RowLayout *ls[2] = {&in, &out};
+    for (const RowLayout *l : ls)
+        if ((long long)rows * l->rstride * act_bytes(pool) >= kMaxOffset) return UNIPIN_EINVAL;
     const int rpb = rows_per_block(pool, prefill);
     const long long blocks = (long long)B * H * ((rows + rpb - 1) / rpb);
     if (blocks > 0x7fffffffLL) return UNIPIN_EINVAL;
     unipin::AttnArgs a{};
-    int rc = resolve_scale(scale, D, &a.c);
+    int rc = resolve_scale(scale, D, a);
     if (rc) return rc;
     fill_pool_args(a, pool, layer);
     a.q = q;
@@ -124,7 +169,8 @@ int attention_call(bool prefill, const void *q, const void *k, const void *v, Ro
     a.out_bstride = out.bstride;
     a.out_hstride = out.hstride;
     a.out_rstride = out.rstride;
-    if (unipin::device_status_word(&a.status) != hipSuccess) return UNIPIN_EHIP;
+    rc = pool_kernel_prologue(pool, static_cast<hipStream_t>(stream), &a.status);
+    if (rc) return rc;
     return launch(a, pool, prefill, stream);
 }
 
@@ -141,17 +187,27 @@ int unipin_pool_create(unipin_pool_t **out, void *k_pool, void *v_pool, int L, i
     if (dtype != UNIPIN_FP32 && dtype != UNIPIN_BF16 && dtype != UNIPIN_FP8_E4M3) return UNIPIN_EDTYPE;
     if (dtype == UNIPIN_FP8_E4M3 && D != 64 && D != 128) return UNIPIN_EINVAL;
     if (!aligned(k_pool, 16) || !aligned(v_pool, 16)) return UNIPIN_EALIGN;
+    const int elem = dtype == UNIPIN_FP32 ? 4 : dtype == UNIPIN_BF16 ? 2 : 1;
     const long long elems = (long long)L * S * H * n_max * D;
     if (elems / L / S / H / n_max != D || elems > (1LL << 46)) return UNIPIN_EINVAL;
+    if ((long long)n_max * D * elem >= kMaxOffset) return UNIPIN_EINVAL;   // one slot row block
     unipin_pool *p = new (std::nothrow) unipin_pool;
     if (!p) return UNIPIN_ENOMEM;
-    p->gen = new (std::nothrow) std::atomic<uint64_t>[S];
-    if (!p->gen) {
+    p->ring_own = new (std::nothrow) uint64_t[(size_t)S + 1];
+    if (!p->ring_own) {
         delete p;
         return UNIPIN_ENOMEM;
     }
-    for (int i = 0; i < S; ++i) p->gen[i].store(0, std::memory_order_relaxed);
-    p->cursor.store(0, std::memory_order_relaxed);
+    bool dirty = false;
+    p->flag_index = take_flag_index(&dirty);
+    if (p->flag_index < 0) {
+        delete[] p->ring_own;
+        delete p;
+        return UNIPIN_ENOMEM;
+    }
+    p->clear_flags.store(dirty, std::memory_order_relaxed);
+    for (int i = 0; i <= S; ++i) p->ring_own[i] = 0;
+    p->ring = p->ring_own;
     p->k = k_pool;
     p->v = v_pool;
     p->L = L;
@@ -160,33 +216,40 @@ int unipin_pool_create(unipin_pool_t **out, void *k_pool, void *v_pool, int L, i
     p->n_max = n_max;
     p->D = D;
     p->dtype = dtype;
-    p->elem = dtype == UNIPIN_FP32 ? 4 : dtype == UNIPIN_BF16 ? 2 : 1;
+    p->elem = elem;
+    p->readonly = false;
+    p->shm_addr = nullptr;
+    p->shm_bytes = 0;
+    p->shm_name[0] = 0;
+    p->shm_owner = false;
+    p->ipc_k = p->ipc_v = nullptr;
     *out = p;
     return UNIPIN_OK;
 }
 
 int unipin_pool_destroy(unipin_pool_t *pool) {
     if (!pool) return UNIPIN_OK;
-    delete[] pool->gen;
+    unipin::pool_share_release(pool);
+    release_flag_index(pool->flag_index);
+    delete[] pool->ring_own;
     delete pool;
     return UNIPIN_OK;
 }
 
 int unipin_pool_acquire(unipin_pool_t *pool, int32_t *slot, uint64_t *generation) {
     if (!pool || !slot) return UNIPIN_EINVAL;
-    const uint64_t i = pool->cursor.fetch_add(1, std::memory_order_relaxed);
+    if (pool->readonly) return UNIPIN_EPERM;
+    const uint64_t i = __atomic_fetch_add(&pool->ring[0], 1, __ATOMIC_RELAXED);
     const int32_t s = (int32_t)(i % (uint64_t)pool->S);
-    const uint64_t g = pool->gen[s].fetch_add(1, std::memory_order_acq_rel) + 1;
+    const uint64_t g = __atomic_add_fetch(&pool->ring[1 + s], 1, __ATOMIC_ACQ_REL);
     *slot = s;
     if (generation) *generation = g;
     return UNIPIN_OK;
 }
 
-int unipin_pool_generation(const unipin_pool_t *pool, int32_t slot, uint64_t *generation) {
-    if (!pool || !generation) return UNIPIN_EINVAL;
-    if (slot < 0 || slot >= pool->S) return UNIPIN_ERANGE;
-    *generation = pool->gen[slot].load(std::memory_order_acquire);
-    return UNIPIN_OK;
+uint64_t unipin_pool_generation(const unipin_pool_t *pool, int32_t slot) {
+    if (!pool || slot < 0 || slot >= pool->S) return 0;
+    return unipin::ring_load(&pool->ring[1 + slot]);
 }
 
 int unipin_pool_dims(const unipin_pool_t *pool, int *L, int *S, int *H, int *n_max, int *D,
@@ -226,12 +289,13 @@ int unipin_ar_decode(const void *q, const void *k, const void *v, unipin_pool_t 
     if (!pool || !q || !k || !v || !lens || !slot || !o) return UNIPIN_EINVAL;
     if (B < 1) return UNIPIN_EINVAL;
     if (layer < 0 || layer >= pool->L) return UNIPIN_ERANGE;
+    if (pool->readonly) return UNIPIN_EPERM;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
         !aligned(lens, 4) || !aligned(slot, 4))
         return UNIPIN_EALIGN;
     if ((long long)B * pool->H > 0x7fffffffLL) return UNIPIN_EINVAL;
     unipin::AttnArgs a{};
-    int rc = resolve_scale(scale, pool->D, &a.c);
+    int rc = resolve_scale(scale, pool->D, a);
     if (rc) return rc;
     fill_pool_args(a, pool, layer);
     a.q = q;
@@ -251,9 +315,13 @@ int unipin_ar_decode(const void *q, const void *k, const void *v, unipin_pool_t 
         parts = unipin::ar_splits((long)B * pool->H, pool->n_max, pool->D, kind);
         if (workspace_bytes < unipin::ar_workspace_bytes((long)B * pool->H, parts, pool->D)) return UNIPIN_EINVAL;
     }
-    if (unipin::device_status_word(&a.status) != hipSuccess) return UNIPIN_EHIP;
-    const hipError_t e = unipin::launch_ar_decode(a, pool->D, kind, static_cast<float *>(workspace), parts,
-                                                  static_cast<hipStream_t>(stream));
+    rc = unipin::pool_kernel_prologue(pool, static_cast<hipStream_t>(stream), &a.status);
+    if (rc) return rc;
+    const hipError_t e =
+        kind == UNIPIN_FP32
+            ? unipin::launch_ar_decode_fp32(a, pool->D, static_cast<hipStream_t>(stream))
+            : unipin::launch_ar_decode(a, pool->D, kind, static_cast<float *>(workspace), parts,
+                                       static_cast<hipStream_t>(stream));
     return e == hipSuccess ? UNIPIN_OK : UNIPIN_EHIP;
 }
 
@@ -264,17 +332,19 @@ size_t unipin_ar_decode_workspace_bytes(const unipin_pool_t *pool, int B) {
                                       pool->D);
 }
 
-int unipin_device_status(void *stream, int *flags) {
+int unipin_pool_status(unipin_pool_t *pool, void *stream, int *flags) {
     if (flags) *flags = 0;
-    unsigned int *word = nullptr;
-    if (unipin::device_status_word(&word) != hipSuccess) return UNIPIN_EHIP;
+    if (!pool) return UNIPIN_EINVAL;
     const hipStream_t st = static_cast<hipStream_t>(stream);
+    // a reused entry's earlier flags are dropped by the exchange below like any others;
+    // they belong to no call on this pool only if nothing ran on it yet
+    const bool stale = pool->clear_flags.exchange(false);
     unsigned int host = 0;
-    if (hipStreamSynchronize(st) != hipSuccess) return UNIPIN_EHIP;
-    if (hipMemcpy(&host, word, sizeof(host), hipMemcpyDeviceToHost) != hipSuccess) return UNIPIN_EHIP;
-    if (host) {
-        if (hipMemset(word, 0, sizeof(host)) != hipSuccess) return UNIPIN_EHIP;
+    if (unipin::take_pool_flags(pool->flag_index, st, &host) != hipSuccess) {
+        if (stale) pool->clear_flags.store(true);
+        return UNIPIN_EHIP;
     }
+    if (stale) host = 0;
     if (flags) *flags = (int)host;
     return host ? UNIPIN_EDEVICE : UNIPIN_OK;
 }
@@ -288,7 +358,9 @@ const char *unipin_strerror(int status) {
         case UNIPIN_EALIGN: return "tensor pointer not 16-byte aligned";
         case UNIPIN_EDEVICE: return "a kernel skipped a user with an invalid slot or length";
         case UNIPIN_EHIP: return "HIP runtime error";
-        case UNIPIN_ENOMEM: return "out of host memory";
+        case UNIPIN_ENOMEM: return "out of host memory or pool descriptors";
+        case UNIPIN_EPERM: return "the pool is imported read-only (rank decode only)";
+        case UNIPIN_EIO: return "a pool share file or shared page could not be written, read or mapped";
         default: return "unknown status";
     }
 }

@@ -35,7 +35,8 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_strerror():
     assert lib.unipin_version() == 10000
-    for code in (fa.OK, fa.EINVAL, fa.ERANGE, fa.EDTYPE, fa.EALIGN, fa.EDEVICE, fa.EHIP, fa.ENOMEM):
+    for code in (fa.OK, fa.EINVAL, fa.ERANGE, fa.EDTYPE, fa.EALIGN, fa.EDEVICE, fa.EHIP, fa.ENOMEM, fa.EPERM,
+                 fa.EIO):
         text = lib.unipin_strerror(code).decode()
         assert text and text != "unknown status"
     assert lib.unipin_strerror(-99).decode() == "unknown status"
@@ -87,12 +88,11 @@ def test_acquire_matches_round_robin_oracle():
         assert lib.unipin_pool_acquire(h, ctypes.byref(s), ctypes.byref(g)) == fa.OK
         assert (s.value, g.value) == ring.acquire()
     for slot in range(S):
-        g = ctypes.c_uint64()
-        assert lib.unipin_pool_generation(h, slot, ctypes.byref(g)) == fa.OK
-        assert g.value == ring.gen[slot]
-    g = ctypes.c_uint64()
-    assert lib.unipin_pool_generation(h, S, ctypes.byref(g)) == fa.ERANGE
-    assert lib.unipin_pool_generation(h, -1, ctypes.byref(g)) == fa.ERANGE
+        assert lib.unipin_pool_generation(h, slot) == ring.gen[slot]
+    # out of range and a null pool read as 0 (the value of a slot never handed out)
+    assert lib.unipin_pool_generation(h, S) == 0
+    assert lib.unipin_pool_generation(h, -1) == 0
+    assert lib.unipin_pool_generation(None, 0) == 0
     s = ctypes.c_int32()
     assert lib.unipin_pool_acquire(h, ctypes.byref(s), None) == fa.OK   # generation optional
     assert lib.unipin_pool_acquire(None, ctypes.byref(s), None) == fa.EINVAL
@@ -126,9 +126,7 @@ def test_acquire_is_thread_safe():
     # round-robin over `total` hand-outs: every slot gets floor or ceil of total / S
     assert sorted(counts) == sorted([total // S + (1 if i < total % S else 0) for i in range(S)])
     for s in range(S):
-        g = ctypes.c_uint64()
-        lib.unipin_pool_generation(h, s, ctypes.byref(g))
-        assert g.value == counts[s]
+        assert lib.unipin_pool_generation(h, s) == counts[s]
     lib.unipin_pool_destroy(h)
 
 
@@ -211,8 +209,8 @@ def test_ar_decode_workspace_bytes():
     h = make_pool(L=1, S=4, H=1, n_max=40001, D=128)   # 625 chunks: capped at 64 parts
     assert lib.unipin_ar_decode_workspace_bytes(h, 1) == 64 * (128 + 4) * 4
     lib.unipin_pool_destroy(h)
-    h = make_pool(L=1, S=4, H=2, n_max=4097, D=64, dtype=fa.FP32)   # 2 MiB per pair, 64 chunks
-    assert lib.unipin_ar_decode_workspace_bytes(h, 3) == 6 * 16 * (64 + 4) * 4
+    h = make_pool(L=1, S=4, H=2, n_max=4097, D=64, dtype=fa.FP32)   # fp32 pools: fp64 one pass, no split
+    assert lib.unipin_ar_decode_workspace_bytes(h, 3) == 0
     lib.unipin_pool_destroy(h)
 
 
@@ -284,3 +282,68 @@ def test_binding_rejects_mismatched_tensors():
     with pytest.raises(fa.UnipinError):
         fa.ar_decode(t, t, t, pool, [0], [3], 0)
     pool.close()
+
+
+def test_pool_status_host_checks():
+    flags = ctypes.c_int(5)
+    assert lib.unipin_pool_status(None, None, ctypes.byref(flags)) == fa.EINVAL
+    assert flags.value == 0
+
+
+def test_offsets_stay_within_32_bits():
+    """One (user, head)'s rows of an operand, and one slot's rows of one head in the pool,
+    are addressed with 32-bit byte offsets in the kernels: larger shapes are refused on the
+    host instead of wrapping."""
+    h = vp()
+    # n_max * D * elem = 2^24 * 128 * 1 = 2^31 bytes (E4M3) -> refused; one row less fits
+    assert lib.unipin_pool_create(ctypes.byref(h), FAKE, FAKE, 1, 1, 1, 1 << 24, 128, fa.FP8_E4M3) == fa.EINVAL
+    assert lib.unipin_pool_create(ctypes.byref(h), FAKE, FAKE, 1, 1, 1, (1 << 23) - 1, 128, fa.BF16) == fa.OK
+    lib.unipin_pool_destroy(h)
+    assert lib.unipin_pool_create(ctypes.byref(h), FAKE, FAKE, 1, 1, 1, 1 << 23, 128, fa.BF16) == fa.EINVAL
+    pool = make_pool(L=1, S=1, H=1, n_max=16, D=128)
+    # k * D * 2 bytes = 2^23 * 128 * 2 = 2^31: the candidate rows of one (user, head)
+    k = 1 << 23
+    assert lib.unipin_rank_decode(FAKE, FAKE, FAKE, pool, FAKE, FAKE, 0, 1, k, 0.0, FAKE, None) == fa.EINVAL
+    lib.unipin_pool_destroy(pool)
+
+
+def test_pool_limit_and_flag_entries_are_reused():
+    """4096 live descriptors per process; destroying one frees its flag entry."""
+    hs = []
+    try:
+        while True:
+            h = vp()
+            rc = lib.unipin_pool_create(ctypes.byref(h), FAKE, FAKE, 1, 1, 1, 8, 64, fa.BF16)
+            if rc != fa.OK:
+                assert rc == fa.ENOMEM
+                break
+            hs.append(h)
+            assert len(hs) <= 4096
+        assert len(hs) >= 4000   # other tests may hold a few
+        lib.unipin_pool_destroy(hs.pop())
+        h = vp()
+        assert lib.unipin_pool_create(ctypes.byref(h), FAKE, FAKE, 1, 1, 1, 8, 64, fa.BF16) == fa.OK
+        hs.append(h)
+    finally:
+        for h in hs:
+            lib.unipin_pool_destroy(h)
+
+
+def test_share_host_checks(tmp_path):
+    """Export/import argument and file checks that need no GPU."""
+    h = vp()
+    assert lib.unipin_pool_export(None, b"/tmp/x") == fa.EINVAL
+    pool = make_pool()
+    assert lib.unipin_pool_export(pool, None) == fa.EINVAL
+    assert lib.unipin_pool_export(pool, b"") == fa.EINVAL
+    lib.unipin_pool_destroy(pool)
+    assert lib.unipin_pool_import(None, b"/tmp/x") == fa.EINVAL
+    assert lib.unipin_pool_import(ctypes.byref(h), None) == fa.EINVAL
+    assert lib.unipin_pool_import(ctypes.byref(h), str(tmp_path / "missing").encode()) == fa.EIO
+    bad = tmp_path / "bad"
+    bad.write_bytes(b"not a pool share file" * 40)
+    assert lib.unipin_pool_import(ctypes.byref(h), str(bad).encode()) == fa.EIO
+    short = tmp_path / "short"
+    short.write_bytes(b"UNIPINP1")
+    assert lib.unipin_pool_import(ctypes.byref(h), str(short).encode()) == fa.EIO
+    assert h.value is None

@@ -1,6 +1,7 @@
 """GPU parity of the autoregressive retrieval step (unipin_ar_decode) against the oracle.
 
-Same tolerances as the other GPU parity tests: fp32 normwise 1e-5; bf16 max abs 2e-2
+Same tolerances as the other GPU parity tests: fp32 1e-5 relative, normwise and element
+by element (floored at 1e-3); bf16 max abs 2e-2
 and mean abs 2e-3.  Pool contents are compared bit for bit: the step must store the
 new token's K/V at row lens[b] of its slot and leave every other entry as it was.
 """
@@ -32,6 +33,8 @@ def check_close(got: torch.Tensor, ref: np.ndarray, dtype: torch.dtype, what: st
     if dtype == torch.float32:
         rel = diff.max() / max(np.abs(r).max(), 1e-30)
         assert rel <= 1e-5, f"{what}: normwise relative error {rel:.3e} > 1e-5"
+        elem = (diff / np.maximum(np.abs(r), 1e-3)).max()
+        assert elem <= 1e-5, f"{what}: element-wise relative error {elem:.3e} > 1e-5 (floor 1e-3)"
         return
     assert diff.max() <= 2e-2, f"{what}: max abs error {diff.max():.3e} > 2e-2"
     assert diff.mean() <= 2e-3, f"{what}: mean abs error {diff.mean():.3e} > 2e-3"
@@ -58,7 +61,7 @@ def test_ar_decode_one_step(dtype, D):
     pool = fa.Pool(pk, pv)
     o = fa.ar_decode(q, k, v, pool, slots, lens, layer)
     torch.cuda.synchronize()
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     ref_o, ref_k, ref_v = oracle.ar_decode(q.cpu(), k.cpu(), v.cpu(), before_k, before_v, slots, lens, layer)
     check_close(o, ref_o, dtype, f"ar_decode {dtype} D={D}")
     exp_k, exp_v = before_k.clone(), before_v.clone()
@@ -93,7 +96,7 @@ def test_ar_decode_steps_replay_the_prefill(scale):
                                  scale=scale))
         lens = lens + 1
     torch.cuda.synchronize()
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     full = oracle.prefill(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), [n_max] * B, scale)
     for j in range(T):
         ref = np.stack([full[b, :, hist[b] + j] for b in range(B)])[:, :, None]
@@ -124,11 +127,11 @@ def test_ar_decode_invalid_users_flagged_and_skipped():
     o = torch.full_like(tok["q"][0], 7.0)
     fa.ar_decode(tok["q"][0], tok["k"][0], tok["v"][0], pool, [0, 5, 1], [n_max, 3, -1], 0, o=o)
     torch.cuda.synchronize()
-    flags = fa.device_status()
+    flags = pool.status()
     assert flags == fa.FLAG_BAD_SLOT | fa.FLAG_BAD_LEN
     assert torch.all(o == 7.0), "skipped users' outputs must stay untouched"
     assert torch.equal(pk, before_k) and torch.equal(pv, before_v), "skipped users must not write the pool"
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     pool.close()
 
 
@@ -150,7 +153,7 @@ def test_ar_decode_serving_shape_sampled():
     before = {b: (pk[layer, b, :, :lens[b]].cpu(), pv[layer, b, :, :lens[b]].cpu()) for b in users}
     o = fa.ar_decode(tok["q"][0], tok["k"][0], tok["v"][0], pool, slots, lens, layer)
     torch.cuda.synchronize()
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     for b in users:
         # the user's slot as a one-layer, one-slot pool with one free row for the new token
         hk, hv = (np.concatenate([oracle.as_f64(x), np.zeros((w.H, 1, w.D))], axis=1)[None, None]
@@ -165,15 +168,15 @@ def test_ar_decode_serving_shape_sampled():
 
 
 SPLIT_CASES = [(torch.bfloat16, 64), (torch.bfloat16, 128), (torch.bfloat16, 32), (torch.float32, 64),
-               (torch.float32, 128)]
+               (torch.float32, 128)]   # fp32 pools never split (fp64 one-pass kernel): the same cases, one pass
 
 
 @pytest.mark.parametrize("dtype,D", SPLIT_CASES, ids=lambda x: str(x))
 def test_ar_decode_split_path(dtype, D):
     """Few (user, head) pairs on a long slot: the rows are split across workgroups and the
-    parts merged by a second pass.  Lengths cover an empty slot, fewer chunks than parts,
-    part boundaries and the last free row; the one-pass kernel must agree with the oracle
-    on the same inputs too."""
+    parts merged by a second pass (bf16; fp32 pools run their one-pass fp64 kernel).
+    Lengths cover an empty slot, fewer chunks than parts, part boundaries and the last
+    free row; the one-pass kernel must agree with the oracle on the same inputs too."""
     L, S, H, n_max, layer = 1, 12, 2, 4600, 0
     lens = [0, 1, 64, 65, 200, 511, 513, 1024, 2047, 3000, 4100, n_max - 1]
     slots = [3, 0, 11, 2, 7, 1, 4, 6, 5, 10, 9, 8]
@@ -189,10 +192,14 @@ def test_ar_decode_split_path(dtype, D):
         pv.copy_(before_v.to(DEV))
         pool = fa.Pool(pk, pv)
         if split:
-            assert fa.ar_decode_workspace_bytes(pool, B) > 0, "this shape must take the split path"
+            need = fa.ar_decode_workspace_bytes(pool, B)
+            if dtype == torch.float32:
+                assert need == 0, "fp32 pools run one pass"
+            else:
+                assert need > 0, "this shape must take the split path"
         o = fa.ar_decode(q, k, v, pool, slots, lens, layer, split=split)
         torch.cuda.synchronize()
-        assert fa.device_status() == 0
+        assert pool.status() == 0
         check_close(o, ref_o, dtype, f"ar_decode split={split} {dtype} D={D}")
         assert np.array_equal(oracle.as_f64(pk), ref_k) and np.array_equal(oracle.as_f64(pv), ref_v)
         pool.close()
@@ -214,7 +221,7 @@ def test_ar_decode_split_invalid_users_and_reused_workspace():
     slots, lens = [0, 9, 1, 2], [2000, 5, n_max, 2999]
     fa.ar_decode(tok["q"][0], tok["k"][0], tok["v"][0], pool, slots, lens, 0, o=o, workspace=ws)
     torch.cuda.synchronize()
-    assert fa.device_status() == fa.FLAG_BAD_SLOT | fa.FLAG_BAD_LEN
+    assert pool.status() == fa.FLAG_BAD_SLOT | fa.FLAG_BAD_LEN
     assert torch.all(o[1:3] == 7.0), "skipped users' outputs must stay untouched"
     ref, _, _ = oracle.ar_decode(tok["q"][0].cpu(), tok["k"][0].cpu(), tok["v"][0].cpu(), before_k, before_v,
                                  [0, 0, 0, 2], [2000, 0, 0, 2999], 0)
@@ -250,7 +257,7 @@ def _long_history_case(B, H, D, lens, n_max, seed, split_expected):
     before = {b: (pk[0, b, :, :lens[b]].cpu(), pv[0, b, :, :lens[b]].cpu()) for b in users}
     o = fa.ar_decode(tok["q"][0], tok["k"][0], tok["v"][0], pool, slots, lens, 0)
     torch.cuda.synchronize()
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     for b in users:
         hk, hv = (np.concatenate([oracle.as_f64(x), np.zeros((H, 1, D))], axis=1)[None, None]
                   for x in before[b])

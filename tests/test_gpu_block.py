@@ -78,7 +78,7 @@ def test_block_history_then_candidates(B, n, K, H, D, gemm):
     fa.block_forward(ctx, w, fa.BLOCK_HISTORY, xh, pool, slots, lens, layer)
     fa.block_forward(ctx, w, fa.BLOCK_CANDIDATES, xc, pool, slots, lens, layer)
     torch.cuda.synchronize()
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     wc = {k: v.cpu() for k, v in w.items()}
     nanpool = np.full((2, B, H, n, D), np.nan)
     rh, rk, rv = oracle.block_history(xh0.cpu(), lens, wc, H, nanpool, nanpool.copy(), slots, layer)
@@ -139,7 +139,7 @@ def test_block_table2_shape_sampled():
     fa.block_forward(ctx, w, fa.BLOCK_HISTORY, xh, pool, slots, lens, 0)
     fa.block_forward(ctx, w, fa.BLOCK_CANDIDATES, xc, pool, slots, lens, 0)
     torch.cuda.synchronize()
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     wc = {k: v.cpu() for k, v in w.items()}
     for b in (0, 5):
         _, jc = oracle.block_joint(xh0[b:b + 1].cpu(), xc0[b:b + 1].cpu(), [n], wc, H)
@@ -187,7 +187,7 @@ def test_block_twelve_layer_stack():
         fa.block_forward(ctx, ws[l], fa.BLOCK_CANDIDATES, xc, pool, slots, lens, l)
         rh, rc = oracle.block_joint(rh, rc, lens, {k: v.cpu() for k, v in ws[l].items()}, H)
     torch.cuda.synchronize()
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     check_rel(xc, rc, "candidates after 12 layers", 12, 4)
     for b, N in enumerate(lens):
         check_rel(xh[b, :N], rh[b, :N], f"history of user {b} after 12 layers", 12, 4)

@@ -59,7 +59,7 @@ def test_prefill_stores_the_code_of_every_finite_bf16_value():
     pool = fa.Pool(torch.zeros((1, 1, 1, n, D), dtype=F8, device=DEV), torch.zeros((1, 1, 1, n, D), dtype=F8, device=DEV))
     fa.prefill(q, k, v, [n], pool, [0], 0)
     torch.cuda.synchronize()
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     got = codes(pool.k).reshape(-1)
     ref = oracle.e4m3_encode(k.cpu()).reshape(-1)
     bad = np.nonzero(got != ref)[0]
@@ -83,7 +83,7 @@ def test_ar_step_reads_every_code_exactly():
     z = torch.zeros((B, 1, 1, D), dtype=torch.bfloat16, device=DEV)
     o = fa.ar_decode(z, z, z, pool, list(range(B)), [1] * B, 0)
     torch.cuda.synchronize()
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     exp = oracle.e4m3_decode(np.array(cs, dtype=np.uint8)) / 2
     got = o[:, 0, 0].double().cpu().numpy()
     assert np.array_equal(got, np.repeat(exp[:, None], D, axis=1)), "decoded values differ"
@@ -107,7 +107,7 @@ def test_ar_step_stores_nan_and_extreme_tokens_as_the_oracle_does():
     ref = oracle.e4m3_encode(k.cpu().reshape(-1))
     assert np.array_equal(got, ref), (got.tolist()[:16], ref.tolist()[:16])
     assert np.array_equal(codes(pool.v)[0, 0, 0, 2], ref)
-    fa.device_status()   # NaN attention output is expected; clear nothing else
+    pool.status()   # NaN attention output is expected; clear nothing else
     pool.close()
 
 
@@ -127,7 +127,7 @@ def test_ar_step_on_e4m3_pool(D, n_max):
     before_k, before_v = codes(pool.k), codes(pool.v)
     o = fa.ar_decode(q, k, v, pool, slots, lens, layer)
     torch.cuda.synchronize()
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     ref, rk, rv = oracle.ar_decode_e4m3(q.cpu(), k.cpu(), v.cpu(), before_k, before_v, slots, lens, layer)
     check_close(o, ref, f"e4m3 step D={D}")
     assert np.array_equal(codes(pool.k), rk) and np.array_equal(codes(pool.v), rv), "pool codes"
@@ -146,7 +146,7 @@ def test_prefill_on_e4m3_pool(D):
     before_k, before_v = codes(pool.k), codes(pool.v)
     o = fa.prefill(inp["q"], inp["k"], inp["v"], lens, pool, slots, 0)
     torch.cuda.synchronize()
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     ref = oracle.prefill(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), lens)
     for b, N in enumerate(lens):
         if N:
@@ -170,7 +170,7 @@ def test_rank_decode_reads_every_code_exactly():
     z = torch.zeros((B, 1, 1, D), dtype=torch.bfloat16, device=DEV)
     oc = fa.rank_decode(z, z, z, pool, list(range(B)), [1] * B, 0)
     torch.cuda.synchronize()
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     exp = oracle.e4m3_decode(np.array(cs, dtype=np.uint8)) / 2
     assert np.array_equal(oc[:, 0, 0].double().cpu().numpy(), np.repeat(exp[:, None], D, axis=1))
     pool.close()
@@ -189,7 +189,7 @@ def test_rank_decode_on_e4m3_pool(D, k):
     inp = W.small_case(B, H, D, 8, k, [1] * B, seed=56, device=DEV)
     oc = fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, slots, lens, layer)
     torch.cuda.synchronize()
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     pk, pv = oracle.e4m3_decode(codes(pool.k)), oracle.e4m3_decode(codes(pool.v))
     ref = oracle.rank_decode(inp["qc"].cpu(), inp["kc"].cpu(), inp["vc"].cpu(), pk, pv, slots, lens, layer)
     check_close(oc, ref, f"e4m3 ranking decode D={D} k={k}")
@@ -215,7 +215,7 @@ def test_serving_shape_on_e4m3_pool_sampled():
             if cl == l:
                 outs[(l, b)] = (oc[b:b + 1].cpu(), {kk: vv[b:b + 1].cpu() for kk, vv in x.items()})
     torch.cuda.synchronize()
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     for (l, b), (got, x) in outs.items():
         s = slots[b]
         pk = oracle.e4m3_decode(codes(pool.k[l:l + 1, s:s + 1]))
@@ -243,7 +243,7 @@ def test_block_on_e4m3_pool():
     fa.block_forward(ctx, w, fa.BLOCK_HISTORY, xh, pool, slots, lens, 0)
     fa.block_forward(ctx, w, fa.BLOCK_CANDIDATES, xc, pool, slots, lens, 0)
     torch.cuda.synchronize()
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     pk, pv = oracle.e4m3_decode(codes(pool.k)), oracle.e4m3_decode(codes(pool.v))
     ref = oracle.block_candidates(xc0, {kk: vv.cpu() for kk, vv in w.items()}, H, pk, pv, slots, lens, 0)
     g = oracle.as_f64(xc)
