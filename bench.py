@@ -20,12 +20,11 @@ token per user and head appended to its slot) on the serving shape and on the lo
 history shape; it is a secondary figure and does not enter `value`.
 
 `--block-only` runs only the Table 2 transformer measurement (3 timed passes).
-`--sdpa-reference` times torch's fused attention beside this library at one layer.
 `--workloads` replaces all of this with a per-kernel table over every bf16 workload
 (one layer each, cold and back to back).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ar-step] [--no-block] [--no-e4m3]
-                       [--workloads] [--block-only] [--sdpa-reference]
+                       [--workloads] [--block-only]
 """
 from __future__ import annotations
 
@@ -66,10 +65,6 @@ def parse_args():
     p.add_argument("--workloads", action="store_true",
                    help="instead of the serving step, time one layer's prefill and decode on every bf16 "
                         "workload, cold (a 512 MiB overwrite before each launch) and back to back")
-    p.add_argument("--sdpa-reference", action="store_true",
-                   help="instead of the serving step, time torch's scaled-dot-product attention (the "
-                        "platform's fused attention, the pages' own baseline) at one layer of the serving "
-                        "shape, beside this library's kernels on the same inputs")
     p.add_argument("--block-only", action="store_true",
                    help="instead of the serving step, run only the Table 2 transformer measurement "
                         "(3 timed passes after 1 warm-up; a short program for a kernel trace)")
@@ -125,7 +120,7 @@ def ar_step(fa, W, torch, dev, w, lens, steps: int, warmup: int, pool_dtype=None
         if j >= warmup:
             ev[2 * (j - warmup) + 1].record(stream)
     torch.cuda.synchronize()
-    if fa.device_status(dev) != 0:
+    if pool.status() != 0:
         raise RuntimeError("the autoregressive step flagged an invalid slot or length")
     avg_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / (steps * w.L)
     rows = sum(lens) + w.B * (warmup + (steps - 1) / 2)   # mean slot fill over the timed steps
@@ -166,7 +161,7 @@ def serving_step_e4m3(fa, torch, dev, w, layers, lens, steps: int, warmup: int):
         if e:
             e[2].record(stream)
     torch.cuda.synchronize()
-    if fa.device_status(dev) != 0:
+    if pool.status() != 0:
         raise RuntimeError("a kernel flagged an invalid slot or length")
     pf = sum(e[0].elapsed_time(e[1]) for e in ev) / (steps * w.L)
     dc = sum(e[1].elapsed_time(e[2]) for e in ev) / (steps * w.L)
@@ -218,7 +213,7 @@ def block_table2(fa, W, torch, dev, steps: int, warmup: int):
         if e:
             e[2].record(stream)
     torch.cuda.synchronize()
-    if fa.device_status(dev) != 0:
+    if pool.status() != 0:
         raise RuntimeError("a block flagged an invalid slot or length")
     hist_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     cand_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
@@ -283,69 +278,11 @@ def workload_kernels(fa, W, torch, dev, launches: int = 10, warmup: int = 3):
                            "cold_mfma_frac": round(flop / (t / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                            "cold_gbs": round(byts / (t / 1e3) / 1e9, 1),
                            "cold_hbm_frac": round(byts / (t / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
-        if fa.device_status(dev) != 0:
+        if pool.status() != 0:
             raise RuntimeError("a kernel flagged an invalid slot or length")
         pool.close()
         res[w.name] = entry
         del x, o, oc
-    return res
-
-
-def sdpa_reference(fa, W, torch, dev, launches: int = 20):
-    """One layer of the serving shape through torch's scaled-dot-product attention (ROCm's
-    fused attention kernels) and through this library, back to back on the same inputs:
-    the decode-shaped product (1000 queries over the 512 history keys, without the
-    candidate's own key), the causal prefill over 512 rows (without the pool write) and
-    one new token per user and head over the 512 rows (without its own key and the
-    append)."""
-    import torch.nn.functional as F
-    w = W.WORKLOADS[3]
-    x = W.layer_inputs(w, 0, dev)
-    lens = W.history_lengths(w).tolist()
-    lens_d = torch.as_tensor(lens, dtype=torch.int32, device=dev)
-    pool = fa.Pool.allocate(1, w.S, w.H, w.n, w.D, w.dtype, dev)
-    slots = torch.tensor(pool.acquire_many(w.B), dtype=torch.int32, device=dev)
-    fa.prefill(x["q"], x["k"], x["v"], lens_d, pool, slots, 0)
-
-    def timed(fn):
-        for _ in range(3):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(launches):
-            fn()
-        e1.record()
-        e1.synchronize()
-        return e0.elapsed_time(e1) / launches
-
-    pf, _, df, _ = algorithmic(w, lens)
-    q1, k1, v1 = (x[n][:, :, :1].contiguous() for n in ("qc", "kc", "vc"))   # one new token per (user, head)
-    # the library's step appends at row lens[b]: a pool one row longer, lens kept at 512
-    pool1 = fa.Pool.allocate(1, w.S, w.H, w.n + 1, w.D, w.dtype, dev)
-    slots1 = torch.tensor(pool1.acquire_many(w.B), dtype=torch.int32, device=dev)
-    fa.prefill(x["q"], x["k"], x["v"], lens_d, pool1, slots1, 0)
-    res = {}
-    for name, backend in (("flash", torch.nn.attention.SDPBackend.FLASH_ATTENTION),
-                          ("efficient", torch.nn.attention.SDPBackend.EFFICIENT_ATTENTION)):
-        try:
-            with torch.nn.attention.sdpa_kernel(backend):
-                d_ms = timed(lambda: F.scaled_dot_product_attention(x["qc"], x["k"], x["v"]))
-                p_ms = timed(lambda: F.scaled_dot_product_attention(x["q"], x["k"], x["v"], is_causal=True))
-                t_ms = timed(lambda: F.scaled_dot_product_attention(q1, x["k"], x["v"]))
-            res["torch_sdpa_" + name] = {"decode_shaped_ms": round(d_ms, 5), "causal_prefill_ms": round(p_ms, 5),
-                                         "one_token_ms": round(t_ms, 5)}
-        except RuntimeError as e:  # a backend the build does not have
-            res["torch_sdpa_" + name] = {"unavailable": str(e)[:200]}
-    d_ms = timed(lambda: fa.rank_decode(x["qc"], x["kc"], x["vc"], pool, slots, lens_d, 0))
-    p_ms = timed(lambda: fa.prefill(x["q"], x["k"], x["v"], lens_d, pool, slots, 0))
-    t_ms = timed(lambda: fa.ar_decode(q1, k1, v1, pool1, slots1, lens_d, 0))
-    res["this_library"] = {"rank_decode_ms": round(d_ms, 5), "prefill_ms": round(p_ms, 5), "ar_step_ms": round(t_ms, 5),
-                           "rank_decode_tflops": round(df / (d_ms / 1e3) / 1e12, 1),
-                           "prefill_tflops": round(pf / (p_ms / 1e3) / 1e12, 1)}
-    res["note"] = ("one layer of the serving shape, warm (the same inputs back to back); torch's "
-                   "decode-shaped call omits the candidate's own key and its prefill the pool write")
-    pool.close()
-    pool1.close()
     return res
 
 
@@ -464,9 +401,6 @@ def main():
     w = W.WORKLOADS[3]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.sdpa_reference:
-        print(json.dumps({"sdpa_reference": sdpa_reference(fa, W, torch, dev)}), flush=True)
-        return
     if args.block_only:
         print(json.dumps({"block_table2": block_table2(fa, W, torch, dev, steps=3, warmup=1)}), flush=True)
         return
@@ -512,7 +446,7 @@ def main():
         step(all_events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    if fa.device_status(dev) != 0:
+    if pool.status() != 0:
         raise RuntimeError("a kernel flagged an invalid slot or length")
 
     pf_per_step = sorted(ev[0].elapsed_time(ev[1]) / w.L for ev in all_events)

@@ -1,7 +1,10 @@
 """GPU parity: the HIP path (through the C ABI) against the float64 oracle.
 
 Tolerances (applied to history rows t < lens[b] and to every candidate row):
-  * fp32: normwise max|gpu - oracle| / max|oracle| <= 1e-5 per output tensor;
+  * fp32: max relative error <= 1e-5, checked two ways: normwise,
+    max|gpu - oracle| / max|oracle| per output tensor, and element by element,
+    max |gpu - oracle| / max(|oracle|, 1e-3) (the floor keeps outputs near zero, whose
+    relative error is undefined, from deciding the figure);
   * bf16 inputs with fp32 accumulation: max|gpu - oracle| <= 2e-2 and
     mean|gpu - oracle| <= 2e-3.
 The oracle runs on the exact bits the GPU received (upcast to float64).  Integer and
@@ -37,7 +40,9 @@ def check_close(got: torch.Tensor, ref: np.ndarray, dtype: torch.dtype, what: st
     if dtype == torch.float32:
         rel = diff.max() / max(np.abs(r).max(), 1e-30)
         assert rel <= 1e-5, f"{what}: normwise relative error {rel:.3e} > 1e-5"
-        return rel
+        elem = (diff / np.maximum(np.abs(r), 1e-3)).max()
+        assert elem <= 1e-5, f"{what}: element-wise relative error {elem:.3e} > 1e-5 (floor 1e-3)"
+        return max(rel, elem)
     mx, mean = diff.max(), diff.mean()
     assert mx <= 2e-2, f"{what}: max abs error {mx:.3e} > 2e-2"
     assert mean <= 2e-3, f"{what}: mean abs error {mean:.3e} > 2e-3"
@@ -90,7 +95,7 @@ def test_workload_full(idx):
     inp = W.layer_inputs(w, 0, DEV)
     o, oc = run_layer(pool, inp, lens, slots, 0)
     full_check(inp, lens, o, oc, pool, slots, 0, w.dtype, tag=f"w{idx}")
-    assert fa.device_status() == 0
+    assert pool.status() == 0
 
 
 def test_workload_ragged_sampled_users():
@@ -102,9 +107,12 @@ def test_workload_ragged_sampled_users():
     inp = W.layer_inputs(w, 0, DEV)
     o, oc = run_layer(pool, inp, lens, slots, 0)
     order = np.argsort(lens)
-    users = sorted(set([int(order[0]), int(order[-1]), 0, 17, 31, 63]))
+    # the shortest and longest histories, the users around the length quartiles, and
+    # every fourth user (all heads, all rows of each)
+    users = sorted(set([int(order[i]) for i in (0, 1, 16, 32, 48, 62, 63)] + list(range(0, 64, 4))))
+    assert len(users) >= 16
     full_check(inp, lens, o, oc, pool, slots, 0, w.dtype, users=users, tag="w2")
-    assert fa.device_status() == 0
+    assert pool.status() == 0
 
 
 def test_serving_shape_twelve_layers_sampled():
@@ -138,10 +146,14 @@ def test_serving_shape_twelve_layers_sampled():
                                                 pool.k[l, slots[b], h].cpu(), pool.v[l, slots[b], h].cpu(),
                                                 range(1000))
                 check_close(outc[l][b, h], ref_c, w.dtype, f"decode layer {l} b{b} h{h}")
-    assert fa.device_status() == 0
+    assert pool.status() == 0
 
 
 def test_long_history_sampled():
+    """Long histories (D = 128): every head of the shortest, the longest and two more
+    users.  Per (user, head): the first and last row of every 256-row query tile and of
+    every 256-candidate tile, the rows around each 64-key tile edge of the first tile,
+    and random rows; pool rows bit for bit."""
     w = W.WORKLOADS[4]
     announce(f"workload 4 sampled rows: {w.name}")
     lens = W.history_lengths(w).tolist()
@@ -151,19 +163,25 @@ def test_long_history_sampled():
     o, oc = run_layer(pool, inp, lens, slots, 0)
     rng = np.random.default_rng(4)
     order = np.argsort(lens)
-    for b in (int(order[0]), int(order[-1]), 5):
-        h = int(rng.integers(w.H))
+    users = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2]), 5]))
+    assert len(users) >= 4
+    tile = 256
+    for b in users:
         N = lens[b]
         assert torch.equal(pool.k[0, slots[b], :, :N].cpu(), inp["k"][b, :, :N].cpu())
         assert torch.equal(pool.v[0, slots[b], :, :N].cpu(), inp["v"][b, :, :N].cpu())
-        rows = sorted(set([0, 1, 63, 64, 255, 256, N - 1] + rng.integers(0, N, 40).tolist()))
-        ref = oracle.prefill_rows(inp["q"][b, h].cpu(), inp["k"][b, h].cpu(), inp["v"][b, h].cpu(), N, rows)
-        check_close(o[b, h, rows], ref, w.dtype, f"prefill b{b} h{h} N={N}")
-        crow = sorted(set([0, 255, 256, 2047] + rng.integers(0, w.k, 60).tolist()))
-        ref = oracle.rank_decode_rows(inp["qc"][b, h].cpu(), inp["kc"][b, h].cpu(), inp["vc"][b, h].cpu(),
-                                      inp["k"][b, h, :N].cpu(), inp["v"][b, h, :N].cpu(), crow)
-        check_close(oc[b, h, crow], ref, w.dtype, f"decode b{b} h{h} N={N}")
-    assert fa.device_status() == 0
+        edges = [r for t in range(0, N, tile) for r in (t, min(t + tile, N) - 1)]
+        crow_edges = [r for t in range(0, w.k, tile) for r in (t, min(t + tile, w.k) - 1)]
+        for h in range(w.H):
+            rows = sorted(set(edges + [1, 63, 64, 65, 127, 128] + rng.integers(0, N, 12).tolist()))
+            rows = [r for r in rows if r < N]
+            ref = oracle.prefill_rows(inp["q"][b, h].cpu(), inp["k"][b, h].cpu(), inp["v"][b, h].cpu(), N, rows)
+            check_close(o[b, h, rows], ref, w.dtype, f"prefill b{b} h{h} N={N}")
+            crow = sorted(set(crow_edges + rng.integers(0, w.k, 16).tolist()))
+            ref = oracle.rank_decode_rows(inp["qc"][b, h].cpu(), inp["kc"][b, h].cpu(), inp["vc"][b, h].cpu(),
+                                          inp["k"][b, h, :N].cpu(), inp["v"][b, h, :N].cpu(), crow)
+            check_close(oc[b, h, crow], ref, w.dtype, f"decode b{b} h{h} N={N}")
+    assert pool.status() == 0
 
 
 # ------------------------------------------------------------------ edge cases
@@ -199,7 +217,7 @@ def test_edge_shapes(case):
     if 0 in lens:
         b = lens.index(0)
         assert torch.equal(oc[b], inp["vc"][b]), "empty history must return vc exactly"
-    assert fa.device_status() == 0
+    assert pool.status() == 0
 
 
 def test_nan_poison_rows_past_history_are_never_read():
@@ -295,7 +313,7 @@ def test_repeated_launches_are_bitwise_identical():
             assert torch.equal(oc, ref), f"rank_decode differs at launch {it}"
             assert torch.equal(o, ref_o), f"prefill differs at launch {it}"
     torch.cuda.synchronize()
-    assert fa.device_status(torch.device(DEV)) == 0
+    assert pool.status() == 0
 
 
 def test_same_data_other_slot_or_layer_is_bitwise_identical():
@@ -341,16 +359,51 @@ def test_device_side_invalid_user_is_skipped_and_flagged():
     announce("device status flags")
     inp = W.small_case(B, H, D, n, k, [128, 64, 10], seed=13, device=DEV)
     pool = fa.Pool.allocate(1, 2, H, n, D, torch.bfloat16, DEV)
-    assert fa.device_status() == 0
+    assert pool.status() == 0
     o = torch.full_like(inp["q"], 7.0)
     fa.prefill(inp["q"], inp["k"], inp["v"], [128, 64, 10], pool, [0, 5, 1], 0, o=o)  # slot 5 >= S
-    assert fa.device_status() == fa.FLAG_BAD_SLOT
+    assert pool.status() == fa.FLAG_BAD_SLOT
     assert (o[1] == 7.0).all(), "a skipped user's output must stay untouched"
     fa.prefill(inp["q"], inp["k"], inp["v"], [128, 129, 10], pool, [0, 1, 1], 0, o=o)  # len > n
-    assert fa.device_status() == fa.FLAG_BAD_LEN
+    assert pool.status() == fa.FLAG_BAD_LEN
     oc = torch.full_like(inp["qc"], 7.0)
     fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, [0, -1, 1], [128, 64, 10], 0, oc=oc)
-    assert fa.device_status() == fa.FLAG_BAD_SLOT
+    assert pool.status() == fa.FLAG_BAD_SLOT
     assert (oc[1] == 7.0).all()
     assert torch.isfinite(oc[0]).all() and torch.isfinite(oc[2]).all()
-    assert fa.device_status() == 0
+    assert pool.status() == 0
+
+
+def test_flags_belong_to_the_pool_whose_call_raised_them():
+    """Two pools on one device: an invalid user in a call on one pool raises that pool's
+    flag only."""
+    B, H, D, n, k = 2, 2, 64, 64, 32
+    announce("per-pool status flags")
+    inp = W.small_case(B, H, D, n, k, [64, 20], seed=14, device=DEV)
+    pa = fa.Pool.allocate(1, 2, H, n, D, torch.bfloat16, DEV)
+    pb = fa.Pool.allocate(1, 3, H, n, D, torch.bfloat16, DEV)
+    assert pa.status() == 0 and pb.status() == 0
+    fa.prefill(inp["q"], inp["k"], inp["v"], [64, 20], pa, [0, 2], 0)      # slot 2 >= S of pool a
+    fa.prefill(inp["q"], inp["k"], inp["v"], [64, 20], pb, [0, 2], 0)      # valid on pool b
+    assert pb.status() == 0
+    assert pa.status() == fa.FLAG_BAD_SLOT
+    fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pb, [0, 2], [64, n + 1], 0)   # len > n_max on b
+    fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pa, [0, 1], [64, 20], 0)
+    assert pa.status() == 0
+    assert pb.status() == fa.FLAG_BAD_LEN
+    # a flag raised by a kernel on another stream is kept until a status call takes it
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pa, [0, -1], [64, 20], 0)
+    side.synchronize()
+    assert pb.status() == 0
+    assert pa.status() == fa.FLAG_BAD_SLOT
+    assert pa.status() == 0
+    # a new descriptor that reuses a released entry does not inherit its flags
+    fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pa, [0, 7], [64, 20], 0)
+    torch.cuda.synchronize()
+    pa.close()
+    pc = fa.Pool(pb.k, pb.v)
+    assert pc.status() == 0
+    pc.close()
+    pb.close()
