@@ -25,14 +25,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libunipin.so")
 
 FP32, BF16, FP8_E4M3 = 0, 1, 2
-OK, EINVAL, ERANGE, EDTYPE, EALIGN, EDEVICE, EHIP, ENOMEM, EPERM, EIO = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+OK, EINVAL, ERANGE, EDTYPE, EALIGN, EDEVICE, EHIP, ENOMEM, EPERM, EIO, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
 FLAG_BAD_SLOT, FLAG_BAD_LEN = 1, 2
 
 # Every symbol include/unipin.h declares.
 EXPORTS = ("unipin_pool_create", "unipin_pool_destroy", "unipin_pool_acquire",
            "unipin_pool_generation", "unipin_pool_dims", "unipin_pool_export",
            "unipin_pool_import", "unipin_prefill",
-           "unipin_rank_decode", "unipin_ar_decode", "unipin_ar_decode_workspace_bytes",
+           "unipin_rank_decode", "unipin_ar_decode", "unipin_ar_decode_noalloc", "unipin_ar_decode_workspace_bytes",
            "unipin_pool_status", "unipin_strerror", "unipin_version",
            "unipin_block_ctx_create", "unipin_block_ctx_destroy", "unipin_block_workspace_bytes",
            "unipin_block_ctx_tune", "unipin_block_ctx_set_gemm", "unipin_block_forward")
@@ -71,6 +71,7 @@ def _load() -> ctypes.CDLL:
     lib.unipin_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp]
     lib.unipin_rank_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp]
     lib.unipin_ar_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+    lib.unipin_ar_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp]
     lib.unipin_ar_decode_workspace_bytes.argtypes = [vp, i32]
     lib.unipin_block_ctx_create.argtypes = [ctypes.POINTER(vp)]
     lib.unipin_block_ctx_destroy.argtypes = [vp]

@@ -22,10 +22,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "attn_launch.h"
 #include "e4m3.h"
 
 namespace unipin {
+
+// The split path's part states for callers that cannot allocate
+// (unipin_ar_decode_noalloc): one array per device, held until the process ends, shared
+// by every such call on that device.  Its size covers every shape the split rule makes:
+// at most 256 (user, head, part) states of D + 4 floats, D <= 128.
+constexpr size_t kArScratchBytes = (size_t)256 << 10;
+static __device__ __align__(256) float scratch[kArScratchBytes / sizeof(float)];
+
 namespace {
 
 typedef __bf16 bf16;
@@ -574,6 +585,31 @@ int ar_splits(long bh, int n_max, int D, int kind) {
 }
 
 size_t ar_workspace_bytes(long bh, int P, int D) { return P <= 1 ? 0 : (size_t)bh * P * (D + 4) * sizeof(float); }
+
+size_t ar_scratch_bytes() { return kArScratchBytes; }
+
+hipError_t ar_scratch(float **out) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<float *> ptrs[kMaxDevices];
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    float *p = ptrs[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(mu);
+        p = ptrs[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            // the device address of this device's copy; the host-side name is not one
+            e = hipGetSymbolAddress((void **)&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            ptrs[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 hipError_t launch_ar_decode(const AttnArgs &a, int D, int kind, float *ws, int P, hipStream_t stream) {
     if ((long)a.B * a.H <= 0) return hipSuccess;

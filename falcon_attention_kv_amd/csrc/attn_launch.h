@@ -75,6 +75,10 @@ hipError_t launch_ar_decode_fp32(const AttnArgs &a, int D, hipStream_t stream);
 int ar_splits(long bh, int n_max, int D, int kind);
 size_t ar_workspace_bytes(long bh, int P, int D);
 hipError_t launch_ar_decode(const AttnArgs &a, int D, int kind, float *ws, int P, hipStream_t stream);
+// The library's own split-path state array on the current device (for callers that cannot
+// allocate): its device address, looked up once per device, and its size in bytes.
+hipError_t ar_scratch(float **out);
+size_t ar_scratch_bytes();
 
 // Per-pool sticky flag words: one entry per live pool descriptor, in file-scope device
 // arrays on every device (addresses looked up once per device with hipGetSymbolAddress).

@@ -283,9 +283,15 @@ int unipin_rank_decode(const void *qc, const void *kc, const void *vc,
                                   layer, B, k, scale, stream);
 }
 
-int unipin_ar_decode(const void *q, const void *k, const void *v, unipin_pool_t *pool,
-                     const int32_t *slot, const int32_t *lens, int layer, int B, float scale,
-                     void *o, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The autoregressive step's shared body.  ws: the split path's state buffer (null: one
+// pass), or, with own_scratch, the library's static array.
+int ar_decode_call(const void *q, const void *k, const void *v, unipin_pool_t *pool, const int32_t *slot,
+                   const int32_t *lens, int layer, int B, float scale, void *o, void *workspace,
+                   size_t workspace_bytes, bool own_scratch, void *stream) {
     if (!pool || !q || !k || !v || !lens || !slot || !o) return UNIPIN_EINVAL;
     if (B < 1) return UNIPIN_EINVAL;
     if (layer < 0 || layer >= pool->L) return UNIPIN_ERANGE;
@@ -310,19 +316,41 @@ int unipin_ar_decode(const void *q, const void *k, const void *v, unipin_pool_t 
     a.tiles = 1;
     const int kind = pool->dtype;
     int parts = 1;
-    if (workspace) {
+    float *ws = nullptr;
+    if (own_scratch) {
+        parts = unipin::ar_splits((long)B * pool->H, pool->n_max, pool->D, kind);
+        if (unipin::ar_workspace_bytes((long)B * pool->H, parts, pool->D) > unipin::ar_scratch_bytes())
+            return UNIPIN_ESCRATCH;
+        if (parts > 1 && unipin::ar_scratch(&ws) != hipSuccess) return UNIPIN_EHIP;
+    } else if (workspace) {
         if (!aligned(workspace, 16)) return UNIPIN_EALIGN;
         parts = unipin::ar_splits((long)B * pool->H, pool->n_max, pool->D, kind);
         if (workspace_bytes < unipin::ar_workspace_bytes((long)B * pool->H, parts, pool->D)) return UNIPIN_EINVAL;
+        ws = static_cast<float *>(workspace);
     }
     rc = unipin::pool_kernel_prologue(pool, static_cast<hipStream_t>(stream), &a.status);
     if (rc) return rc;
     const hipError_t e =
         kind == UNIPIN_FP32
             ? unipin::launch_ar_decode_fp32(a, pool->D, static_cast<hipStream_t>(stream))
-            : unipin::launch_ar_decode(a, pool->D, kind, static_cast<float *>(workspace), parts,
-                                       static_cast<hipStream_t>(stream));
+            : unipin::launch_ar_decode(a, pool->D, kind, ws, parts, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? UNIPIN_OK : UNIPIN_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int unipin_ar_decode(const void *q, const void *k, const void *v, unipin_pool_t *pool,
+                     const int32_t *slot, const int32_t *lens, int layer, int B, float scale,
+                     void *o, void *workspace, size_t workspace_bytes, void *stream) {
+    return ar_decode_call(q, k, v, pool, slot, lens, layer, B, scale, o, workspace, workspace_bytes, false, stream);
+}
+
+int unipin_ar_decode_noalloc(const void *q, const void *k, const void *v, unipin_pool_t *pool,
+                             const int32_t *slot, const int32_t *lens, int layer, int B, float scale,
+                             void *o, void *stream) {
+    return ar_decode_call(q, k, v, pool, slot, lens, layer, B, scale, o, nullptr, 0, true, stream);
 }
 
 size_t unipin_ar_decode_workspace_bytes(const unipin_pool_t *pool, int B) {
@@ -361,6 +389,7 @@ const char *unipin_strerror(int status) {
         case UNIPIN_ENOMEM: return "out of host memory or pool descriptors";
         case UNIPIN_EPERM: return "the pool is imported read-only (rank decode only)";
         case UNIPIN_EIO: return "a pool share file or shared page could not be written, read or mapped";
+        case UNIPIN_ESCRATCH: return "the call needs more scratch than the library's static array holds";
         default: return "unknown status";
     }
 }

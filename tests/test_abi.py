@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 def test_version_and_strerror():
     assert lib.unipin_version() == 10000
     for code in (fa.OK, fa.EINVAL, fa.ERANGE, fa.EDTYPE, fa.EALIGN, fa.EDEVICE, fa.EHIP, fa.ENOMEM, fa.EPERM,
-                 fa.EIO):
+                 fa.EIO, fa.ESCRATCH):
         text = lib.unipin_strerror(code).decode()
         assert text and text != "unknown status"
     assert lib.unipin_strerror(-99).decode() == "unknown status"
@@ -185,6 +185,11 @@ def _ar(h, q=FAKE, k=FAKE, v=FAKE, slot=FAKE, lens=FAKE, layer=0, B=1, scale=0.0
 def test_ar_decode_host_checks(kw, code):
     h = make_pool(L=2, n_max=16)
     assert _ar(h, **kw) == code
+    # the allocation-free variant checks its arguments the same way
+    a = dict(q=FAKE, k=FAKE, v=FAKE, slot=FAKE, lens=FAKE, layer=0, B=1, scale=0.0, o=FAKE)
+    a.update(kw)
+    assert lib.unipin_ar_decode_noalloc(a["q"], a["k"], a["v"], h, a["slot"], a["lens"], a["layer"], a["B"],
+                                        a["scale"], a["o"], None) == code
     lib.unipin_pool_destroy(h)
 
 
