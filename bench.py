@@ -19,12 +19,19 @@ serving step and the retrieval step with the pool stored as E4M3 codes, and `ar_
 token per user and head appended to its slot) on the serving shape and on the long
 history shape; it is a secondary figure and does not enter `value`.
 
+`long_history` times one layer of the long-history workload (B=16, H=16, D=128, histories
+1024..4096, 2048 candidates: the workload bound by the matrix cores), cold.  `probes`
+reports the matrix-core rate a plain MFMA loop reaches and whether a SIMD overlaps
+matrix-core with exponential work (libunipin_probe.so), beside `hbm_copy_reference`.
+
 `--block-only` runs only the Table 2 transformer measurement (3 timed passes).
+`--probes` runs only the probes.
 `--workloads` replaces all of this with a per-kernel table over every bf16 workload
-(one layer each, cold and back to back).
+(one layer each, cold and back to back), with the ragged/full time ratios of the two
+ragged workloads beside the ratios of their algorithmic work.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ar-step] [--no-block] [--no-e4m3]
-                       [--workloads] [--block-only]
+                       [--no-long-history] [--workloads] [--block-only] [--probes]
 """
 from __future__ import annotations
 
@@ -62,6 +69,10 @@ def parse_args():
                    help="skip the secondary measurement of the 12-layer transformer at the Table 2 shape")
     p.add_argument("--no-e4m3", action="store_true",
                    help="skip the secondary measurements on an E4M3 pool")
+    p.add_argument("--no-long-history", action="store_true",
+                   help="skip the secondary one-layer measurement of the long-history workload (D = 128)")
+    p.add_argument("--probes", action="store_true",
+                   help="instead of the serving step, run only the matrix-core and overlap probes")
     p.add_argument("--workloads", action="store_true",
                    help="instead of the serving step, time one layer's prefill and decode on every bf16 "
                         "workload, cold (a 512 MiB overwrite before each launch) and back to back")
@@ -227,63 +238,112 @@ def block_table2(fa, W, torch, dev, steps: int, warmup: int):
             "candidate_mfma_frac": round(cand_flop / cand_ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
 
 
+def layer_kernels(fa, W, torch, dev, w, lens, flush, launches: int = 10, warmup: int = 3):
+    """One layer's prefill and rank decode of workload w with history lengths `lens`.
+    Cold: before each launch the 512 MiB `flush` buffer is overwritten, so inputs and pool
+    come from HBM, and HIP events bracket the launch alone (median reported).  Warm:
+    `launches` back-to-back launches on the same inputs (mean reported)."""
+    stream = torch.cuda.current_stream(dev)
+    lens_d = torch.as_tensor(lens, dtype=torch.int32, device=dev)
+    x = W.layer_inputs(w, 0, dev)
+    pool = fa.Pool.allocate(1, w.S, w.H, w.n, w.D, w.dtype, dev)
+    slots = torch.tensor(pool.acquire_many(w.B), dtype=torch.int32, device=dev)
+    o, oc = torch.empty_like(x["q"]), torch.empty_like(x["qc"])
+    calls = {
+        "prefill": lambda: fa.prefill(x["q"], x["k"], x["v"], lens_d, pool, slots, 0, o=o),
+        "rank_decode": lambda: fa.rank_decode(x["qc"], x["kc"], x["vc"], pool, slots, lens_d, 0, oc=oc),
+    }
+    pf, pb, df, db = algorithmic(w, lens)
+    work = {"prefill": (pf, pb), "rank_decode": (df, db)}
+    entry = {}
+    for name, call in calls.items():
+        for _ in range(warmup):
+            call()
+        cold = []
+        for _ in range(launches):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            e1.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        cold.sort()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            call()
+        e1.record(stream)
+        e1.synchronize()
+        warm = e0.elapsed_time(e1) / launches
+        flop, byts = work[name]
+        t = cold[len(cold) // 2]
+        entry[name] = {"cold_median_ms": round(t, 5), "warm_mean_ms": round(warm, 5),
+                       "algorithmic_gflop": round(flop / 1e9, 3), "algorithmic_mb": round(byts / 1e6, 2),
+                       "cold_tflops": round(flop / (t / 1e3) / 1e12, 1),
+                       "cold_mfma_frac": round(flop / (t / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                       "cold_gbs": round(byts / (t / 1e3) / 1e9, 1),
+                       "cold_hbm_frac": round(byts / (t / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if pool.status() != 0:
+        raise RuntimeError("a kernel flagged an invalid slot or length")
+    pool.close()
+    del x, o, oc
+    return entry
+
+
 def workload_kernels(fa, W, torch, dev, launches: int = 10, warmup: int = 3):
     """One layer's prefill and rank decode on each bf16 workload (the parity shapes and
-    the serving shape's first layer).  Cold: before each launch a 512 MiB buffer is
-    overwritten, so inputs and pool come from HBM, and HIP events bracket the launch
-    alone (median reported).  Warm: `launches` back-to-back launches on the same inputs
-    between two events (mean reported)."""
+    the serving shape's first layer), cold and warm (layer_kernels).  For the two ragged
+    workloads the same launches also run with every history at full length, and the
+    ragged/full time ratios are reported beside the ratios of the algorithmic FLOPs
+    (decode: sum(len + 1) / (B (n + 1)); prefill: sum(len (len + 1)) / (B n (n + 1))) and
+    bytes (the candidates' rows do not shrink with the history), with the roof that binds
+    the full-length launch: a kernel whose time follows the real work, not the padded
+    extent, matches the ratio of that roof."""
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
     res = {}
     for w in W.WORKLOADS[1:]:
         lens = W.history_lengths(w).tolist()
-        lens_d = torch.as_tensor(lens, dtype=torch.int32, device=dev)
-        x = W.layer_inputs(w, 0, dev)
-        pool = fa.Pool.allocate(1, w.S, w.H, w.n, w.D, w.dtype, dev)
-        slots = torch.tensor(pool.acquire_many(w.B), dtype=torch.int32, device=dev)
-        o, oc = torch.empty_like(x["q"]), torch.empty_like(x["qc"])
-        calls = {
-            "prefill": lambda: fa.prefill(x["q"], x["k"], x["v"], lens_d, pool, slots, 0, o=o),
-            "rank_decode": lambda: fa.rank_decode(x["qc"], x["kc"], x["vc"], pool, slots, lens_d, 0, oc=oc),
-        }
-        pf, pb, df, db = algorithmic(w, lens)
-        work = {"prefill": (pf, pb), "rank_decode": (df, db)}
-        entry = {}
-        for name, call in calls.items():
-            for _ in range(warmup):
-                call()
-            cold = []
-            for _ in range(launches):
-                flush.fill_(1)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                call()
-                e1.record(stream)
-                e1.synchronize()
-                cold.append(e0.elapsed_time(e1))
-            cold.sort()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(launches):
-                call()
-            e1.record(stream)
-            e1.synchronize()
-            warm = e0.elapsed_time(e1) / launches
-            flop, byts = work[name]
-            t = cold[len(cold) // 2]
-            entry[name] = {"cold_median_ms": round(t, 5), "warm_mean_ms": round(warm, 5),
-                           "algorithmic_gflop": round(flop / 1e9, 3), "algorithmic_mb": round(byts / 1e6, 2),
-                           "cold_tflops": round(flop / (t / 1e3) / 1e12, 1),
-                           "cold_mfma_frac": round(flop / (t / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                           "cold_gbs": round(byts / (t / 1e3) / 1e9, 1),
-                           "cold_hbm_frac": round(byts / (t / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
-        if pool.status() != 0:
-            raise RuntimeError("a kernel flagged an invalid slot or length")
-        pool.close()
+        entry = layer_kernels(fa, W, torch, dev, w, lens, flush, launches, warmup)
+        if w.len_lo != w.len_hi:
+            full = layer_kernels(fa, W, torch, dev, w, [w.n] * w.B, flush, launches, warmup)
+            flen = [w.n] * w.B
+            (pf, pb, df, db), (fpf, fpb, fdf, fdb) = algorithmic(w, lens), algorithmic(w, flen)
+            entry["full_length"] = full
+            ratios = {}
+            for name, flop, byts, fflop, fbyts in (("prefill", pf, pb, fpf, fpb), ("rank_decode", df, db, fdf, fdb)):
+                # the roof that binds the full-length launch decides which work ratio applies
+                bound = "mfma" if fflop / BF16_PEAK_TFLOPS / 1e12 > fbyts / HBM_PEAK_GBS / 1e9 else "hbm"
+                ratios[name] = {"cold": round(entry[name]["cold_median_ms"] / full[name]["cold_median_ms"], 4),
+                                "flop_ratio": round(flop / fflop, 4), "byte_ratio": round(byts / fbyts, 4),
+                                "bound": bound}
+            entry["ragged_over_full"] = ratios
         res[w.name] = entry
-        del x, o, oc
     return res
+
+
+def probes(torch, dev) -> dict:
+    """The chip's achievable matrix-core rate and whether a SIMD overlaps matrix-core and
+    exponential work (libunipin_probe.so; two waves per SIMD on every CU)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "falcon_attention_kv_amd", "libunipin_probe.so"))
+    lib.unipin_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.unipin_probe_overlap.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    buf = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+    tf = ctypes.c_double()
+    if lib.unipin_probe_mfma(buf.data_ptr(), cus, 20000, ctypes.byref(tf)) != 0:
+        raise RuntimeError("unipin_probe_mfma failed")
+    ns = (ctypes.c_double * 4)()
+    if lib.unipin_probe_overlap(buf.data_ptr(), cus, 20000, ns) != 0:
+        raise RuntimeError("unipin_probe_overlap failed")
+    m, e, both, split = (round(v, 2) for v in ns)
+    return {"mfma_loop": {"tflops": round(tf.value, 1), "frac_of_peak": round(tf.value / BF16_PEAK_TFLOPS, 4),
+                          "what": f"{cus} CUs x 8 waves of independent 32x32x16 bf16 MFMAs"},
+            "mfma_exp_overlap_ns_per_iter": {
+                "mfma_only": m, "exp_only": e, "both_in_each_wave": both, "mfma_wave_beside_exp_wave": split,
+                "what": "per SIMD and loop iteration, two waves: 8 MFMAs and/or 32 (v_exp_f32 + subtract) "
+                        "per wave; full overlap would give max(mfma_only, exp_only), none their sum"}}
 
 
 def copy_calibration(torch, dev, mib: int) -> int:
@@ -401,6 +461,9 @@ def main():
     w = W.WORKLOADS[3]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.probes:
+        print(json.dumps({"probes": probes(torch, dev)}), flush=True)
+        return
     if args.block_only:
         print(json.dumps({"block_table2": block_table2(fa, W, torch, dev, steps=3, warmup=1)}), flush=True)
         return
@@ -508,6 +571,14 @@ def main():
         out["copy_calibration_bytes"] = copy_calibration(torch, dev, args.copy_calib_mib)
     else:  # kept out of the counter runs, whose calibration picks the run's largest copies
         out["hbm_copy_reference"] = hbm_copy_reference(torch, dev)
+        out["probes"] = probes(torch, dev)
+    if not args.no_long_history:
+        # the matrix-core-bound workload (D = 128, long ragged histories), one layer, cold
+        wl = W.WORKLOADS[4]
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        lh = layer_kernels(fa, W, torch, dev, wl, W.history_lengths(wl).tolist(), flush, launches=5, warmup=2)
+        del flush
+        out["long_history"] = {"workload": wl.name, **lh}
     if not args.no_cpu_baseline:
         layers_cpu = [{k: v.cpu() for k, v in x.items()} for x in layers]
         out["cpu_baseline"] = cpu_baseline(w, layers_cpu, lens, args.cpu_seconds)

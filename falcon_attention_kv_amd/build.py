@@ -17,6 +17,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libunipin.so")
+# measurement probes (matrix-core peak, matrix/vector overlap): their own library, loaded
+# only by the benchmark
+PROBE_SOURCES = ["probe.hip"]
+PROBE_LIB = os.path.join(PKG, "libunipin_probe.so")
 SOURCES = ["unipin.cpp", "pool_share.cpp", "pool_status.hip", "attn_bf16.hip", "attn_fp32.hip", "attn_ar.hip",
            "block.cpp", "block_kernels.hip", "gemm_bf16.hip"]
 # hipBLASLt is one of the two GEMM kernel families of the block; found at run time through
@@ -52,18 +56,24 @@ def _compile(src: str, extra, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra, verbose), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs + LINK
+def _link(objs, out, link, verbose):
+    tmp = out + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs + link
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB, LINK, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB, [], verbose)
     return LIB
 
 

@@ -541,6 +541,91 @@ __device__ __forceinline__ bool user_valid(const AttnArgs &a, int N, int s, bool
     return !(bad_len || bad_slot);
 }
 
+// ------------------------------------------------------------------ longest-first schedules
+// Both kernels hand their blocks out longest history first, so that the long (user,
+// head) pairs start at once and the short ones fill the CUs at the end, and the prefill
+// launches no block for query tiles past a history.  The order is by the key
+// ceil(len / 64) (the history's 64-row tiles), descending, ties by user index; a length
+// outside [0, limit] ranks as the longest (its blocks only raise the flag).  Every wave
+// loads the keys of all B users (up to kOrderUsers, one register per 64 users) and
+// finds the user of a rank by a binary search over key values, one ballot per 64 users
+// per probe.  Beyond kOrderUsers users the blocks keep the user order.
+constexpr int kOrderUsers = 256;
+
+struct UserKeys {
+    int key[kOrderUsers / 64];   // this lane's users lane, 64 + lane, ...; -1 past B
+    int len[kOrderUsers / 64];   // their lengths and slots (read only when asked for)
+    int slot[kOrderUsers / 64];
+    int chunks, kmax;
+};
+
+// slots may be null (the slots are then not loaded).
+__device__ __forceinline__ UserKeys load_keys(const int32_t *__restrict__ lens, const int32_t *__restrict__ slots,
+                                              int B, int limit) {
+    UserKeys k;
+    k.chunks = (B + 63) / 64;
+    k.kmax = (limit + kTK - 1) / kTK;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int c = 0; c < kOrderUsers / 64; ++c) {
+        const int u = c * 64 + lane;
+        k.len[c] = u < B ? lens[u] : 0;
+        k.slot[c] = (slots && u < B) ? slots[u] : 0;
+    }
+#pragma unroll
+    for (int c = 0; c < kOrderUsers / 64; ++c) {
+        const int u = c * 64 + lane, N = k.len[c];
+        k.key[c] = u >= B ? -1 : (N < 0 || N > limit) ? k.kmax : (N + kTK - 1) / kTK;
+    }
+    return k;
+}
+
+// User b's length and slot out of the loaded registers (wave-uniform b < B).
+__device__ __forceinline__ void user_len_slot(const UserKeys &k, int b, int &N, int &s) {
+    const int c = b >> 6, l = b & 63;
+    N = s = 0;
+#pragma unroll
+    for (int i = 0; i < kOrderUsers / 64; ++i)
+        if (i == c) {
+            N = __builtin_amdgcn_readlane(k.len[i], l);
+            s = __builtin_amdgcn_readlane(k.slot[i], l);
+        }
+}
+
+// Users whose key is at least K (wave-uniform).
+__device__ __forceinline__ int users_key_ge(const UserKeys &k, int K) {
+    int n = 0;
+#pragma unroll
+    for (int c = 0; c < kOrderUsers / 64; ++c)
+        if (c < k.chunks) n += __builtin_popcountll(__ballot(k.key[c] >= K));
+    return n;
+}
+
+// The user at rank r (0 <= r < B) of the longest-first order (wave-uniform).
+__device__ __forceinline__ int user_at_rank(const UserKeys &k, int r) {
+    int lo = 0, hi = k.kmax;   // the rank's key: the largest K with more than r users at >= K
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (users_key_ge(k, mid) > r) lo = mid;
+        else hi = mid - 1;
+    }
+    int j = r - users_key_ge(k, lo + 1);   // its place among the users with key lo
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int c = 0; c < kOrderUsers / 64; ++c) {
+        if (c >= k.chunks) break;
+        const unsigned long long m = __ballot(k.key[c] == lo);
+        const int n = __builtin_popcountll(m);
+        if (j < n) {
+            const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0));
+            const unsigned long long pick = __ballot(((m >> lane) & 1) && below == j);
+            return c * 64 + __builtin_ctzll(pick);
+        }
+        j -= n;
+    }
+    return r;   // not reached for 0 <= r < B
+}
+
 // ------------------------------------------------------------------ causal prefill
 
 // Maps the linear block id to (user*H + head, query tile).  With xcd_remap, blocks are
@@ -593,14 +678,38 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
     __shared__ __attribute__((aligned(1024))) char smem_raw[kBufs * T::BUF_BYTES];
     LDS_AS char *smem = (LDS_AS char *)smem_raw;
 
-    int group, tile;
-    block_coords<UNIPIN_PREFILL_TILE_MAJOR>(a, group, tile);
-    const int b = group / a.H, h = group % a.H;
-    if (b >= a.B) return;
-    const int qtile = a.tiles - 1 - tile;   // heaviest (last) query tiles first
-    const int N = lens[b];
-    const int s = slots[b];
-    if (!user_valid(a, N, s, tile == 0)) return;
+    int b, h, qtile, N, s;
+    if (a.B <= kOrderUsers) {
+        // Rounds q = tiles-1 .. 0 of query tile q, longest histories first; a round holds
+        // all heads of the users with more than q * 256 rows (key above 4 q).  Blocks past
+        // the last round have nothing to do.
+        static_assert(QT == 4 * kTK, "a query tile is four key tiles");
+        const UserKeys keys = load_keys(lens, slots, a.B, a.len_limit);
+        int rem = blockIdx.x;
+        qtile = -1;
+        for (int q = a.tiles - 1; q >= 0; --q) {
+            const int items = users_key_ge(keys, 4 * q + 1) * a.H;
+            if (rem < items) {
+                qtile = q;
+                break;
+            }
+            rem -= items;
+        }
+        if (qtile < 0) return;
+        b = user_at_rank(keys, rem / a.H);
+        h = rem % a.H;
+        user_len_slot(keys, b, N, s);
+    } else {
+        int group, tile;
+        block_coords<UNIPIN_PREFILL_TILE_MAJOR>(a, group, tile);
+        b = group / a.H;
+        h = group % a.H;
+        if (b >= a.B) return;
+        qtile = a.tiles - 1 - tile;   // heaviest (last) query tiles first
+        N = lens[b];
+        s = slots[b];
+    }
+    if (!user_valid(a, N, s, qtile == a.tiles - 1)) return;
     const int q0 = qtile * QT;
     if (q0 >= N) return;
 
@@ -735,8 +844,16 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
 
     int group, ctile;
     block_coords<false>(a, group, ctile);
-    const int b = group / a.H, h = group % a.H;
-    if (b >= a.B) return;
+    if (group >= a.B * a.H) return;
+    // the group's rank in the longest-first order of the users, and its head
+#ifndef UNIPIN_DECODE_ORDER
+#define UNIPIN_DECODE_ORDER 1
+#endif
+    const bool ordered = UNIPIN_DECODE_ORDER && a.B <= kOrderUsers;
+    UserKeys keys;
+    if (ordered) keys = load_keys(lens, slots, a.B, a.len_limit);
+    const int b = ordered ? user_at_rank(keys, group / a.H) : group / a.H;
+    const int h = group % a.H;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -756,8 +873,13 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
                                lane, in_rs);
     dma_rows<D, W, kBlockRows>(smem + 2 * T::BUF_BYTES, rsrc_words(static_cast<const bf16 *>(a.k) + in_off, rows_bytes),
                                row0, wave, lane, in_rs);
-    const int N = lens[b];
-    const int s = slots[b];
+    int N, s;
+    if (ordered) {
+        user_len_slot(keys, b, N, s);
+    } else {
+        N = lens[b];
+        s = slots[b];
+    }
     if (!user_valid(a, N, s, ctile == 0)) {
         wait_vmcnt<0>();
         return;

@@ -193,6 +193,10 @@ EDGE = [
     (torch.bfloat16, 2, 4, 32, 257, 257, [257, 100]),          # D = 32, no XCD remap (B*H = 8 -> remap)
     (torch.bfloat16, 1, 3, 128, 520, 300, [511]),              # D = 128, B*H not a multiple of 8
     (torch.bfloat16, 8, 1, 64, 512, 256, [512, 256, 255, 257, 1, 2, 500, 384]),
+    # 70 users, lengths in ties of one 64-row key and zeros: the longest-first schedules
+    (torch.bfloat16, 70, 1, 64, 200, 40, [(i * 37) % 201 if i % 9 else 0 for i in range(70)]),
+    # 300 users: past the ordered schedules' user limit (user order)
+    (torch.bfloat16, 300, 1, 64, 70, 9, [(i * 7) % 71 for i in range(300)]),
     (torch.float32, 2, 2, 64, 100, 33, [100, 37]),
     (torch.float32, 1, 2, 128, 70, 5, [0]),
     (torch.float32, 3, 1, 32, 65, 64, [65, 64, 1]),
