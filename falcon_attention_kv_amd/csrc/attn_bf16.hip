@@ -6,9 +6,10 @@
 // cached history key of its user plus its own key, never to another candidate.
 //
 // Work decomposition:
-//   * a workgroup covers 256 query rows: 8 waves of 32 rows at D <= 64 (4 waves per
-//     SIMD), 4 waves of 64 rows at D = 128; a wave holds its rows in registers as the
-//     B operand of v_mfma_f32_32x32x16_bf16;
+//   * a workgroup covers 256 query rows: 8 waves of 32 rows at every head dimension; a
+//     wave holds its rows in registers as the B operand of v_mfma_f32_32x32x16_bf16.  At
+//     D <= 64 two workgroups share a CU (4 waves per SIMD); at D = 128 the LDS ring (four
+//     32 KB slots) leaves room for one (2 waves per SIMD, up to 256 registers);
 //   * everything a workgroup reads from HBM arrives through the buffer-to-LDS DMA path
 //     (buffer_load_dwordx4 ... lds) into a ring of four LDS slots: 64-key tiles of K
 //     and V, up to three tiles ahead of use, and the 256-row blocks of queries (and, in
@@ -30,8 +31,9 @@
 //     normaliser matches the weights the PV product used;
 //   * masking runs only on tiles that cross the history end or the causal diagonal.
 //
-// The prefill launches one workgroup per (user, head, 256-row query tile), the ranking
-// decode one per (user, head, 256-candidate tile).
+// The prefill launches one workgroup per (user, head, 256-row query tile) that holds
+// history rows, the ranking decode one per (user, head, 256-candidate tile); both hand
+// out their work longest history first (see the schedules below).
 //
 // Hardware facts relied on (checked on gfx950 with small in-bounds probes):
 //   * v_mfma_f32_32x32x16_bf16 result element i of lane l is row 8*(i/4) + 4*(l/32)
@@ -58,9 +60,6 @@ constexpr int kTK = 64;                   // keys per LDS tile
 // LDS slots of the DMA ring (one 64-key K/V tile or 128 query rows each): 64 KB per
 // workgroup at D = 64, so that two workgroups share a CU.
 constexpr int kBufs = 4;
-#ifndef UNIPIN_PREFILL_TILE_MAJOR
-#define UNIPIN_PREFILL_TILE_MAJOR 1
-#endif
 
 // A workgroup covers 256 query rows: 8 waves of one 32-row query block each (QB = 1; the
 // tile code is written for QB blocks per wave, and two blocks per wave measured slower
@@ -701,7 +700,7 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
         user_len_slot(keys, b, N, s);
     } else {
         int group, tile;
-        block_coords<UNIPIN_PREFILL_TILE_MAJOR>(a, group, tile);
+        block_coords<true>(a, group, tile);
         b = group / a.H;
         h = group % a.H;
         if (b >= a.B) return;
@@ -846,10 +845,7 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
     block_coords<false>(a, group, ctile);
     if (group >= a.B * a.H) return;
     // the group's rank in the longest-first order of the users, and its head
-#ifndef UNIPIN_DECODE_ORDER
-#define UNIPIN_DECODE_ORDER 1
-#endif
-    const bool ordered = UNIPIN_DECODE_ORDER && a.B <= kOrderUsers;
+    const bool ordered = a.B <= kOrderUsers;
     UserKeys keys;
     if (ordered) keys = load_keys(lens, slots, a.B, a.len_limit);
     const int b = ordered ? user_at_rank(keys, group / a.H) : group / a.H;
