@@ -49,10 +49,21 @@ sys.path.insert(0, ROOT)
 METRIC = "ranked candidates/sec + TFLOP/s (frac of MFMA/HBM roofline), 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published (no sparsity)
-# the sources compiled into the bf16 attention kernels (the counters' validity check)
-KERNEL_SRC = [os.path.join(ROOT, "falcon_attention_kv_amd", "csrc", f)
-              for f in ("attn_bf16.hip", "lds_dma.h", "e4m3.h", "attn_launch.h")]
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "rank_decode_serving_shape_pmc.txt")
+CSRC = os.path.join(ROOT, "falcon_attention_kv_amd", "csrc")
+# The sources each committed profile summary depends on.  A summary records the hash of
+# its set (fields `sources:` and `kernel_source_sha256:`); it is current while that hash
+# matches the tree (`profiles` in the output line), and the decode traffic it holds
+# enters `roofline.traffic` only then.
+PROFILE_SOURCES = {
+    "attention": ["attn_bf16.hip", "lds_dma.h", "e4m3.h", "attn_launch.h"],
+    "ar": ["attn_ar.hip", "attn_fp32.hip", "e4m3.h", "attn_launch.h"],
+    "block": ["block.cpp", "block_kernels.hip", "gemm_bf16.hip", "block_launch.h", "lds_dma.h", "attn_bf16.hip",
+              "e4m3.h", "attn_launch.h"],
+    "probe": ["probe.hip"],
+}
+KERNEL_SRC = [os.path.join(CSRC, f) for f in PROFILE_SOURCES["attention"]]
+PROFILES = os.path.join(ROOT, "profiles")
+PMC_SUMMARY = os.path.join(PROFILES, "rank_decode_serving_shape_pmc.txt")
 
 
 def parse_args():
@@ -380,24 +391,51 @@ def hbm_copy_reference(torch, dev, mib: int = 1024, launches: int = 10) -> dict:
             "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def kernel_source_hash() -> str:
+def source_hash(kind: str) -> str:
+    """sha256[:16] over the sources of PROFILE_SOURCES[kind], in order."""
     h = hashlib.sha256()
-    for path in KERNEL_SRC:
-        with open(path, "rb") as f:
+    for name in PROFILE_SOURCES[kind]:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def kernel_source_hash() -> str:
+    return source_hash("attention")
+
+
+def summary_fields(path: str) -> dict:
+    """The `key: value` lines of a profile summary (comment lines start with '#')."""
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    return fields
+
+
+def profile_status() -> dict:
+    """Every committed profile summary with the source set it was taken on and whether
+    that set is unchanged since."""
+    out = {}
+    for name in sorted(os.listdir(PROFILES)):
+        try:
+            fields = summary_fields(os.path.join(PROFILES, name))
+            kind = fields.get("sources")
+            out[name] = {"sources": kind,
+                         "current": bool(kind in PROFILE_SOURCES and
+                                         fields.get("kernel_source_sha256") == source_hash(kind))}
+        except OSError:
+            out[name] = {"sources": None, "current": False}
+    return out
 
 
 def measured_traffic():
     """HBM bytes per decode launch from the committed rocprofv3 counter summary, or None
     when it is missing or was taken on a different kernel source."""
     try:
-        fields = {}
-        with open(PMC_SUMMARY) as f:
-            for line in f:
-                if ":" in line and not line.startswith("#"):
-                    k, v = line.split(":", 1)
-                    fields[k.strip()] = v.strip()
+        fields = summary_fields(PMC_SUMMARY)
         if fields.get("kernel_source_sha256") != kernel_source_hash():
             return None
         return float(fields["hbm_bytes_per_launch"])
@@ -565,6 +603,7 @@ def main():
                             "decode_candidates_per_s": round(cand_per_step / (w.L * dc_avg / 1e3), 1)},
         },
     }
+    out["profiles"] = profile_status()
     if not args.no_block:
         out["block_table2"] = block_table2(fa, W, torch, dev, steps=5, warmup=2)
     if args.copy_calib_mib:

@@ -46,3 +46,23 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["n_gpus"] == 2 and "--gpus must be 1" in line["error"]
+
+
+def test_every_profile_summary_names_its_sources_and_command():
+    # each committed rocprofv3 summary records the source set it was taken on, that
+    # set's hash as of the run, and the command that made it
+    import os
+    import re
+    status = bench.profile_status()
+    assert status, "no profile summaries"
+    for name, st in status.items():
+        assert st["sources"] in bench.PROFILE_SOURCES, name
+        fields = bench.summary_fields(os.path.join(bench.PROFILES, name))
+        assert re.fullmatch(r"[0-9a-f]{16}", fields["kernel_source_sha256"]), name
+        with open(os.path.join(bench.PROFILES, name)) as f:
+            text = f.read()
+        assert "# Commands" in text, name
+        assert "_work" not in text, name
+    for kind, files in bench.PROFILE_SOURCES.items():
+        for f in files:
+            assert os.path.isfile(os.path.join(bench.CSRC, f)), (kind, f)
