@@ -197,6 +197,9 @@ EDGE = [
     (torch.bfloat16, 70, 1, 64, 200, 40, [(i * 37) % 201 if i % 9 else 0 for i in range(70)]),
     # 300 users: past the ordered schedules' user limit (user order)
     (torch.bfloat16, 300, 1, 64, 70, 9, [(i * 7) % 71 for i in range(300)]),
+    # every history 257 .. 512 rows: two query tiles per (user, head), ragged tails
+    (torch.bfloat16, 16, 8, 64, 512, 40, [257, 512, 320, 511, 300, 448, 258, 400, 384, 500, 290, 333, 449, 510, 260, 385]),
+    (torch.bfloat16, 2, 8, 128, 400, 30, [257, 400]),
     (torch.float32, 2, 2, 64, 100, 33, [100, 37]),
     (torch.float32, 1, 2, 128, 70, 5, [0]),
     (torch.float32, 3, 1, 32, 65, 64, [65, 64, 1]),
@@ -376,6 +379,24 @@ def test_device_side_invalid_user_is_skipped_and_flagged():
     assert (oc[1] == 7.0).all()
     assert torch.isfinite(oc[0]).all() and torch.isfinite(oc[2]).all()
     assert pool.status() == 0
+
+
+def test_invalid_length_ranks_longest_and_only_flags():
+    """One invalid length among two-tile histories: the longest-first schedule ranks the
+    invalid user first; its blocks only raise the flag, the other user is exact."""
+    B, H, D, n, k = 2, 8, 64, 300, 16
+    announce("invalid length in the longest-first prefill schedule")
+    inp = W.small_case(B, H, D, n, k, [300, 280], seed=15, device=DEV)
+    pool = fa.Pool.allocate(1, 2, H, n, D, torch.bfloat16, DEV)
+    o = torch.full_like(inp["q"], 7.0)
+    fa.prefill(inp["q"], inp["k"], inp["v"], [300, 301], pool, [1, 0], 0, o=o)   # 301 > n
+    torch.cuda.synchronize()
+    assert pool.status() == fa.FLAG_BAD_LEN
+    assert (o[1] == 7.0).all(), "a skipped user's output must stay untouched"
+    sub = {kk: v[0:1].cpu() for kk, v in inp.items() if kk in ("q", "k", "v")}
+    ref = oracle.prefill(sub["q"], sub["k"], sub["v"], [300])
+    check_close(o[0:1], ref, torch.bfloat16, "valid user beside an invalid one")
+    assert torch.equal(pool.k[0, 1].cpu(), inp["k"][0].cpu()) and torch.equal(pool.v[0, 1].cpu(), inp["v"][0].cpu())
 
 
 def test_flags_belong_to_the_pool_whose_call_raised_them():
