@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libunipin.so")
 
 FP32, BF16, FP8_E4M3 = 0, 1, 2
 OK, EINVAL, ERANGE, EDTYPE, EALIGN, EDEVICE, EHIP, ENOMEM, EPERM, EIO, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
-FLAG_BAD_SLOT, FLAG_BAD_LEN = 1, 2
+FLAG_BAD_SLOT, FLAG_BAD_LEN, FLAG_DUP_SLOT = 1, 2, 4
 
 # Every symbol include/unipin.h declares.
 EXPORTS = ("unipin_pool_create", "unipin_pool_destroy", "unipin_pool_acquire",
@@ -201,9 +201,10 @@ class Pool:
         return int(lib.unipin_pool_generation(self.handle, int(slot)))
 
     def status(self, stream: Optional[torch.cuda.Stream] = None) -> int:
-        """unipin_pool_status: the sticky flags (FLAG_BAD_SLOT | FLAG_BAD_LEN) that kernels of
-        calls on this pool raised since the last call; clears them.  Synchronises `stream`
-        (default: the current stream of the pool's device)."""
+        """unipin_pool_status: the sticky flags (FLAG_BAD_SLOT | FLAG_BAD_LEN |
+        FLAG_DUP_SLOT) that kernels of calls on this pool raised since the last call;
+        clears them.  Synchronises `stream` (default: the current stream of the pool's
+        device)."""
         st = stream.cuda_stream if stream is not None else _stream_handle(self.device)
         flags = ctypes.c_int()
         with torch.cuda.device(self.device):

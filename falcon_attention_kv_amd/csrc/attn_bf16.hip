@@ -625,6 +625,22 @@ __device__ __forceinline__ int user_at_rank(const UserKeys &k, int r) {
     return r;   // not reached for 0 <= r < B
 }
 
+// Whether a user other than b with a valid, non-empty history (1 .. limit rows) names
+// slot s (wave-uniform b and s): then both prefills write the slot and race.  One
+// ballot per 64 users.
+__device__ __forceinline__ bool slot_shared(const int32_t *__restrict__ lens, const int32_t *__restrict__ slots,
+                                            int B, int b, int s, int limit) {
+    const int lane = threadIdx.x & 63;
+    bool dup = false;
+    for (int u0 = 0; u0 < B && !dup; u0 += 64) {
+        const int u = u0 + lane;
+        const int n = u < B ? lens[u] : 0;
+        const int su = u < B ? slots[u] : -1;
+        dup = __ballot(u != b && n > 0 && n <= limit && su == s) != 0;
+    }
+    return dup;
+}
+
 // ------------------------------------------------------------------ causal prefill
 
 // Maps the linear block id to (user*H + head, query tile).  With xcd_remap, blocks are
@@ -711,6 +727,10 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
     if (!user_valid(a, N, s, qtile == a.tiles - 1)) return;
     const int q0 = qtile * QT;
     if (q0 >= N) return;
+    // two users writing one slot: one block per user (its first query tile, head 0)
+    // raises the flag; both prefills still run
+    if (qtile == 0 && h == 0 && slot_shared(lens, slots, a.B, b, s, a.len_limit) && threadIdx.x == 0)
+        atomicOr(a.status, kFlagDupSlot);
 
     const long in_off = (long)b * a.in_bstride + (long)h * a.in_hstride;
     const int in_rs = a.in_rstride * (int)sizeof(bf16);   // bytes between rows of q, k, v

@@ -121,6 +121,17 @@ __global__ void __launch_bounds__(block_threads<D>()) attn_f64_kernel(AttnArgs a
             atomicOr(a.status, (N < 0 || N > a.len_limit ? kFlagBadLen : 0u) | (s < 0 || s >= a.S ? kFlagBadSlot : 0u));
         return;
     }
+    // two users writing one slot (prefill): one block per user raises the flag, both run
+    if (M == kPrefill && tile == 0 && h == 0 && N > 0 && (threadIdx.x >> 6) == 0) {
+        bool dup = false;
+        for (int u0 = 0; u0 < a.B && !dup; u0 += 64) {
+            const int u = u0 + (int)threadIdx.x;
+            const int n = u < a.B ? a.lens[u] : 0;
+            const int su = u < a.B ? a.slot[u] : -1;
+            dup = __ballot(u != b && n > 0 && n <= a.len_limit && su == s) != 0;
+        }
+        if (dup && threadIdx.x == 0) atomicOr(a.status, kFlagDupSlot);
+    }
     const int tid = threadIdx.x;
     const int r = tid / G, gi = tid % G;
     const int d0 = gi * kDS;

@@ -53,6 +53,7 @@ int attention_call(bool prefill, const void *q, const void *k, const void *v, Ro
 // Flags raised on the device (mirrors UNIPIN_FLAG_* of the public header).
 constexpr unsigned int kFlagBadSlot = 1u;
 constexpr unsigned int kFlagBadLen = 2u;
+constexpr unsigned int kFlagDupSlot = 4u;
 
 // Query rows one workgroup (prefill) or one work item (decode) covers.
 constexpr int kFp32RowsPerBlock = 64;

@@ -42,6 +42,16 @@ def test_version_and_strerror():
     assert lib.unipin_strerror(-99).decode() == "unknown status"
 
 
+def test_binding_constants_match_the_header():
+    # every UNIPIN_<NAME> = <value> of the header's enums has the same value in the binding
+    text = HEADER.read_text()
+    pairs = re.findall(r"\bUNIPIN_([A-Z0-9_]+)\s*=\s*(-?\d+)", text)
+    assert len(pairs) >= 17
+    for name, value in pairs:
+        assert hasattr(fa, name), name
+        assert getattr(fa, name) == int(value), (name, getattr(fa, name), value)
+
+
 def make_pool(L=2, S=3, H=2, n_max=16, D=64, dtype=fa.BF16):
     h = vp()
     rc = lib.unipin_pool_create(ctypes.byref(h), FAKE, FAKE * 2, L, S, H, n_max, D, dtype)

@@ -399,6 +399,29 @@ def test_invalid_length_ranks_longest_and_only_flags():
     assert torch.equal(pool.k[0, 1].cpu(), inp["k"][0].cpu()) and torch.equal(pool.v[0, 1].cpu(), inp["v"][0].cpu())
 
 
+def test_two_users_naming_one_slot_are_flagged():
+    """A prefill in which two users with histories name the same slot raises
+    FLAG_DUP_SLOT (both still run); an empty or invalid history sharing the slot does not
+    count.  Also past the ordered schedules' user limit, and on an fp32 pool."""
+    announce("duplicate slots in one prefill")
+    for dtype, B, lens, slots, want in (
+            (torch.bfloat16, 3, [10, 20, 30], [0, 1, 0], fa.FLAG_DUP_SLOT),
+            (torch.bfloat16, 3, [10, 20, 0], [0, 1, 0], 0),
+            (torch.bfloat16, 3, [10, 65, 30], [0, 0, 1], fa.FLAG_BAD_LEN),        # 65 > n: skipped
+            (torch.bfloat16, 3, [64, 64, 64], [2, 1, 0], 0),
+            (torch.float32, 3, [10, 20, 30], [1, 1, 0], fa.FLAG_DUP_SLOT),
+            (torch.float32, 3, [10, 0, 30], [1, 1, 0], 0),
+            (torch.bfloat16, 300, [(i % 64) + 1 for i in range(300)], [i % 300 for i in range(299)] + [7],
+             fa.FLAG_DUP_SLOT)):
+        H, D, n, k = 1, 64, 64, 8
+        inp = W.small_case(B, H, D, n, k, lens, dtype=dtype, seed=16, device=DEV)
+        pool = fa.Pool.allocate(1, max(slots) + 1, H, n, D, dtype, DEV)
+        fa.prefill(inp["q"], inp["k"], inp["v"], lens, pool, slots, 0)
+        torch.cuda.synchronize()
+        assert pool.status() == want, (dtype, B, lens[:4], slots[:4])
+        pool.close()
+
+
 def test_flags_belong_to_the_pool_whose_call_raised_them():
     """Two pools on one device: an invalid user in a call on one pool raises that pool's
     flag only."""
