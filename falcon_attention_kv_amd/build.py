@@ -67,6 +67,58 @@ def _link(objs, out, link, verbose):
     os.replace(tmp, out)
 
 
+# Host sources (no device code): the ones the sanitized host build instruments.
+HOST_SOURCES = [s for s in SOURCES if s.endswith(".cpp")]
+SANITIZED_DIR = os.path.join(OUT_DIR, "sanitized")
+SANITIZED_LIB = os.path.join(SANITIZED_DIR, "libunipin_host_sanitized.so")
+# AddressSanitizer and UndefinedBehaviorSanitizer on the host side only (-Xarch_host before
+# each option); the kernels are the ordinary objects of build().
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-shared-libasan", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (preloaded into the process
+    that loads the sanitized library)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/lib/llvm/bin/clang"
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("AddressSanitizer runtime not found")
+    return path
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """libunipin with its host code (descriptors, checks, dispatch, sharing, the block's
+    plans) built with AddressSanitizer and UndefinedBehaviorSanitizer, linked against the
+    kernel objects of the last build().  For CPU tests of the host paths; never loaded
+    by the package."""
+    os.makedirs(SANITIZED_DIR, exist_ok=True)
+    kernels = [os.path.join(OUT_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES if s.endswith(".hip")]
+    missing = [k for k in kernels if not os.path.exists(k)]
+    if missing:
+        raise RuntimeError(f"run build() first (missing {missing[0]})")
+
+    def compile_host(src: str) -> str:
+        obj = os.path.join(SANITIZED_DIR, os.path.splitext(src)[0] + ".o")
+        flags = [f for f in common_flags() if f != "-O3"]
+        cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + flags + ["-O1", "-g", "-fno-omit-frame-pointer"]
+        cmd += SANITIZE
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=len(HOST_SOURCES)) as ex:
+        objs = list(ex.map(compile_host, HOST_SOURCES))
+    _link(objs + kernels, SANITIZED_LIB, LINK + SANITIZE, verbose)
+    return SANITIZED_LIB
+
+
 def build(verbose: bool = False, extra=()) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
     srcs = SOURCES + PROBE_SOURCES

@@ -253,7 +253,7 @@ int unipin_block_ctx_tune(unipin_block_ctx_t *ctx, const unipin_pool_t *pool, in
     hipEvent_t e0, e1;
     if (hipEventCreate(&e0) != hipSuccess) return UNIPIN_EHIP;
     if (hipEventCreate(&e1) != hipSuccess) {
-        hipEventDestroy(e0);
+        (void)hipEventDestroy(e0);
         return UNIPIN_EHIP;
     }
     int rc = UNIPIN_OK;
@@ -349,8 +349,8 @@ int unipin_block_ctx_tune(unipin_block_ctx_t *ctx, const unipin_pool_t *pool, in
             }
         }
     }
-    hipEventDestroy(e0);
-    hipEventDestroy(e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
     return rc;
 }
 

@@ -84,8 +84,8 @@ bool write_file(const char *path, const ShareRecord &r) {
 namespace unipin {
 
 void pool_share_release(unipin_pool *pool) {
-    if (pool->ipc_k) hipIpcCloseMemHandle(pool->ipc_k);
-    if (pool->ipc_v && pool->ipc_v != pool->ipc_k) hipIpcCloseMemHandle(pool->ipc_v);
+    if (pool->ipc_k) (void)hipIpcCloseMemHandle(pool->ipc_k);
+    if (pool->ipc_v && pool->ipc_v != pool->ipc_k) (void)hipIpcCloseMemHandle(pool->ipc_v);
     pool->ipc_k = pool->ipc_v = nullptr;
     if (pool->shm_addr) {
         munmap(pool->shm_addr, pool->shm_bytes);
@@ -180,15 +180,15 @@ int unipin_pool_import(unipin_pool_t **out, const char *path) {
     if (r.same_alloc) {
         vb = kb;
     } else if (hipIpcOpenMemHandle(&vb, r.v_handle, hipIpcMemLazyEnablePeerAccess) != hipSuccess) {
-        hipIpcCloseMemHandle(kb);
+        (void)hipIpcCloseMemHandle(kb);
         return UNIPIN_EHIP;
     }
     unipin_pool_t *p = nullptr;
     int rc = unipin_pool_create(&p, static_cast<char *>(kb) + r.k_offset, static_cast<char *>(vb) + r.v_offset, r.L,
                                 r.S, r.H, r.n_max, r.D, r.dtype);
     if (rc) {
-        if (vb != kb) hipIpcCloseMemHandle(vb);
-        hipIpcCloseMemHandle(kb);
+        if (vb != kb) (void)hipIpcCloseMemHandle(vb);
+        (void)hipIpcCloseMemHandle(kb);
         return rc == UNIPIN_ENOMEM ? rc : UNIPIN_EIO;
     }
     p->ipc_k = kb;
