@@ -454,19 +454,22 @@ def cpu_baseline(w, layers_cpu, lens, budget_s):
     except Exception:  # pragma: no cover
         threads = 1
     rng = np.random.default_rng(0)
-    units, t_total = 0, 0.0
-    while t_total < budget_s and units < w.L * w.B * w.H:
+    units, t_pre, t_dec = 0, 0.0, 0.0
+    while t_pre + t_dec < budget_s and units < w.L * w.B * w.H:
         l, b, h = int(rng.integers(w.L)), int(rng.integers(w.B)), int(rng.integers(w.H))
         x = layers_cpu[l]
         N = lens[b]
         t0 = time.perf_counter()
         oracle.prefill(x["q"][b:b + 1, h:h + 1], x["k"][b:b + 1, h:h + 1], x["v"][b:b + 1, h:h + 1], [N])
+        t1 = time.perf_counter()
         pk = oracle.as_f64(x["k"][b:b + 1, h:h + 1, :N]).reshape(1, 1, 1, N, w.D)
         pv = oracle.as_f64(x["v"][b:b + 1, h:h + 1, :N]).reshape(1, 1, 1, N, w.D)
         oracle.rank_decode(x["qc"][b:b + 1, h:h + 1], x["kc"][b:b + 1, h:h + 1],
                            x["vc"][b:b + 1, h:h + 1], pk, pv, [0], [N], 0)
-        t_total += time.perf_counter() - t0
+        t_pre += t1 - t0
+        t_dec += time.perf_counter() - t1
         units += 1
+    t_total = t_pre + t_dec
     per_unit = t_total / units
     step_s = per_unit * w.L * w.B * w.H
     # algorithmic FLOPs of one (layer, user, head) unit: prefill N(N+1)/2 pairs, decode
@@ -482,7 +485,13 @@ def cpu_baseline(w, layers_cpu, lens, budget_s):
     return {"value": w.B * w.k / step_s, "unit": "candidates/s", "cores": threads, "kind": "oracle",
             "sample": f"{units} (layer, user, head) units of prefill + rank decode "
                       f"(float64 numpy, {t_total:.1f} s), scaled x{w.L * w.B * w.H} to one step",
-            "algorithmic_gflops": round(unit_flop / per_unit / 1e9, 2), "cpu_model": model}
+            "algorithmic_gflops": round(unit_flop / per_unit / 1e9, 2), "cpu_model": model,
+            # the two oracle calls timed apart, per (layer, user, head) unit; the oracle
+            # evaluates its dense masked blocks (N x N for the prefill, k x (N + k) for the
+            # decode), this many times the algorithmic pairs
+            "prefill_ms_per_unit": round(t_pre / units * 1e3, 3), "decode_ms_per_unit": round(t_dec / units * 1e3, 3),
+            "dense_over_algorithmic": {"prefill": round(2 * N / (N + 1), 3),
+                                       "decode": round((N + w.k) / (N + 1), 3)}}
 
 
 def main():
