@@ -483,14 +483,17 @@ __device__ __forceinline__ void store_o(const WaveState<D> &ws, LDS_AS char *sta
     }
 }
 
-// The candidate's own key.  Its score s_j = scale*log2(e) * qc_j . kc_j starts the
-// running max (m = s_j, empty row sum and accumulator), and after the history its value
-// is merged with weight exp2(s_j - m) <= 1 (m only grows).  An empty history therefore
-// yields vc_j exactly, and nothing in a candidate's arithmetic depends on another
-// candidate.  kc and vc come from staged row blocks.
+// The candidate's own key, score s_j = scale*log2(e) * qc_j . kc_j, merged after the
+// history.  On the bf16 pool the own keys arrive with the values at the end of the
+// stream, so the history starts from an empty state (m = -inf) and the merge moves the
+// max to max(m, s_j), scaling what the history summed by exp2(m - m'); on the E4M3 pool
+// the own score starts the running max (m = s_j) and the merge weight exp2(s_j - m) is
+// at most 1.  An empty history yields vc_j exactly on both, and nothing in a
+// candidate's arithmetic depends on another candidate.  kc and vc come from staged row
+// blocks.
 template <int D>
-__device__ __forceinline__ void self_key_scores(WaveState<D> &ws, float (&sself)[query_blocks<D>()],
-                                                const LDS_AS char *kc_rows, const LaneAddr<D> &la, float c) {
+__device__ __forceinline__ void self_key_score(const WaveState<D> &ws, float (&sself)[query_blocks<D>()],
+                                               const LDS_AS char *kc_rows, const LaneAddr<D> &la, float c) {
     bf16x8 kk[query_blocks<D>()][Tile<D>::KC];
     staged_operand<D>(kk, kc_rows, la);
 #pragma unroll
@@ -505,11 +508,29 @@ __device__ __forceinline__ void self_key_scores(WaveState<D> &ws, float (&sself)
                 part = __builtin_amdgcn_fdot2_f32_bf16(qa, ka, part, false);
             }
         sself[qb] = half_sum(part) * c;
-        ws.m[qb] = sself[qb];
+    }
+}
+
+// The state before any key: no max yet, empty sums.
+template <int D>
+__device__ __forceinline__ void reset_state(WaveState<D> &ws) {
+#pragma unroll
+    for (int qb = 0; qb < query_blocks<D>(); ++qb) {
+        ws.m[qb] = -INFINITY;
         ws.l[qb] = 0.f;
 #pragma unroll
         for (int db = 0; db < Tile<D>::DB; ++db) ws.acc[db][qb] = f32x16{};
     }
+}
+
+// The own score, which then starts the running max (the E4M3 path).
+template <int D>
+__device__ __forceinline__ void self_key_scores(WaveState<D> &ws, float (&sself)[query_blocks<D>()],
+                                                const LDS_AS char *kc_rows, const LaneAddr<D> &la, float c) {
+    self_key_score<D>(ws, sself, kc_rows, la, c);
+    reset_state<D>(ws);
+#pragma unroll
+    for (int qb = 0; qb < query_blocks<D>(); ++qb) ws.m[qb] = sself[qb];
 }
 
 template <int D>
@@ -518,8 +539,13 @@ __device__ __forceinline__ void self_key_merge(WaveState<D> &ws, const float (&s
     using T = Tile<D>;
 #pragma unroll
     for (int qb = 0; qb < query_blocks<D>(); ++qb) {
-        const float ps = __builtin_amdgcn_exp2f(sself[qb] - ws.m[qb]);
-        ws.l[qb] += g == 0 ? ps : 0.f;   // counted once per row, by the lower lane half
+        // the max moves to the own score if that is larger (always with an empty history,
+        // whose m is -inf: then alpha = 0 on empty sums and the output is vc exactly)
+        const float mn = fmaxf(ws.m[qb], sself[qb]);
+        const float alpha = __builtin_amdgcn_exp2f(ws.m[qb] - mn);
+        const float ps = __builtin_amdgcn_exp2f(sself[qb] - mn);
+        ws.m[qb] = mn;
+        ws.l[qb] = ws.l[qb] * alpha + (g == 0 ? ps : 0.f);   // counted once per row, by the lower lane half
 #pragma unroll
         for (int db = 0; db < T::DB; ++db)
 #pragma unroll
@@ -527,7 +553,7 @@ __device__ __forceinline__ void self_key_merge(WaveState<D> &ws, const float (&s
                 const bf16x4 vv = *reinterpret_cast<const LDS_AS bf16x4 *>(vc_rows + staged_acc_off<D>(qb, db, j, col, g));
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    ws.acc[db][qb][4 * j + e] = __builtin_fmaf(ps, (float)vv[e], ws.acc[db][qb][4 * j + e]);
+                    ws.acc[db][qb][4 * j + e] = __builtin_fmaf(ps, (float)vv[e], ws.acc[db][qb][4 * j + e] * alpha);
             }
     }
 }
@@ -881,14 +907,15 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
     const long in_off = (long)b * a.in_bstride + (long)h * a.in_hstride;
     const int in_rs = a.in_rstride * (int)sizeof(bf16);   // bytes between candidate rows
     const uint32_t rows_bytes = (uint32_t)a.rows * in_rs;
-    // The candidates' q and own keys do not depend on the user's slot or history length:
-    // their DMA goes out before those are read, so the two loads overlap.  A user with an
-    // invalid slot or length waits for that DMA before it leaves (no LDS write may
-    // outlive the workgroup).
-    dma_rows<D, W, kBlockRows>(smem, rsrc_words(static_cast<const bf16 *>(a.q) + in_off, rows_bytes), row0, wave,
-                               lane, in_rs);
-    dma_rows<D, W, kBlockRows>(smem + 2 * T::BUF_BYTES, rsrc_words(static_cast<const bf16 *>(a.k) + in_off, rows_bytes),
-                               row0, wave, lane, in_rs);
+    // The candidates' q (and, for the E4M3 pool, their own keys) do not depend on the
+    // user's slot or history length: their DMA goes out before those are read, so the two
+    // loads overlap.  A user with an invalid slot or length waits for that DMA before it
+    // leaves (no LDS write may outlive the workgroup).  On the bf16 pool q goes to slots
+    // 2 and 3, and the first two steps of the stream follow in the same round trip.
+    const i32x4 rsrc_kc = rsrc_words(static_cast<const bf16 *>(a.k) + in_off, rows_bytes);
+    dma_rows<D, W, kBlockRows>(smem + (P8 ? 0 : 2 * T::BUF_BYTES),
+                               rsrc_words(static_cast<const bf16 *>(a.q) + in_off, rows_bytes), row0, wave, lane, in_rs);
+    if constexpr (P8) dma_rows<D, W, kBlockRows>(smem + 2 * T::BUF_BYTES, rsrc_kc, row0, wave, lane, in_rs);
     int N, s;
     if (ordered) {
         user_len_slot(keys, b, N, s);
@@ -909,27 +936,34 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
     dma_offsets<D, W>(voff, wave, lane, T::ROW_BYTES);   // the pool's K/V rows
     const LaneAddr<D> la = lane_addr<D>(lane);
     const int ntiles = (N + kTK - 1) / kTK;
-    const int nsteps = ntiles + 2;
     const int wrows = wave * wave_rows<D>() * T::ROW_BYTES;   // this wave's rows inside a staged block
-
-    wait_vmcnt<0>();
-    __syncthreads();
     WaveState<D> ws;
     float sself[query_blocks<D>()];
-    staged_operand<D>(ws.qreg, smem + wrows, la);
-    self_key_scores<D>(ws, sself, smem + 2 * T::BUF_BYTES + wrows, la, a.c);
-    __syncthreads();   // the header slots are free again
 
     if constexpr (!P8) {
+        // Steps: the ntiles K/V tiles of the history, then per half hv of the candidates
+        // (waves hv*W/2 ..) its own keys and its values, 128 rows each.  Step u lives in
+        // slot u % kBufs; steps 0 and 1 went out with q (in slots 2 and 3).  The own key
+        // is merged last: the running max starts empty and the merge moves it.
+        const int nsteps = ntiles + 4;
         auto issue = [&](int u) {
             LDS_AS char *dst = smem + (u % kBufs) * T::BUF_BYTES;
-            if (u < ntiles) dma_tile<D, W>(dst, rsrc, u * kTK, voff, wave, T::ROW_BYTES);
-            else dma_rows<D, W, HALF>(dst, rsrc_vc, row0 + (u - ntiles) * HALF, wave, lane, in_rs);
+            if (u < ntiles) {
+                dma_tile<D, W>(dst, rsrc, u * kTK, voff, wave, T::ROW_BYTES);
+            } else {
+                const int e = u - ntiles;   // 0: own keys of half 0, 1: values of half 0, 2, 3: half 1
+                dma_rows<D, W, HALF>(dst, (e & 1) ? rsrc_vc : rsrc_kc, row0 + (e >> 1) * HALF, wave, lane, in_rs);
+            }
         };
         int issued = 0;
-        for (; issued < kBufs - 1 && issued < nsteps; ++issued) issue(issued);
+        for (; issued < 2; ++issued) issue(issued);
+        wait_pieces_after<DPW>(issued);   // q has landed
+        __syncthreads();
+        staged_operand<D>(ws.qreg, smem + 2 * T::BUF_BYTES + wrows, la);
+        reset_state<D>(ws);
         // Makes step u current: waits for its DMA, workgroup barrier (after which the slot
-        // of step u-1 is free), and lets the DMA run up to step u+kBufs-1.
+        // of step u-1, and for u = 0 the q slots, are free), and lets the DMA run up to
+        // step u+kBufs-1.
         auto next_step = [&](int u) -> const LDS_AS char * {
             wait_pieces_after<DPW>(issued - u - 1);
             __syncthreads();
@@ -937,13 +971,20 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
             return smem + (u % kBufs) * T::BUF_BYTES;
         };
         run_tiles<D, false>(ws, ntiles, active ? ntiles - 1 : -1, N, wq0, la, col, g, a.c, next_step);
+        const int hrows = (wave % (W / 2)) * wave_rows<D>() * T::ROW_BYTES;   // this wave's rows in its half
 #pragma unroll
         for (int hv = 0; hv < 2; ++hv) {
-            const LDS_AS char *vc_half = next_step(ntiles + hv);
-            if (active && wave / (W / 2) == hv)
-                self_key_merge<D>(ws, sself, vc_half + (wave % (W / 2)) * wave_rows<D>() * T::ROW_BYTES, col, g);
+            const LDS_AS char *kc_half = next_step(ntiles + 2 * hv);
+            if (active && wave / (W / 2) == hv) self_key_score<D>(ws, sself, kc_half + hrows, la, a.c);
+            const LDS_AS char *vc_half = next_step(ntiles + 2 * hv + 1);
+            if (active && wave / (W / 2) == hv) self_key_merge<D>(ws, sself, vc_half + hrows, col, g);
         }
     } else {
+        wait_vmcnt<0>();
+        __syncthreads();
+        staged_operand<D>(ws.qreg, smem + wrows, la);
+        self_key_scores<D>(ws, sself, smem + 2 * T::BUF_BYTES + wrows, la, a.c);
+        __syncthreads();   // the header slots are free again
         // E4M3 pool.  LDS: slot 0 the current tile decoded to bf16, slot 1 two staged
         // E4M3 tiles (tile t at half t % 2), slots 2 and 3 the two vc halves.  DMA order
         // per wave: tiles 0 and 1, then one tile per step (tile t + 2 after tile t is
