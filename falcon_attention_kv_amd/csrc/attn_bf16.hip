@@ -972,12 +972,16 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
         };
         run_tiles<D, false>(ws, ntiles, active ? ntiles - 1 : -1, N, wq0, la, col, g, a.c, next_step);
         const int hrows = (wave % (W / 2)) * wave_rows<D>() * T::ROW_BYTES;   // this wave's rows in its half
+        // one barrier per half: making the values current also covers the own keys, one
+        // step older (the DMA issue is the same as with a barrier per step)
 #pragma unroll
         for (int hv = 0; hv < 2; ++hv) {
-            const LDS_AS char *kc_half = next_step(ntiles + 2 * hv);
-            if (active && wave / (W / 2) == hv) self_key_score<D>(ws, sself, kc_half + hrows, la, a.c);
             const LDS_AS char *vc_half = next_step(ntiles + 2 * hv + 1);
-            if (active && wave / (W / 2) == hv) self_key_merge<D>(ws, sself, vc_half + hrows, col, g);
+            const LDS_AS char *kc_half = smem + ((ntiles + 2 * hv) % kBufs) * T::BUF_BYTES;
+            if (active && wave / (W / 2) == hv) {
+                self_key_score<D>(ws, sself, kc_half + hrows, la, a.c);
+                self_key_merge<D>(ws, sself, vc_half + hrows, col, g);
+            }
         }
     } else {
         wait_vmcnt<0>();
