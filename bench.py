@@ -345,16 +345,18 @@ def probes(torch, dev) -> dict:
     tf = ctypes.c_double()
     if lib.unipin_probe_mfma(buf.data_ptr(), cus, 20000, ctypes.byref(tf)) != 0:
         raise RuntimeError("unipin_probe_mfma failed")
-    ns = (ctypes.c_double * 4)()
+    ns = (ctypes.c_double * 6)()
     if lib.unipin_probe_overlap(buf.data_ptr(), cus, 20000, ns) != 0:
         raise RuntimeError("unipin_probe_overlap failed")
-    m, e, both, split = (round(v, 2) for v in ns)
+    m, e, both, split, m16, both16 = (round(v, 2) for v in ns)
     return {"mfma_loop": {"tflops": round(tf.value, 1), "frac_of_peak": round(tf.value / BF16_PEAK_TFLOPS, 4),
                           "what": f"{cus} CUs x 8 waves of independent 32x32x16 bf16 MFMAs"},
             "mfma_exp_overlap_ns_per_iter": {
                 "mfma_only": m, "exp_only": e, "both_in_each_wave": both, "mfma_wave_beside_exp_wave": split,
+                "mfma_only_16x16x32": m16, "both_in_each_wave_16x16x32": both16,
                 "what": "per SIMD and loop iteration, two waves: 8 MFMAs and/or 32 (v_exp_f32 + subtract) "
-                        "per wave; full overlap would give max(mfma_only, exp_only), none their sum"}}
+                        "per wave; full overlap would give max(mfma_only, exp_only), none their sum; the "
+                        "16x16x32 entries issue the same matrix work as 16 MFMAs of 16x16x32 bf16"}}
 
 
 def copy_calibration(torch, dev, mib: int) -> int:

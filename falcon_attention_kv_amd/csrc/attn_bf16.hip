@@ -750,7 +750,11 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, const int32_t *_
         N = lens[b];
         s = slots[b];
     }
-    if (!user_valid(a, N, s, qtile == a.tiles - 1)) return;
+    // One block per (user, head) reports an invalid user: in the longest-first schedule
+    // the one of tile 0, which every user with history rows (and every invalid length,
+    // ranked longest) has; in user order the one of the last tile.  An empty history
+    // writes nothing, and its slot is left to the ranking decode's check.
+    if (!user_valid(a, N, s, a.B <= kOrderUsers ? qtile == 0 : qtile == a.tiles - 1)) return;
     const int q0 = qtile * QT;
     if (q0 >= N) return;
     // two users writing one slot: one block per user (its first query tile, head 0)

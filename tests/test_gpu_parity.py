@@ -381,6 +381,26 @@ def test_device_side_invalid_user_is_skipped_and_flagged():
     assert pool.status() == 0
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_short_user_with_an_invalid_slot_is_flagged(D):
+    """A user shorter than the call's padded extent has only its first query tiles in
+    the longest-first schedule; an invalid slot of such a user is still flagged (and its
+    rows skipped)."""
+    B, H, n, k = 3, 8, 600, 16
+    announce(f"short user with an invalid slot, D={D}")
+    inp = W.small_case(B, H, D, n, k, [600, 50, 300], seed=17, device=DEV)
+    pool = fa.Pool.allocate(1, 3, H, n, D, torch.bfloat16, DEV)
+    o = torch.full_like(inp["q"], 7.0)
+    fa.prefill(inp["q"], inp["k"], inp["v"], [600, 50, 300], pool, [0, 9, 2], 0, o=o)   # slot 9 >= S
+    torch.cuda.synchronize()
+    assert pool.status() == fa.FLAG_BAD_SLOT
+    assert (o[1] == 7.0).all(), "a skipped user's output must stay untouched"
+    for b, N in ((0, 600), (2, 300)):
+        sub = {kk: v[b:b + 1].cpu() for kk, v in inp.items() if kk in ("q", "k", "v")}
+        ref = oracle.prefill(sub["q"], sub["k"], sub["v"], [N])
+        check_close(o[b:b + 1, :, :N], ref[:, :, :N], torch.bfloat16, f"user {b} beside the invalid one")
+
+
 def test_invalid_length_ranks_longest_and_only_flags():
     """One invalid length among two-tile histories: the longest-first schedule ranks the
     invalid user first; its blocks only raise the flag, the other user is exact."""
