@@ -155,10 +155,10 @@ __device__ __forceinline__ void dma_tile(LDS_AS char *buf, i32x4 rsrc, int kbase
 }
 
 // DMA of ROWS consecutive query (or candidate) rows from row0 into LDS with the K
-// swizzle: 16-byte block bi of the block in LDS order is row bi / R, logical block
-// (bi % R) ^ k_swz(row).  Rows past the record count read as zero.  A 256-row block
-// fills two LDS slots, a 128-row half block one.
-template <int D, int W, int ROWS>
+// swizzle (or, VL, the V swizzle): 16-byte block bi of the block in LDS order is row
+// bi / R, logical block (bi % R) ^ swz(row).  Rows past the record count read as zero.
+// A 256-row block fills two LDS slots, a 128-row half block one.
+template <int D, int W, int ROWS, bool VL = false>
 __device__ __forceinline__ void dma_rows(LDS_AS char *dst, i32x4 rsrc, int row0, int wave, int lane,
                                          int row_stride) {
     using T = Tile<D>;
@@ -170,7 +170,7 @@ __device__ __forceinline__ void dma_rows(LDS_AS char *dst, i32x4 rsrc, int row0,
     for (int j = 0; j < PW; ++j) {
         const int piece = wave * PW + j;
         const int bi = piece * 64 + lane;
-        const int row = bi / T::R, blk = (bi % T::R) ^ k_swz<D>(row);
+        const int row = bi / T::R, blk = (bi % T::R) ^ (VL ? v_swz<D>(row) : k_swz<D>(row));
         dma16(base + piece * 1024, rsrc, row * row_stride + blk * 16, soff);
     }
 }
@@ -488,9 +488,9 @@ __device__ __forceinline__ void store_o(const WaveState<D> &ws, LDS_AS char *sta
 // stream, so the history starts from an empty state (m = -inf) and the merge moves the
 // max to max(m, s_j), scaling what the history summed by exp2(m - m'); on the E4M3 pool
 // the own score starts the running max (m = s_j) and the merge weight exp2(s_j - m) is
-// at most 1.  An empty history yields vc_j exactly on both, and nothing in a
-// candidate's arithmetic depends on another candidate.  kc and vc come from staged row
-// blocks.
+// at most 1.  An empty history yields vc_j exactly on both, and for finite inputs
+// nothing of another candidate reaches a candidate's output.  kc and vc come from staged
+// row blocks.
 template <int D>
 __device__ __forceinline__ void self_key_score(const WaveState<D> &ws, float (&sself)[query_blocks<D>()],
                                                const LDS_AS char *kc_rows, const LaneAddr<D> &la, float c) {
@@ -533,29 +533,51 @@ __device__ __forceinline__ void self_key_scores(WaveState<D> &ws, float (&sself)
     for (int qb = 0; qb < query_blocks<D>(); ++qb) ws.m[qb] = sself[qb];
 }
 
+// Adds the own key: weight w_j = exp2(s_j - m) on vc_j.  While every row of the wave has
+// s_j <= m + 64 (the lazy bound of the history's weights) the max stays; otherwise
+// (an own score far above the history's, or an empty history with m = -inf) each row
+// moves it to max(m, s_j) and scales its sums by exp2(m - m').  The weight is rounded to
+// bf16 like the history's, counted once in the row sum, and vc_j w_j enters O^T through
+// the matrix cores: O^T += Vc^T diag(w) over the wave's 32 candidates, with vc staged in
+// the V layout and diag(w) built in the register layout of the P^T operand (lane (col,
+// g) element e stands for key 16 c2 + 4 g + e, or 8 + 4 g + e - 4 for e >= 4).  An empty
+// history gives w = 1 and vc_j exactly; for finite inputs nothing of another candidate
+// reaches a row (its terms are vc times an exact zero).
 template <int D>
 __device__ __forceinline__ void self_key_merge(WaveState<D> &ws, const float (&sself)[query_blocks<D>()],
-                                               const LDS_AS char *vc_rows, int col, int g) {
+                                               const LDS_AS char *vc_rows, const LaneAddr<D> &la, int col, int g) {
     using T = Tile<D>;
+    constexpr int QB = query_blocks<D>();
+    bool far = false;
 #pragma unroll
-    for (int qb = 0; qb < query_blocks<D>(); ++qb) {
-        // the max moves to the own score if that is larger (always with an empty history,
-        // whose m is -inf: then alpha = 0 on empty sums and the output is vc exactly)
-        const float mn = fmaxf(ws.m[qb], sself[qb]);
-        const float alpha = __builtin_amdgcn_exp2f(ws.m[qb] - mn);
-        const float ps = __builtin_amdgcn_exp2f(sself[qb] - mn);
-        ws.m[qb] = mn;
-        ws.l[qb] = ws.l[qb] * alpha + (g == 0 ? ps : 0.f);   // counted once per row, by the lower lane half
+    for (int qb = 0; qb < QB; ++qb) far |= !(sself[qb] <= ws.m[qb] + 64.f);
+    if (__any(far)) {
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db)
+        for (int qb = 0; qb < QB; ++qb) {
+            const float mn = fmaxf(ws.m[qb], sself[qb]);
+            const float alpha = __builtin_amdgcn_exp2f(ws.m[qb] - mn);
+            ws.m[qb] = mn;
+            ws.l[qb] *= alpha;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x4 vv = *reinterpret_cast<const LDS_AS bf16x4 *>(vc_rows + staged_acc_off<D>(qb, db, j, col, g));
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    ws.acc[db][qb][4 * j + e] = __builtin_fmaf(ps, (float)vv[e], ws.acc[db][qb][4 * j + e] * alpha);
-            }
+            for (int db = 0; db < T::DB; ++db) ws.acc[db][qb] *= alpha;
+        }
     }
+    // lane (col, g) holds its row's weight at chunk col / 16, element e* when g matches
+    const int r = col & 15;
+    const bool mine = g == ((r >> 2) & 1);
+    const int estar = (r & 3) + ((r >> 3) << 2);
+    bf16x8 pd[2][QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const bf16 w = (bf16)__builtin_amdgcn_exp2f(sself[qb] - ws.m[qb]);
+        ws.l[qb] += g == 0 ? (float)w : 0.f;
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                pd[c2][qb][e] = (mine && (col >> 4) == c2 && e == estar) ? w : (bf16)0.f;
+    }
+    tile_pv<D>(ws, pd, 0, vc_rows, la);
 }
 
 __device__ __forceinline__ bool user_valid(const AttnArgs &a, int N, int s, bool report) {
@@ -956,7 +978,8 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
                 dma_tile<D, W>(dst, rsrc, u * kTK, voff, wave, T::ROW_BYTES);
             } else {
                 const int e = u - ntiles;   // 0: own keys of half 0, 1: values of half 0, 2, 3: half 1
-                dma_rows<D, W, HALF>(dst, (e & 1) ? rsrc_vc : rsrc_kc, row0 + (e >> 1) * HALF, wave, lane, in_rs);
+                if (e & 1) dma_rows<D, W, HALF, true>(dst, rsrc_vc, row0 + (e >> 1) * HALF, wave, lane, in_rs);
+                else dma_rows<D, W, HALF>(dst, rsrc_kc, row0 + (e >> 1) * HALF, wave, lane, in_rs);
             }
         };
         int issued = 0;
@@ -984,7 +1007,7 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
             const LDS_AS char *kc_half = smem + ((ntiles + 2 * hv) % kBufs) * T::BUF_BYTES;
             if (active && wave / (W / 2) == hv) {
                 self_key_score<D>(ws, sself, kc_half + hrows, la, a.c);
-                self_key_merge<D>(ws, sself, vc_half + hrows, col, g);
+                self_key_merge<D>(ws, sself, vc_half + hrows, la, col, g);
             }
         }
     } else {
@@ -1002,8 +1025,8 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
         LDS_AS char *stage = smem + T::BUF_BYTES;
         LDS_AS char *cur = smem;
         auto issue_vc = [&]() {
-            dma_rows<D, W, HALF>(smem + 2 * T::BUF_BYTES, rsrc_vc, row0, wave, lane, in_rs);
-            dma_rows<D, W, HALF>(smem + 3 * T::BUF_BYTES, rsrc_vc, row0 + HALF, wave, lane, in_rs);
+            dma_rows<D, W, HALF, true>(smem + 2 * T::BUF_BYTES, rsrc_vc, row0, wave, lane, in_rs);
+            dma_rows<D, W, HALF, true>(smem + 3 * T::BUF_BYTES, rsrc_vc, row0 + HALF, wave, lane, in_rs);
         };
         if (ntiles > 0) dma_tile8<D, W>(stage, rsrc, 0, wave, lane);
         if (ntiles > 1) dma_tile8<D, W>(stage + F::BYTES, rsrc, kTK, wave, lane);
@@ -1029,7 +1052,7 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
             __syncthreads();
             const LDS_AS char *vc_half = smem + (2 + hv) * T::BUF_BYTES;
             if (active && wave / (W / 2) == hv)
-                self_key_merge<D>(ws, sself, vc_half + (wave % (W / 2)) * wave_rows<D>() * T::ROW_BYTES, col, g);
+                self_key_merge<D>(ws, sself, vc_half + (wave % (W / 2)) * wave_rows<D>() * T::ROW_BYTES, la, col, g);
         }
     }
     __syncthreads();   // every wave is done with the slots
