@@ -42,7 +42,7 @@ EXPORTS = ("unipin_pool_create", "unipin_pool_destroy", "unipin_pool_acquire",
 BLOCK_WEIGHT_NAMES = ("ln1_w", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_w", "ln2_b", "w_fc", "b_fc",
                       "w_proj", "b_proj")
 BLOCK_HISTORY, BLOCK_CANDIDATES = 0, 1
-# unipin_block_ctx_set_gemm: AUTO, hipBLASLt only, or the library's kernel with tile 0, 1, 2
+# unipin_block_ctx_set_gemm: AUTO, hipBLASLt only, or the library's kernel with tile 0, 1, 2, 3
 GEMM_AUTO, GEMM_LIBRARY = -2, -1
 
 
@@ -349,12 +349,12 @@ class BlockContext:
 
     def set_gemm(self, kernel: int) -> None:
         """unipin_block_ctx_set_gemm: GEMM_AUTO, GEMM_LIBRARY (hipBLASLt) or the library's
-        kernel with tile configuration 0, 1 or 2; drops the plans made so far."""
+        kernel with tile configuration 0, 1, 2 or 3; drops the plans made so far."""
         _check(lib.unipin_block_ctx_set_gemm(self.handle, int(kernel)), "unipin_block_ctx_set_gemm")
 
     def tune(self, pool: "Pool", B: int, rows: int, workspace: Optional[torch.Tensor] = None) -> None:
         """unipin_block_ctx_tune: time the candidate GEMM kernels (the library's own in each
-        tile size, hipBLASLt's) for the block at B users x rows rows and keep the fastest
+        tile configuration, hipBLASLt's) for the block at B users x rows rows and keep the fastest
         (blocks until done)."""
         dev = pool.device
         if workspace is None:

@@ -6,7 +6,7 @@
 // The four projections are bf16 GEMMs with fp32 accumulation and fused epilogues (bias,
 // tanh-form GELU, residual add into the hidden state).  They run on hipBLASLt (its
 // epilogues, beta = 1 on the hidden state for the residual) or on this library's MFMA
-// kernel (gemm_bf16.hip, three workgroup tile sizes), whichever the tuner timed fastest
+// kernel (gemm_bf16.hip, four workgroup tile configurations), whichever the tuner timed fastest
 // for the shape; untuned, on hipBLASLt's first heuristic choice.  LayerNorm is this library's
 // kernel (block_kernels.hip), and the attention is the library's own prefill and rank-decode
 // kernels, which read q, k and v straight from the fused projection's rows
@@ -83,7 +83,7 @@ GemmPlan *plan_for(unipin_block_ctx *ctx, long M, int N, int K, hipblasLtEpilogu
     auto it = ctx->plans.find(key);
     if (it != ctx->plans.end()) return &it->second;
     GemmPlan p;
-    if (ctx->kernel >= 0 && unipin::gemm_bf16_supported(M, N, K)) p.own = ctx->kernel;
+    if (ctx->kernel >= 0 && unipin::gemm_bf16_supported(M, N, K, ctx->kernel)) p.own = ctx->kernel;
     const hipblasOperation_t op = HIPBLAS_OP_N;
     const hipDataType bias_type = HIP_R_16BF;
     hipblasLtMatmulPreference_t pref = nullptr;
@@ -273,10 +273,17 @@ int unipin_block_ctx_tune(unipin_block_ctx_t *ctx, const unipin_pool_t *pool, in
             hipblasLtMatmulAlgo_t algo;
         };
         std::vector<Cand> cands;
-        const bool own_ok = unipin::gemm_bf16_supported(M, g[i].N, g[i].K);
-        if (own_ok && ctx->kernel >= 0) cands.push_back({ctx->kernel, {}});
-        if (own_ok && ctx->kernel == UNIPIN_GEMM_AUTO)
-            for (int c = 0; c < unipin::kGemmConfigs; ++c) cands.push_back({c, {}});
+        bool own_ok = false;
+        if (ctx->kernel >= 0 && unipin::gemm_bf16_supported(M, g[i].N, g[i].K, ctx->kernel)) {
+            cands.push_back({ctx->kernel, {}});
+            own_ok = true;
+        }
+        if (ctx->kernel == UNIPIN_GEMM_AUTO)
+            for (int c = 0; c < unipin::kGemmConfigs; ++c)
+                if (unipin::gemm_bf16_supported(M, g[i].N, g[i].K, c)) {
+                    cands.push_back({c, {}});
+                    own_ok = true;
+                }
         const bool lib = ctx->kernel == UNIPIN_GEMM_LIBRARY || (ctx->kernel == UNIPIN_GEMM_AUTO) || !own_ok;
         hipblasLtMatmulPreference_t pref = nullptr;
         const uint64_t wsz = kGemmWorkspace;
@@ -313,40 +320,68 @@ int unipin_block_ctx_tune(unipin_block_ctx_t *ctx, const unipin_pool_t *pool, in
                 }
             }
         }
-        float best = 1e30f;
-        GemmPlan trial = *p;
-        for (auto &c : cands) {
-            trial.own = c.own;
-            trial.algo = c.algo;
+        // One timing of a candidate: two untimed runs, then `reps` runs between events.
+        // 1: the candidate cannot run this problem; -1: an event call failed.
+        auto time_plan = [&](GemmPlan &t, int reps, float *ms) -> int {
             auto run = [&]() {
-                return run_plan(ctx, &trial, in_of[i], W, bias, out_of[i], M, g[i].N, g[i].K, g[i].ep, g[i].residual,
+                return run_plan(ctx, &t, in_of[i], W, bias, out_of[i], M, g[i].N, g[i].K, g[i].ep, g[i].residual,
                                 ws + lo.gemm, st);
             };
-            if (run() != UNIPIN_OK || run() != UNIPIN_OK) continue;
-            if (hipEventRecord(e0, st) != hipSuccess) {
-                rc = UNIPIN_EHIP;
-                break;
-            }
+            if (run() != UNIPIN_OK || run() != UNIPIN_OK) return 1;
+            if (hipEventRecord(e0, st) != hipSuccess) return -1;
             bool ok = true;
-            for (int r = 0; r < 5 && ok; ++r) ok = run() == UNIPIN_OK;
-            float ms = 0.f;
+            for (int r = 0; r < reps && ok; ++r) ok = run() == UNIPIN_OK;
             if (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
-                hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
-                rc = UNIPIN_EHIP;
-                break;
-            }
-            if (ok && ms < best) {
-                best = ms;
-                p->own = c.own;
-                p->algo = c.algo;
-            }
-            // the residual GEMMs add into their output each run; start the next from
-            // the same values as the first so that no candidate sees overflowing data
+                hipEventElapsedTime(ms, e0, e1) != hipSuccess)
+                return -1;
+            // the residual GEMMs add into their output each run; start the next timing
+            // from the same values as the first so that no candidate sees overflowing data
             if (g[i].residual &&
-                unipin::launch_fill_random(out_of[i], (size_t)M * g[i].N, 5u, 1.f, st) != hipSuccess) {
+                unipin::launch_fill_random(out_of[i], (size_t)M * g[i].N, 5u, 1.f, st) != hipSuccess)
+                return -1;
+            return ok ? 0 : 1;
+        };
+        // The sweep keeps the fastest of this library's kernels and the fastest of
+        // hipBLASLt's.  With over a thousand library candidates, the minimum of single
+        // noisy timings favours the library; the two finalists are therefore timed again
+        // against each other, in alternating rounds, and the faster in total is kept.
+        GemmPlan own_pick = *p, lib_pick = *p;
+        float own_ms = 1e30f, lib_ms = 1e30f;
+        for (auto &c : cands) {
+            GemmPlan trial = *p;
+            trial.own = c.own;
+            trial.algo = c.algo;
+            float ms = 0.f;
+            const int r = time_plan(trial, 5, &ms);
+            if (r < 0) {
                 rc = UNIPIN_EHIP;
                 break;
             }
+            if (r > 0) continue;
+            float &best = c.own >= 0 ? own_ms : lib_ms;
+            if (ms < best) {
+                best = ms;
+                (c.own >= 0 ? own_pick : lib_pick) = trial;
+            }
+        }
+        if (rc != UNIPIN_OK) break;
+        if (own_ms < 1e30f && lib_ms < 1e30f) {
+            float own_total = 0.f, lib_total = 0.f;
+            for (int round = 0; round < 4 && rc == UNIPIN_OK; ++round) {
+                float a = 0.f, b = 0.f;
+                const int ra = time_plan(own_pick, 10, &a), rb = ra < 0 ? -1 : time_plan(lib_pick, 10, &b);
+                if (ra < 0 || rb < 0) rc = UNIPIN_EHIP;
+                own_total += ra == 0 ? a : 1e30f;
+                lib_total += rb == 0 ? b : 1e30f;
+            }
+            if (rc != UNIPIN_OK) break;
+            own_ms = own_total;
+            lib_ms = lib_total;
+        }
+        if (own_ms < 1e30f || lib_ms < 1e30f) {
+            const GemmPlan &pick = own_ms <= lib_ms ? own_pick : lib_pick;
+            p->own = pick.own;
+            p->algo = pick.algo;
         }
     }
     (void)hipEventDestroy(e0);

@@ -15,13 +15,13 @@ hipError_t launch_fill_random(void *dst, size_t n, unsigned seed, float amp, hip
 
 // y[M, N] = epilogue(x[M, K] @ w[K, N] + bias[N]) with this library's MFMA kernel
 // (gemm_bf16.hip), fp32 accumulation, one rounding to bf16.  kGemmBiasResidual adds the
-// old y (in place).  Needs N % 128 == 0, K % 32 == 0 and byte sizes below 2^31
-// (gemm_bf16_supported).  cfg 0 .. kGemmConfigs-1 picks the workgroup tile: 64, 128 or 256
-// rows (gemm_bf16_rows_per_tile) by 128 columns.
+// old y (in place).  cfg 0 .. kGemmConfigs-1 picks the workgroup tile: 64, 128 or 256
+// rows by 128 columns with 32-deep stages, or 128 x 128 with 64-deep stages.  Needs
+// N % 128 == 0, K a multiple of the stage depth and byte sizes below 2^31
+// (gemm_bf16_supported).
 enum GemmEpilogue : int { kGemmBias = 0, kGemmBiasGelu = 1, kGemmBiasResidual = 2 };
-constexpr int kGemmConfigs = 3;
-bool gemm_bf16_supported(long M, int N, int K);
-int gemm_bf16_rows_per_tile(int cfg);
+constexpr int kGemmConfigs = 4;
+bool gemm_bf16_supported(long M, int N, int K, int cfg);
 hipError_t launch_gemm_bf16(const void *x, const void *w, const void *bias, void *y, long M, int N, int K, int epi,
                             int cfg, hipStream_t stream);
 

@@ -2,14 +2,18 @@
 // Y[M, N] = epilogue(X[M, K] W[K, N] + b), all row-major bf16, fp32 accumulation, on
 // v_mfma_f32_32x32x16_bf16.  W is "x @ W" [fan_in, fan_out] as the block stores it.
 //
-//   * a workgroup computes a BM x 128 tile of Y (BM = 64, 128 or 256); its waves sit WM
-//     along the rows and 2 along the columns, and each holds 32*MB rows x 64 columns of
-//     the tile as MFMA accumulators of Y^T = W^T X^T (the attention's O^T = V^T P^T);
-//   * the contraction runs in 32-deep steps: the tile rows' 32 columns of X and the tile
-//     columns' 32 rows of W arrive by buffer-to-LDS DMA in a ring of NS stages, NS - 1
-//     steps ahead of use; rows of X past M read as zero;
+//   * a workgroup computes a BM x BN tile of Y; its waves sit WM along the rows and WN
+//     along the columns, and each holds 32*MB rows x 32*NB columns of the tile as MFMA
+//     accumulators of Y^T = W^T X^T (the attention's O^T = V^T P^T);
+//   * the contraction runs in KT-deep stages (32 or 64): the tile rows' KT columns of X
+//     and the tile columns' KT rows of W arrive by buffer-to-LDS DMA in a ring of NS
+//     stages, NS - 1 stages ahead of use; rows of X past M read as zero.  Each wave
+//     moves a fixed share of every stage (XPW 1 KB pieces of X, WPW of W);
 //   * X is read from LDS 16 bytes per lane as the B operand; W stays in its [k][n]
-//     layout and ds_read_b64_tr_b16 delivers W^T as the A operand;
+//     layout and ds_read_b64_tr_b16 delivers W^T as the A operand.  The operands of the
+//     next 16-deep slice are read while the current slice's MFMAs run, across the stage
+//     boundary too: the wait for the next stage and the workgroup barrier come before
+//     the last slice of a stage is multiplied;
 //   * the epilogue adds the bias and applies the tanh-form GELU or adds the residual (the
 //     output's old value) in fp32, rounds once to bf16 and stores whole rows through LDS;
 //   * workgroup b runs on XCD b % 8.  The column tiles of one row tile go to consecutive
@@ -31,61 +35,77 @@
 namespace unipin {
 namespace {
 
-constexpr int kKT = 32;                 // contraction depth of one stage
-constexpr int kBN = 128;                // columns of Y per workgroup
-constexpr int kXRow = kKT * 2;          // bytes of one X row within a stage: 4 blocks of 16
-constexpr int kWRow = kBN * 2;          // bytes of one W row within a stage: 16 blocks of 16
-constexpr int kWStage = kKT * kWRow;    // 8 KB
-
-// 16-byte block swizzles (XOR inside a row).  The X read serves 16 lanes at a time: 16
-// consecutive rows, one logical block; (row >> 2) & 3 puts them on 64 distinct banks.
-// The W transpose read serves 32 lanes at a time: 4 consecutive rows x 64 bytes;
-// (row & 3) << 2 puts them on 64 distinct banks.
-__device__ __forceinline__ int x_swz(int row) { return (row >> 2) & 3; }
-__device__ __forceinline__ int w_swz(int row) { return (row & 3) << 2; }
-
-template <int WM, int MB, int NS>
+template <int WM, int WN, int MB, int NB, int KT, int NS>
 struct GemmCfg {
-    static constexpr int W = 2 * WM;                  // waves per workgroup
-    static constexpr int BM = WM * 32 * MB;           // rows of Y per workgroup
-    static constexpr int XBYTES = BM * kXRow;         // the X part of a stage
-    static constexpr int SBYTES = XBYTES + kWStage;   // one stage: X, then W
-    static constexpr int XP = XBYTES / 1024;          // 1 KB DMA pieces of X per stage
-    static constexpr int PW = SBYTES / 1024 / W;      // pieces per wave per stage
-    static constexpr int STAGE_OUT = 32 * MB * 128;   // one wave's output rows, bf16
-    static_assert(PW * W * 1024 == SBYTES, "a stage must split evenly over the waves");
+    static constexpr int W = WM * WN;              // waves per workgroup
+    static constexpr int BM = WM * 32 * MB;        // rows of Y per workgroup
+    static constexpr int BN = WN * 32 * NB;        // columns of Y per workgroup
+    static constexpr int KK = KT / 16;             // 16-deep slices per stage
+    static constexpr int XROW = KT * 2;            // bytes of one X row within a stage
+    static constexpr int XBLK = KT / 8;            // its 16-byte blocks
+    static constexpr int WROW = BN * 2;            // bytes of one W row within a stage
+    static constexpr int WBLK = BN / 8;
+    static constexpr int XBYTES = BM * XROW;       // a stage: X, then W
+    static constexpr int WBYTES = KT * WROW;
+    static constexpr int SBYTES = XBYTES + WBYTES;
+    static constexpr int XPW = XBYTES / 1024 / W;  // 1 KB DMA pieces per wave per stage
+    static constexpr int WPW = WBYTES / 1024 / W;
+    static constexpr int PW = XPW + WPW;
+    static constexpr int OROW = NB * 64;           // bytes of one staged output row of a wave
+    static constexpr int OBLK = NB * 4;
+    static constexpr int STAGE_OUT = 32 * MB * OROW;
+    static_assert(KT == 32 || KT == 64, "stage depth");
+    static_assert(KK % 2 == 0, "every stage starts in operand buffer 0");
+    static_assert(XPW * W * 1024 == XBYTES && WPW * W * 1024 == WBYTES && XPW >= 1 && WPW >= 1,
+                  "a stage must split evenly over the waves");
     static_assert(NS * SBYTES >= W * STAGE_OUT, "the output staging must fit in the ring");
-    static_assert(NS >= 2 && NS <= 4, "waits cover up to three steps in flight");
+    static_assert(NS >= 2 && (NS - 2) * PW < 64, "vmcnt range");
+    static_assert(BN >= 128, "W rows of at least 16 blocks (the W swizzle)");
 };
 
-// Waits until this wave's pieces of the step issued `after` steps before the newest
-// have landed (loads complete in issue order).
-template <int PW>
-__device__ __forceinline__ void wait_steps_after(int after) {
-    if (after >= 3) wait_vmcnt<3 * PW>();
-    else if (after == 2) wait_vmcnt<2 * PW>();
-    else if (after == 1) wait_vmcnt<PW>();
-    else wait_vmcnt<0>();
+// 16-byte block swizzles (XOR inside a row).  The X read serves 16 lanes at a time: 16
+// consecutive rows, one logical block; the XOR puts them on 64 distinct banks (rows of
+// 4 blocks: (row >> 2) & 3; rows of 8 blocks: (row >> 1) & 7).  The W transpose read
+// serves 32 lanes at a time: 4 consecutive rows x 64 bytes; (row & 3) << 2 puts them on
+// 64 distinct banks.
+template <int XBLK>
+__device__ __forceinline__ int x_swz(int row) {
+    return XBLK == 4 ? ((row >> 2) & 3) : ((row >> 1) & 7);
+}
+__device__ __forceinline__ int w_swz(int row) { return (row & 3) << 2; }
+
+// Waits until at most `after` of this wave's stages are still in flight (loads complete
+// in issue order); `after` never exceeds MAXA.
+template <int PW, int MAXA>
+__device__ __forceinline__ void wait_stages_after(int after) {
+    if constexpr (MAXA == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (after >= MAXA) wait_vmcnt<MAXA * PW>();
+        else wait_stages_after<PW, MAXA - 1>(after);
+    }
 }
 
 // GELU, tanh form: 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3), written as
-// x / (1 + e^(-2u)), which has no cancellation for large negative x.
+// x / (1 + 2^z) with z = -2 log2(e) u = x (a + b x^2), which has no cancellation for
+// large negative x.  The reciprocal is v_rcp_f32 (1 ulp), far below the bf16 rounding
+// of the result, instead of a full-precision division.
 __device__ __forceinline__ float gelu_tanh(float x) {
-    const float u = 0.7978845608028654f * __builtin_fmaf(0.044715f * x, x * x, x);
-    return x / (1.f + __builtin_amdgcn_exp2f(-2.8853900817779268f * u));   // e^(-2u) = 2^(-2u log2 e)
+    constexpr float a = -2.f * 1.4426950408889634f * 0.7978845608028654f;
+    constexpr float b = a * 0.044715f;
+    const float z = x * __builtin_fmaf(b, x * x, a);
+    return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z));
 }
 
-template <int WM> constexpr int gemm_threads() { return 2 * WM * 64; }   // = GemmCfg::W * 64
-
-template <int WM, int MB, int NS, int WPS, int EPI>
-__global__ void __launch_bounds__(gemm_threads<WM>(), WPS)
+template <int WM, int WN, int MB, int NB, int KT, int NS, int WPS, int EPI>
+__global__ void __launch_bounds__(WM *WN * 64, WPS)
     gemm_bf16_kernel(const bf16 *__restrict__ x, const bf16 *__restrict__ w, const bf16 *__restrict__ bias, bf16 *y,
                      int M, int N, int K, int mtiles) {
-    using G = GemmCfg<WM, MB, NS>;
+    using G = GemmCfg<WM, WN, MB, NB, KT, NS>;
     __shared__ __attribute__((aligned(1024))) char smem_raw[NS * G::SBYTES];
     LDS_AS char *smem = (LDS_AS char *)smem_raw;
 
-    const int ntn = N / kBN;
+    const int ntn = N / G::BN;
     const int bid = blockIdx.x, xcd = bid & 7, j = bid >> 3;
     const int whole = (mtiles >> 3) * ntn;   // per XCD: workgroups of its whole row tiles
     int mt, nt;
@@ -98,40 +118,38 @@ __global__ void __launch_bounds__(gemm_threads<WM>(), WPS)
         nt = r % ntn;
     }
     if (mt >= mtiles) return;
-    const int m0 = mt * G::BM, n0 = nt * kBN;
+    const int m0 = mt * G::BM, n0 = nt * G::BN;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 31, g = lane >> 5;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
 
-    // DMA: piece p of a stage (1 KB, lane l its 16-byte block 64 p + l in LDS order) is
-    // X block p*64 + l (row / 4, swizzled) for p < XP, else W block (p - XP)*64 + l
-    // (row / 16, swizzled).  X is addressed from row m0 on, so that rows past M fall
-    // past the record count.
+    // DMA: X piece p of a stage (1 KB, lane l its 16-byte block 64 p + l in LDS order) is
+    // X block 64 p + l (row / XBLK, swizzled); W piece p likewise (row / WBLK).  Wave v
+    // moves X pieces v*XPW .. and W pieces v*WPW ...  X is addressed from row m0 on, so
+    // that rows past M fall past the record count.
     const i32x4 xr = rsrc_words(x + (long)m0 * K, (uint32_t)((long)(M - m0) * K * 2));
     const i32x4 wr = rsrc_words(w + n0, (uint32_t)(((long)K * N - n0) * 2));
     int voff[G::PW];
 #pragma unroll
-    for (int q = 0; q < G::PW; ++q) {
-        const int p = wave * G::PW + q;
-        if (p < G::XP) {
-            const int bi = p * 64 + lane, row = bi >> 2;
-            voff[q] = row * K * 2 + (((bi & 3) ^ x_swz(row)) * 16);
-        } else {
-            const int bi = (p - G::XP) * 64 + lane, row = bi >> 4;
-            voff[q] = row * N * 2 + (((bi & 15) ^ w_swz(row)) * 16);
-        }
+    for (int q = 0; q < G::XPW; ++q) {
+        const int bi = (wave * G::XPW + q) * 64 + lane, row = bi / G::XBLK;
+        voff[q] = row * K * 2 + (((bi % G::XBLK) ^ x_swz<G::XBLK>(row)) * 16);
+    }
+#pragma unroll
+    for (int q = 0; q < G::WPW; ++q) {
+        const int bi = (wave * G::WPW + q) * 64 + lane, row = bi / G::WBLK;
+        voff[G::XPW + q] = row * N * 2 + (((bi % G::WBLK) ^ w_swz(row)) * 16);
     }
     const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
     auto issue = [&](int s) {
         const uint32_t stage = lds0 + (uint32_t)((s % NS) * G::SBYTES);
-        const int k0 = s * kKT;
+        const int k0 = s * KT;
 #pragma unroll
-        for (int q = 0; q < G::PW; ++q) {
-            const int p = wave * G::PW + q;
-            if (p < G::XP) dma16(stage + p * 1024, xr, voff[q], k0 * 2);
-            else dma16(stage + p * 1024, wr, voff[q], k0 * N * 2);
-        }
+        for (int q = 0; q < G::XPW; ++q) dma16(stage + (wave * G::XPW + q) * 1024, xr, voff[q], k0 * 2);
+#pragma unroll
+        for (int q = 0; q < G::WPW; ++q)
+            dma16(stage + G::XBYTES + (wave * G::WPW + q) * 1024, wr, voff[G::XPW + q], k0 * N * 2);
     };
 
     // operand reads: X rows of this wave; W transpose reads, 16-lane group (g, sub):
@@ -140,65 +158,85 @@ __global__ void __launch_bounds__(gemm_threads<WM>(), WPS)
     const int xrow0 = wm * 32 * MB + col;
     const int ti = lane & 15, sub = (lane >> 4) & 1;
     const int wrow = 8 * g + (ti >> 2);
-    const int w_off = wrow * kWRow + (ti & 1) * 8;
-    int w_blk[2];
+    const int w_off = wrow * G::WROW + (ti & 1) * 8;
+    int w_blk[NB];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) w_blk[nb] = (((wn * 2 + nb) * 4 + 2 * sub + ((ti & 3) >> 1)) ^ w_swz(wrow)) * 16;
+    for (int nb = 0; nb < NB; ++nb)
+        w_blk[nb] = (((wn * NB + nb) * 4 + 2 * sub + ((ti & 3) >> 1)) ^ w_swz(wrow)) * 16;
 
-    f32x16 acc[2][MB];
+    f32x16 acc[NB][MB];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x16{};
 
-    const int steps = K / kKT;
-    int issued = 0;
-    for (; issued < NS - 1 && issued < steps; ++issued) issue(issued);
-    for (int s = 0; s < steps; ++s) {
-        wait_steps_after<G::PW>(issued - s - 1);
-        __syncthreads();   // step s has landed everywhere; the slot of step s-1 is free
-        if (issued < steps) issue(issued++);
+    // operands of two 16-deep slices: the one multiplied and the next one being read
+    bf16x8 xb[2][MB], va[2][NB];
+    auto read = [&](int s, int kk, int buf) {
         const LDS_AS char *xs = smem + (s % NS) * G::SBYTES;
         const LDS_AS char *ws = xs + G::XBYTES;
 #pragma unroll
-        for (int kk = 0; kk < kKT / 16; ++kk) {
-            bf16x8 xb[MB];
+        for (int mb = 0; mb < MB; ++mb) {
+            const int row = xrow0 + mb * 32;
+            xb[buf][mb] = *reinterpret_cast<const LDS_AS bf16x8 *>(xs + row * G::XROW +
+                                                                  (((2 * kk + g) ^ x_swz<G::XBLK>(row)) * 16));
+        }
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const int row = xrow0 + mb * 32;
-                xb[mb] = *reinterpret_cast<const LDS_AS bf16x8 *>(xs + row * kXRow + (((2 * kk + g) ^ x_swz(row)) * 16));
+        for (int nb = 0; nb < NB; ++nb) {
+            const LDS_AS char *src = ws + w_off + w_blk[nb] + kk * 16 * G::WROW;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)src);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(src + 4 * G::WROW));
+            const i16x4 lh[2] = {lo, hi};
+            va[buf][nb] = __builtin_bit_cast(bf16x8, lh);
+        }
+    };
+    auto mfma = [&](int buf) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[buf][nb], xb[buf][mb], acc[nb][mb], 0, 0, 0);
+    };
+
+    // Stage s + NS - 1 is issued into the slot of stage s - 1 once the barrier before
+    // stage s has shown that every wave is done reading it.
+    const int steps = K / KT;
+    int issued = 0;
+    for (; issued < NS - 1 && issued < steps; ++issued) issue(issued);
+    wait_stages_after<G::PW, NS - 2>(issued - 1);
+    __syncthreads();   // stage 0 has landed everywhere
+    if (issued < steps) issue(issued++);
+    read(0, 0, 0);
+    for (int s = 0; s < steps; ++s) {
+#pragma unroll
+        for (int kk = 0; kk < G::KK; ++kk) {
+            const int cur = kk & 1;
+            if (kk + 1 < G::KK) {
+                read(s, kk + 1, cur ^ 1);
+            } else if (s + 1 < steps) {
+                wait_stages_after<G::PW, NS - 2>(issued - s - 2);
+                __syncthreads();   // stage s + 1 has landed everywhere; stage s is read
+                if (issued < steps) issue(issued++);
+                read(s + 1, 0, cur ^ 1);
             }
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const LDS_AS char *src = ws + w_off + w_blk[nb] + kk * 16 * kWRow;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)src);
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(src + 4 * kWRow));
-                const i16x4 lh[2] = {lo, hi};
-                const bf16x8 va = __builtin_bit_cast(bf16x8, lh);
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, xb[mb], acc[nb][mb], 0, 0, 0);
-            }
+            mfma(cur);
         }
     }
 
     // Epilogue.  Element i of acc[nb][mb] in lane (col, g) is Y[m][n] with m = m0 + wm*32*MB
-    // + mb*32 + col, n = n0 + (wn*2 + nb)*32 + 8(i/4) + 4g + i%4.  Each wave stages its
-    // 32*MB x 64 outputs as bf16 rows of 128 bytes (16-byte blocks swizzled by row & 7),
+    // + mb*32 + col, n = n0 + (wn*NB + nb)*32 + 8(i/4) + 4g + i%4.  Each wave stages its
+    // 32*MB x 32*NB outputs as bf16 rows of OROW bytes (16-byte blocks swizzled by row),
     // then stores them as whole 16-byte pieces of rows.
     __syncthreads();   // every wave is done with the ring
     LDS_AS char *stg = smem + wave * G::STAGE_OUT;
-    // The epilogue's global loads go out together, one round trip per column block: the
-    // bias of the wave's columns, and for the residual the old outputs (a row past M
-    // reads row M-1 instead, and its result is never stored).
-    bf16x4 bv[2][4];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < NB; ++nb) {
+        // the bias of the column block, and for the residual the old outputs (a row past
+        // M reads row M-1 instead, and its result is never stored), loaded together
+        bf16x4 bv[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-            bv[nb][jj] = *reinterpret_cast<const bf16x4 *>(bias + n0 + (wn * 2 + nb) * 32 + 8 * jj + 4 * g);
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+            bv[jj] = *reinterpret_cast<const bf16x4 *>(bias + n0 + (wn * NB + nb) * 32 + 8 * jj + 4 * g);
         bf16x4 rv[4][MB];
         if (EPI == kGemmBiasResidual) {
 #pragma unroll
@@ -206,8 +244,8 @@ __global__ void __launch_bounds__(gemm_threads<WM>(), WPS)
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
                     const int m = min(m0 + wm * 32 * MB + mb * 32 + col, M - 1);
-                    rv[jj][mb] = *reinterpret_cast<const bf16x4 *>(y + (long)m * N + n0 + (wn * 2 + nb) * 32 + 8 * jj +
-                                                                   4 * g);
+                    rv[jj][mb] = *reinterpret_cast<const bf16x4 *>(y + (long)m * N + n0 + (wn * NB + nb) * 32 +
+                                                                   8 * jj + 4 * g);
                 }
         }
 #pragma unroll
@@ -218,31 +256,33 @@ __global__ void __launch_bounds__(gemm_threads<WM>(), WPS)
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    v[e] = acc[nb][mb][4 * jj + e] + (float)bv[nb][jj][e];
+                    v[e] = acc[nb][mb][4 * jj + e] + (float)bv[jj][e];
                     if (EPI == kGemmBiasGelu) v[e] = gelu_tanh(v[e]);
                     if (EPI == kGemmBiasResidual) v[e] += (float)rv[jj][mb][e];
                 }
                 const bf16x4 o = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};   // round to nearest even
-                *reinterpret_cast<LDS_AS bf16x4 *>(stg + r * 128 + (((nb * 4 + jj) ^ (r & 7)) * 16) + g * 8) = o;
+                *reinterpret_cast<LDS_AS bf16x4 *>(stg + r * G::OROW + (((nb * 4 + jj) ^ (r & (G::OBLK - 1))) * 16) +
+                                                   g * 8) = o;
             }
         }
     }
     asm volatile("" ::: "memory");   // a wave's LDS operations run in order: the reads see the writes
 #pragma unroll
-    for (int i = lane; i < 32 * MB * 8; i += 64) {
-        const int r = i >> 3, b = i & 7;
-        const u32x4 val = *reinterpret_cast<const LDS_AS u32x4 *>(stg + r * 128 + ((b ^ (r & 7)) * 16));
+    for (int i = lane; i < 32 * MB * G::OBLK; i += 64) {
+        const int r = i / G::OBLK, b = i % G::OBLK;
+        const u32x4 val = *reinterpret_cast<const LDS_AS u32x4 *>(stg + r * G::OROW + ((b ^ (r & (G::OBLK - 1))) * 16));
         const int m = m0 + wm * 32 * MB + r;
-        if (m < M) *reinterpret_cast<u32x4 *>(y + (long)m * N + n0 + wn * 64 + b * 8) = val;
+        if (m < M) *reinterpret_cast<u32x4 *>(y + (long)m * N + n0 + wn * 32 * NB + b * 8) = val;
     }
 }
 
-template <int WM, int MB, int NS, int WPS>
+template <int WM, int WN, int MB, int NB, int KT, int NS, int WPS>
 hipError_t launch_cfg(const void *x, const void *w, const void *bias, void *y, int M, int N, int K, int epi,
                       hipStream_t stream) {
-    using G = GemmCfg<WM, MB, NS>;
+    using G = GemmCfg<WM, WN, MB, NB, KT, NS>;
+    if (N % G::BN || K % KT) return hipErrorInvalidValue;
     const int mtiles = (M + G::BM - 1) / G::BM;
-    const long ntn = N / kBN;
+    const long ntn = N / G::BN;
     const long blocks = 8L * ((mtiles / 8) * ntn + ((mtiles % 8) * ntn + 7) / 8);
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks), block(G::W * 64);
@@ -251,16 +291,16 @@ hipError_t launch_cfg(const void *x, const void *w, const void *bias, void *y, i
     bf16 *ys = static_cast<bf16 *>(y);
     switch (epi) {
         case kGemmBias:
-            hipLaunchKernelGGL((gemm_bf16_kernel<WM, MB, NS, WPS, kGemmBias>), grid, block, 0, stream, xs, ws, bs, ys,
-                               M, N, K, mtiles);
+            hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, MB, NB, KT, NS, WPS, kGemmBias>), grid, block, 0, stream, xs,
+                               ws, bs, ys, M, N, K, mtiles);
             break;
         case kGemmBiasGelu:
-            hipLaunchKernelGGL((gemm_bf16_kernel<WM, MB, NS, WPS, kGemmBiasGelu>), grid, block, 0, stream, xs, ws, bs,
-                               ys, M, N, K, mtiles);
+            hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, MB, NB, KT, NS, WPS, kGemmBiasGelu>), grid, block, 0, stream,
+                               xs, ws, bs, ys, M, N, K, mtiles);
             break;
         case kGemmBiasResidual:
-            hipLaunchKernelGGL((gemm_bf16_kernel<WM, MB, NS, WPS, kGemmBiasResidual>), grid, block, 0, stream, xs, ws,
-                               bs, ys, M, N, K, mtiles);
+            hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, MB, NB, KT, NS, WPS, kGemmBiasResidual>), grid, block, 0,
+                               stream, xs, ws, bs, ys, M, N, K, mtiles);
             break;
         default:
             return hipErrorInvalidValue;
@@ -268,31 +308,30 @@ hipError_t launch_cfg(const void *x, const void *w, const void *bias, void *y, i
     return hipGetLastError();
 }
 
+// The stage depth of each tile configuration (the contraction must be a multiple of it).
+constexpr int kStageDepth[kGemmConfigs] = {32, 32, 32, 64};
+
 }  // namespace
 
-bool gemm_bf16_supported(long M, int N, int K) {
+bool gemm_bf16_supported(long M, int N, int K, int cfg) {
     constexpr long kLim = 1L << 31;   // byte offsets of the buffer descriptors
-    return M >= 1 && N >= kBN && N % kBN == 0 && K >= kKT && K % kKT == 0 && M * (long)K * 2 < kLim &&
-           (long)K * N * 2 < kLim && M * (long)N * 2 < kLim;
-}
-
-int gemm_bf16_rows_per_tile(int cfg) {
-    switch (cfg) {
-        case 0: return GemmCfg<2, 1, 4>::BM;
-        case 1: return GemmCfg<2, 2, 4>::BM;
-        case 2: return GemmCfg<4, 2, 3>::BM;
-        default: return 0;
-    }
+    if (cfg < 0 || cfg >= kGemmConfigs) return false;
+    return M >= 1 && N >= 128 && N % 128 == 0 && K >= kStageDepth[cfg] && K % kStageDepth[cfg] == 0 &&
+           M * (long)K * 2 < kLim && (long)K * N * 2 < kLim && M * (long)N * 2 < kLim;
 }
 
 hipError_t launch_gemm_bf16(const void *x, const void *w, const void *bias, void *y, long M, int N, int K, int epi,
                             int cfg, hipStream_t stream) {
-    if (!gemm_bf16_supported(M, N, K)) return hipErrorInvalidValue;
+    if (!gemm_bf16_supported(M, N, K, cfg)) return hipErrorInvalidValue;
     switch (cfg) {
-        // LDS per workgroup 48, 64 and 72 KB: 3, 2 and 2 workgroups per CU (3, 2 and 4 waves per SIMD)
-        case 0: return launch_cfg<2, 1, 4, 3>(x, w, bias, y, (int)M, N, K, epi, stream);
-        case 1: return launch_cfg<2, 2, 4, 2>(x, w, bias, y, (int)M, N, K, epi, stream);
-        case 2: return launch_cfg<4, 2, 3, 4>(x, w, bias, y, (int)M, N, K, epi, stream);
+        // workgroup tiles 64, 128 and 256 x 128 with 32-deep stages (4, 4 and 8 waves of
+        // 32 x 64, 64 x 64 and 64 x 64), and 128 x 128 with 64-deep stages (8 waves of
+        // 64 x 32); LDS per workgroup 48, 64, 72 and 128 KB (3, 2, 2 and 1 workgroups
+        // per CU: 3, 2, 4 and 2 waves per SIMD)
+        case 0: return launch_cfg<2, 2, 1, 2, 32, 4, 3>(x, w, bias, y, (int)M, N, K, epi, stream);
+        case 1: return launch_cfg<2, 2, 2, 2, 32, 4, 2>(x, w, bias, y, (int)M, N, K, epi, stream);
+        case 2: return launch_cfg<4, 2, 2, 2, 32, 3, 4>(x, w, bias, y, (int)M, N, K, epi, stream);
+        case 3: return launch_cfg<2, 4, 2, 1, 64, 4, 2>(x, w, bias, y, (int)M, N, K, epi, stream);
         default: return hipErrorInvalidValue;
     }
 }

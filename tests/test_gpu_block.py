@@ -58,7 +58,7 @@ SHAPES = [(3, 70, 33, 4, 32), (2, 130, 65, 8, 64), (2, 64, 20, 2, 128)]
 
 
 # the block's GEMMs: hipBLASLt, or the library's kernel with each workgroup tile
-GEMM_KERNELS = [fa.GEMM_LIBRARY, 0, 1, 2]
+GEMM_KERNELS = [fa.GEMM_LIBRARY, 0, 1, 2, 3]
 
 
 @pytest.mark.parametrize("gemm", GEMM_KERNELS, ids=lambda k: "hipblaslt" if k == fa.GEMM_LIBRARY else f"tile{k}")
