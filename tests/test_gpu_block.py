@@ -123,25 +123,31 @@ def test_block_candidates_independent_of_each_other():
     ctx.close()
 
 
-def test_block_table2_shape_sampled():
+@pytest.mark.parametrize("gemm", ["tuned", 0, 1, 2, 3], ids=lambda k: k if k == "tuned" else f"tile{k}")
+def test_block_table2_shape_sampled(gemm):
     """The pages' Table 2 shape (B=8, history 992, 656 candidates) at width 512
-    (8 heads x 64), with the GEMM kernels the tuner picks: history then candidate
-    forward, sampled users against the oracle."""
+    (8 heads x 64), with the GEMM kernels the tuner picks and with each tile
+    configuration of the library's GEMM pinned: history then candidate forward, sampled
+    users against the oracle.  User 7's candidate rows hold the last, partial 256-row
+    tile of the candidate-side GEMMs (5248 rows)."""
     B, n, K, H, D = 8, 992, 656, 8, 64
-    announce("block Table 2 shape")
+    announce(f"block Table 2 shape gemm={gemm}")
     w, xh, xc, pool = make(B, n, K, H, D, L=1, seed=70)
     lens = [n] * B
     slots = list(range(B))
     ctx = fa.BlockContext()
-    ctx.tune(pool, B, n)   # the kernels the benchmark times
-    ctx.tune(pool, B, K)
+    if gemm == "tuned":
+        ctx.tune(pool, B, n)   # the kernels the benchmark times
+        ctx.tune(pool, B, K)
+    else:
+        ctx.set_gemm(gemm)
     xh0, xc0 = xh.clone(), xc.clone()
     fa.block_forward(ctx, w, fa.BLOCK_HISTORY, xh, pool, slots, lens, 0)
     fa.block_forward(ctx, w, fa.BLOCK_CANDIDATES, xc, pool, slots, lens, 0)
     torch.cuda.synchronize()
     assert pool.status() == 0
     wc = {k: v.cpu() for k, v in w.items()}
-    for b in (0, 5):
+    for b in (0, 7):
         _, jc = oracle.block_joint(xh0[b:b + 1].cpu(), xc0[b:b + 1].cpu(), [n], wc, H)
         check_rel(xc[b:b + 1], jc, f"Table 2 shape, candidates of user {b}")
     pool.close()
