@@ -203,10 +203,13 @@ def block_table2(fa, W, torch, dev, steps: int, warmup: int):
     forward (the pages' "decode with KV reuse"), each timed over its 12 layers with HIP
     events.  FLOPs per layer: 24 M C^2 in the four projections (M hidden rows) plus the
     attention's 2 D N (N + 1) per (user, head) for the history, 4 D k (N + 1) for the
-    candidates."""
+    candidates.  Each layer's LayerNorms are folded into its weights once, before the
+    timing (fold_layernorm); the tuner then chooses per projection between the GEMM on
+    the hidden state with the statistics applied in its epilogue and the LayerNorm
+    kernel followed by the best plain GEMM."""
     L, B, n, K, H, D = 12, 8, 992, 656, 8, 64
     C = H * D
-    ws = [W.block_weights(C, torch.bfloat16, seed=300 + l, device=dev) for l in range(L)]
+    ws = [fa.fold_layernorm(W.block_weights(C, torch.bfloat16, seed=300 + l, device=dev)) for l in range(L)]
     xh0 = W.block_inputs(B, n, C, torch.bfloat16, seed=298, device=dev)
     xc0 = W.block_inputs(B, K, C, torch.bfloat16, seed=299, device=dev)
     xh, xc = xh0.clone(), xc0.clone()

@@ -35,19 +35,22 @@ EXPORTS = ("unipin_pool_create", "unipin_pool_destroy", "unipin_pool_acquire",
            "unipin_rank_decode", "unipin_ar_decode", "unipin_ar_decode_noalloc", "unipin_ar_decode_workspace_bytes",
            "unipin_pool_status", "unipin_strerror", "unipin_version",
            "unipin_block_ctx_create", "unipin_block_ctx_destroy", "unipin_block_workspace_bytes",
-           "unipin_block_ctx_tune", "unipin_block_ctx_set_gemm", "unipin_block_forward")
+           "unipin_block_ctx_tune", "unipin_block_ctx_set_gemm", "unipin_block_fold_layernorm",
+           "unipin_block_forward")
 
 
 # Weights of one transformer block, in the order of unipin_block_weights_t.
 BLOCK_WEIGHT_NAMES = ("ln1_w", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_w", "ln2_b", "w_fc", "b_fc",
                       "w_proj", "b_proj")
+# The optional folded LayerNorm weights (fold_layernorm), after them in the struct.
+BLOCK_FOLDED_NAMES = ("w_qkv_ln", "uv_qkv", "w_fc_ln", "uv_fc")
 BLOCK_HISTORY, BLOCK_CANDIDATES = 0, 1
 # unipin_block_ctx_set_gemm: AUTO, hipBLASLt only, or the library's kernel with tile 0, 1, 2, 3
 GEMM_AUTO, GEMM_LIBRARY = -2, -1
 
 
 class BlockWeights(ctypes.Structure):
-    _fields_ = [(name, ctypes.c_void_p) for name in BLOCK_WEIGHT_NAMES]
+    _fields_ = [(name, ctypes.c_void_p) for name in BLOCK_WEIGHT_NAMES + BLOCK_FOLDED_NAMES]
 
 
 def _load() -> ctypes.CDLL:
@@ -80,6 +83,7 @@ def _load() -> ctypes.CDLL:
     lib.unipin_block_ctx_set_gemm.argtypes = [vp, i32]
     lib.unipin_block_forward.argtypes = [vp, ctypes.POINTER(BlockWeights), i32, vp, vp, vp, vp, i32, i32, i32,
                                          ctypes.c_float, vp, ctypes.c_size_t, vp]
+    lib.unipin_block_fold_layernorm.argtypes = [ctypes.POINTER(BlockWeights), i32, vp, vp, vp, vp, vp]
     lib.unipin_pool_status.argtypes = [vp, vp, ip]
     lib.unipin_strerror.argtypes = [i32]
     lib.unipin_strerror.restype = ctypes.c_char_p
@@ -380,12 +384,55 @@ def block_workspace_bytes(pool: Pool, B: int, rows: int) -> int:
     return int(lib.unipin_block_workspace_bytes(pool.handle, int(B), int(rows)))
 
 
+def _block_weights(weights, C: int, dev) -> BlockWeights:
+    """The weights dict as unipin_block_weights_t, every tensor checked (the folded ones
+    only when present)."""
+    shapes = {"ln1_w": (C,), "ln1_b": (C,), "w_qkv": (C, 3 * C), "b_qkv": (3 * C,), "w_o": (C, C), "b_o": (C,),
+              "ln2_w": (C,), "ln2_b": (C,), "w_fc": (C, 4 * C), "b_fc": (4 * C,), "w_proj": (4 * C, C),
+              "b_proj": (C,)}
+    folded = {"w_qkv_ln": ((C, 3 * C), torch.bfloat16), "uv_qkv": ((2, 3 * C), torch.float32),
+              "w_fc_ln": ((C, 4 * C), torch.bfloat16), "uv_fc": ((2, 4 * C), torch.float32)}
+    ptrs = []
+    for name in BLOCK_WEIGHT_NAMES:
+        if name not in weights:
+            raise UnipinError(EINVAL, f"weights lack {name}")
+        _check_tensor(weights[name], name, shapes[name], torch.bfloat16, dev)
+        ptrs.append(weights[name].data_ptr())
+    for name in BLOCK_FOLDED_NAMES:
+        if name in weights:
+            _check_tensor(weights[name], name, folded[name][0], folded[name][1], dev)
+            ptrs.append(weights[name].data_ptr())
+        else:
+            ptrs.append(None)
+    return BlockWeights(*ptrs)
+
+
+def fold_layernorm(weights) -> dict:
+    """unipin_block_fold_layernorm: a copy of the weights dict with the folded LayerNorm
+    weights added (w_qkv_ln, uv_qkv, w_fc_ln, uv_fc; new device tensors, enqueued on the
+    current stream).  block_forward then may run the QKV and MLP-up projections on the
+    hidden state itself."""
+    C = weights["ln1_w"].shape[0]
+    dev = weights["ln1_w"].device
+    bw = _block_weights({k: weights[k] for k in BLOCK_WEIGHT_NAMES}, C, dev)
+    out = dict(weights)
+    out["w_qkv_ln"] = torch.empty((C, 3 * C), dtype=torch.bfloat16, device=dev)
+    out["uv_qkv"] = torch.empty((2, 3 * C), dtype=torch.float32, device=dev)
+    out["w_fc_ln"] = torch.empty((C, 4 * C), dtype=torch.bfloat16, device=dev)
+    out["uv_fc"] = torch.empty((2, 4 * C), dtype=torch.float32, device=dev)
+    _check(lib.unipin_block_fold_layernorm(ctypes.byref(bw), C, out["w_qkv_ln"].data_ptr(), out["uv_qkv"].data_ptr(),
+                                           out["w_fc_ln"].data_ptr(), out["uv_fc"].data_ptr(), _stream_handle(dev)),
+           "unipin_block_fold_layernorm")
+    return out
+
+
 def block_forward(ctx: BlockContext, weights, mode: int, x: torch.Tensor, pool: Pool, slot, lens, layer: int,
                   scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """unipin_block_forward: one transformer block, in place on x [B, rows, C] (bf16).
 
     weights: a dict with the BLOCK_WEIGHT_NAMES keys (bf16 device tensors; matrices
-    row-major [fan_in, fan_out]).  mode: BLOCK_HISTORY (causal over each user's lens[b]
+    row-major [fan_in, fan_out]), and optionally the BLOCK_FOLDED_NAMES ones that
+    fold_layernorm adds.  mode: BLOCK_HISTORY (causal over each user's lens[b]
     rows; their k, v go to the pool) or BLOCK_CANDIDATES (the candidates attend to the
     pool's lens[b] rows and themselves).  workspace: a device tensor of at least
     block_workspace_bytes(pool, B, rows) bytes, or None for one from torch's allocator.
@@ -397,14 +444,7 @@ def block_forward(ctx: BlockContext, weights, mode: int, x: torch.Tensor, pool: 
     if C != pool.H * pool.D:
         raise UnipinError(EINVAL, f"x has width {C}, the pool's heads give {pool.H * pool.D}")
     _check_tensor(x, "x", (B, rows, C), torch.bfloat16, dev)
-    shapes = {"ln1_w": (C,), "ln1_b": (C,), "w_qkv": (C, 3 * C), "b_qkv": (3 * C,), "w_o": (C, C), "b_o": (C,),
-              "ln2_w": (C,), "ln2_b": (C,), "w_fc": (C, 4 * C), "b_fc": (4 * C,), "w_proj": (4 * C, C),
-              "b_proj": (C,)}
-    for name in BLOCK_WEIGHT_NAMES:
-        if name not in weights:
-            raise UnipinError(EINVAL, f"weights lack {name}")
-        _check_tensor(weights[name], name, shapes[name], torch.bfloat16, dev)
-    bw = BlockWeights(*(weights[name].data_ptr() for name in BLOCK_WEIGHT_NAMES))
+    bw = _block_weights(weights, C, dev)
     lens_t, slot_t = _i32_on(lens, dev), _i32_on(slot, dev)
     if lens_t.numel() != B or slot_t.numel() != B:
         raise UnipinError(EINVAL, "lens and slot need one entry per user")

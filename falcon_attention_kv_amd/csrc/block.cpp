@@ -47,6 +47,9 @@ struct GemmPlan {
     hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
     hipblasLtMatmulAlgo_t algo{};
     int own = -1;   // >= 0: this library's kernel with that tile configuration; -1: hipBLASLt
+    // >= 0: given folded LayerNorm weights, the QKV or MLP-up projection runs on the hidden
+    // state itself in this library's kernel with that configuration (no LayerNorm kernel)
+    int ln_own = -1;
 };
 
 using PlanKey = std::tuple<long, int, int, int, bool>;   // M, N, K, epilogue, residual
@@ -83,7 +86,7 @@ GemmPlan *plan_for(unipin_block_ctx *ctx, long M, int N, int K, hipblasLtEpilogu
     auto it = ctx->plans.find(key);
     if (it != ctx->plans.end()) return &it->second;
     GemmPlan p;
-    if (ctx->kernel >= 0 && unipin::gemm_bf16_supported(M, N, K, ctx->kernel)) p.own = ctx->kernel;
+    if (ctx->kernel >= 0 && unipin::gemm_bf16_supported(M, N, K, ctx->kernel)) p.own = p.ln_own = ctx->kernel;
     const hipblasOperation_t op = HIPBLAS_OP_N;
     const hipDataType bias_type = HIP_R_16BF;
     hipblasLtMatmulPreference_t pref = nullptr;
@@ -139,13 +142,22 @@ int gemm(unipin_block_ctx *ctx, const void *in, const void *W, const void *bias,
     return run_plan(ctx, p, in, W, bias, out, M, N, K, ep, residual, ws, stream);
 }
 
+// The configuration of this library's kernel that runs the projection with its
+// LayerNorm folded in, or -1 (LayerNorm kernel, then the planned GEMM).
+int ln_choice(unipin_block_ctx *ctx, long M, int N, int K, hipblasLtEpilogue_t ep) {
+    std::lock_guard<std::mutex> lock(ctx->mu);
+    GemmPlan *p = plan_for(ctx, M, N, K, ep, false);
+    return p ? p->ln_own : -1;
+}
+
 // Workspace layout for M = B * rows hidden rows of width C (bytes, 256-aligned):
 //   [gemm]  hipBLASLt workspace
 //   [big]   M x 4C: the fused QKV output (M x 3C), later the MLP's hidden layer
 //   [ln]    M x C:  LayerNorm output, then the attention output, then LayerNorm again
 //   [tune]  4C x C + 4C: weights and bias for timing the GEMM kernels (tuning only)
+//   [uv]    2 x 4C fp32: the folded LayerNorm's column terms for timing (tuning only)
 struct Layout {
-    size_t gemm, big, ln, tune, total;
+    size_t gemm, big, ln, tune, uv, total;
 };
 
 Layout layout(long M, int C) {
@@ -155,7 +167,8 @@ Layout layout(long M, int C) {
     l.big = up(kGemmWorkspace);
     l.ln = l.big + up((size_t)M * 4 * C * e);
     l.tune = l.ln + up((size_t)M * C * e);
-    l.total = l.tune + up(((size_t)4 * C * C + 4 * C) * e);
+    l.uv = l.tune + up(((size_t)4 * C * C + 4 * C) * e);
+    l.total = l.uv + up((size_t)8 * C * sizeof(float));
     return l;
 }
 
@@ -172,6 +185,13 @@ void block_gemms(int C, GemmShape (&g)[4]) {
     g[1] = {C, C, HIPBLASLT_EPILOGUE_BIAS, true};
     g[2] = {4 * C, C, HIPBLASLT_EPILOGUE_GELU_BIAS, false};
     g[3] = {C, 4 * C, HIPBLASLT_EPILOGUE_BIAS, true};
+}
+
+// The optional folded LayerNorm weights: 0 none, 1 both parts of a projection given
+// (aligned), -1 half given or misaligned.
+int folded(const void *wf, const void *uv) {
+    if (!wf && !uv) return 0;
+    return wf && uv && aligned16(wf) && aligned16(uv) ? 1 : -1;
 }
 
 bool weights_present(const unipin_block_weights_t *w) {
@@ -243,6 +263,8 @@ int unipin_block_ctx_tune(unipin_block_ctx_t *ctx, const unipin_pool_t *pool, in
         unipin::launch_fill_random(ws + lo.tune, (size_t)4 * C * C + 4 * C, 2u, 0.05f, st) != hipSuccess ||
         unipin::launch_fill_random(ws + lo.ln, (size_t)M * C, 3u, 1.f, st) != hipSuccess)
         return UNIPIN_EHIP;
+    // and the folded LayerNorm's column terms, values of the size the block sees
+    if (unipin::launch_fill_random_f32(ws + lo.uv, (size_t)8 * C, 4u, 1.f, st) != hipSuccess) return UNIPIN_EHIP;
     GemmShape g[4];
     block_gemms(C, g);
     // QKV: ln -> big; output projection: ln -> big (M x C of it); MLP up: ln -> big;
@@ -383,10 +405,88 @@ int unipin_block_ctx_tune(unipin_block_ctx_t *ctx, const unipin_pool_t *pool, in
             p->own = pick.own;
             p->algo = pick.algo;
         }
+        // The QKV and MLP-up projections can instead run with their LayerNorm folded into
+        // the weights (unipin_block_fold_layernorm): this library's kernel on the hidden
+        // state, the row statistics taken inside the GEMM.  The fastest configuration is
+        // timed against the LayerNorm kernel followed by the GEMM just chosen, in
+        // alternating rounds; a pinned kernel is used as it is.
+        if (g[i].residual) continue;
+        p->ln_own = -1;
+        if (ctx->kernel >= 0) {
+            if (unipin::gemm_bf16_supported(M, g[i].N, g[i].K, ctx->kernel)) p->ln_own = ctx->kernel;
+            continue;
+        }
+        if (ctx->kernel != UNIPIN_GEMM_AUTO) continue;
+        const int lepi = g[i].ep == HIPBLASLT_EPILOGUE_GELU_BIAS ? unipin::kGemmLnBiasGelu : unipin::kGemmLnBias;
+        const void *gamma = bias, *beta = static_cast<const char *>(bias) + (size_t)C * 2;
+        auto timed = [&](auto &&run, int reps, float *ms) -> int {
+            if (!run() || !run()) return 1;
+            if (hipEventRecord(e0, st) != hipSuccess) return -1;
+            bool ok = true;
+            for (int r = 0; r < reps && ok; ++r) ok = run();
+            if (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                hipEventElapsedTime(ms, e0, e1) != hipSuccess)
+                return -1;
+            return ok ? 0 : 1;
+        };
+        int best_cfg = -1;
+        float best_ms = 1e30f;
+        for (int c = 0; c < unipin::kGemmConfigs && rc == UNIPIN_OK; ++c) {
+            if (!unipin::gemm_bf16_supported(M, g[i].N, g[i].K, c)) continue;
+            float ms = 0.f;
+            const int r = timed([&]() {
+                return unipin::launch_gemm_bf16(in_of[i], W, ws + lo.uv, out_of[i], M, g[i].N, g[i].K, lepi, c, st) ==
+                       hipSuccess;
+            }, 5, &ms);
+            if (r < 0) rc = UNIPIN_EHIP;
+            if (r == 0 && ms < best_ms) {
+                best_ms = ms;
+                best_cfg = c;
+            }
+        }
+        if (rc != UNIPIN_OK) break;
+        if (best_cfg < 0) continue;
+        float fused_total = 0.f, plain_total = 0.f;
+        for (int round = 0; round < 4 && rc == UNIPIN_OK; ++round) {
+            float a = 0.f, b = 0.f;
+            const int ra = timed([&]() {
+                return unipin::launch_gemm_bf16(in_of[i], W, ws + lo.uv, out_of[i], M, g[i].N, g[i].K, lepi,
+                                                best_cfg, st) == hipSuccess;
+            }, 10, &a);
+            // the plain path: LayerNorm (in place, which keeps the operands bounded), then the GEMM
+            const int rb = ra < 0 ? -1 : timed([&]() {
+                return unipin::launch_layernorm(in_of[i], gamma, beta, in_of[i], M, C, kLnEps, st) == hipSuccess &&
+                       run_plan(ctx, p, in_of[i], W, bias, out_of[i], M, g[i].N, g[i].K, g[i].ep, false,
+                                ws + lo.gemm, st) == UNIPIN_OK;
+            }, 10, &b);
+            if (ra < 0 || rb < 0) rc = UNIPIN_EHIP;
+            fused_total += ra == 0 ? a : 1e30f;
+            plain_total += rb == 0 ? b : 1e30f;
+        }
+        if (rc != UNIPIN_OK) break;
+        if (fused_total < plain_total) p->ln_own = best_cfg;
     }
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     return rc;
+}
+
+int unipin_block_fold_layernorm(const unipin_block_weights_t *w, int C, void *w_qkv_ln, void *uv_qkv,
+                                void *w_fc_ln, void *uv_fc, void *stream) {
+    if (!w || !w_qkv_ln || !uv_qkv || !w_fc_ln || !uv_fc) return UNIPIN_EINVAL;
+    if (C < 8 || C % 8 != 0 || C > 2048) return UNIPIN_EINVAL;
+    if (!weights_present(w)) return w->ln1_w && w->ln1_b && w->w_qkv && w->b_qkv && w->w_o && w->b_o &&
+                                           w->ln2_w && w->ln2_b && w->w_fc && w->b_fc && w->w_proj && w->b_proj
+                                       ? UNIPIN_EALIGN
+                                       : UNIPIN_EINVAL;
+    if (!aligned16(w_qkv_ln) || !aligned16(uv_qkv) || !aligned16(w_fc_ln) || !aligned16(uv_fc)) return UNIPIN_EALIGN;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (unipin::launch_fold_layernorm(w->ln1_w, w->ln1_b, w->w_qkv, w->b_qkv, C, 3 * C, w_qkv_ln, uv_qkv, st) !=
+            hipSuccess ||
+        unipin::launch_fold_layernorm(w->ln2_w, w->ln2_b, w->w_fc, w->b_fc, C, 4 * C, w_fc_ln, uv_fc, st) !=
+            hipSuccess)
+        return UNIPIN_EHIP;
+    return UNIPIN_OK;
 }
 
 int unipin_block_forward(unipin_block_ctx_t *ctx, const unipin_block_weights_t *w, int mode, void *x,
@@ -407,6 +507,11 @@ int unipin_block_forward(unipin_block_ctx_t *ctx, const unipin_block_weights_t *
                                        ? UNIPIN_EALIGN
                                        : UNIPIN_EINVAL;
     if (!aligned16(x) || !aligned16(workspace) || !aligned16(slot) || !aligned16(lens)) return UNIPIN_EALIGN;
+    const int fold1 = folded(w->w_qkv_ln, w->uv_qkv), fold2 = folded(w->w_fc_ln, w->uv_fc);
+    if (fold1 < 0 || fold2 < 0) return (w->w_qkv_ln == nullptr) != (w->uv_qkv == nullptr) ||
+                                               (w->w_fc_ln == nullptr) != (w->uv_fc == nullptr)
+                                           ? UNIPIN_EINVAL
+                                           : UNIPIN_EALIGN;
     const long M = (long)B * rows;
     const Layout lo = layout(M, C);
     if (workspace_bytes < lo.total) return UNIPIN_EINVAL;
@@ -422,17 +527,33 @@ int unipin_block_forward(unipin_block_ctx_t *ctx, const unipin_block_weights_t *
     // attention half: x += (attention of LN1(x)) @ W_o + b_o.  The QKV rows are
     // [B, rows, 3, H, D]: q, k, v of head h start at columns h*D, C + h*D, 2C + h*D of a
     // row; the heads' outputs land at columns h*D of the merged rows [B, rows, C].
-    if (unipin::launch_layernorm(x, w->ln1_w, w->ln1_b, ln, M, C, kLnEps, st) != hipSuccess) return UNIPIN_EHIP;
-    if ((rc = gemm(ctx, ln, w->w_qkv, w->b_qkv, big, M, 3 * C, C, HIPBLASLT_EPILOGUE_BIAS, false, gws, st))) return rc;
+    // With the LayerNorm folded into the weights, the planned kernel may take x itself.
+    const int f1 = fold1 ? ln_choice(ctx, M, 3 * C, C, HIPBLASLT_EPILOGUE_BIAS) : -1;
+    if (f1 >= 0) {
+        if (unipin::launch_gemm_bf16(x, w->w_qkv_ln, w->uv_qkv, big, M, 3 * C, C, unipin::kGemmLnBias, f1, st) !=
+            hipSuccess)
+            return UNIPIN_EHIP;
+    } else {
+        if (unipin::launch_layernorm(x, w->ln1_w, w->ln1_b, ln, M, C, kLnEps, st) != hipSuccess) return UNIPIN_EHIP;
+        if ((rc = gemm(ctx, ln, w->w_qkv, w->b_qkv, big, M, 3 * C, C, HIPBLASLT_EPILOGUE_BIAS, false, gws, st)))
+            return rc;
+    }
     const unipin::RowLayout qkv_rows{(long)rows * 3 * C, D, 3 * C}, merged_rows{(long)rows * C, D, C};
     rc = unipin::attention_call(mode == UNIPIN_BLOCK_HISTORY, big, big + (size_t)C * 2, big + (size_t)2 * C * 2,
                                 qkv_rows, ln, merged_rows, pool, slot, lens, layer, B, rows, scale, stream);
     if (rc) return rc;
     if ((rc = gemm(ctx, ln, w->w_o, w->b_o, x, M, C, C, HIPBLASLT_EPILOGUE_BIAS, true, gws, st))) return rc;
     // MLP half: x += GELU(LN2(x) @ W_fc + b_fc) @ W_proj + b_proj
-    if (unipin::launch_layernorm(x, w->ln2_w, w->ln2_b, ln, M, C, kLnEps, st) != hipSuccess) return UNIPIN_EHIP;
-    if ((rc = gemm(ctx, ln, w->w_fc, w->b_fc, big, M, 4 * C, C, HIPBLASLT_EPILOGUE_GELU_BIAS, false, gws, st)))
-        return rc;
+    const int f2 = fold2 ? ln_choice(ctx, M, 4 * C, C, HIPBLASLT_EPILOGUE_GELU_BIAS) : -1;
+    if (f2 >= 0) {
+        if (unipin::launch_gemm_bf16(x, w->w_fc_ln, w->uv_fc, big, M, 4 * C, C, unipin::kGemmLnBiasGelu, f2, st) !=
+            hipSuccess)
+            return UNIPIN_EHIP;
+    } else {
+        if (unipin::launch_layernorm(x, w->ln2_w, w->ln2_b, ln, M, C, kLnEps, st) != hipSuccess) return UNIPIN_EHIP;
+        if ((rc = gemm(ctx, ln, w->w_fc, w->b_fc, big, M, 4 * C, C, HIPBLASLT_EPILOGUE_GELU_BIAS, false, gws, st)))
+            return rc;
+    }
     return gemm(ctx, big, w->w_proj, w->b_proj, x, M, C, 4 * C, HIPBLASLT_EPILOGUE_BIAS, true, gws, st);
 }
 

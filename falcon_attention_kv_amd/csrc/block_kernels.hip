@@ -123,6 +123,43 @@ __global__ void __launch_bounds__(256) fill_random_kernel(bf16 *__restrict__ dst
     dst[i] = (bf16)(amp * ((float)(h >> 8) * (1.f / 8388608.f) - 1.f));
 }
 
+// The LayerNorm folded into the product after it: for column n of W [C, N],
+// wf[k][n] = bf16(gamma[k] W[k][n]), u[n] = sum_k wf[k][n] (of the rounded values, so that
+// the mean term cancels what x wf carries of it) and v[n] = sum_k beta[k] W[k][n] + b[n],
+// in fp32.  One thread per column; the rows are read and written coalesced.
+__global__ void __launch_bounds__(256) fold_layernorm_kernel(const bf16 *__restrict__ gamma,
+                                                             const bf16 *__restrict__ beta,
+                                                             const bf16 *__restrict__ w, const bf16 *__restrict__ b,
+                                                             int C, int N, bf16 *__restrict__ wf,
+                                                             float *__restrict__ uv) {
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    if (n >= N) return;
+    float u = 0.f, v = 0.f;
+    for (int k = 0; k < C; ++k) {
+        const float wk = (float)w[(long)k * N + n];
+        const bf16 f = (bf16)((float)gamma[k] * wk);   // round to nearest even
+        wf[(long)k * N + n] = f;
+        u += (float)f;
+        v = __builtin_fmaf((float)beta[k], wk, v);
+    }
+    uv[n] = u;
+    uv[N + n] = v + (float)b[n];
+}
+
+// The same sequence as fp32 values (operands for timing, tuning only).
+__global__ void __launch_bounds__(256) fill_random_f32_kernel(float *__restrict__ dst, size_t n, unsigned seed,
+                                                              float amp) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    uint32_t h = (uint32_t)i * 0x9e3779b1u ^ seed * 0x85ebca77u;
+    h ^= h >> 15;
+    h *= 0x2c1b3c6du;
+    h ^= h >> 12;
+    h *= 0x297a2d39u;
+    h ^= h >> 15;
+    dst[i] = amp * ((float)(h >> 8) * (1.f / 8388608.f) - 1.f);
+}
+
 unsigned blocks_for(long threads) { return (unsigned)((threads + 255) / 256); }
 
 }  // namespace
@@ -145,10 +182,26 @@ hipError_t launch_layernorm(const void *x, const void *w, const void *b, void *y
     return hipGetLastError();
 }
 
+hipError_t launch_fold_layernorm(const void *gamma, const void *beta, const void *w, const void *b, int C, int N,
+                                 void *wf, void *uv, hipStream_t stream) {
+    if (C <= 0 || N <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fold_layernorm_kernel, dim3(blocks_for(N)), dim3(256), 0, stream, static_cast<const bf16 *>(gamma),
+                       static_cast<const bf16 *>(beta), static_cast<const bf16 *>(w), static_cast<const bf16 *>(b), C,
+                       N, static_cast<bf16 *>(wf), static_cast<float *>(uv));
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_random(void *dst, size_t n, unsigned seed, float amp, hipStream_t stream) {
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(fill_random_kernel, dim3(blocks_for((long)n)), dim3(256), 0, stream, static_cast<bf16 *>(dst),
                        n, seed, amp);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_random_f32(void *dst, size_t n, unsigned seed, float amp, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_random_f32_kernel, dim3(blocks_for((long)n)), dim3(256), 0, stream,
+                       static_cast<float *>(dst), n, seed, amp);
     return hipGetLastError();
 }
 

@@ -16,6 +16,8 @@
 //     the last slice of a stage is multiplied;
 //   * the epilogue adds the bias and applies the tanh-form GELU or adds the residual (the
 //     output's old value) in fp32, rounds once to bf16 and stores whole rows through LDS;
+//     with a LayerNorm folded into the weights it first applies each row's mean and
+//     1/std, which the workgroup sums from the X tiles as they pass through LDS;
 //   * workgroup b runs on XCD b % 8.  The column tiles of one row tile go to consecutive
 //     workgroups of one XCD, so that they share its L2 copy of the X rows, for the first
 //     8 floor(mtiles / 8) row tiles; the workgroups of the rest are spread over all XCDs,
@@ -34,6 +36,8 @@
 
 namespace unipin {
 namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int WM, int WN, int MB, int NB, int KT, int NS>
 struct GemmCfg {
@@ -54,7 +58,10 @@ struct GemmCfg {
     static constexpr int OROW = NB * 64;           // bytes of one staged output row of a wave
     static constexpr int OBLK = NB * 4;
     static constexpr int STAGE_OUT = 32 * MB * OROW;
+    static constexpr int TPR = W * 64 / BM;        // LayerNorm epilogues: threads per row of X
+    static constexpr int BPT = XBLK / TPR;         // and the 16-byte blocks each takes per stage
     static_assert(KT == 32 || KT == 64, "stage depth");
+    static_assert(TPR >= 1 && TPR <= 4 && 64 % TPR == 0 && BPT * TPR == XBLK, "row statistics split");
     static_assert(KK % 2 == 0, "every stage starts in operand buffer 0");
     static_assert(XPW * W * 1024 == XBYTES && WPW * W * 1024 == WBYTES && XPW >= 1 && WPW >= 1,
                   "a stage must split evenly over the waves");
@@ -99,10 +106,12 @@ __device__ __forceinline__ float gelu_tanh(float x) {
 
 template <int WM, int WN, int MB, int NB, int KT, int NS, int WPS, int EPI>
 __global__ void __launch_bounds__(WM *WN * 64, WPS)
-    gemm_bf16_kernel(const bf16 *__restrict__ x, const bf16 *__restrict__ w, const bf16 *__restrict__ bias, bf16 *y,
+    gemm_bf16_kernel(const bf16 *__restrict__ x, const bf16 *__restrict__ w, const void *__restrict__ bias_, bf16 *y,
                      int M, int N, int K, int mtiles) {
     using G = GemmCfg<WM, WN, MB, NB, KT, NS>;
-    __shared__ __attribute__((aligned(1024))) char smem_raw[NS * G::SBYTES];
+    constexpr bool LN = EPI == kGemmLnBias || EPI == kGemmLnBiasGelu;
+    // the ring, then (LayerNorm epilogues) the mean and 1/std of the tile's rows
+    __shared__ __attribute__((aligned(1024))) char smem_raw[NS * G::SBYTES + (LN ? G::BM * 8 : 0)];
     LDS_AS char *smem = (LDS_AS char *)smem_raw;
 
     const int ntn = N / G::BN;
@@ -198,6 +207,27 @@ __global__ void __launch_bounds__(WM *WN * 64, WPS)
                 acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[buf][nb], xb[buf][mb], acc[nb][mb], 0, 0, 0);
     };
 
+    // LayerNorm epilogues: the row statistics of X come from the stages as they pass
+    // through LDS.  Thread t sums blocks (t % TPR)*BPT .. of row t / TPR of every stage,
+    // shifted by the row's first value (one pass; the shift keeps the variance free of
+    // cancellation for rows whose mean is large against their spread).
+    const int srow = tid / G::TPR, spart = tid % G::TPR;
+    float sshift = 0.f, s1 = 0.f, s2 = 0.f;
+    auto stats = [&](int s) {
+        const LDS_AS char *xs = smem + (s % NS) * G::SBYTES + srow * G::XROW;
+#pragma unroll
+        for (int j = 0; j < G::BPT; ++j) {
+            const u32x4 v = *reinterpret_cast<const LDS_AS u32x4 *>(
+                xs + (((spart * G::BPT + j) ^ x_swz<G::XBLK>(srow)) * 16));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo = __uint_as_float(v[e] << 16) - sshift, hi = __uint_as_float(v[e] & 0xffff0000u) - sshift;
+                s1 += lo + hi;
+                s2 = __builtin_fmaf(lo, lo, __builtin_fmaf(hi, hi, s2));
+            }
+        }
+    };
+
     // Stage s + NS - 1 is issued into the slot of stage s - 1 once the barrier before
     // stage s has shown that every wave is done reading it.
     const int steps = K / KT;
@@ -207,6 +237,12 @@ __global__ void __launch_bounds__(WM *WN * 64, WPS)
     __syncthreads();   // stage 0 has landed everywhere
     if (issued < steps) issue(issued++);
     read(0, 0, 0);
+    if constexpr (LN) {
+        sshift = __uint_as_float((uint32_t)*reinterpret_cast<const LDS_AS uint16_t *>(
+                                     smem + srow * G::XROW + x_swz<G::XBLK>(srow) * 16)
+                                 << 16);
+        stats(0);
+    }
     for (int s = 0; s < steps; ++s) {
 #pragma unroll
         for (int kk = 0; kk < G::KK; ++kk) {
@@ -218,6 +254,7 @@ __global__ void __launch_bounds__(WM *WN * 64, WPS)
                 __syncthreads();   // stage s + 1 has landed everywhere; stage s is read
                 if (issued < steps) issue(issued++);
                 read(s + 1, 0, cur ^ 1);
+                if constexpr (LN) stats(s + 1);
             }
             mfma(cur);
         }
@@ -227,16 +264,44 @@ __global__ void __launch_bounds__(WM *WN * 64, WPS)
     // + mb*32 + col, n = n0 + (wn*NB + nb)*32 + 8(i/4) + 4g + i%4.  Each wave stages its
     // 32*MB x 32*NB outputs as bf16 rows of OROW bytes (16-byte blocks swizzled by row),
     // then stores them as whole 16-byte pieces of rows.
-    __syncthreads();   // every wave is done with the ring
+    LDS_AS float *rstats = (LDS_AS float *)(smem + NS * G::SBYTES);
+    if constexpr (LN) {
+#pragma unroll
+        for (int o = 1; o < G::TPR; o <<= 1) {
+            s1 += __shfl_xor(s1, o);
+            s2 += __shfl_xor(s2, o);
+        }
+        if (spart == 0) {
+            const float d = s1 / (float)K;
+            rstats[2 * srow] = sshift + d;
+            rstats[2 * srow + 1] = 1.f / sqrtf(fmaxf(s2 / (float)K - d * d, 0.f) + kGemmLnEps);
+        }
+    }
+    __syncthreads();   // every wave is done with the ring (and the row statistics are written)
     LDS_AS char *stg = smem + wave * G::STAGE_OUT;
+    const bf16 *bias = static_cast<const bf16 *>(bias_);
+    const float *uv = static_cast<const float *>(bias_);   // LayerNorm epilogues: u[N], then v[N]
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         // the bias of the column block, and for the residual the old outputs (a row past
         // M reads row M-1 instead, and its result is never stored), loaded together
-        bf16x4 bv[4];
+        float bu[4][4], bv[4][4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-            bv[jj] = *reinterpret_cast<const bf16x4 *>(bias + n0 + (wn * NB + nb) * 32 + 8 * jj + 4 * g);
+        for (int jj = 0; jj < 4; ++jj) {
+            const int n = n0 + (wn * NB + nb) * 32 + 8 * jj + 4 * g;
+            if constexpr (LN) {
+                const f32x4 u4 = *reinterpret_cast<const f32x4 *>(uv + n), v4 = *reinterpret_cast<const f32x4 *>(uv + N + n);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bu[jj][e] = u4[e];
+                    bv[jj][e] = v4[e];
+                }
+            } else {
+                const bf16x4 b4 = *reinterpret_cast<const bf16x4 *>(bias + n);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bv[jj][e] = (float)b4[e];
+            }
+        }
         bf16x4 rv[4][MB];
         if (EPI == kGemmBiasResidual) {
 #pragma unroll
@@ -253,11 +318,18 @@ __global__ void __launch_bounds__(WM *WN * 64, WPS)
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int r = mb * 32 + col;
+                float mu = 0.f, rs = 1.f;
+                if constexpr (LN) {
+                    mu = rstats[2 * (wm * 32 * MB + r)];
+                    rs = rstats[2 * (wm * 32 * MB + r) + 1];
+                }
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    v[e] = acc[nb][mb][4 * jj + e] + (float)bv[jj][e];
-                    if (EPI == kGemmBiasGelu) v[e] = gelu_tanh(v[e]);
+                    // LN(x) W + b = rstd (x W' - mean u) + v, W' = diag(gamma) W, u its column sums
+                    if constexpr (LN) v[e] = __builtin_fmaf(rs, __builtin_fmaf(-mu, bu[jj][e], acc[nb][mb][4 * jj + e]), bv[jj][e]);
+                    else v[e] = acc[nb][mb][4 * jj + e] + bv[jj][e];
+                    if (EPI == kGemmBiasGelu || EPI == kGemmLnBiasGelu) v[e] = gelu_tanh(v[e]);
                     if (EPI == kGemmBiasResidual) v[e] += (float)rv[jj][mb][e];
                 }
                 const bf16x4 o = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};   // round to nearest even
@@ -286,8 +358,8 @@ hipError_t launch_cfg(const void *x, const void *w, const void *bias, void *y, i
     const long blocks = 8L * ((mtiles / 8) * ntn + ((mtiles % 8) * ntn + 7) / 8);
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks), block(G::W * 64);
-    const bf16 *xs = static_cast<const bf16 *>(x), *ws = static_cast<const bf16 *>(w),
-               *bs = static_cast<const bf16 *>(bias);
+    const bf16 *xs = static_cast<const bf16 *>(x), *ws = static_cast<const bf16 *>(w);
+    const void *bs = bias;
     bf16 *ys = static_cast<bf16 *>(y);
     switch (epi) {
         case kGemmBias:
@@ -300,6 +372,14 @@ hipError_t launch_cfg(const void *x, const void *w, const void *bias, void *y, i
             break;
         case kGemmBiasResidual:
             hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, MB, NB, KT, NS, WPS, kGemmBiasResidual>), grid, block, 0,
+                               stream, xs, ws, bs, ys, M, N, K, mtiles);
+            break;
+        case kGemmLnBias:
+            hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, MB, NB, KT, NS, WPS, kGemmLnBias>), grid, block, 0, stream,
+                               xs, ws, bs, ys, M, N, K, mtiles);
+            break;
+        case kGemmLnBiasGelu:
+            hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, MB, NB, KT, NS, WPS, kGemmLnBiasGelu>), grid, block, 0,
                                stream, xs, ws, bs, ys, M, N, K, mtiles);
             break;
         default:

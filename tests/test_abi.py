@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert lib.unipin_version() == 10000
+    assert lib.unipin_version() == 10100
     for code in (fa.OK, fa.EINVAL, fa.ERANGE, fa.EDTYPE, fa.EALIGN, fa.EDEVICE, fa.EHIP, fa.ENOMEM, fa.EPERM,
                  fa.EIO, fa.ESCRATCH):
         text = lib.unipin_strerror(code).decode()
@@ -240,13 +240,13 @@ def test_ar_decode_workspace_checks():
 
 def test_block_workspace_bytes():
     """The block's workspace: 32 MiB for the GEMM library, then M x 4C and M x C bf16
-    regions (M = B * rows) and 4C x C + 4C values for the GEMM tuner, each rounded up
-    to 256 bytes."""
+    regions (M = B * rows), 4C x C + 4C bf16 values and 2 x 4C fp32 values for the GEMM
+    tuner, each rounded up to 256 bytes."""
     up = lambda x: (x + 255) // 256 * 256
     h = make_pool(L=1, S=8, H=8, n_max=992, D=64)
     M, C = 8 * 656, 512
     assert lib.unipin_block_workspace_bytes(h, 8, 656) == (32 << 20) + up(M * 4 * C * 2) + up(M * C * 2) \
-        + up((4 * C * C + 4 * C) * 2)
+        + up((4 * C * C + 4 * C) * 2) + up(8 * C * 4)
     assert lib.unipin_block_workspace_bytes(h, 0, 656) == 0
     assert lib.unipin_block_workspace_bytes(None, 8, 656) == 0
     lib.unipin_pool_destroy(h)
@@ -262,6 +262,22 @@ def test_block_host_checks():
     assert lib.unipin_block_ctx_create(None) == fa.EINVAL
     assert lib.unipin_block_ctx_set_gemm(None, fa.GEMM_AUTO) == fa.EINVAL
     lib.unipin_pool_destroy(h)
+
+
+def test_block_fold_layernorm_checks():
+    """unipin_block_fold_layernorm rejects its arguments before any device work."""
+    w = fa.BlockWeights(*([FAKE] * len(fa.BLOCK_WEIGHT_NAMES)))
+    fold = lambda wp, C, a=FAKE, b=FAKE, c=FAKE, d=FAKE: lib.unipin_block_fold_layernorm(wp, C, a, b, c, d, None)
+    assert fold(None, 512) == fa.EINVAL                       # no weights
+    assert fold(ctypes.byref(w), 512, a=None) == fa.EINVAL    # an output missing
+    assert fold(ctypes.byref(w), 512, d=None) == fa.EINVAL
+    for C in (0, 4, 12, 2056):                                # C a multiple of 8 in [8, 2048]
+        assert fold(ctypes.byref(w), C) == fa.EINVAL
+    assert fold(ctypes.byref(w), 512, c=FAKE_ODD) == fa.EALIGN
+    odd = fa.BlockWeights(*([FAKE] * 5 + [FAKE_ODD] + [FAKE] * 6))
+    assert fold(ctypes.byref(odd), 512) == fa.EALIGN          # a misaligned weight
+    part = fa.BlockWeights(*([FAKE] * 11 + [None]))
+    assert fold(ctypes.byref(part), 512) == fa.EINVAL         # a weight missing
 
 
 def test_e4m3_pool_dims():

@@ -61,22 +61,26 @@ SHAPES = [(3, 70, 33, 4, 32), (2, 130, 65, 8, 64), (2, 64, 20, 2, 128)]
 GEMM_KERNELS = [fa.GEMM_LIBRARY, 0, 1, 2, 3]
 
 
+@pytest.mark.parametrize("fold", [False, True], ids=["plain", "folded"])
 @pytest.mark.parametrize("gemm", GEMM_KERNELS, ids=lambda k: "hipblaslt" if k == fa.GEMM_LIBRARY else f"tile{k}")
 @pytest.mark.parametrize("B,n,K,H,D", SHAPES, ids=lambda x: str(x))
-def test_block_history_then_candidates(B, n, K, H, D, gemm):
+def test_block_history_then_candidates(B, n, K, H, D, gemm, fold):
     """History forward (fills the pool), then the candidate-only forward, against the
     oracle's two forwards and its joint pass; the pool rows against the oracle's.  Every
-    shape is run with each GEMM kernel (rows B*n and B*K leave ragged row tiles)."""
-    announce(f"block history+candidates B={B} n={n} K={K} H={H} D={D} gemm={gemm}")
+    shape is run with each GEMM kernel (rows B*n and B*K leave ragged row tiles), with
+    the plain weights and with the LayerNorms folded into them (with this library's
+    kernel pinned, the QKV and MLP-up projections then take the hidden state itself)."""
+    announce(f"block history+candidates B={B} n={n} K={K} H={H} D={D} gemm={gemm} fold={fold}")
     w, xh, xc, pool = make(B, n, K, H, D, seed=50)
+    wrun = fa.fold_layernorm(w) if fold else w
     lens = [n, n // 2, 0][:B]
     slots = [B - 1 - b for b in range(B)]
     layer = 1
     ctx = fa.BlockContext()
     ctx.set_gemm(gemm)
     xh0, xc0 = xh.clone(), xc.clone()
-    fa.block_forward(ctx, w, fa.BLOCK_HISTORY, xh, pool, slots, lens, layer)
-    fa.block_forward(ctx, w, fa.BLOCK_CANDIDATES, xc, pool, slots, lens, layer)
+    fa.block_forward(ctx, wrun, fa.BLOCK_HISTORY, xh, pool, slots, lens, layer)
+    fa.block_forward(ctx, wrun, fa.BLOCK_CANDIDATES, xc, pool, slots, lens, layer)
     torch.cuda.synchronize()
     assert pool.status() == 0
     wc = {k: v.cpu() for k, v in w.items()}
@@ -123,16 +127,19 @@ def test_block_candidates_independent_of_each_other():
     ctx.close()
 
 
+@pytest.mark.parametrize("fold", [False, True], ids=["plain", "folded"])
 @pytest.mark.parametrize("gemm", ["tuned", 0, 1, 2, 3], ids=lambda k: k if k == "tuned" else f"tile{k}")
-def test_block_table2_shape_sampled(gemm):
+def test_block_table2_shape_sampled(gemm, fold):
     """The pages' Table 2 shape (B=8, history 992, 656 candidates) at width 512
     (8 heads x 64), with the GEMM kernels the tuner picks and with each tile
-    configuration of the library's GEMM pinned: history then candidate forward, sampled
-    users against the oracle.  User 7's candidate rows hold the last, partial 256-row
-    tile of the candidate-side GEMMs (5248 rows)."""
+    configuration of the library's GEMM pinned, with plain and with folded LayerNorm
+    weights: history then candidate forward, sampled users against the oracle.  User
+    7's candidate rows hold the last, partial 256-row tile of the candidate-side GEMMs
+    (5248 rows)."""
     B, n, K, H, D = 8, 992, 656, 8, 64
-    announce(f"block Table 2 shape gemm={gemm}")
-    w, xh, xc, pool = make(B, n, K, H, D, L=1, seed=70)
+    announce(f"block Table 2 shape gemm={gemm} fold={fold}")
+    w0, xh, xc, pool = make(B, n, K, H, D, L=1, seed=70)
+    w = fa.fold_layernorm(w0) if fold else w0
     lens = [n] * B
     slots = list(range(B))
     ctx = fa.BlockContext()
@@ -146,12 +153,30 @@ def test_block_table2_shape_sampled(gemm):
     fa.block_forward(ctx, w, fa.BLOCK_CANDIDATES, xc, pool, slots, lens, 0)
     torch.cuda.synchronize()
     assert pool.status() == 0
-    wc = {k: v.cpu() for k, v in w.items()}
+    wc = {k: v.cpu() for k, v in w0.items()}
     for b in (0, 7):
         _, jc = oracle.block_joint(xh0[b:b + 1].cpu(), xc0[b:b + 1].cpu(), [n], wc, H)
         check_rel(xc[b:b + 1], jc, f"Table 2 shape, candidates of user {b}")
     pool.close()
     ctx.close()
+
+
+def test_fold_layernorm_values():
+    """The folded weights: W' bit for bit the bf16 rounding of gamma W, u the column sums
+    of W', v = beta W + b (fp32, summation order aside)."""
+    C = 512
+    w = W.block_weights(C, torch.bfloat16, seed=90, device=DEV)
+    f = fa.fold_layernorm(w)
+    torch.cuda.synchronize()
+    for g, b, wm, bias, wl, uv in (("ln1_w", "ln1_b", "w_qkv", "b_qkv", "w_qkv_ln", "uv_qkv"),
+                                   ("ln2_w", "ln2_b", "w_fc", "b_fc", "w_fc_ln", "uv_fc")):
+        ref = (w[g].float()[:, None] * w[wm].float()).to(torch.bfloat16)
+        assert torch.equal(f[wl], ref), wl
+        u = f[wl].double().sum(0)
+        v = w[b].double() @ w[wm].double() + w[bias].double()
+        got = f[uv].double()
+        assert torch.allclose(got[0], u, rtol=1e-5, atol=1e-5 * u.abs().max().item()), uv
+        assert torch.allclose(got[1], v, rtol=1e-5, atol=1e-5 * v.abs().max().item()), uv
 
 
 def test_block_bad_arguments():
@@ -169,6 +194,11 @@ def test_block_bad_arguments():
     bad["w_o"] = w["w_qkv"]   # [C, 3C] where [C, C] belongs
     with pytest.raises(fa.UnipinError):
         fa.block_forward(ctx, bad, fa.BLOCK_CANDIDATES, xc, pool, [0], [n], 0)
+    half = fa.fold_layernorm(w)
+    del half["uv_qkv"]        # one of a folded pair without the other
+    with pytest.raises(fa.UnipinError) as e:
+        fa.block_forward(ctx, half, fa.BLOCK_CANDIDATES, xc, pool, [0], [n], 0)
+    assert e.value.status == fa.EINVAL
     pool.close()
     ctx.close()
 
