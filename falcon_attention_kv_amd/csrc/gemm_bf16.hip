@@ -17,7 +17,8 @@
 //   * the epilogue adds the bias and applies the tanh-form GELU or adds the residual (the
 //     output's old value) in fp32, rounds once to bf16 and stores whole rows through LDS;
 //     with a LayerNorm folded into the weights it first applies each row's mean and
-//     1/std, which the workgroup sums from the X tiles as they pass through LDS;
+//     1/std, which the workgroup sums from the X tiles as they pass through LDS (exactly,
+//     from global memory, for a row whose mean is far above its spread);
 //   * workgroup b runs on XCD b % 8.  The column tiles of one row tile go to consecutive
 //     workgroups of one XCD, so that they share its L2 copy of the X rows, for the first
 //     8 floor(mtiles / 8) row tiles; the workgroups of the rest are spread over all XCDs,
@@ -208,12 +209,15 @@ __global__ void __launch_bounds__(WM *WN * 64, WPS)
     };
 
     // LayerNorm epilogues: the row statistics of X come from the stages as they pass
-    // through LDS.  Thread t sums blocks (t % TPR)*BPT .. of row t / TPR of every stage,
-    // shifted by the row's first value (one pass; the shift keeps the variance free of
-    // cancellation for rows whose mean is large against their spread).
+    // through LDS.  Thread t sums blocks (t % TPR)*BPT .. of row t / TPR of every stage:
+    // the values and their squares, two v_dot2 per pair of values.  Such one-pass sums
+    // lose the variance to cancellation only when a row's mean is far above its spread;
+    // a row with mean^2 > 64 var is recomputed exactly (two passes over the row in global
+    // memory) before the epilogue.
     const int srow = tid / G::TPR, spart = tid % G::TPR;
-    float sshift = 0.f, s1 = 0.f, s2 = 0.f;
+    float s1 = 0.f, s2 = 0.f;
     auto stats = [&](int s) {
+        const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
         const LDS_AS char *xs = smem + (s % NS) * G::SBYTES + srow * G::XROW;
 #pragma unroll
         for (int j = 0; j < G::BPT; ++j) {
@@ -221,9 +225,10 @@ __global__ void __launch_bounds__(WM *WN * 64, WPS)
                 xs + (((spart * G::BPT + j) ^ x_swz<G::XBLK>(srow)) * 16));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float lo = __uint_as_float(v[e] << 16) - sshift, hi = __uint_as_float(v[e] & 0xffff0000u) - sshift;
-                s1 += lo + hi;
-                s2 = __builtin_fmaf(lo, lo, __builtin_fmaf(hi, hi, s2));
+                const uint32_t word = v[e];   // a plain value first: a bit cast of the vector element reads element 0
+                const bf16x2 p = __builtin_bit_cast(bf16x2, word);
+                s1 = __builtin_amdgcn_fdot2_f32_bf16(p, ones, s1, false);
+                s2 = __builtin_amdgcn_fdot2_f32_bf16(p, p, s2, false);
             }
         }
     };
@@ -237,12 +242,7 @@ __global__ void __launch_bounds__(WM *WN * 64, WPS)
     __syncthreads();   // stage 0 has landed everywhere
     if (issued < steps) issue(issued++);
     read(0, 0, 0);
-    if constexpr (LN) {
-        sshift = __uint_as_float((uint32_t)*reinterpret_cast<const LDS_AS uint16_t *>(
-                                     smem + srow * G::XROW + x_swz<G::XBLK>(srow) * 16)
-                                 << 16);
-        stats(0);
-    }
+    if constexpr (LN) stats(0);
     for (int s = 0; s < steps; ++s) {
 #pragma unroll
         for (int kk = 0; kk < G::KK; ++kk) {
@@ -271,10 +271,35 @@ __global__ void __launch_bounds__(WM *WN * 64, WPS)
             s1 += __shfl_xor(s1, o);
             s2 += __shfl_xor(s2, o);
         }
+        float mean = s1 / (float)K, var = s2 / (float)K - mean * mean;
+        // the TPR threads of a row hold the same sums and take this branch together
+        if (!(mean * mean <= 64.f * var) && m0 + srow < M) {
+            const bf16 *row = x + (long)(m0 + srow) * K;
+            float t = 0.f;
+            for (int k = spart * 8; k < K; k += 8 * G::TPR) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(row + k);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t += __uint_as_float(v[e] << 16) + __uint_as_float(v[e] & 0xffff0000u);
+            }
+#pragma unroll
+            for (int o = 1; o < G::TPR; o <<= 1) t += __shfl_xor(t, o);
+            mean = t / (float)K;
+            float q = 0.f;
+            for (int k = spart * 8; k < K; k += 8 * G::TPR) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(row + k);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = __uint_as_float(v[e] << 16) - mean, hi = __uint_as_float(v[e] & 0xffff0000u) - mean;
+                    q = __builtin_fmaf(lo, lo, __builtin_fmaf(hi, hi, q));
+                }
+            }
+#pragma unroll
+            for (int o = 1; o < G::TPR; o <<= 1) q += __shfl_xor(q, o);
+            var = q / (float)K;
+        }
         if (spart == 0) {
-            const float d = s1 / (float)K;
-            rstats[2 * srow] = sshift + d;
-            rstats[2 * srow + 1] = 1.f / sqrtf(fmaxf(s2 / (float)K - d * d, 0.f) + kGemmLnEps);
+            rstats[2 * srow] = mean;
+            rstats[2 * srow + 1] = 1.f / sqrtf(fmaxf(var, 0.f) + kGemmLnEps);
         }
     }
     __syncthreads();   // every wave is done with the ring (and the row statistics are written)

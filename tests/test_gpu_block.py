@@ -161,6 +161,39 @@ def test_block_table2_shape_sampled(gemm, fold):
     ctx.close()
 
 
+@pytest.mark.parametrize("gemm", [0, 1, 2, 3], ids=lambda k: f"tile{k}")
+def test_block_folded_rows_far_off_centre(gemm):
+    """Rows whose mean is far above their spread (20 standard deviations; every other row
+    of one user, so such rows share tiles with ordinary ones): the folded LayerNorm takes
+    their statistics exactly, so the folded and the plain path agree within the block's
+    rounding, and both match the oracle."""
+    B, n, K, H, D = 2, 130, 65, 8, 64
+    announce(f"block folded, rows far off centre, gemm={gemm}")
+    w, xh, xc, pool = make(B, n, K, H, D, seed=95)
+    for x in (xh, xc):
+        x[0] += 20.0
+        x[1, ::2] += 20.0
+    lens, slots = [n, n], [0, 1]
+    outs = {}
+    for fold in (False, True):
+        ctx = fa.BlockContext()
+        ctx.set_gemm(gemm)
+        wr = fa.fold_layernorm(w) if fold else w
+        a, c = xh.clone(), xc.clone()
+        fa.block_forward(ctx, wr, fa.BLOCK_HISTORY, a, pool, slots, lens, 0)
+        fa.block_forward(ctx, wr, fa.BLOCK_CANDIDATES, c, pool, slots, lens, 0)
+        torch.cuda.synchronize()
+        assert pool.status() == 0
+        outs[fold] = (a, c)
+        ctx.close()
+    check_rel(outs[True][0], oracle.as_f64(outs[False][0]), "history, folded vs plain")
+    check_rel(outs[True][1], oracle.as_f64(outs[False][1]), "candidates, folded vs plain")
+    wc = {k: v.cpu() for k, v in w.items()}
+    _, jc = oracle.block_joint(xh.cpu(), xc.cpu(), lens, wc, H)
+    check_rel(outs[True][1], jc, "candidates (folded) vs the joint pass")
+    pool.close()
+
+
 def test_fold_layernorm_values():
     """The folded weights: W' bit for bit the bf16 rounding of gamma W, u the column sums
     of W', v = beta W + b (fp32, summation order aside)."""
