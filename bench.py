@@ -158,6 +158,46 @@ def ar_step(fa, W, torch, dev, w, lens, steps: int, warmup: int, pool_dtype=None
                      f"{steps} timed steps"}
 
 
+def one_request_decode(fa, W, torch, dev, H: int, D: int, N: int, k: int, launches: int = 20, warmup: int = 3):
+    """The ranking decode of a single request (B = 1, one layer): one user's history of N
+    rows in its slot and k candidates, timed as the one-pass kernel and as the split over
+    the history (rank_decode(split=True)), `launches` back-to-back launches each after
+    `warmup`.  FLOPs per head 4 D k (N + 1); bytes per head the slot's K and V read once
+    (2 N D 2) and the candidates' q, k, v, o (4 k D 2)."""
+    pk, pv = W.random_pool(1, 1, H, N, D, torch.bfloat16, seed=51, device=dev)
+    pool = fa.Pool(pk, pv)
+    g = torch.Generator(device="cpu").manual_seed(52)
+    qc, kc, vc = (torch.randn((1, H, k, D), generator=g).to(torch.bfloat16).to(dev) for _ in range(3))
+    oc = torch.empty_like(qc)
+    slot = torch.zeros(1, dtype=torch.int32, device=dev)
+    lens = torch.full((1,), N, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(fa.rank_decode_workspace_bytes(pool, 1, k), 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for name, split in (("one_pass", False), ("split", True)):
+        for _ in range(warmup):
+            fa.rank_decode(qc, kc, vc, pool, slot, lens, 0, oc=oc, split=split, workspace=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            fa.rank_decode(qc, kc, vc, pool, slot, lens, 0, oc=oc, split=split, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / launches * 1e3
+    if pool.status() != 0:
+        raise RuntimeError("the one-request decode flagged an invalid slot or length")
+    flop = 4.0 * D * k * (N + 1) * H
+    nbytes = (2 * N * D * 2 + 4 * k * D * 2) * H
+    out = {"shape": f"B=1 H={H} D={D} history {N} k={k}, one layer", "split_workspace_bytes":
+           fa.rank_decode_workspace_bytes(pool, 1, k)}
+    for name, us in res.items():
+        out[name] = {"avg_us": round(us, 2), "candidates_per_s": round(k / (us / 1e6), 1),
+                     "tflops": round(flop / us / 1e6, 1), "gbs": round(nbytes / us / 1e3, 1)}
+    out["split_speedup"] = round(res["one_pass"] / res["split"], 3)
+    pool.close()
+    return out
+
+
 def serving_step_e4m3(fa, torch, dev, w, layers, lens, steps: int, warmup: int):
     """The serving-shape step of the headline (12 prefills, then 12 ranking decodes over
     the same layer inputs) with the pool stored as E4M3 codes.  Decode bytes per (user,
@@ -653,6 +693,11 @@ def main():
             "long_history": ar_step(fa, W, torch, dev, wl, W.history_lengths(wl).tolist(), steps=8, warmup=2),
             "one_request_long_history": ar_step(fa, W, torch, dev, replace(wl, B=1, S=1), [4000], steps=8,
                                                 warmup=2),
+        }
+        # the ranking side of a single request, one-pass against split over the history
+        out["rank_decode_one_request"] = {
+            "serving_shape": one_request_decode(fa, W, torch, dev, H=w.H, D=w.D, N=w.n, k=w.k),
+            "long_history": one_request_decode(fa, W, torch, dev, H=wl.H, D=wl.D, N=4000, k=wl.k),
         }
     print(json.dumps(out), flush=True)
 

@@ -32,7 +32,7 @@ FLAG_BAD_SLOT, FLAG_BAD_LEN, FLAG_DUP_SLOT = 1, 2, 4
 EXPORTS = ("unipin_pool_create", "unipin_pool_destroy", "unipin_pool_acquire",
            "unipin_pool_generation", "unipin_pool_dims", "unipin_pool_export",
            "unipin_pool_import", "unipin_prefill",
-           "unipin_rank_decode", "unipin_ar_decode", "unipin_ar_decode_noalloc", "unipin_ar_decode_workspace_bytes",
+           "unipin_rank_decode", "unipin_rank_decode_split", "unipin_rank_decode_workspace_bytes", "unipin_ar_decode", "unipin_ar_decode_noalloc", "unipin_ar_decode_workspace_bytes",
            "unipin_pool_status", "unipin_strerror", "unipin_version",
            "unipin_block_ctx_create", "unipin_block_ctx_destroy", "unipin_block_workspace_bytes",
            "unipin_block_ctx_tune", "unipin_block_ctx_set_gemm", "unipin_block_fold_layernorm",
@@ -73,6 +73,9 @@ def _load() -> ctypes.CDLL:
     lib.unipin_pool_import.argtypes = [ctypes.POINTER(vp), ctypes.c_char_p]
     lib.unipin_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp]
     lib.unipin_rank_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp]
+    lib.unipin_rank_decode_split.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp,
+                                             ctypes.c_size_t, vp]
+    lib.unipin_rank_decode_workspace_bytes.argtypes = [vp, i32, i32]
     lib.unipin_ar_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
     lib.unipin_ar_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp]
     lib.unipin_ar_decode_workspace_bytes.argtypes = [vp, i32]
@@ -90,10 +93,12 @@ def _load() -> ctypes.CDLL:
     lib.unipin_version.argtypes = []
     for name in EXPORTS:
         if name not in ("unipin_strerror", "unipin_ar_decode_workspace_bytes", "unipin_block_workspace_bytes",
+                        "unipin_rank_decode_workspace_bytes",
                         "unipin_pool_generation"):
             getattr(lib, name).restype = ctypes.c_int
     lib.unipin_pool_generation.restype = ctypes.c_uint64
     lib.unipin_ar_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.unipin_rank_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.unipin_block_workspace_bytes.restype = ctypes.c_size_t
     return lib
 
@@ -271,11 +276,22 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lens, pool: Pool,
     return o
 
 
+def rank_decode_workspace_bytes(pool: Pool, B: int, k: int) -> int:
+    """unipin_rank_decode_workspace_bytes: bytes rank_decode(split=True) uses for B users of
+    k candidates (0: it runs the one-pass kernel)."""
+    return int(lib.unipin_rank_decode_workspace_bytes(pool.handle, int(B), int(k)))
+
+
 def rank_decode(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, pool: Pool, slot, lens,
-                layer: int, oc: Optional[torch.Tensor] = None, scale: Optional[float] = None) -> torch.Tensor:
+                layer: int, oc: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                split: bool = False, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """unipin_rank_decode: candidates attend to their slot's cached history plus themselves.
 
-    qc, kc, vc [B, H, k, D]; slot, lens: B ints.  Returns oc [B, H, k, D].
+    qc, kc, vc [B, H, k, D]; slot, lens: B ints.  Returns oc [B, H, k, D].  split=True calls
+    unipin_rank_decode_split, which splits each candidate tile's history over several
+    workgroups when B*H pairs are too few to fill the GPU, with `workspace` (a device
+    tensor of at least rank_decode_workspace_bytes(pool, B, k) bytes) or, when it is None,
+    a buffer from torch's caching allocator.
     """
     dev = pool.device
     B, H, kk, D = qc.shape
@@ -287,10 +303,23 @@ def rank_decode(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, pool: Pool
     lens_t, slot_t = _i32_on(lens, dev), _i32_on(slot, dev)
     if lens_t.numel() != B or slot_t.numel() != B:
         raise UnipinError(EINVAL, "lens and slot need one entry per user")
-    _check(lib.unipin_rank_decode(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), pool.handle,
-                                  slot_t.data_ptr(), lens_t.data_ptr(), layer, B, kk,
-                                  0.0 if scale is None else float(scale), oc.data_ptr(),
-                                  _stream_handle(dev)), "unipin_rank_decode")
+    sc = 0.0 if scale is None else float(scale)
+    if not split:
+        _check(lib.unipin_rank_decode(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), pool.handle,
+                                      slot_t.data_ptr(), lens_t.data_ptr(), layer, B, kk, sc, oc.data_ptr(),
+                                      _stream_handle(dev)), "unipin_rank_decode")
+        return oc
+    need = rank_decode_workspace_bytes(pool, B, kk)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise UnipinError(EINVAL, "workspace must be a contiguous tensor on the pool's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib.unipin_rank_decode_split(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), pool.handle,
+                                        slot_t.data_ptr(), lens_t.data_ptr(), layer, B, kk, sc, oc.data_ptr(),
+                                        ws_ptr, ws_bytes, _stream_handle(dev)), "unipin_rank_decode_split")
     return oc
 
 

@@ -1060,6 +1060,159 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
                wq0, col, g, lane, a.out_rstride);
 }
 
+// ------------------------------------------------------------------ split ranking decode
+// For few (user, head) pairs the candidate tiles alone do not fill the GPU: each tile's
+// history is then split over `parts` workgroups.  Part p takes the 64-key tiles
+// p * part_tiles .. of the slot and runs the decode's tile loop over them (the same tile
+// step, with the key end counted from the part's first tile); it leaves each candidate
+// row's running max, row sum and unnormalised accumulator (fp32) in the workspace.  The
+// merge then adds the own key and normalises: the online softmax over the parts' states
+// and one more key.  bf16 pool, contiguous q, k, v and o.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <int D>
+__device__ __forceinline__ void decode_part_body(const AttnArgs &a, const int32_t *__restrict__ lens,
+                                                 const int32_t *__restrict__ slots) {
+    using T = Tile<D>;
+    constexpr int W = block_waves<D>();
+    constexpr int QT = W * wave_rows<D>();
+    constexpr int DPW = KvDma<D, W>::PER_WAVE;
+    static_assert(QT * T::ROW_BYTES == 2 * T::BUF_BYTES, "a 256-row block fills two slots");
+    __shared__ __attribute__((aligned(1024))) char smem_raw[kBufs * T::BUF_BYTES];
+    LDS_AS char *smem = (LDS_AS char *)smem_raw;
+
+    const int item = blockIdx.x / a.parts, part = blockIdx.x % a.parts;
+    const int group = item / a.tiles, ctile = item % a.tiles;
+    if (group >= a.B * a.H) return;
+    const int b = group / a.H, h = group % a.H;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int col = lane & 31, g = lane >> 5;
+    const int row0 = ctile * QT;
+    const int wq0 = row0 + wave * wave_rows<D>();
+    const bool active = wq0 < a.rows;
+    const long in_off = (long)b * a.in_bstride + (long)h * a.in_hstride;
+    const int in_rs = a.in_rstride * (int)sizeof(bf16);
+    const uint32_t rows_bytes = (uint32_t)a.rows * in_rs;
+    // q to slots 2 and 3 (its DMA overlaps the reads of the length and slot)
+    dma_rows<D, W, kBlockRows>(smem + 2 * T::BUF_BYTES, rsrc_words(static_cast<const bf16 *>(a.q) + in_off, rows_bytes),
+                               row0, wave, lane, in_rs);
+    const int N = lens[b], s = slots[b];
+    if (!user_valid(a, N, s, ctile == 0 && part == 0)) {
+        wait_vmcnt<0>();
+        return;
+    }
+    const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
+    const i32x4 rsrc = rsrc_words(static_cast<const char *>(wave < W / 2 ? a.pool_k : a.pool_v) +
+                                      slot_off * (long)sizeof(bf16),
+                                  (uint32_t)N * T::ROW_BYTES);
+    int voff[DPW];
+    dma_offsets<D, W>(voff, wave, lane, T::ROW_BYTES);
+    const LaneAddr<D> la = lane_addr<D>(lane);
+    const int ntiles = (N + kTK - 1) / kTK;
+    const int t0 = part * a.part_tiles;
+    const int nt = max(min(ntiles, t0 + a.part_tiles) - t0, 0);   // this part's tiles
+    const int wrows = wave * wave_rows<D>() * T::ROW_BYTES;
+    WaveState<D> ws;
+    // step u: the part's tile t0 + u, in slot u % kBufs; steps 0 and 1 go out with q
+    auto issue = [&](int u) { dma_tile<D, W>(smem + (u % kBufs) * T::BUF_BYTES, rsrc, (t0 + u) * kTK, voff, wave, T::ROW_BYTES); };
+    int issued = 0;
+    for (; issued < 2 && issued < nt; ++issued) issue(issued);
+    wait_pieces_after<DPW>(issued);   // q has landed
+    __syncthreads();
+    staged_operand<D>(ws.qreg, smem + 2 * T::BUF_BYTES + wrows, la);
+    reset_state<D>(ws);
+    auto next_step = [&](int u) -> const LDS_AS char * {
+        wait_pieces_after<DPW>(issued - u - 1);
+        __syncthreads();
+        for (; issued < nt && issued <= u + kBufs - 1; ++issued) issue(issued);
+        return smem + (u % kBufs) * T::BUF_BYTES;
+    };
+    run_tiles<D, false>(ws, nt, active ? nt - 1 : -1, N - t0 * kTK, wq0, la, col, g, a.c, next_step);
+    // the state of the wave's rows: accumulators (lane (col, g) holds head dims
+    // db*32 + 8j + 4g .. +3 of row col), then (m, l) from the lanes of half 0
+    const long pbase = ((long)item * a.parts + part) * QT;
+    float *acc_out = a.part_state;
+    float *ml_out = a.part_state + (long)a.B * a.H * a.tiles * a.parts * QT * D;
+#pragma unroll
+    for (int qb = 0; qb < query_blocks<D>(); ++qb) {
+        const long r = pbase + wave * wave_rows<D>() + qb * 32 + col;
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 v = {ws.acc[db][qb][4 * j], ws.acc[db][qb][4 * j + 1], ws.acc[db][qb][4 * j + 2],
+                                 ws.acc[db][qb][4 * j + 3]};
+                *reinterpret_cast<f32x4 *>(acc_out + r * D + db * 32 + 8 * j + 4 * g) = v;
+            }
+        const float lrow = half_sum(ws.l[qb]);
+        if (g == 0) *reinterpret_cast<f32x2 *>(ml_out + 2 * r) = f32x2{ws.m[qb], lrow};
+    }
+}
+
+// One wave per candidate row (b, h, j): the parts' states and the own key (score
+// scale * qc_j . kc_j, value vc_j) merged in fp32 and normalised; lane d holds head dims
+// d, d + 64.  A user with an invalid length or slot is skipped, as by the one-pass decode.
+template <int D>
+__global__ void __launch_bounds__(256) decode_merge_kernel(AttnArgs a, const int32_t *__restrict__ lens,
+                                                           const int32_t *__restrict__ slots) {
+    constexpr int QT = block_waves<D>() * wave_rows<D>();
+    constexpr int E = (D + 63) / 64;   // head dims per lane
+    const int lane = threadIdx.x & 63;
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (long)a.B * a.H * a.rows) return;
+    const int j = (int)(row % a.rows);
+    const int group = (int)(row / a.rows), b = group / a.H, h = group % a.H;
+    const int N = lens[b], s = slots[b];
+    if (N < 0 || N > a.len_limit || s < 0 || s >= a.S) return;
+    const long item = (long)group * a.tiles + j / QT;
+    const long in_row = (long)b * a.in_bstride + (long)h * a.in_hstride + (long)j * a.in_rstride;
+    const bf16 *q = static_cast<const bf16 *>(a.q) + in_row, *kc = static_cast<const bf16 *>(a.k) + in_row,
+               *vc = static_cast<const bf16 *>(a.v) + in_row;
+    float dot = 0.f, vv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int d = lane + 64 * e;
+        vv[e] = d < D ? (float)vc[d] : 0.f;
+        if (d < D) dot = __builtin_fmaf((float)q[d], (float)kc[d], dot);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) dot += __shfl_xor(dot, o);
+    const float sself = dot * a.c;   // log2 domain, like the parts' maxima
+    const float *accs = a.part_state;
+    const float *mls = a.part_state + (long)a.B * a.H * a.tiles * a.parts * QT * D;
+    float m = sself;
+    for (int p = 0; p < a.parts; ++p) m = fmaxf(m, mls[2 * ((item * a.parts + p) * QT + j % QT)]);
+    const float ws = __builtin_amdgcn_exp2f(sself - m);
+    float l = ws, acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = vv[e] * ws;
+    for (int p = 0; p < a.parts; ++p) {
+        const long r = (item * a.parts + p) * QT + j % QT;
+        const f32x2 ml = *reinterpret_cast<const f32x2 *>(mls + 2 * r);
+        const float f = __builtin_amdgcn_exp2f(ml[0] - m);   // 0 for a part with no key (m = -inf)
+        l = __builtin_fmaf(ml[1], f, l);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int d = lane + 64 * e;
+            if (d < D) acc[e] = __builtin_fmaf(accs[r * D + d], f, acc[e]);
+        }
+    }
+    bf16 *o = static_cast<bf16 *>(a.o) + (long)b * a.out_bstride + (long)h * a.out_hstride + (long)j * a.out_rstride;
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int d = lane + 64 * e;
+        if (d < D) o[d] = (bf16)(acc[e] * inv);
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(block_waves<D>() * 64, min_waves_per_simd<D>()) rank_decode_part_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
+    decode_part_body<D>(a, lens, slots);
+}
+
 template <int D, bool P8>
 __global__ void __launch_bounds__(block_waves<D>() * 64, min_waves_per_simd<D>()) prefill_bf16_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
     prefill_body<D, P8>(a, lens, slots);
@@ -1113,6 +1266,27 @@ hipError_t launch_decode_bf16(const AttnArgs &a, int D, bool pool8, hipStream_t 
         default: return hipErrorInvalidValue;
     }
 #undef UNIPIN_DECODE
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_split_bf16(const AttnArgs &a, int D, hipStream_t stream) {
+    const long items = (long)a.B * a.H * a.tiles * a.parts;
+    const long rows = (long)a.B * a.H * a.rows;
+    if (items <= 0 || rows <= 0) return hipSuccess;
+    if (items > 0x7fffffffL || (rows + 3) / 4 > 0x7fffffffL || a.parts < 1 || a.part_tiles < 1 || !a.part_state)
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)items), mgrid((unsigned)((rows + 3) / 4));
+#define UNIPIN_SPLIT(DD)                                                                                             \
+    hipLaunchKernelGGL((rank_decode_part_kernel<DD>), grid, dim3(block_waves<DD>() * 64), 0, stream, a, a.lens,      \
+                       a.slot);                                                                                      \
+    hipLaunchKernelGGL((decode_merge_kernel<DD>), mgrid, dim3(256), 0, stream, a, a.lens, a.slot)
+    switch (D) {
+        case 32: UNIPIN_SPLIT(32); break;
+        case 64: UNIPIN_SPLIT(64); break;
+        case 128: UNIPIN_SPLIT(128); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef UNIPIN_SPLIT
     return hipGetLastError();
 }
 

@@ -34,6 +34,12 @@ struct AttnArgs {
     // autoregressive step only the contiguous one).
     long in_bstride, in_hstride, out_bstride, out_hstride;
     int in_rstride, out_rstride;
+    // The ranking decode split over the history (launch_decode_split_bf16): each of the
+    // `parts` workgroups of a candidate tile takes `part_tiles` 64-key tiles and leaves its
+    // state in part_state (fp32: the accumulators [item][part][256][D], then (m, l) pairs
+    // [item][part][256]).
+    int parts, part_tiles;
+    float *part_state;
 };
 
 // Row layout of one attention operand, in elements (see AttnArgs).
@@ -46,9 +52,19 @@ struct RowLayout {
 // and o written in the given layouts: the public entry points' shared body, after
 // their argument checks.  bf16 pools only for a non-contiguous layout.  Returns a
 // UNIPIN_* status.
+// For the ranking decode, part_state (parts >= 2) selects the split over the history
+// (launch_decode_split_bf16; bf16 pools only).
 int attention_call(bool prefill, const void *q, const void *k, const void *v, RowLayout in, void *o, RowLayout out,
                    ::unipin_pool *pool, const int32_t *slot, const int32_t *lens, int layer, int B, int rows,
-                   float scale, void *stream);
+                   float scale, void *stream, float *part_state = nullptr, int parts = 1, int part_tiles = 0);
+
+// The split of the ranking decode over the history for B users of k candidates: parts
+// (1: the one-pass kernel), 64-key tiles per part and the workspace bytes it needs.
+struct DecodeSplit {
+    int parts, part_tiles;
+    size_t bytes;
+};
+DecodeSplit decode_split_plan(const ::unipin_pool *pool, int B, int k);
 
 // Flags raised on the device (mirrors UNIPIN_FLAG_* of the public header).
 constexpr unsigned int kFlagBadSlot = 1u;
@@ -64,6 +80,9 @@ int bf16_decode_rows_per_item(int D);
 // pool write, decoded by the ranking decode as its tiles arrive), else bf16.
 hipError_t launch_prefill_bf16(const AttnArgs &a, int D, bool pool8, hipStream_t stream);
 hipError_t launch_decode_bf16(const AttnArgs &a, int D, bool pool8, hipStream_t stream);
+// The split ranking decode on a bf16 pool (contiguous layout): the parts, then the merge of
+// the parts with each candidate's own key into o.
+hipError_t launch_decode_split_bf16(const AttnArgs &a, int D, hipStream_t stream);
 // fp32 pools: fp32 in and out, fp64 arithmetic inside.
 hipError_t launch_prefill_fp32(const AttnArgs &a, int D, hipStream_t stream);
 hipError_t launch_decode_fp32(const AttnArgs &a, int D, hipStream_t stream);

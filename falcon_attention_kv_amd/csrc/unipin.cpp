@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -117,9 +118,38 @@ int rows_per_block(const unipin_pool *pool, bool prefill) {
 
 namespace unipin {
 
+DecodeSplit decode_split_plan(const ::unipin_pool *pool, int B, int k) {
+    // Histories shorter than 16 tiles (1024 keys) take the one-pass kernel: their decode
+    // is short enough that the merge's launch and the parts' states cost more than the
+    // split gains (measured: 0.88-0.90x at 512 keys, 1.2-1.6x at 2048-4000).  A part
+    // takes at least four 64-key tiles.  The decode keeps two workgroups per CU
+    // resident at D <= 64 and one at D = 128 (256 CUs): the split starts when the
+    // candidate tiles fill at most half of those, and gives each tile's history as many
+    // parts as fill them.  The plan counts on histories up to n_max (the lengths are on
+    // the device); parts past a shorter history leave at once.
+    constexpr int kMinPartTiles = 4;
+    DecodeSplit p{1, 0, 0};
+    if (!pool || B < 1 || k < 1 || pool->dtype != UNIPIN_BF16) return p;
+    const int rpb = bf16_decode_rows_per_item(pool->D);
+    const long items = (long)B * pool->H * ((k + rpb - 1) / rpb);
+    const long resident = pool->D <= 64 ? 512 : 256;
+    if (items * 2 > resident) return p;
+    const int hist_tiles = (pool->n_max + 63) / 64;
+    if (hist_tiles < 16) return p;
+    int parts = (int)std::min<long>((resident + items - 1) / items, hist_tiles / kMinPartTiles);
+    if (parts < 2) return p;
+    const int part_tiles = (hist_tiles + parts - 1) / parts;
+    parts = (hist_tiles + part_tiles - 1) / part_tiles;
+    if (parts < 2) return p;
+    p.parts = parts;
+    p.part_tiles = part_tiles;
+    p.bytes = (size_t)items * parts * rpb * (pool->D + 2) * sizeof(float);
+    return p;
+}
+
 int attention_call(bool prefill, const void *q, const void *k, const void *v, RowLayout in, void *o, RowLayout out,
                    ::unipin_pool *pool, const int32_t *slot, const int32_t *lens, int layer, int B, int rows,
-                   float scale, void *stream) {
+                   float scale, void *stream, float *part_state, int parts, int part_tiles) {
     if (!pool || !q || !k || !v || !lens || !slot || !o) return UNIPIN_EINVAL;
     if (B < 1 || rows < 1 || (prefill && rows > pool->n_max)) return UNIPIN_EINVAL;
     if (layer < 0 || layer >= pool->L) return UNIPIN_ERANGE;
@@ -171,6 +201,13 @@ int attention_call(bool prefill, const void *q, const void *k, const void *v, Ro
     a.out_rstride = out.rstride;
     rc = pool_kernel_prologue(pool, static_cast<hipStream_t>(stream), &a.status);
     if (rc) return rc;
+    if (!prefill && part_state && parts >= 2 && pool->dtype == UNIPIN_BF16) {
+        a.parts = parts;
+        a.part_tiles = part_tiles;
+        a.part_state = part_state;
+        return launch_decode_split_bf16(a, D, static_cast<hipStream_t>(stream)) == hipSuccess ? UNIPIN_OK
+                                                                                                : UNIPIN_EHIP;
+    }
     return launch(a, pool, prefill, stream);
 }
 
@@ -281,6 +318,27 @@ int unipin_rank_decode(const void *qc, const void *kc, const void *vc,
     const unipin::RowLayout dense{(long)pool->H * k * pool->D, (long)k * pool->D, pool->D};
     return unipin::attention_call(false, qc, kc, vc, dense, oc, dense, const_cast<unipin_pool_t *>(pool), slot, lens,
                                   layer, B, k, scale, stream);
+}
+
+size_t unipin_rank_decode_workspace_bytes(const unipin_pool_t *pool, int B, int k) {
+    return unipin::decode_split_plan(pool, B, k).bytes;
+}
+
+int unipin_rank_decode_split(const void *qc, const void *kc, const void *vc, const unipin_pool_t *pool,
+                             const int32_t *slot, const int32_t *lens, int layer, int B, int k, float scale,
+                             void *oc, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!pool || !qc || !kc || !vc || !lens || !slot || !oc) return UNIPIN_EINVAL;
+    if (B < 1 || k < 1) return UNIPIN_EINVAL;
+    const unipin::RowLayout dense{(long)pool->H * k * pool->D, (long)k * pool->D, pool->D};
+    const unipin::DecodeSplit plan = unipin::decode_split_plan(pool, B, k);
+    float *ws = nullptr;
+    if (workspace && plan.parts >= 2) {
+        if (!aligned(workspace, 16)) return UNIPIN_EALIGN;
+        if (workspace_bytes < plan.bytes) return UNIPIN_EINVAL;
+        ws = static_cast<float *>(workspace);
+    }
+    return unipin::attention_call(false, qc, kc, vc, dense, oc, dense, const_cast<unipin_pool_t *>(pool), slot, lens,
+                                  layer, B, k, scale, stream, ws, ws ? plan.parts : 1, plan.part_tiles);
 }
 
 }  // extern "C"

@@ -264,6 +264,44 @@ def test_block_host_checks():
     lib.unipin_pool_destroy(h)
 
 
+def test_rank_decode_split_plan():
+    """The split of the ranking decode: for few (user, head) pairs and histories of at least
+    1024 keys, parts of at least four 64-key tiles that fill the resident workgroups (512
+    at D <= 64, 256 at D = 128); the workspace holds (D + 2) fp32 per candidate row of
+    every part of every 256-row tile."""
+    h = make_pool(L=1, S=2, H=8, n_max=1024, D=64)
+    # 8 pairs x 4 candidate tiles = 32 items: min(512 / 32, 16 tiles / 4) = 4 parts
+    assert lib.unipin_rank_decode_workspace_bytes(h, 1, 1000) == 32 * 4 * 256 * 66 * 4
+    assert lib.unipin_rank_decode_workspace_bytes(h, 64, 1000) == 0     # enough pairs: one pass
+    assert lib.unipin_rank_decode_workspace_bytes(h, 0, 1000) == 0
+    assert lib.unipin_rank_decode_workspace_bytes(None, 1, 1000) == 0
+    lib.unipin_pool_destroy(h)
+    h = make_pool(L=1, S=2, H=4, n_max=1024, D=128)
+    # 4 pairs x 2 tiles = 8 items: min(256 / 8, 16 / 4) = 4 parts of 4 tiles
+    assert lib.unipin_rank_decode_workspace_bytes(h, 1, 300) == 8 * 4 * 256 * 130 * 4
+    lib.unipin_pool_destroy(h)
+    h = make_pool(L=1, S=2, H=8, n_max=960, D=64)   # 15 tiles of history: one pass
+    assert lib.unipin_rank_decode_workspace_bytes(h, 1, 1000) == 0
+    lib.unipin_pool_destroy(h)
+    h = make_pool(L=1, S=2, H=8, n_max=1024, D=64, dtype=fa.FP8_E4M3)
+    assert lib.unipin_rank_decode_workspace_bytes(h, 1, 1000) == 0      # E4M3: one pass
+    lib.unipin_pool_destroy(h)
+
+
+def test_rank_decode_split_checks():
+    """Argument checks of unipin_rank_decode_split before any device work."""
+    h = make_pool(L=1, S=2, H=8, n_max=1024, D=64)
+    need = lib.unipin_rank_decode_workspace_bytes(h, 1, 1000)
+    call = lambda ws, nbytes, B=1: lib.unipin_rank_decode_split(FAKE, FAKE, FAKE, h, FAKE, FAKE, 0, B, 1000, 0.0,
+                                                                FAKE, ws, nbytes, None)
+    assert call(FAKE_ODD, need) == fa.EALIGN
+    assert call(FAKE, need - 1) == fa.EINVAL
+    assert call(FAKE, need, B=0) == fa.EINVAL
+    assert lib.unipin_rank_decode_split(None, FAKE, FAKE, h, FAKE, FAKE, 0, 1, 1000, 0.0, FAKE, FAKE, need,
+                                        None) == fa.EINVAL
+    lib.unipin_pool_destroy(h)
+
+
 def test_block_fold_layernorm_checks():
     """unipin_block_fold_layernorm rejects its arguments before any device work."""
     w = fa.BlockWeights(*([FAKE] * len(fa.BLOCK_WEIGHT_NAMES)))

@@ -1,0 +1,125 @@
+"""GPU parity of the ranking decode split over the history (unipin_rank_decode_split)
+against the float64 oracle, with the bf16 tolerances of test_gpu_parity.py
+(max |gpu - oracle| <= 2e-2, mean <= 2e-3).
+
+The split runs when few (user, head) pairs leave the GPU mostly idle: each candidate
+tile's history goes to several workgroups, whose softmax states a second kernel merges
+with the candidate's own key.  Every case here is small enough that the library plans
+such a split (rank_decode_workspace_bytes > 0), and each is also run through the
+one-pass kernel as a cross-check.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import falcon_attention_kv_amd as fa
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def announce(msg: str) -> None:
+    sys.__stderr__.write(f"[gpu case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def check_bf16(got: torch.Tensor, ref, what: str) -> float:
+    g = got.detach().to("cpu").to(torch.float64).numpy()
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    d = np.abs(g - r)
+    assert d.max() <= 2e-2, f"{what}: max abs error {d.max():.3e} > 2e-2"
+    assert d.mean() <= 2e-3, f"{what}: mean abs error {d.mean():.3e} > 2e-3"
+    return float(d.max())
+
+
+# (B, H, D, n_max, k, lens)
+CASES = [
+    (1, 8, 64, 1024, 1000, [1024]),         # one request, full history: four parts of four tiles
+    (2, 4, 128, 1024, 300, [1000, 37]),     # ragged: most of the short user's parts are empty
+    (1, 2, 32, 1024, 40, [0]),              # empty history: the own value exactly
+    (3, 2, 64, 1100, 257, [1100, 1, 64]),   # a partial candidate tile, a one-key history
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}D{c[2]}n{c[3]}k{c[4]}")
+def test_split_decode_against_the_oracle(case):
+    B, H, D, n, k, lens = case
+    announce(f"split decode {case}")
+    inp = W.small_case(B, H, D, n, k, lens, seed=3000 + n + k, device=DEV)
+    pool = fa.Pool.allocate(1, B + 1, H, n, D, torch.bfloat16, DEV)
+    pool.k.fill_(float("nan"))
+    pool.v.fill_(float("nan"))
+    slots = list(range(B, 0, -1))
+    fa.prefill(inp["q"], inp["k"], inp["v"], lens, pool, slots, 0)
+    need = fa.rank_decode_workspace_bytes(pool, B, k)
+    assert need > 0, "the case must take the split path"
+    oc = fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, slots, lens, 0, split=True)
+    one = fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, slots, lens, 0)
+    torch.cuda.synchronize()
+    assert pool.status() == 0
+    for b, N in enumerate(lens):
+        s = slots[b]
+        pk = oracle.as_f64(pool.k[0, s, :, :N].cpu()).reshape(1, 1, H, N, D)
+        pv = oracle.as_f64(pool.v[0, s, :, :N].cpu()).reshape(1, 1, H, N, D)
+        sub = {key: inp[key][b:b + 1].cpu() for key in ("qc", "kc", "vc")}
+        ref = oracle.rank_decode(sub["qc"], sub["kc"], sub["vc"], pk, pv, [0], [N], 0, None)
+        check_bf16(oc[b:b + 1], ref, f"split decode user {b} N={N}")
+        check_bf16(one[b:b + 1], ref, f"one-pass decode user {b} N={N}")
+        if N == 0:
+            assert torch.equal(oc[b], inp["vc"][b]), "an empty history must return vc exactly"
+
+
+def test_split_decode_repeated_calls_are_bitwise_identical():
+    B, H, D, n, k = 1, 8, 64, 1024, 600
+    inp = W.small_case(B, H, D, n, k, [980], seed=3100, device=DEV)
+    pool = fa.Pool.allocate(1, 1, H, n, D, torch.bfloat16, DEV)
+    fa.prefill(inp["q"], inp["k"], inp["v"], [980], pool, [0], 0)
+    ws = torch.empty(fa.rank_decode_workspace_bytes(pool, B, k), dtype=torch.uint8, device=DEV)
+    a = fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, [0], [980], 0, split=True, workspace=ws)
+    ws.fill_(0xff)   # the workspace is scratch: its contents before a call do not matter
+    b = fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, [0], [980], 0, split=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_split_decode_invalid_user_is_skipped_and_flagged():
+    B, H, D, n, k = 3, 2, 64, 1024, 64
+    announce("split decode status flags")
+    inp = W.small_case(B, H, D, n, k, [1024, 64, 10], seed=3200, device=DEV)
+    pool = fa.Pool.allocate(1, 3, H, n, D, torch.bfloat16, DEV)
+    fa.prefill(inp["q"], inp["k"], inp["v"], [1024, 64, 10], pool, [0, 1, 2], 0)
+    assert pool.status() == 0
+    assert fa.rank_decode_workspace_bytes(pool, B, k) > 0
+    oc = torch.full_like(inp["qc"], 7.0)
+    fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, [0, -1, 2], [1024, 64, 10], 0, oc=oc, split=True)
+    assert pool.status() == fa.FLAG_BAD_SLOT
+    assert (oc[1] == 7.0).all(), "a skipped user's output must stay untouched"
+    assert torch.isfinite(oc[0]).all() and torch.isfinite(oc[2]).all()
+    fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, [0, 1, 2], [1024, 1025, 10], 0, oc=oc, split=True)
+    assert pool.status() == fa.FLAG_BAD_LEN
+    assert pool.status() == 0
+
+
+def test_split_decode_workspace_checks():
+    B, H, D, n, k = 1, 4, 64, 1024, 100
+    inp = W.small_case(B, H, D, n, k, [300], seed=3300, device=DEV)
+    pool = fa.Pool.allocate(1, 1, H, n, D, torch.bfloat16, DEV)
+    need = fa.rank_decode_workspace_bytes(pool, B, k)
+    assert need > 0
+    small = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(fa.UnipinError) as e:
+        fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, [0], [300], 0, split=True, workspace=small)
+    assert e.value.status == fa.EINVAL
+    odd = torch.empty(need + 16, dtype=torch.uint8, device=DEV)[4:]
+    with pytest.raises(fa.UnipinError) as e:
+        fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, [0], [300], 0, split=True, workspace=odd)
+    assert e.value.status == fa.EALIGN
+    # E4M3 pools always take the one-pass kernel
+    p8 = fa.Pool.allocate(1, 1, H, n, D, torch.float8_e4m3fn, DEV)
+    assert fa.rank_decode_workspace_bytes(p8, B, k) == 0
