@@ -6,9 +6,12 @@
 // The four projections are bf16 GEMMs with fp32 accumulation and fused epilogues (bias,
 // tanh-form GELU, residual add into the hidden state).  They run on hipBLASLt (its
 // epilogues, beta = 1 on the hidden state for the residual) or on this library's MFMA
-// kernel (gemm_bf16.hip, four workgroup tile configurations), whichever the tuner timed fastest
-// for the shape; untuned, on hipBLASLt's first heuristic choice.  LayerNorm is this library's
-// kernel (block_kernels.hip), and the attention is the library's own prefill and rank-decode
+// kernel (gemm_bf16.hip, four workgroup tile configurations), whichever the tuner timed
+// fastest for the shape; untuned, on hipBLASLt's first heuristic choice.  LayerNorm is this
+// library's kernel (block_kernels.hip); with the weights unipin_block_fold_layernorm
+// prepares, the QKV and MLP-up projections may instead run this library's kernel on the
+// hidden state itself, the LayerNorm's row statistics taken inside the GEMM and applied in
+// its epilogue (the tuner chooses per shape).  The attention is the library's own prefill and rank-decode
 // kernels, which read q, k and v straight from the fused projection's rows
 // [B, rows, 3, H, D] and write the heads' outputs straight into the merged rows
 // [B, rows, H, D] that the output projection reads.  Host code here allocates nothing on
