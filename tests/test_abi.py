@@ -280,6 +280,14 @@ def test_rank_decode_split_plan():
     # 4 pairs x 2 tiles = 8 items: min(256 / 8, 16 / 4) = 4 parts of 4 tiles
     assert lib.unipin_rank_decode_workspace_bytes(h, 1, 300) == 8 * 4 * 256 * 130 * 4
     lib.unipin_pool_destroy(h)
+    h = make_pool(L=2, S=2, H=4, n_max=2048, D=32)
+    # 4 pairs x 2 tiles = 8 items: min(512 / 8, 32 / 4) = 8 parts of 4 tiles
+    assert lib.unipin_rank_decode_workspace_bytes(h, 1, 500) == 8 * 8 * 256 * 34 * 4
+    lib.unipin_pool_destroy(h)
+    h = make_pool(L=1, S=2, H=4, n_max=2100, D=32)
+    # 33 tiles: min(64, 33 / 4 = 8) parts of ceil(33 / 8) = 5 tiles, so 7 parts
+    assert lib.unipin_rank_decode_workspace_bytes(h, 1, 500) == 8 * 7 * 256 * 34 * 4
+    lib.unipin_pool_destroy(h)
     h = make_pool(L=1, S=2, H=8, n_max=960, D=64)   # 15 tiles of history: one pass
     assert lib.unipin_rank_decode_workspace_bytes(h, 1, 1000) == 0
     lib.unipin_pool_destroy(h)

@@ -38,35 +38,38 @@ def check_bf16(got: torch.Tensor, ref, what: str) -> float:
     return float(d.max())
 
 
-# (B, H, D, n_max, k, lens)
+# (B, H, D, n_max, k, lens, layer)
 CASES = [
-    (1, 8, 64, 1024, 1000, [1024]),         # one request, full history: four parts of four tiles
-    (2, 4, 128, 1024, 300, [1000, 37]),     # ragged: most of the short user's parts are empty
-    (1, 2, 32, 1024, 40, [0]),              # empty history: the own value exactly
-    (3, 2, 64, 1100, 257, [1100, 1, 64]),   # a partial candidate tile, a one-key history
+    (1, 8, 64, 1024, 1000, [1024], 0),         # one request, full history: four parts of four tiles
+    (2, 4, 128, 1024, 300, [1000, 37], 0),     # ragged: most of the short user's parts are empty
+    (1, 2, 32, 1024, 40, [0], 0),              # empty history: the own value exactly
+    (3, 2, 64, 1100, 257, [1100, 1, 64], 0),   # a partial candidate tile, a one-key history
+    # D = 32 on the second layer of the pool: eight parts of four tiles over 2048 rows, a
+    # 1500-key history ends inside part 5 (its last tile holds 28 keys), parts 6 and 7 are empty
+    (1, 4, 32, 2048, 500, [1500], 1),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}D{c[2]}n{c[3]}k{c[4]}")
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}D{c[2]}n{c[3]}k{c[4]}L{c[6]}")
 def test_split_decode_against_the_oracle(case):
-    B, H, D, n, k, lens = case
+    B, H, D, n, k, lens, layer = case
     announce(f"split decode {case}")
     inp = W.small_case(B, H, D, n, k, lens, seed=3000 + n + k, device=DEV)
-    pool = fa.Pool.allocate(1, B + 1, H, n, D, torch.bfloat16, DEV)
+    pool = fa.Pool.allocate(layer + 1, B + 1, H, n, D, torch.bfloat16, DEV)
     pool.k.fill_(float("nan"))
     pool.v.fill_(float("nan"))
     slots = list(range(B, 0, -1))
-    fa.prefill(inp["q"], inp["k"], inp["v"], lens, pool, slots, 0)
+    fa.prefill(inp["q"], inp["k"], inp["v"], lens, pool, slots, layer)
     need = fa.rank_decode_workspace_bytes(pool, B, k)
     assert need > 0, "the case must take the split path"
-    oc = fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, slots, lens, 0, split=True)
-    one = fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, slots, lens, 0)
+    oc = fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, slots, lens, layer, split=True)
+    one = fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, slots, lens, layer)
     torch.cuda.synchronize()
     assert pool.status() == 0
     for b, N in enumerate(lens):
         s = slots[b]
-        pk = oracle.as_f64(pool.k[0, s, :, :N].cpu()).reshape(1, 1, H, N, D)
-        pv = oracle.as_f64(pool.v[0, s, :, :N].cpu()).reshape(1, 1, H, N, D)
+        pk = oracle.as_f64(pool.k[layer, s, :, :N].cpu()).reshape(1, 1, H, N, D)
+        pv = oracle.as_f64(pool.v[layer, s, :, :N].cpu()).reshape(1, 1, H, N, D)
         sub = {key: inp[key][b:b + 1].cpu() for key in ("qc", "kc", "vc")}
         ref = oracle.rank_decode(sub["qc"], sub["kc"], sub["vc"], pk, pv, [0], [N], 0, None)
         check_bf16(oc[b:b + 1], ref, f"split decode user {b} N={N}")
