@@ -158,14 +158,21 @@ def ar_step(fa, W, torch, dev, w, lens, steps: int, warmup: int, pool_dtype=None
                      f"{steps} timed steps"}
 
 
-def one_request_decode(fa, W, torch, dev, H: int, D: int, N: int, k: int, launches: int = 20, warmup: int = 3):
+def one_request_decode(fa, W, torch, dev, H: int, D: int, N: int, k: int, launches: int = 20, warmup: int = 3,
+                       e4m3: bool = False):
     """The ranking decode of a single request (B = 1, one layer): one user's history of N
     rows in its slot and k candidates, timed as the one-pass kernel and as the split over
     the history (rank_decode(split=True)), `launches` back-to-back launches each after
     `warmup`.  FLOPs per head 4 D k (N + 1); bytes per head the slot's K and V read once
-    (2 N D 2) and the candidates' q, k, v, o (4 k D 2)."""
-    pk, pv = W.random_pool(1, 1, H, N, D, torch.bfloat16, seed=51, device=dev)
-    pool = fa.Pool(pk, pv)
+    (2 N D e, e = 2 for a bf16 pool, 1 for an E4M3 pool) and the candidates' q, k, v, o
+    (4 k D 2)."""
+    if e4m3:
+        pk, pv = W.random_pool(1, 1, H, N, D, torch.float32, seed=51, device=dev)
+        pool = fa.Pool(pk.to(torch.float8_e4m3fn), pv.to(torch.float8_e4m3fn))
+        del pk, pv
+    else:
+        pk, pv = W.random_pool(1, 1, H, N, D, torch.bfloat16, seed=51, device=dev)
+        pool = fa.Pool(pk, pv)
     g = torch.Generator(device="cpu").manual_seed(52)
     qc, kc, vc = (torch.randn((1, H, k, D), generator=g).to(torch.bfloat16).to(dev) for _ in range(3))
     oc = torch.empty_like(qc)
@@ -187,9 +194,9 @@ def one_request_decode(fa, W, torch, dev, H: int, D: int, N: int, k: int, launch
     if pool.status() != 0:
         raise RuntimeError("the one-request decode flagged an invalid slot or length")
     flop = 4.0 * D * k * (N + 1) * H
-    nbytes = (2 * N * D * 2 + 4 * k * D * 2) * H
-    out = {"shape": f"B=1 H={H} D={D} history {N} k={k}, one layer", "split_workspace_bytes":
-           fa.rank_decode_workspace_bytes(pool, 1, k)}
+    nbytes = (2 * N * D * (1 if e4m3 else 2) + 4 * k * D * 2) * H
+    out = {"shape": f"B=1 H={H} D={D} history {N} k={k}, one layer" + (", E4M3 pool" if e4m3 else ""),
+           "split_workspace_bytes": fa.rank_decode_workspace_bytes(pool, 1, k)}
     for name, us in res.items():
         out[name] = {"avg_us": round(us, 2), "candidates_per_s": round(k / (us / 1e6), 1),
                      "tflops": round(flop / us / 1e6, 1), "gbs": round(nbytes / us / 1e3, 1)}
@@ -698,6 +705,7 @@ def main():
         out["rank_decode_one_request"] = {
             "serving_shape": one_request_decode(fa, W, torch, dev, H=w.H, D=w.D, N=w.n, k=w.k),
             "long_history": one_request_decode(fa, W, torch, dev, H=wl.H, D=wl.D, N=4000, k=wl.k),
+            "long_history_e4m3": one_request_decode(fa, W, torch, dev, H=wl.H, D=wl.D, N=4000, k=wl.k, e4m3=True),
         }
     print(json.dumps(out), flush=True)
 

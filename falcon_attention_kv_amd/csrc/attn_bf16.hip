@@ -1067,11 +1067,11 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, const int32_t *__
 // step, with the key end counted from the part's first tile); it leaves each candidate
 // row's running max, row sum and unnormalised accumulator (fp32) in the workspace.  The
 // merge then adds the own key and normalises: the online softmax over the parts' states
-// and one more key.  bf16 pool, contiguous q, k, v and o.
+// and one more key.  bf16 or E4M3 pool (P8), contiguous q, k, v and o.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-template <int D>
+template <int D, bool P8>
 __device__ __forceinline__ void decode_part_body(const AttnArgs &a, const int32_t *__restrict__ lens,
                                                  const int32_t *__restrict__ slots) {
     using T = Tile<D>;
@@ -1103,33 +1103,65 @@ __device__ __forceinline__ void decode_part_body(const AttnArgs &a, const int32_
         wait_vmcnt<0>();
         return;
     }
-    const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;
-    const i32x4 rsrc = rsrc_words(static_cast<const char *>(wave < W / 2 ? a.pool_k : a.pool_v) +
-                                      slot_off * (long)sizeof(bf16),
-                                  (uint32_t)N * T::ROW_BYTES);
-    int voff[DPW];
-    dma_offsets<D, W>(voff, wave, lane, T::ROW_BYTES);
+    const long slot_off = ((long)s * a.H + h) * (long)a.n_max * D;   // in elements
+    constexpr int PROW = P8 ? D : T::ROW_BYTES;                      // bytes of one pool row
+    const i32x4 rsrc = rsrc_words(static_cast<const char *>(wave < W / 2 ? a.pool_k : a.pool_v) + slot_off * (PROW / D),
+                                  (uint32_t)N * PROW);
     const LaneAddr<D> la = lane_addr<D>(lane);
     const int ntiles = (N + kTK - 1) / kTK;
     const int t0 = part * a.part_tiles;
     const int nt = max(min(ntiles, t0 + a.part_tiles) - t0, 0);   // this part's tiles
     const int wrows = wave * wave_rows<D>() * T::ROW_BYTES;
     WaveState<D> ws;
-    // step u: the part's tile t0 + u, in slot u % kBufs; steps 0 and 1 go out with q
-    auto issue = [&](int u) { dma_tile<D, W>(smem + (u % kBufs) * T::BUF_BYTES, rsrc, (t0 + u) * kTK, voff, wave, T::ROW_BYTES); };
-    int issued = 0;
-    for (; issued < 2 && issued < nt; ++issued) issue(issued);
-    wait_pieces_after<DPW>(issued);   // q has landed
-    __syncthreads();
-    staged_operand<D>(ws.qreg, smem + 2 * T::BUF_BYTES + wrows, la);
-    reset_state<D>(ws);
-    auto next_step = [&](int u) -> const LDS_AS char * {
-        wait_pieces_after<DPW>(issued - u - 1);
+    if constexpr (!P8) {
+        // step u: the part's tile t0 + u, in slot u % kBufs; steps 0 and 1 go out with q
+        int voff[DPW];
+        dma_offsets<D, W>(voff, wave, lane, T::ROW_BYTES);
+        auto issue = [&](int u) {
+            dma_tile<D, W>(smem + (u % kBufs) * T::BUF_BYTES, rsrc, (t0 + u) * kTK, voff, wave, T::ROW_BYTES);
+        };
+        int issued = 0;
+        for (; issued < 2 && issued < nt; ++issued) issue(issued);
+        wait_pieces_after<DPW>(issued);   // q has landed
         __syncthreads();
-        for (; issued < nt && issued <= u + kBufs - 1; ++issued) issue(issued);
-        return smem + (u % kBufs) * T::BUF_BYTES;
-    };
-    run_tiles<D, false>(ws, nt, active ? nt - 1 : -1, N - t0 * kTK, wq0, la, col, g, a.c, next_step);
+        staged_operand<D>(ws.qreg, smem + 2 * T::BUF_BYTES + wrows, la);
+        reset_state<D>(ws);
+        auto next_step = [&](int u) -> const LDS_AS char * {
+            wait_pieces_after<DPW>(issued - u - 1);
+            __syncthreads();
+            for (; issued < nt && issued <= u + kBufs - 1; ++issued) issue(issued);
+            return smem + (u % kBufs) * T::BUF_BYTES;
+        };
+        run_tiles<D, false>(ws, nt, active ? nt - 1 : -1, N - t0 * kTK, wq0, la, col, g, a.c, next_step);
+    } else {
+        // E4M3 pool: slot 0 holds the current tile decoded to bf16, slot 1 two staged
+        // tiles of codes (the part's tile t0 + u at half u % 2).  Tiles 0 and 1 go out
+        // right after q (slots 2 and 3); tile u + 2 once tile u is decoded.
+        using F = F8Tile<D, W>;
+        constexpr int FP = F::PER_WAVE;   // this wave's pieces per staged tile
+        LDS_AS char *stage = smem + T::BUF_BYTES;
+        LDS_AS char *cur = smem;
+        auto issue8 = [&](int u) { dma_tile8<D, W>(stage + (u % 2) * F::BYTES, rsrc, (t0 + u) * kTK, wave, lane); };
+        if (nt > 0) issue8(0);
+        if (nt > 1) issue8(1);
+        // q has landed once at most the staged tiles' pieces are in flight
+        if (nt > 1) wait_vmcnt<2 * FP>();
+        else if (nt == 1) wait_vmcnt<FP>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        staged_operand<D>(ws.qreg, smem + 2 * T::BUF_BYTES + wrows, la);
+        reset_state<D>(ws);
+        auto next_tile8 = [&](int u) -> const LDS_AS char * {
+            if (u + 1 < nt) wait_vmcnt<FP>();   // tile u + 1 may still be in flight
+            else wait_vmcnt<0>();
+            __syncthreads();   // tile u has landed; every wave is done with slot 0
+            decode_tile8<D, W>(stage + (u % 2) * F::BYTES, cur, tid);
+            __syncthreads();   // slot 0 holds tile u; its staging half is free
+            if (u + 2 < nt) issue8(u + 2);
+            return cur;
+        };
+        run_tiles<D, false>(ws, nt, active ? nt - 1 : -1, N - t0 * kTK, wq0, la, col, g, a.c, next_tile8);
+    }
     // the state of the wave's rows: accumulators (lane (col, g) holds head dims
     // db*32 + 8j + 4g .. +3 of row col), then (m, l) from the lanes of half 0
     const long pbase = ((long)item * a.parts + part) * QT;
@@ -1208,9 +1240,9 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(AttnArgs a, const int
     }
 }
 
-template <int D>
+template <int D, bool P8>
 __global__ void __launch_bounds__(block_waves<D>() * 64, min_waves_per_simd<D>()) rank_decode_part_kernel(AttnArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ slots) {
-    decode_part_body<D>(a, lens, slots);
+    decode_part_body<D, P8>(a, lens, slots);
 }
 
 template <int D, bool P8>
@@ -1269,21 +1301,21 @@ hipError_t launch_decode_bf16(const AttnArgs &a, int D, bool pool8, hipStream_t 
     return hipGetLastError();
 }
 
-hipError_t launch_decode_split_bf16(const AttnArgs &a, int D, hipStream_t stream) {
+hipError_t launch_decode_split_bf16(const AttnArgs &a, int D, bool pool8, hipStream_t stream) {
     const long items = (long)a.B * a.H * a.tiles * a.parts;
     const long rows = (long)a.B * a.H * a.rows;
     if (items <= 0 || rows <= 0) return hipSuccess;
     if (items > 0x7fffffffL || (rows + 3) / 4 > 0x7fffffffL || a.parts < 1 || a.part_tiles < 1 || !a.part_state)
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)items), mgrid((unsigned)((rows + 3) / 4));
-#define UNIPIN_SPLIT(DD)                                                                                             \
-    hipLaunchKernelGGL((rank_decode_part_kernel<DD>), grid, dim3(block_waves<DD>() * 64), 0, stream, a, a.lens,      \
+#define UNIPIN_SPLIT(DD, P8)                                                                                         \
+    hipLaunchKernelGGL((rank_decode_part_kernel<DD, P8>), grid, dim3(block_waves<DD>() * 64), 0, stream, a, a.lens,  \
                        a.slot);                                                                                      \
     hipLaunchKernelGGL((decode_merge_kernel<DD>), mgrid, dim3(256), 0, stream, a, a.lens, a.slot)
     switch (D) {
-        case 32: UNIPIN_SPLIT(32); break;
-        case 64: UNIPIN_SPLIT(64); break;
-        case 128: UNIPIN_SPLIT(128); break;
+        case 32: if (pool8) return hipErrorInvalidValue; UNIPIN_SPLIT(32, false); break;
+        case 64: if (pool8) { UNIPIN_SPLIT(64, true); } else { UNIPIN_SPLIT(64, false); } break;
+        case 128: if (pool8) { UNIPIN_SPLIT(128, true); } else { UNIPIN_SPLIT(128, false); } break;
         default: return hipErrorInvalidValue;
     }
 #undef UNIPIN_SPLIT

@@ -53,7 +53,7 @@ struct RowLayout {
 // their argument checks.  bf16 pools only for a non-contiguous layout.  Returns a
 // UNIPIN_* status.
 // For the ranking decode, part_state (parts >= 2) selects the split over the history
-// (launch_decode_split_bf16; bf16 pools only).
+// (launch_decode_split_bf16; bf16 and E4M3 pools).
 int attention_call(bool prefill, const void *q, const void *k, const void *v, RowLayout in, void *o, RowLayout out,
                    ::unipin_pool *pool, const int32_t *slot, const int32_t *lens, int layer, int B, int rows,
                    float scale, void *stream, float *part_state = nullptr, int parts = 1, int part_tiles = 0);
@@ -80,9 +80,10 @@ int bf16_decode_rows_per_item(int D);
 // pool write, decoded by the ranking decode as its tiles arrive), else bf16.
 hipError_t launch_prefill_bf16(const AttnArgs &a, int D, bool pool8, hipStream_t stream);
 hipError_t launch_decode_bf16(const AttnArgs &a, int D, bool pool8, hipStream_t stream);
-// The split ranking decode on a bf16 pool (contiguous layout): the parts, then the merge of
-// the parts with each candidate's own key into o.
-hipError_t launch_decode_split_bf16(const AttnArgs &a, int D, hipStream_t stream);
+// The split ranking decode with bf16 activations (contiguous layout) on a bf16 pool or,
+// with pool8, an E4M3 pool: the parts, then the merge of the parts with each candidate's
+// own key into o.
+hipError_t launch_decode_split_bf16(const AttnArgs &a, int D, bool pool8, hipStream_t stream);
 // fp32 pools: fp32 in and out, fp64 arithmetic inside.
 hipError_t launch_prefill_fp32(const AttnArgs &a, int D, hipStream_t stream);
 hipError_t launch_decode_fp32(const AttnArgs &a, int D, hipStream_t stream);

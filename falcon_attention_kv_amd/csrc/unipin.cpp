@@ -129,7 +129,7 @@ DecodeSplit decode_split_plan(const ::unipin_pool *pool, int B, int k) {
     // the device); parts past a shorter history leave at once.
     constexpr int kMinPartTiles = 4;
     DecodeSplit p{1, 0, 0};
-    if (!pool || B < 1 || k < 1 || pool->dtype != UNIPIN_BF16) return p;
+    if (!pool || B < 1 || k < 1 || !bf16_kernels(pool)) return p;
     const int rpb = bf16_decode_rows_per_item(pool->D);
     const long items = (long)B * pool->H * ((k + rpb - 1) / rpb);
     const long resident = pool->D <= 64 ? 512 : 256;
@@ -201,12 +201,14 @@ int attention_call(bool prefill, const void *q, const void *k, const void *v, Ro
     a.out_rstride = out.rstride;
     rc = pool_kernel_prologue(pool, static_cast<hipStream_t>(stream), &a.status);
     if (rc) return rc;
-    if (!prefill && part_state && parts >= 2 && pool->dtype == UNIPIN_BF16) {
+    if (!prefill && part_state && parts >= 2 && bf16_kernels(pool)) {
         a.parts = parts;
         a.part_tiles = part_tiles;
         a.part_state = part_state;
-        return launch_decode_split_bf16(a, D, static_cast<hipStream_t>(stream)) == hipSuccess ? UNIPIN_OK
-                                                                                                : UNIPIN_EHIP;
+        return launch_decode_split_bf16(a, D, pool->dtype == UNIPIN_FP8_E4M3, static_cast<hipStream_t>(stream)) ==
+                       hipSuccess
+                   ? UNIPIN_OK
+                   : UNIPIN_EHIP;
     }
     return launch(a, pool, prefill, stream);
 }

@@ -266,9 +266,9 @@ def test_block_host_checks():
 
 def test_rank_decode_split_plan():
     """The split of the ranking decode: for few (user, head) pairs and histories of at least
-    1024 keys, parts of at least four 64-key tiles that fill the resident workgroups (512
-    at D <= 64, 256 at D = 128); the workspace holds (D + 2) fp32 per candidate row of
-    every part of every 256-row tile."""
+    16 tiles of 64 keys, parts of at least four tiles that fill the resident workgroups
+    (512 at D <= 64, 256 at D = 128), on bf16 and E4M3 pools; the workspace holds (D + 2)
+    fp32 per candidate row of every part of every 256-row tile."""
     h = make_pool(L=1, S=2, H=8, n_max=1024, D=64)
     # 8 pairs x 4 candidate tiles = 32 items: min(512 / 32, 16 tiles / 4) = 4 parts
     assert lib.unipin_rank_decode_workspace_bytes(h, 1, 1000) == 32 * 4 * 256 * 66 * 4
@@ -291,8 +291,11 @@ def test_rank_decode_split_plan():
     h = make_pool(L=1, S=2, H=8, n_max=960, D=64)   # 15 tiles of history: one pass
     assert lib.unipin_rank_decode_workspace_bytes(h, 1, 1000) == 0
     lib.unipin_pool_destroy(h)
-    h = make_pool(L=1, S=2, H=8, n_max=1024, D=64, dtype=fa.FP8_E4M3)
-    assert lib.unipin_rank_decode_workspace_bytes(h, 1, 1000) == 0      # E4M3: one pass
+    h = make_pool(L=1, S=2, H=8, n_max=1024, D=64, dtype=fa.FP8_E4M3)   # E4M3: the same plan
+    assert lib.unipin_rank_decode_workspace_bytes(h, 1, 1000) == 32 * 4 * 256 * 66 * 4
+    lib.unipin_pool_destroy(h)
+    h = make_pool(L=1, S=2, H=8, n_max=1024, D=64, dtype=fa.FP32)
+    assert lib.unipin_rank_decode_workspace_bytes(h, 1, 1000) == 0      # fp32: one pass
     lib.unipin_pool_destroy(h)
 
 

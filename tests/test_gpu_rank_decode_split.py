@@ -1,6 +1,6 @@
-"""GPU parity of the ranking decode split over the history (unipin_rank_decode_split)
-against the float64 oracle, with the bf16 tolerances of test_gpu_parity.py
-(max |gpu - oracle| <= 2e-2, mean <= 2e-3).
+"""GPU parity of the ranking decode split over the history (unipin_rank_decode_split),
+on bf16 and E4M3 pools, against the float64 oracle, with the bf16 tolerances of
+test_gpu_parity.py (max |gpu - oracle| <= 2e-2, mean <= 2e-3).
 
 The split runs when few (user, head) pairs leave the GPU mostly idle: each candidate
 tile's history goes to several workgroups, whose softmax states a second kernel merges
@@ -78,6 +78,43 @@ def test_split_decode_against_the_oracle(case):
             assert torch.equal(oc[b], inp["vc"][b]), "an empty history must return vc exactly"
 
 
+F8 = torch.float8_e4m3fn
+
+# (B, H, D, n_max, k, lens, layer) on a pool of E4M3 codes of N(0, 1) draws
+E4M3_CASES = [
+    (1, 8, 64, 1024, 1000, [1024], 0),          # one request, full history: four parts of four tiles
+    (2, 4, 128, 1100, 300, [1100, 37], 1),      # ragged, second layer: the short user's parts mostly empty
+    (3, 2, 64, 2048, 257, [1500, 0, 65], 0),    # a history ending inside a part, an empty one, a partial tile
+]
+
+
+@pytest.mark.parametrize("case", E4M3_CASES, ids=lambda c: f"B{c[0]}H{c[1]}D{c[2]}n{c[3]}k{c[4]}L{c[6]}")
+def test_split_decode_on_e4m3_pool(case):
+    """The split path on an E4M3 pool: each part decodes its staged tiles of codes to bf16
+    in LDS; against the oracle on the decoded pool, and through the one-pass kernel."""
+    B, H, D, n, k, lens, layer = case
+    announce(f"split decode, E4M3 pool {case}")
+    kp, vp = W.random_pool(layer + 1, B + 1, H, n, D, torch.float32, seed=3400 + n + k, device=DEV)
+    pool = fa.Pool(kp.to(F8), vp.to(F8))
+    del kp, vp
+    slots = list(range(B, 0, -1))
+    inp = W.small_case(B, H, D, 8, k, [1] * B, seed=3500 + n + k, device=DEV)   # qc, kc, vc
+    assert fa.rank_decode_workspace_bytes(pool, B, k) > 0, "the case must take the split path"
+    oc = fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, slots, lens, layer, split=True)
+    one = fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, slots, lens, layer)
+    torch.cuda.synchronize()
+    assert pool.status() == 0
+    pk = oracle.e4m3_decode(pool.k.detach().cpu().view(torch.uint8).numpy())
+    pv = oracle.e4m3_decode(pool.v.detach().cpu().view(torch.uint8).numpy())
+    ref = oracle.rank_decode(inp["qc"].cpu(), inp["kc"].cpu(), inp["vc"].cpu(), pk, pv, slots, lens, layer)
+    check_bf16(oc, ref, f"E4M3 split decode {case}")
+    check_bf16(one, ref, f"E4M3 one-pass decode {case}")
+    for b, N in enumerate(lens):
+        if N == 0:
+            assert torch.equal(oc[b], inp["vc"][b]), "an empty history must return vc exactly"
+    pool.close()
+
+
 def test_split_decode_repeated_calls_are_bitwise_identical():
     B, H, D, n, k = 1, 8, 64, 1024, 600
     inp = W.small_case(B, H, D, n, k, [980], seed=3100, device=DEV)
@@ -123,6 +160,6 @@ def test_split_decode_workspace_checks():
     with pytest.raises(fa.UnipinError) as e:
         fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, [0], [300], 0, split=True, workspace=odd)
     assert e.value.status == fa.EALIGN
-    # E4M3 pools always take the one-pass kernel
-    p8 = fa.Pool.allocate(1, 1, H, n, D, torch.float8_e4m3fn, DEV)
-    assert fa.rank_decode_workspace_bytes(p8, B, k) == 0
+    # fp32 pools always take the one-pass kernel
+    p32 = fa.Pool.allocate(1, 1, H, n, D, torch.float32, DEV)
+    assert fa.rank_decode_workspace_bytes(p32, B, k) == 0
