@@ -121,12 +121,18 @@ namespace unipin {
 DecodeSplit decode_split_plan(const ::unipin_pool *pool, int B, int k) {
     // Histories shorter than 16 tiles (1024 keys) take the one-pass kernel: their decode
     // is short enough that the merge's launch and the parts' states cost more than the
-    // split gains (measured: 0.88-0.90x at 512 keys, 1.2-1.6x at 2048-4000).  A part
-    // takes at least four 64-key tiles.  The decode keeps two workgroups per CU
-    // resident at D <= 64 and one at D = 128 (256 CUs): the split starts when the
-    // candidate tiles fill at most half of those, and gives each tile's history as many
-    // parts as fill them.  The plan counts on histories up to n_max (the lengths are on
-    // the device); parts past a shorter history leave at once.
+    // split gains (measured: 0.88-0.90x at 512 keys).  A part takes at least four 64-key
+    // tiles, and each part costs a header and an fp32 state of its 256 rows, written and
+    // merged again: as many bytes as four bf16 K/V tiles at D = 64.  So the split pays
+    // only while the candidate tiles (items) are few next to the history's tiles: at
+    // most 2 per tile at D <= 64 and 3 per tile at D = 128 (one workgroup per CU there),
+    // the break-even points of a sweep over requests, history and candidate counts
+    // (beyond them the split took 0.5-0.9x of the one-pass time, inside them 1.1-2.4x).
+    // The decode keeps two workgroups per CU resident at D <= 64 and one at D = 128 (256
+    // CUs): the split also needs the candidate tiles to fill at most half of those, and
+    // gives each tile's history as many parts as fit in one round of them.  The plan
+    // counts on histories up to n_max (the lengths are on the device); parts past a
+    // shorter history leave at once.
     constexpr int kMinPartTiles = 4;
     DecodeSplit p{1, 0, 0};
     if (!pool || B < 1 || k < 1 || !bf16_kernels(pool)) return p;
@@ -136,7 +142,8 @@ DecodeSplit decode_split_plan(const ::unipin_pool *pool, int B, int k) {
     if (items * 2 > resident) return p;
     const int hist_tiles = (pool->n_max + 63) / 64;
     if (hist_tiles < 16) return p;
-    int parts = (int)std::min<long>((resident + items - 1) / items, hist_tiles / kMinPartTiles);
+    if (items > (pool->D <= 64 ? 2L : 3L) * hist_tiles) return p;
+    int parts = (int)std::min<long>(resident / items, hist_tiles / kMinPartTiles);
     if (parts < 2) return p;
     const int part_tiles = (hist_tiles + parts - 1) / parts;
     parts = (hist_tiles + part_tiles - 1) / part_tiles;

@@ -265,10 +265,12 @@ def test_block_host_checks():
 
 
 def test_rank_decode_split_plan():
-    """The split of the ranking decode: for few (user, head) pairs and histories of at least
-    16 tiles of 64 keys, parts of at least four tiles that fill the resident workgroups
-    (512 at D <= 64, 256 at D = 128), on bf16 and E4M3 pools; the workspace holds (D + 2)
-    fp32 per candidate row of every part of every 256-row tile."""
+    """The split of the ranking decode: for histories of at least 16 tiles of 64 keys and
+    few candidate tiles (items): at most half the resident workgroups (512 at D <= 64,
+    256 at D = 128) and at most 2 (D <= 64) or 3 (D = 128) per history tile; parts of
+    at least four tiles, as many as fit in one round of the resident workgroups; bf16
+    and E4M3 pools.  The workspace holds (D + 2) fp32 per candidate row of every part of
+    every 256-row tile."""
     h = make_pool(L=1, S=2, H=8, n_max=1024, D=64)
     # 8 pairs x 4 candidate tiles = 32 items: min(512 / 32, 16 tiles / 4) = 4 parts
     assert lib.unipin_rank_decode_workspace_bytes(h, 1, 1000) == 32 * 4 * 256 * 66 * 4
@@ -279,6 +281,16 @@ def test_rank_decode_split_plan():
     h = make_pool(L=1, S=2, H=4, n_max=1024, D=128)
     # 4 pairs x 2 tiles = 8 items: min(256 / 8, 16 / 4) = 4 parts of 4 tiles
     assert lib.unipin_rank_decode_workspace_bytes(h, 1, 300) == 8 * 4 * 256 * 130 * 4
+    lib.unipin_pool_destroy(h)
+    h = make_pool(L=1, S=2, H=8, n_max=1024, D=64)
+    # 2 users: 64 items, more than 2 per history tile (16): one pass
+    assert lib.unipin_rank_decode_workspace_bytes(h, 2, 1000) == 0
+    lib.unipin_pool_destroy(h)
+    h = make_pool(L=1, S=2, H=16, n_max=2048, D=128)
+    # 2 x 16 pairs x 3 tiles = 96 items, 3 per history tile (32): floor(256 / 96) = 2 parts
+    # of 16 tiles, all resident at once
+    assert lib.unipin_rank_decode_workspace_bytes(h, 2, 656) == 96 * 2 * 256 * 130 * 4
+    assert lib.unipin_rank_decode_workspace_bytes(h, 2, 1000) == 0     # 128 items: one pass
     lib.unipin_pool_destroy(h)
     h = make_pool(L=2, S=2, H=4, n_max=2048, D=32)
     # 4 pairs x 2 tiles = 8 items: min(512 / 8, 32 / 4) = 8 parts of 4 tiles
