@@ -146,6 +146,25 @@ def test_split_decode_invalid_user_is_skipped_and_flagged():
     assert pool.status() == 0
 
 
+def test_split_decode_without_a_plan_is_the_one_pass_kernel():
+    """Where the plan keeps the one-pass kernel (a 512-row pool; 64 candidate tiles on a
+    1024-row one), the split entry point runs it: outputs bitwise equal, a workspace
+    passed in is ignored."""
+    for (B, H, D, n, k, lens) in ((1, 8, 64, 512, 300, [512]), (2, 8, 64, 1024, 1000, [1024, 700])):
+        announce(f"split entry without a split: B={B} H={H} D={D} n={n} k={k}")
+        inp = W.small_case(B, H, D, n, k, lens, seed=3600 + n + k, device=DEV)
+        pool = fa.Pool.allocate(1, B, H, n, D, torch.bfloat16, DEV)
+        slots = list(range(B))
+        fa.prefill(inp["q"], inp["k"], inp["v"], lens, pool, slots, 0)
+        assert fa.rank_decode_workspace_bytes(pool, B, k) == 0
+        ws = torch.full((64,), 0xff, dtype=torch.uint8, device=DEV)
+        a = fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, slots, lens, 0, split=True, workspace=ws)
+        b = fa.rank_decode(inp["qc"], inp["kc"], inp["vc"], pool, slots, lens, 0)
+        torch.cuda.synchronize()
+        assert pool.status() == 0
+        assert torch.equal(a, b)
+
+
 def test_split_decode_workspace_checks():
     B, H, D, n, k = 1, 4, 64, 1024, 100
     inp = W.small_case(B, H, D, n, k, [300], seed=3300, device=DEV)
