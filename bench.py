@@ -384,14 +384,17 @@ def workload_kernels(fa, W, torch, dev, launches: int = 10, warmup: int = 3):
 
 
 def probes(torch, dev) -> dict:
-    """The chip's achievable matrix-core rate and whether a SIMD overlaps matrix-core and
-    exponential work (libunipin_probe.so; two waves per SIMD on every CU)."""
+    """The chip's achievable matrix-core rate, whether a SIMD overlaps matrix-core and
+    exponential work (two waves per SIMD on every CU), and the LDS read rate of the
+    attention tiles' two operand reads (16 waves per CU), from libunipin_probe.so."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "falcon_attention_kv_amd", "libunipin_probe.so"))
     lib.unipin_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
     lib.unipin_probe_overlap.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.unipin_probe_lds.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.POINTER(ctypes.c_double)]
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    buf = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+    buf = torch.empty(2 * cus * 512, dtype=torch.float32, device=dev)
     tf = ctypes.c_double()
     if lib.unipin_probe_mfma(buf.data_ptr(), cus, 20000, ctypes.byref(tf)) != 0:
         raise RuntimeError("unipin_probe_mfma failed")
@@ -399,8 +402,15 @@ def probes(torch, dev) -> dict:
     if lib.unipin_probe_overlap(buf.data_ptr(), cus, 20000, ns) != 0:
         raise RuntimeError("unipin_probe_overlap failed")
     m, e, both, split, m16, both16 = (round(v, 2) for v in ns)
+    lds = (ctypes.c_double * 2)()
+    if lib.unipin_probe_lds(buf.data_ptr(), 2 * cus, 1000, cus, lds) != 0:
+        raise RuntimeError("unipin_probe_lds failed")
     return {"mfma_loop": {"tflops": round(tf.value, 1), "frac_of_peak": round(tf.value / BF16_PEAK_TFLOPS, 4),
                           "what": f"{cus} CUs x 8 waves of independent 32x32x16 bf16 MFMAs"},
+            "lds_read_bytes_per_ns_per_cu": {
+                "ds_read_b128": round(lds[0], 1), "ds_read_b64_tr_b16": round(lds[1], 1),
+                "what": f"{2 * cus} blocks of 8 waves (16 waves per CU), each wave 8 KiB per loop iteration in "
+                        "reads that are 1 KiB (b128) or 512 B (tr_b64) in a row per instruction"},
             "mfma_exp_overlap_ns_per_iter": {
                 "mfma_only": m, "exp_only": e, "both_in_each_wave": both, "mfma_wave_beside_exp_wave": split,
                 "mfma_only_16x16x32": m16, "both_in_each_wave_16x16x32": both16,

@@ -8,7 +8,10 @@
 //     in each wave, or MFMAs in one wave and exponentials in the other wave of the SIMD;
 //     and the first and third with the same matrix work as v_mfma_f32_16x16x32_bf16
 //     (twice as many instructions of half the work), the finer grain an attention loop
-//     could interleave with its exponentials.
+//     could interleave with its exponentials;
+//   * unipin_probe_lds: the LDS read rate of the two operand reads the attention tiles
+//     use, ds_read_b128 (the K operand) and ds_read_b64_tr_b16 (the transposed V
+//     operand), with 16 waves per CU as in the ranking decode.
 // Each writes one float per thread (so that nothing is optimised away) into a buffer of
 // blocks x threads floats owned by the caller.
 #include <hip/hip_runtime.h>
@@ -18,6 +21,12 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kLdsProbeBytes = 65536;   // LDS per block: two blocks fit on a CU
 
 // ROLE 0: every wave runs the MFMAs (if NM) and the exponentials (if NE); ROLE 1: even
 // waves the MFMAs, odd waves the exponentials.  NM counts 32x32x16 MFMAs; SMALL issues
@@ -67,6 +76,64 @@ __global__ void __launch_bounds__(512) probe_kernel(float *out, int iters) {
     out[blockIdx.x * blockDim.x + tid] = s;
 }
 
+// LDS reads: every wave reads 8 KiB per iteration, as 8 ds_read_b128 (TR false: each
+// lane 16 consecutive bytes, a wave 1 KiB in a row) or 16 ds_read_b64_tr_b16 (TR true:
+// each lane 8 consecutive bytes, a wave 512 B in a row).  The addresses move with the
+// iteration (so no read can be hoisted) and are masked into the block's 64 KiB, aligned
+// to the access; the values are summed into one word per thread, with little enough
+// vector work (one or two three-input adds per read) that the LDS sets the pace.
+template <bool TR>
+__global__ void __launch_bounds__(512) lds_probe_kernel(float *out, int iters) {
+    __shared__ __attribute__((aligned(16))) char lds_raw[kLdsProbeBytes];
+    LDS_AS char *lds = (LDS_AS char *)lds_raw;
+    const int tid = threadIdx.x;
+    for (int i = tid * 16; i < kLdsProbeBytes; i += 512 * 16)
+        *reinterpret_cast<LDS_AS u32x4 *>(lds + i) = u32x4{(unsigned)i, (unsigned)i + 1u, (unsigned)i + 2u,
+                                                             (unsigned)i + 3u};
+    __syncthreads();
+    const int wave = tid >> 6, lane = tid & 63;
+    unsigned acc = 0u;
+    for (int it = 0; it < iters; ++it) {
+        const unsigned base = (unsigned)(wave * 8192 + it * 4096);
+        if (!TR) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const unsigned a = (base + (unsigned)(j * 1024 + lane * 16)) & (unsigned)(kLdsProbeBytes - 16);
+                const u32x4 v = *reinterpret_cast<const LDS_AS u32x4 *>(lds + a);
+                acc = acc + v[0] + v[1] + v[2] + v[3];   // two three-input adds per read
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const unsigned a = (base + (unsigned)(j * 512 + lane * 8)) & (unsigned)(kLdsProbeBytes - 8);
+                const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                              (LDS_AS i16x4 *)(lds + a)));
+                acc = acc + w[0] + w[1];   // one three-input add per read
+            }
+        }
+    }
+    out[blockIdx.x * blockDim.x + tid] = (float)acc;
+}
+
+template <bool TR>
+int timed_lds(float *buf, int blocks, int iters, float *ms) {
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return -1;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return -1;
+    }
+    hipLaunchKernelGGL((lds_probe_kernel<TR>), dim3(blocks), dim3(512), 0, 0, buf, iters);   // warm-up
+    hipError_t e = hipEventRecord(e0, 0);
+    hipLaunchKernelGGL((lds_probe_kernel<TR>), dim3(blocks), dim3(512), 0, 0, buf, iters);
+    if (e == hipSuccess) e = hipEventRecord(e1, 0);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(ms, e0, e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    return e == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 template <int NM, int NE, int ROLE, bool SMALL = false>
 int timed(float *buf, int blocks, int threads, int iters, float *ms) {
     hipEvent_t e0, e1;
@@ -77,8 +144,8 @@ int timed(float *buf, int blocks, int threads, int iters, float *ms) {
     if (e == hipSuccess) e = hipEventRecord(e1, 0);
     if (e == hipSuccess) e = hipEventSynchronize(e1);
     if (e == hipSuccess) e = hipEventElapsedTime(ms, e0, e1);
-    hipEventDestroy(e0);
-    hipEventDestroy(e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
     return e == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -114,6 +181,21 @@ int unipin_probe_overlap(float *buf, int blocks, int iters, double *ns) {
     ns[4] = ms * 1e6 / iters;
     if (timed<8, 32, 0, true>(buf, blocks, 512, iters, &ms)) return -1;
     ns[5] = ms * 1e6 / iters;
+    return 0;
+}
+
+// LDS read rate in bytes per nanosecond and CU, for blocks x 512 threads (two blocks per
+// CU when blocks = 2 x cus: 16 waves per CU), each wave `iters` x 8 KiB: [0] as
+// ds_read_b128, [1] as ds_read_b64_tr_b16.  buf: blocks * 512 floats of device memory;
+// rate: 2 doubles.  Returns 0 or -1 (HIP error or bad sizes).
+int unipin_probe_lds(float *buf, int blocks, int iters, int cus, double *rate) {
+    if (blocks < 1 || iters < 1 || cus < 1) return -1;
+    const double bytes = (double)blocks * 8 * iters * 8192.0;
+    float ms = 0.f;
+    if (timed_lds<false>(buf, blocks, iters, &ms)) return -1;
+    rate[0] = bytes / (ms * 1e6) / cus;
+    if (timed_lds<true>(buf, blocks, iters, &ms)) return -1;
+    rate[1] = bytes / (ms * 1e6) / cus;
     return 0;
 }
 
