@@ -565,23 +565,30 @@ using KindBf16P8 = Kind<bf16, true>;
 }  // namespace
 
 int ar_splits(long bh, int n_max, int D, int kind) {
-    // A pair whose K/V (at the slot's capacity) fit in 256 KiB costs the one-pass kernel
-    // about two memory round trips, less than the merge pass: no split.  Otherwise cut
-    // the rows into parts of at least 4 chunks, up to about 256 workgroups over all
-    // pairs (more only add merge work; HBM is busy by then) and 64 parts per pair (one
-    // per lane of the merge wave).
+    // The one-pass kernel streams a pair's rows from one workgroup, about 3 us plus the
+    // rows' bytes at some 72 GB/s (bf16), while the split costs at least its two
+    // launches, about 13 us.  So a pair is split only when its slot at capacity holds at
+    // least 240 Ki elements per matrix (rows x D; 3840 rows at D = 64, 1920 at D = 128):
+    // in a sweep over 8-1024 pairs and 1024-8192 rows the split lost below that (0.70-0.97x
+    // at 512-750 KB of bf16 per pair) and won above it (1.1-3.3x), on bf16 and E4M3 pools
+    // alike when counted in elements (the E4M3 kernel spends longer per byte decoding).
+    // The rows are then cut into parts of at least 4 chunks, up to about 256 workgroups
+    // over all pairs (more only add merge work; HBM is busy by then) and 64 parts per
+    // pair (one per lane of the merge wave); fewer than 3 parts (128 or more pairs) lost
+    // in that sweep (0.83-0.94x) and keep the one-pass kernel.
     // fp32 pools (kind 0) run the fp64 one-pass kernel and never split.
+    constexpr long kMinSplitElements = 240L << 10;
+    constexpr long kMinParts = 3;
     if (bh <= 0 || n_max < 2 || kind == 0) return 1;
     const long rows = n_max - 1;
-    const int pool_bytes = kind == 1 ? 2 : 1;
-    if (2L * rows * D * pool_bytes <= (256L << 10)) return 1;
+    if (rows * D < kMinSplitElements) return 1;
     const int ch = kind == 1 ? chunk_rows<KindBf16>(D) : chunk_rows<KindBf16P8>(D);
     if (ch == 0) return 1;
     const long nc = (rows + ch - 1) / ch;
     long P = (nc + 3) / 4;
     if (P > 256 / bh) P = 256 / bh;
     if (P > 64) P = 64;
-    return P < 1 ? 1 : (int)P;
+    return P < kMinParts ? 1 : (int)P;
 }
 
 size_t ar_workspace_bytes(long bh, int P, int D) { return P <= 1 ? 0 : (size_t)bh * P * (D + 4) * sizeof(float); }

@@ -204,15 +204,30 @@ def test_ar_decode_host_checks(kw, code):
 
 
 def test_ar_decode_workspace_bytes():
-    """A pair is split only when its slot K/V (at capacity) exceed 256 KiB; then into
-    parts of at least 4 chunks (64 rows each here), at most 256 // (B*H) parts and 64;
-    the buffer holds one fp32 state of D + 4 floats per (user, head, part)."""
+    """A pair is split only when its slot at capacity holds at least 240 Ki elements per
+    matrix (rows x D); then into parts of at least 4 chunks (64 rows each here), at most
+    256 // (B*H) parts and 64, and only with 3 parts or more; the buffer holds one fp32
+    state of D + 4 floats per (user, head, part)."""
     assert lib.unipin_ar_decode_workspace_bytes(None, 4) == 0
     h = make_pool(L=1, S=16, H=16, n_max=4106, D=128)   # 2 MiB of K/V per pair, 65 chunks
     assert lib.unipin_ar_decode_workspace_bytes(h, 0) == 0
     assert lib.unipin_ar_decode_workspace_bytes(h, 1) == 16 * 16 * (128 + 4) * 4   # 256 // 16 parts
     assert lib.unipin_ar_decode_workspace_bytes(h, 4) == 64 * 4 * (128 + 4) * 4    # 256 // 64 parts
+    assert lib.unipin_ar_decode_workspace_bytes(h, 5) == 80 * 3 * (128 + 4) * 4    # 256 // 80 = 3 parts
+    assert lib.unipin_ar_decode_workspace_bytes(h, 8) == 0                         # 2 parts: one pass
     assert lib.unipin_ar_decode_workspace_bytes(h, 16) == 0                        # 256 pairs: one pass
+    lib.unipin_pool_destroy(h)
+    h = make_pool(L=1, S=4, H=2, n_max=1921, D=128)   # 1920 rows x 128: the smallest slot that splits
+    assert lib.unipin_ar_decode_workspace_bytes(h, 1) > 0
+    lib.unipin_pool_destroy(h)
+    h = make_pool(L=1, S=4, H=2, n_max=1920, D=128)   # one row fewer: one pass
+    assert lib.unipin_ar_decode_workspace_bytes(h, 1) == 0
+    lib.unipin_pool_destroy(h)
+    h = make_pool(L=1, S=4, H=2, n_max=3000, D=64)    # 750 KB of bf16 per pair, 192 Ki elements
+    assert lib.unipin_ar_decode_workspace_bytes(h, 1) == 0
+    lib.unipin_pool_destroy(h)
+    h = make_pool(L=1, S=4, H=2, n_max=4600, D=64, dtype=fa.FP8_E4M3)   # 294 Ki elements of codes
+    assert lib.unipin_ar_decode_workspace_bytes(h, 1) > 0
     lib.unipin_pool_destroy(h)
     h = make_pool(L=1, S=64, H=8, n_max=522, D=64)   # history 512 + a few steps: 130 KiB per pair
     assert lib.unipin_ar_decode_workspace_bytes(h, 1) == 0

@@ -177,7 +177,8 @@ def test_ar_decode_split_path(dtype, D):
     parts merged by a second pass (bf16; fp32 pools run their one-pass fp64 kernel).
     Lengths cover an empty slot, fewer chunks than parts, part boundaries and the last
     free row; the one-pass kernel must agree with the oracle on the same inputs too."""
-    L, S, H, n_max, layer = 1, 12, 2, 4600, 0
+    L, S, H, layer = 1, 12, 2, 0
+    n_max = 4600 if D >= 64 else 8200   # at least 240 Ki elements per matrix: the slot splits
     lens = [0, 1, 64, 65, 200, 511, 513, 1024, 2047, 3000, 4100, n_max - 1]
     slots = [3, 0, 11, 2, 7, 1, 4, 6, 5, 10, 9, 8]
     B = len(lens)
@@ -208,7 +209,7 @@ def test_ar_decode_split_path(dtype, D):
 def test_ar_decode_split_invalid_users_and_reused_workspace():
     """Invalid users are flagged and skipped by both passes; a workspace filled with NaN
     from an earlier call does not leak into the next one."""
-    L, S, H, n_max, D = 1, 4, 2, 3000, 64
+    L, S, H, n_max, D = 1, 4, 2, 4600, 64   # 4599 x 64 elements per matrix: the slot splits
     announce("ar_decode split invalid users")
     pk, pv = W.random_pool(L, S, H, n_max, D, torch.bfloat16, seed=40, device=DEV)
     pool = fa.Pool(pk, pv)
@@ -218,17 +219,17 @@ def test_ar_decode_split_invalid_users_and_reused_workspace():
     ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=DEV)
     before_k, before_v = pk.cpu(), pv.cpu()
     o = torch.full_like(tok["q"][0], 7.0)
-    slots, lens = [0, 9, 1, 2], [2000, 5, n_max, 2999]
+    slots, lens = [0, 9, 1, 2], [2000, 5, n_max, n_max - 1]
     fa.ar_decode(tok["q"][0], tok["k"][0], tok["v"][0], pool, slots, lens, 0, o=o, workspace=ws)
     torch.cuda.synchronize()
     assert pool.status() == fa.FLAG_BAD_SLOT | fa.FLAG_BAD_LEN
     assert torch.all(o[1:3] == 7.0), "skipped users' outputs must stay untouched"
     ref, _, _ = oracle.ar_decode(tok["q"][0].cpu(), tok["k"][0].cpu(), tok["v"][0].cpu(), before_k, before_v,
-                                 [0, 0, 0, 2], [2000, 0, 0, 2999], 0)
+                                 [0, 0, 0, 2], [2000, 0, 0, n_max - 1], 0)
     check_close(o[[0, 3]], ref[[0, 3]], torch.bfloat16, "valid users next to invalid ones")
     exp_k = before_k.clone()
     exp_k[0, 0, :, 2000] = tok["k"][0][0, :, 0].cpu()
-    exp_k[0, 2, :, 2999] = tok["k"][0][3, :, 0].cpu()
+    exp_k[0, 2, :, n_max - 1] = tok["k"][0][3, :, 0].cpu()
     assert torch.equal(pk.cpu(), exp_k), "only the valid users' rows may change"
     pool.close()
 

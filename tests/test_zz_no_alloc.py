@@ -49,7 +49,7 @@ def step(pool, tok, slots, lens, layer, noalloc):
 # (pool dtype, D, H, n_max, [(slots, lens) of call 1, then of the smaller call 2])
 CASES = [
     (torch.bfloat16, 128, 2, 4600, [([3, 0, 2, 1], [4100, 0, 2047, 4599]), ([1, 2], [3000, 65])]),
-    (torch.bfloat16, 64, 4, 3000, [([0, 1, 2], [2999, 1024, 700]), ([2], [129])]),
+    (torch.bfloat16, 64, 4, 4600, [([0, 1, 2], [2999, 1024, 700]), ([2], [129])]),
     (torch.float8_e4m3fn, 64, 2, 4600, [([1, 3, 0], [4500, 100, 2600]), ([0, 3], [1500, 1])]),
     (torch.float32, 64, 2, 700, [([0, 1], [699, 5]), ([1], [3])]),
 ]
