@@ -1183,61 +1183,57 @@ __device__ __forceinline__ void decode_part_body(const AttnArgs &a, const int32_
     }
 }
 
-// One wave per candidate row (b, h, j): the parts' states and the own key (score
-// scale * qc_j . kc_j, value vc_j) merged in fp32 and normalised; lane d holds head dims
-// d, d + 64.  A user with an invalid length or slot is skipped, as by the one-pass decode.
+// The merge: per candidate row (b, h, j), the parts' states and the own key (score
+// scale * qc_j . kc_j, value vc_j) merged in fp32 and normalised.  D / 2 lanes serve a
+// row, lane d of them head dims 2d and 2d + 1 (a wave takes 1, 2 or 4 rows at D = 128, 64
+// or 32), so that every load and store moves two values.  A user with an invalid length
+// or slot is skipped, as by the one-pass decode.
+template <int D>
+constexpr int merge_rows_per_wave() { return 128 / D; }
+
 template <int D>
 __global__ void __launch_bounds__(256) decode_merge_kernel(AttnArgs a, const int32_t *__restrict__ lens,
                                                            const int32_t *__restrict__ slots) {
     constexpr int QT = block_waves<D>() * wave_rows<D>();
-    constexpr int E = (D + 63) / 64;   // head dims per lane
+    constexpr int LPR = D / 2;   // lanes per row
+    static_assert(64 % LPR == 0, "a wave holds whole rows");
     const int lane = threadIdx.x & 63;
-    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= (long)a.B * a.H * a.rows) return;
+    const int dl = lane % LPR;
+    const long row = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * merge_rows_per_wave<D>() + lane / LPR;
+    if (row >= (long)a.B * a.H * a.rows) return;   // whole rows leave together
     const int j = (int)(row % a.rows);
     const int group = (int)(row / a.rows), b = group / a.H, h = group % a.H;
     const int N = lens[b], s = slots[b];
     if (N < 0 || N > a.len_limit || s < 0 || s >= a.S) return;
     const long item = (long)group * a.tiles + j / QT;
-    const long in_row = (long)b * a.in_bstride + (long)h * a.in_hstride + (long)j * a.in_rstride;
-    const bf16 *q = static_cast<const bf16 *>(a.q) + in_row, *kc = static_cast<const bf16 *>(a.k) + in_row,
-               *vc = static_cast<const bf16 *>(a.v) + in_row;
-    float dot = 0.f, vv[E];
+    const long in_row = (long)b * a.in_bstride + (long)h * a.in_hstride + (long)j * a.in_rstride + 2 * dl;
+    const bf16x2 q2 = *reinterpret_cast<const bf16x2 *>(static_cast<const bf16 *>(a.q) + in_row);
+    const bf16x2 k2 = *reinterpret_cast<const bf16x2 *>(static_cast<const bf16 *>(a.k) + in_row);
+    const bf16x2 v2 = *reinterpret_cast<const bf16x2 *>(static_cast<const bf16 *>(a.v) + in_row);
+    float dot = __builtin_amdgcn_fdot2_f32_bf16(q2, k2, 0.f, false);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int d = lane + 64 * e;
-        vv[e] = d < D ? (float)vc[d] : 0.f;
-        if (d < D) dot = __builtin_fmaf((float)q[d], (float)kc[d], dot);
-    }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) dot += __shfl_xor(dot, o);
+    for (int o = 1; o < LPR; o <<= 1) dot += __shfl_xor(dot, o);   // within the row's lanes
     const float sself = dot * a.c;   // log2 domain, like the parts' maxima
     const float *accs = a.part_state;
     const float *mls = a.part_state + (long)a.B * a.H * a.tiles * a.parts * QT * D;
+    const long r0 = item * a.parts * QT + j % QT;   // the row's state in part 0; part p is p * QT further
     float m = sself;
-    for (int p = 0; p < a.parts; ++p) m = fmaxf(m, mls[2 * ((item * a.parts + p) * QT + j % QT)]);
+    for (int p = 0; p < a.parts; ++p) m = fmaxf(m, mls[2 * (r0 + (long)p * QT)]);
     const float ws = __builtin_amdgcn_exp2f(sself - m);
-    float l = ws, acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = vv[e] * ws;
+    float l = ws, acc0 = (float)v2[0] * ws, acc1 = (float)v2[1] * ws;
     for (int p = 0; p < a.parts; ++p) {
-        const long r = (item * a.parts + p) * QT + j % QT;
+        const long r = r0 + (long)p * QT;
         const f32x2 ml = *reinterpret_cast<const f32x2 *>(mls + 2 * r);
         const float f = __builtin_amdgcn_exp2f(ml[0] - m);   // 0 for a part with no key (m = -inf)
+        const f32x2 st = *reinterpret_cast<const f32x2 *>(accs + r * D + 2 * dl);
         l = __builtin_fmaf(ml[1], f, l);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int d = lane + 64 * e;
-            if (d < D) acc[e] = __builtin_fmaf(accs[r * D + d], f, acc[e]);
-        }
+        acc0 = __builtin_fmaf(st[0], f, acc0);
+        acc1 = __builtin_fmaf(st[1], f, acc1);
     }
-    bf16 *o = static_cast<bf16 *>(a.o) + (long)b * a.out_bstride + (long)h * a.out_hstride + (long)j * a.out_rstride;
     const float inv = 1.f / l;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int d = lane + 64 * e;
-        if (d < D) o[d] = (bf16)(acc[e] * inv);
-    }
+    const bf16x2 out = {(bf16)(acc0 * inv), (bf16)(acc1 * inv)};
+    *reinterpret_cast<bf16x2 *>(static_cast<bf16 *>(a.o) + (long)b * a.out_bstride + (long)h * a.out_hstride +
+                                (long)j * a.out_rstride + 2 * dl) = out;
 }
 
 template <int D, bool P8>
@@ -1307,11 +1303,14 @@ hipError_t launch_decode_split_bf16(const AttnArgs &a, int D, bool pool8, hipStr
     if (items <= 0 || rows <= 0) return hipSuccess;
     if (items > 0x7fffffffL || (rows + 3) / 4 > 0x7fffffffL || a.parts < 1 || a.part_tiles < 1 || !a.part_state)
         return hipErrorInvalidValue;
-    const dim3 grid((unsigned)items), mgrid((unsigned)((rows + 3) / 4));
+    const dim3 grid((unsigned)items);
+    // merge: 4 waves per block, merge_rows_per_wave<D>() rows per wave
 #define UNIPIN_SPLIT(DD, P8)                                                                                         \
     hipLaunchKernelGGL((rank_decode_part_kernel<DD, P8>), grid, dim3(block_waves<DD>() * 64), 0, stream, a, a.lens,  \
                        a.slot);                                                                                      \
-    hipLaunchKernelGGL((decode_merge_kernel<DD>), mgrid, dim3(256), 0, stream, a, a.lens, a.slot)
+    hipLaunchKernelGGL((decode_merge_kernel<DD>),                                                                    \
+                       dim3((unsigned)((rows + 4 * merge_rows_per_wave<DD>() - 1) / (4 * merge_rows_per_wave<DD>()))), \
+                       dim3(256), 0, stream, a, a.lens, a.slot)
     switch (D) {
         case 32: if (pool8) return hipErrorInvalidValue; UNIPIN_SPLIT(32, false); break;
         case 64: if (pool8) { UNIPIN_SPLIT(64, true); } else { UNIPIN_SPLIT(64, false); } break;
