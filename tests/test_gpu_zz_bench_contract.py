@@ -40,3 +40,19 @@ def test_bench_line_contract():
                                            rel=2e-3)
     assert rf["traffic"] is None or rf["traffic"] > 0
     assert d["hbm_copy_reference"]["gbs"] > 0
+    # the secondary keys of the same run: the probes beside the copy, the long-history
+    # workload with both peaks' fractions, and which profile summaries match the sources
+    pr = d["probes"]
+    assert 0 < pr["mfma_loop"]["frac_of_peak"] < 1 and pr["mfma_loop"]["tflops"] > 0
+    assert pr["lds_read_bytes_per_ns_per_cu"]["ds_read_b128"] > 0
+    assert pr["lds_read_bytes_per_ns_per_cu"]["ds_read_b64_tr_b16"] > 0
+    assert all(v > 0 for k, v in pr["mfma_exp_overlap_ns_per_iter"].items() if k != "what")
+    lh = d["long_history"]
+    for kern in ("prefill", "rank_decode"):
+        k = lh[kern]
+        assert k["cold_median_ms"] > 0 and k["warm_mean_ms"] > 0
+        assert k["cold_tflops"] == pytest.approx(k["algorithmic_gflop"] / k["cold_median_ms"], rel=2e-3)
+        assert 0 < k["cold_mfma_frac"] < 1 and 0 < k["cold_hbm_frac"] < 1
+    summaries = sorted(f for f in os.listdir(os.path.join(ROOT, "profiles")) if f.endswith(".txt"))
+    assert sorted(d["profiles"]) == summaries
+    assert all(isinstance(v["current"], bool) for v in d["profiles"].values())
