@@ -26,12 +26,15 @@ matrix-core with exponential work (libunipin_probe.so), beside `hbm_copy_referen
 
 `--block-only` runs only the Table 2 transformer measurement (3 timed passes).
 `--probes` runs only the probes.
+`--sweep-splits` runs only the sweeps behind the two split plans: the ranking decode and
+the retrieval step, one pass against split, over request counts, history lengths and head
+dimensions (bf16 and E4M3 pools), each with the plan's choice.
 `--workloads` replaces all of this with a per-kernel table over every bf16 workload
 (one layer each, cold and back to back), with the ragged/full time ratios of the two
 ragged workloads beside the ratios of their algorithmic work.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ar-step] [--no-block] [--no-e4m3]
-                       [--no-long-history] [--workloads] [--block-only] [--probes]
+                       [--no-long-history] [--workloads] [--block-only] [--probes] [--sweep-splits]
 """
 from __future__ import annotations
 
@@ -90,6 +93,9 @@ def parse_args():
     p.add_argument("--block-only", action="store_true",
                    help="instead of the serving step, run only the Table 2 transformer measurement "
                         "(3 timed passes after 1 warm-up; a short program for a kernel trace)")
+    p.add_argument("--sweep-splits", action="store_true",
+                   help="instead of the serving step, time the ranking decode and the retrieval step "
+                        "one pass against split over the grids their split plans were set from")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run 3 plain device copies of this many MiB (a known-size "
                         "reference for the HBM byte counters of a profiler run)")
@@ -419,6 +425,87 @@ def probes(torch, dev) -> dict:
                         "16x16x32 entries issue the same matrix work as 16 MFMAs of 16x16x32 bf16"}}
 
 
+def _best_us(fn, launches: int = 20, reps: int = 2) -> float:
+    """Mean launch time of `launches` back-to-back calls, the best of `reps` runs."""
+    import torch
+    for _ in range(3):
+        fn()
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / launches * 1e3)
+    return best
+
+
+def sweep_splits(fa, W, torch, dev) -> dict:
+    """The two split plans' choices over the grids they were set from: the ranking decode
+    (1-8 requests of 8 heads at D = 64 and 16 at D = 128, histories 1024, 2048 and 4000,
+    656-2048 candidates; only where the candidate tiles fill at most half the resident
+    workgroups) and the retrieval step (1-16 requests, slots of 1024-8192 rows, bf16 and
+    E4M3 pools).  Each entry gives whether the plan splits, the one-pass time and, where it
+    splits, the split time and the ratio."""
+    F8 = torch.float8_e4m3fn
+    out = {"rank_decode": [], "ar_step": []}
+    for D, H in ((64, 8), (128, 16)):
+        for N in (1024, 2048, 4000):
+            for B in (1, 2, 4, 8):
+                for k in (656, 1000, 2048):
+                    if B * H * ((k + 255) // 256) * 2 > (512 if D <= 64 else 256):
+                        continue
+                    pk, pv = W.random_pool(1, B, H, N, D, torch.bfloat16, seed=51, device=dev)
+                    pool = fa.Pool(pk, pv)
+                    g = torch.Generator(device="cpu").manual_seed(52)
+                    qc, kc, vc = (torch.randn((B, H, k, D), generator=g).to(torch.bfloat16).to(dev) for _ in range(3))
+                    oc = torch.empty_like(qc)
+                    slot = torch.arange(B, dtype=torch.int32, device=dev)
+                    lens = torch.full((B,), N, dtype=torch.int32, device=dev)
+                    plan = fa.rank_decode_workspace_bytes(pool, B, k)
+                    # the split entry point runs the one-pass kernel wherever the plan
+                    # declines, so only the planned splits get a split time
+                    one = _best_us(lambda: fa.rank_decode(qc, kc, vc, pool, slot, lens, 0, oc=oc))
+                    entry = {"D": D, "H": H, "history": N, "requests": B, "candidates": k, "plan_splits": plan > 0,
+                             "one_pass_us": round(one, 1)}
+                    if plan:
+                        ws = torch.empty(plan, dtype=torch.uint8, device=dev)
+                        sp = _best_us(lambda: fa.rank_decode(qc, kc, vc, pool, slot, lens, 0, oc=oc, split=True,
+                                                             workspace=ws))
+                        entry.update(split_us=round(sp, 1), speedup=round(one / sp, 3))
+                    out["rank_decode"].append(entry)
+                    pool.close()
+                    del pk, pv, qc, kc, vc, oc
+    for fmt, D, H in (("bf16", 64, 8), ("bf16", 128, 16), ("e4m3", 64, 8), ("e4m3", 128, 16)):
+        for n in (1024, 2048, 4096, 8192):
+            for B in (1, 4, 8, 16):
+                if fmt == "e4m3":
+                    pk, pv = W.random_pool(1, B, H, n, D, torch.float32, seed=61, device=dev)
+                    pool = fa.Pool(pk.to(F8), pv.to(F8))
+                else:
+                    pk, pv = W.random_pool(1, B, H, n, D, torch.bfloat16, seed=61, device=dev)
+                    pool = fa.Pool(pk, pv)
+                del pk, pv
+                tok = W.step_tokens(B, H, D, 1, torch.bfloat16, seed=62, device=dev)
+                q, k, v = tok["q"][0], tok["k"][0], tok["v"][0]
+                o = torch.empty_like(q)
+                slot = torch.arange(B, dtype=torch.int32, device=dev)
+                lens = torch.full((B,), n - 1, dtype=torch.int32, device=dev)
+                plan = fa.ar_decode_workspace_bytes(pool, B)
+                one = _best_us(lambda: fa.ar_decode(q, k, v, pool, slot, lens, 0, o=o, split=False))
+                entry = {"pool": fmt, "D": D, "H": H, "slot_rows": n, "requests": B, "plan_splits": plan > 0,
+                         "one_pass_us": round(one, 1)}
+                if plan:
+                    ws = torch.empty(plan, dtype=torch.uint8, device=dev)
+                    sp = _best_us(lambda: fa.ar_decode(q, k, v, pool, slot, lens, 0, o=o, workspace=ws))
+                    entry.update(split_us=round(sp, 1), speedup=round(one / sp, 3))
+                out["ar_step"].append(entry)
+                pool.close()
+    return out
+
+
 def copy_calibration(torch, dev, mib: int) -> int:
     """Three plain device copies of `mib` MiB: a known-size reference for the HBM byte
     counters of a profiler run.  Returns the bytes one copy reads."""
@@ -572,6 +659,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.probes:
         print(json.dumps({"probes": probes(torch, dev)}), flush=True)
+        return
+    if args.sweep_splits:
+        print(json.dumps({"sweep_splits": sweep_splits(fa, W, torch, dev)}), flush=True)
         return
     if args.block_only:
         print(json.dumps({"block_table2": block_table2(fa, W, torch, dev, steps=3, warmup=1)}), flush=True)
