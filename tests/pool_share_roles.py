@@ -1,8 +1,11 @@
 """The two processes of the cross-process pool test (run as fresh subprocesses by
 tests/test_gpu_pool_share.py; not collected by pytest).
 
-    python tests/pool_share_roles.py owner  DIR
-    python tests/pool_share_roles.py ranker DIR
+    python tests/pool_share_roles.py owner  DIR [bf16|e4m3]
+    python tests/pool_share_roles.py ranker DIR [bf16|e4m3]
+
+The last argument is the pool's format (bf16 by default; e4m3: the pool holds E4M3
+codes, the activations stay bf16).
 
 owner:  the retrieval side.  Allocates a pool, hands out a slot per request, prefills two
         layers into the slots, runs the ranking decode itself once (the single-process
@@ -65,9 +68,12 @@ def owner(d):
     import falcon_attention_kv_amd as fa
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    pool = fa.Pool.allocate(SHAPE["L"], SHAPE["S"], SHAPE["H"], SHAPE["n_max"], SHAPE["D"], torch.bfloat16, dev)
-    pool.k.fill_(float("nan"))
-    pool.v.fill_(float("nan"))
+    e4m3 = len(sys.argv) > 3 and sys.argv[3] == "e4m3"
+    pool = fa.Pool.allocate(SHAPE["L"], SHAPE["S"], SHAPE["H"], SHAPE["n_max"], SHAPE["D"],
+                            torch.float8_e4m3fn if e4m3 else torch.bfloat16, dev)
+    if not e4m3:
+        pool.k.fill_(float("nan"))
+        pool.v.fill_(float("nan"))
     got = [pool.acquire() for _ in range(B)]
     slots, gens = [s for s, _ in got], [g for _, g in got]
     say(f"slots {slots} generations {gens}")
@@ -90,8 +96,8 @@ def owner(d):
         pool.acquire()
     post(os.path.join(d, "recycled.json"), {"generations": [pool.generation(s) for s in slots]})
     wait_for(os.path.join(d, "checked.json"))
-    same = bool(torch.equal(pool.k.cpu().view(torch.int16), snap_k.view(torch.int16)) and
-                torch.equal(pool.v.cpu().view(torch.int16), snap_v.view(torch.int16)))
+    same = bool(torch.equal(pool.k.cpu().view(torch.uint8), snap_k.view(torch.uint8)) and
+                torch.equal(pool.v.cpu().view(torch.uint8), snap_v.view(torch.uint8)))
     post(os.path.join(d, "owner_done.json"), {"pool_unchanged": same})
     say(f"pool bytes unchanged by the ranker: {same}")
     pool.close()

@@ -7,7 +7,8 @@ this process's GPU state.  Checked here: the ranker's outputs equal the owner's 
 single-process outputs bit for bit and the oracle within the bf16 tolerance; the
 ranker's generation check sees the request's slots as current before and after its
 decode and as stale once the owner has handed them out again; the ranker cannot write
-the pool (every writing call is refused) and the pool bytes are unchanged.
+the pool (every writing call is refused) and the pool bytes are unchanged.  Run with a
+bf16 pool and with an E4M3 pool (the oracle then reads the history through the codes).
 """
 import json
 import os
@@ -26,11 +27,12 @@ pytestmark = pytest.mark.gpu
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def test_ranking_process_reads_the_owners_pool(tmp_path):
-    sys.__stderr__.write("[gpu case] cross-process pool share: owner + ranker subprocesses\n")
+@pytest.mark.parametrize("fmt", ["bf16", "e4m3"])
+def test_ranking_process_reads_the_owners_pool(tmp_path, fmt):
+    sys.__stderr__.write(f"[gpu case] cross-process pool share ({fmt} pool): owner + ranker subprocesses\n")
     sys.__stderr__.flush()
     script = os.path.join(HERE, "pool_share_roles.py")
-    procs = {role: subprocess.Popen([sys.executable, "-u", script, role, str(tmp_path)],
+    procs = {role: subprocess.Popen([sys.executable, "-u", script, role, str(tmp_path), fmt],
                                     stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
              for role in ("owner", "ranker")}
     logs = {}
@@ -62,6 +64,9 @@ def test_ranking_process_reads_the_owners_pool(tmp_path):
         assert np.array_equal(a, b), f"layer {layer}: cross-process outputs differ from the single-process run"
         x = {k: v.cpu() for k, v in R.layer_case(layer, dev).items()}
         got = torch.from_numpy(b).view(torch.bfloat16).double().numpy()
-        _, ref = oracle.joint(x["q"], x["k"], x["v"], x["qc"], x["kc"], x["vc"], R.LENS)
+        hk, hv = x["k"], x["v"]
+        if fmt == "e4m3":   # the history as the pool holds it: the codes of its rows
+            hk, hv = oracle.e4m3_decode(oracle.e4m3_encode(hk)), oracle.e4m3_decode(oracle.e4m3_encode(hv))
+        _, ref = oracle.joint(x["q"], hk, hv, x["qc"], x["kc"], x["vc"], R.LENS)
         err = np.abs(got - ref)
         assert err.max() <= 2e-2 and err.mean() <= 2e-3, (layer, err.max(), err.mean())
